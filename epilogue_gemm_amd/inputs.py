@@ -1,0 +1,143 @@
+"""Seeded synthetic inputs for C = act(A.B [+ bias]).
+
+This module only draws random numbers and lays them out; it holds none of the
+product's arithmetic.  The GPU tests, the benchmark and the CPU oracle all
+start from the bit patterns it returns, so both sides see identical bytes.
+
+Recipe (the pages draw operands with ``torch.randn``, e.g. the GEMM+ReLU
+example in atlascloud.ai "Writing high-performance kernels in TileLang",
+section "Écrivons un GEMM", and the bias+GELU example in ainew.jp
+"TileLang で GPU カーネル設計を解説", section 4):
+
+  1. ``g = torch.Generator('cpu').manual_seed(seed)``;
+  2. draw, in this order, A (M x K), B (logical K x N) and, when the epilogue
+     has a bias, bias (N), each with ``torch.randn(..., generator=g)`` in fp32;
+  3. scale in fp32: ``B /= b_div``, ``bias *= bias_std``;
+  4. round each to the input format with ``Tensor.to`` (round to nearest even);
+  5. lay out: a column-major operand is the transpose made contiguous.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+import torch
+
+_TORCH_DT = {"f16": torch.float16, "bf16": torch.bfloat16}
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    """One GEMM+epilogue problem: shapes, formats, layouts, value recipe."""
+
+    name: str
+    M: int
+    N: int
+    K: int
+    in_dtype: str  # "f16" | "bf16"
+    out_dtype: str  # "f16" | "bf16" | "f32"
+    layout_a: str  # "row" | "col"
+    layout_b: str  # "row" | "col"
+    epilogue: str  # "none" | "relu" | "bias_relu" | "bias_gelu" | "bias"
+    b_div: float  # B ~ N(0,1) / b_div
+    bias_std: float  # bias ~ N(0, bias_std^2)
+    seed: int
+
+    @property
+    def has_bias(self) -> bool:
+        return self.epilogue in ("bias_relu", "bias_gelu", "bias")
+
+    @property
+    def flops(self) -> int:
+        return 2 * self.M * self.N * self.K
+
+    def compulsory_bytes(self) -> int:
+        isz = 2
+        osz = 4 if self.out_dtype == "f32" else 2
+        b = (self.M * self.K + self.K * self.N) * isz + self.M * self.N * osz
+        if self.has_bias:
+            b += self.N * isz
+        return b
+
+
+# The five workloads the library is measured and checked on.
+WORKLOADS = {
+    w.name: w
+    for w in [
+        # TileFusion global->register GEMM example: A 128x256 row-major,
+        # B 256x64 column-major, fp32 result.
+        Workload("gemm_f16_f32out_128x64x256_rm_cm", 128, 64, 256, "f16", "f32", "row", "col", "none",
+                 16.0, 0.0, 0),
+        Workload("gemm_relu_f16_1024x1024x1024_rm_rm", 1024, 1024, 1024, "f16", "f16", "row", "row", "relu",
+                 32.0, 0.0, 1),
+        Workload("gemm_relu_f16_4096x4096x4096_rm_rm", 4096, 4096, 4096, "f16", "f16", "row", "row", "relu",
+                 64.0, 0.0, 2),
+        Workload("gemm_bias_gelu_bf16_8192x8192x8192_rm_cm", 8192, 8192, 8192, "bf16", "bf16", "row", "col",
+                 "bias_gelu", math.sqrt(8192.0), 0.1, 3),
+        Workload("skinny_gemm_bias_bf16_32x8192x8192_rm_cm", 32, 8192, 8192, "bf16", "bf16", "row", "col", "bias",
+                 math.sqrt(8192.0), 0.1, 4),
+    ]
+}
+WORKLOAD_LIST = list(WORKLOADS.values())
+
+
+def to_bits(t: torch.Tensor) -> np.ndarray:
+    """Bit patterns of a CPU fp16/bf16 tensor as a numpy uint16 array."""
+    return t.contiguous().view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def make_inputs(M: int, N: int, K: int, in_dtype: str, layout_a: str, layout_b: str, with_bias: bool,
+                b_div: float, bias_std: float, seed: int):
+    """Returns dict(A=..., B=..., bias=...) of uint16 bit arrays laid out as asked.
+
+    A is M x K (row-major: shape (M, K); column-major: shape (K, M)), B is the
+    logical K x N matrix (row-major: shape (K, N); column-major: shape (N, K)),
+    bias has length N or is None.
+    """
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    a = torch.randn(M, K, generator=g, dtype=torch.float32)
+    b = torch.randn(K, N, generator=g, dtype=torch.float32)
+    bias = torch.randn(N, generator=g, dtype=torch.float32) if with_bias else None
+    b = b / float(b_div)
+    if bias is not None:
+        bias = bias * float(bias_std)
+    dt = _TORCH_DT[in_dtype]
+    a, b = a.to(dt), b.to(dt)
+    if layout_a == "col":
+        a = a.t().contiguous()
+    if layout_b == "col":
+        b = b.t().contiguous()
+    return {
+        "A": to_bits(a),
+        "B": to_bits(b),
+        "bias": to_bits(bias.to(dt)) if bias is not None else None,
+    }
+
+
+def workload_inputs(w: Workload):
+    return make_inputs(w.M, w.N, w.K, w.in_dtype, w.layout_a, w.layout_b, w.has_bias, w.b_div, w.bias_std, w.seed)
+
+
+def integer_inputs(M: int, N: int, K: int, in_dtype: str, layout_a: str, layout_b: str, with_bias: bool,
+                   seed: int, lo: int = -2, hi: int = 2):
+    """Integer-valued operands in [lo, hi] (exact in fp16 and bf16), laid out
+    as in make_inputs.  Every product and partial sum is a small integer, so
+    any accumulation order in fp32 gives the same exact result."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    a = torch.randint(lo, hi + 1, (M, K), generator=g).to(torch.float32)
+    b = torch.randint(lo, hi + 1, (K, N), generator=g).to(torch.float32)
+    bias = torch.randint(lo, hi + 1, (N,), generator=g).to(torch.float32) if with_bias else None
+    dt = _TORCH_DT[in_dtype]
+    a, b = a.to(dt), b.to(dt)
+    if layout_a == "col":
+        a = a.t().contiguous()
+    if layout_b == "col":
+        b = b.t().contiguous()
+    return {
+        "A": to_bits(a),
+        "B": to_bits(b),
+        "bias": to_bits(bias.to(dt)) if bias is not None else None,
+    }

@@ -1,0 +1,242 @@
+/*
+ * oracle.c -- plain, slow, obviously-correct CPU reference for
+ *             C = act(A.B [+ bias]).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  The GPU library
+ * never links, includes or calls it, and it shares no code, header or table
+ * with the GPU library.
+ *
+ * What it computes (one definition, written out):
+ *
+ *   z[i][j] = sum_{k<K} a(i,k) * b(k,j)   (+ bias[j] when the epilogue has a bias)
+ *   y[i][j] = act(z[i][j])
+ *   C[i][j] = round_to_nearest_even(y[i][j], output format)
+ *
+ *   - The GEMM is the textbook sum over k (TileLang tutorial on csdn,
+ *     ch.10 "GEMM 矩阵乘法" sec. 10.1 definition and sec. 10.2 triple loop;
+ *     second tutorial, sec. 八 "示例四：GEMM 矩阵乘法").
+ *   - 16-bit inputs, wide accumulation, one conversion at output
+ *     (same tutorial, sec. 10.6 "GEMM 的底层数据流").  The oracle widens
+ *     to fp64: a product of two fp16 or two bf16 values is exact in fp64.
+ *   - Bias is added before the activation, on the accumulator
+ *     (same tutorial, sec. 10.8 "GEMM Epilogue 融合"; ainew.jp
+ *     "TileLang で GPU カーネル設計を解説", section 4 "EPILOGUE FUSION").
+ *   - ReLU(x) = max(x, 0) (atlascloud.ai "Writing high-performance kernels
+ *     in TileLang", section "Écrivons un GEMM").
+ *   - GELU is the tanh form written as a logistic: x / (1 + exp(-c1*(x + c2*x^3)))
+ *     with c1 = 1.5957691216 and c2 = 0.044715 as printed in ainew.jp
+ *     section 4; the page's bullet between the last two factors is read as
+ *     a multiplication.
+ *   - Layouts: row-major element (r, c) of an R x C matrix sits at r*C + c,
+ *     column-major at c*R + r (TileFusion "基础GEMM示例": A RowMajor<128,256>,
+ *     B ColMajor<256,64>).  C is always row-major.
+ *
+ * Floating-point formats are decoded and encoded here from their bit-level
+ * definitions (IEEE 754 binary16 and binary32; bfloat16 = the top 16 bits
+ * of binary32).  Encoding is one round-to-nearest-even step straight from
+ * fp64, overflow to +-inf, subnormals kept.
+ *
+ * Build: gcc -O2 -fopenmp -ffp-contract=off -shared -fPIC oracle.c -o liboracle.so -lm
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Format codes used by this file's entry points. */
+#define ORC_F16 0
+#define ORC_BF16 1
+#define ORC_F32 2
+
+#define ORC_ROW 0
+#define ORC_COL 1
+
+#define ORC_EPI_NONE 0
+#define ORC_EPI_RELU 1
+#define ORC_EPI_BIAS_RELU 2
+#define ORC_EPI_BIAS_GELU 3
+#define ORC_EPI_BIAS 4
+
+/* mantissa bits, exponent bits of each format */
+static int fmt_mant(int fmt) { return fmt == ORC_F16 ? 10 : fmt == ORC_BF16 ? 7 : 23; }
+static int fmt_expb(int fmt) { return fmt == ORC_F16 ? 5 : 8; }
+
+/* Value of a bit pattern of a binary floating-point format with the given
+ * field widths (sign | exponent | fraction). */
+static double decode_bits(uint32_t bits, int mant, int expb) {
+  uint32_t expmask = (1u << expb) - 1u;
+  int bias = (1 << (expb - 1)) - 1;
+  uint32_t sign = (bits >> (mant + expb)) & 1u;
+  uint32_t e = (bits >> mant) & expmask;
+  uint32_t f = bits & ((1u << mant) - 1u);
+  double v;
+  if (e == expmask) {
+    if (f != 0) return NAN;
+    v = INFINITY;
+  } else if (e == 0) {
+    v = ldexp((double)f, 1 - bias - mant); /* subnormal: f * 2^(emin - mant) */
+  } else {
+    v = ldexp((double)(f + (1u << mant)), (int)e - bias - mant);
+  }
+  return sign ? -v : v;
+}
+
+/* Bit pattern of x rounded once, to nearest with ties to even, into the
+ * format with the given field widths.  Overflow gives +-inf; NaN gives the
+ * canonical quiet NaN. */
+static uint32_t encode_bits(double x, int mant, int expb) {
+  uint32_t expmask = (1u << expb) - 1u;
+  int bias = (1 << (expb - 1)) - 1;
+  int emin = 1 - bias, emax = bias;
+  uint32_t sign = signbit(x) ? 1u : 0u;
+  uint32_t sbit = sign << (mant + expb);
+  if (isnan(x)) return (expmask << mant) | (1u << (mant - 1));
+  double a = fabs(x);
+  if (isinf(a)) return sbit | (expmask << mant);
+  if (a == 0.0) return sbit;
+  int e2;
+  frexp(a, &e2);          /* a = f * 2^e2 with f in [0.5, 1) */
+  int E = e2 - 1;         /* a in [2^E, 2^(E+1)) */
+  if (E < emin) E = emin; /* subnormal range shares the spacing of emin */
+  /* representable values near a are integer multiples of 2^(E - mant);
+   * scaling by a power of two is exact, so r is a exactly */
+  double r = ldexp(a, mant - E);
+  double n = nearbyint(r); /* default rounding mode: nearest, ties to even */
+  if (n >= ldexp(1.0, mant + 1)) { /* carried into the next binade */
+    n = ldexp(n, -1);
+    E += 1;
+  }
+  if (E > emax) return sbit | (expmask << mant);
+  if (n < ldexp(1.0, mant)) /* subnormal (only possible when E == emin) */
+    return sbit | (uint32_t)n;
+  return sbit | ((uint32_t)(E + bias) << mant) | ((uint32_t)n - (1u << mant));
+}
+
+double oracle_decode(int fmt, uint32_t bits) { return decode_bits(bits, fmt_mant(fmt), fmt_expb(fmt)); }
+
+uint32_t oracle_encode(int fmt, double x) { return encode_bits(x, fmt_mant(fmt), fmt_expb(fmt)); }
+
+/* Element-wise forms of the two conversions above, for n values. */
+void oracle_decode_n(int fmt, const uint32_t* bits, double* out, int64_t n) {
+  for (int64_t p = 0; p < n; ++p) out[p] = oracle_decode(fmt, bits[p]);
+}
+
+void oracle_encode_n(int fmt, const double* x, uint32_t* out, int64_t n) {
+  for (int64_t p = 0; p < n; ++p) out[p] = oracle_encode(fmt, x[p]);
+}
+
+/* GELU, tanh approximation in its logistic form, constants as printed. */
+double oracle_gelu(double x) { return x / (1.0 + exp(-1.5957691216 * (x + 0.044715 * x * x * x))); }
+
+/* Activation applied to z (bias already added). */
+static double apply_act(int epi, double z) {
+  switch (epi) {
+  case ORC_EPI_RELU:
+  case ORC_EPI_BIAS_RELU:
+    return z > 0.0 ? z : 0.0;
+  case ORC_EPI_BIAS_GELU:
+    return oracle_gelu(z);
+  default:
+    return z;
+  }
+}
+
+static int epi_has_bias(int epi) { return epi == ORC_EPI_BIAS_RELU || epi == ORC_EPI_BIAS_GELU || epi == ORC_EPI_BIAS; }
+
+static void store_bits(void* p, int fmt, int64_t idx, uint32_t v) {
+  if (fmt == ORC_F32) ((uint32_t*)p)[idx] = v;
+  else ((uint16_t*)p)[idx] = (uint16_t)v;
+}
+
+/* Decoding table for a 16-bit input format: table[bits] = value. */
+static double* make_table(int fmt) {
+  double* t = (double*)malloc(65536 * sizeof(double));
+  if (!t) return NULL;
+  for (uint32_t b = 0; b < 65536; ++b) t[b] = oracle_decode(fmt, b);
+  return t;
+}
+
+static int check_args(int64_t M, int64_t N, int64_t K, int in_fmt, int out_fmt, int la, int lb, int epi) {
+  if (M <= 0 || N <= 0 || K <= 0) return -1;
+  if (in_fmt != ORC_F16 && in_fmt != ORC_BF16) return -1;
+  if (out_fmt != in_fmt && out_fmt != ORC_F32) return -1;
+  if ((la != ORC_ROW && la != ORC_COL) || (lb != ORC_ROW && lb != ORC_COL)) return -1;
+  if (epi < ORC_EPI_NONE || epi > ORC_EPI_BIAS) return -1;
+  return 0;
+}
+
+/* One output element: y = act(sum_k a(i,k) b(k,j) [+ bias_j]) in fp64. */
+static double one_element(const double* tab, const uint16_t* A, const uint16_t* B, const uint16_t* bias,
+                          int64_t M, int64_t N, int64_t K, int la, int lb, int epi, int64_t i, int64_t j) {
+  double z = 0.0;
+  for (int64_t k = 0; k < K; ++k) {
+    double a = tab[A[la == ORC_ROW ? i * K + k : k * M + i]];
+    double b = tab[B[lb == ORC_ROW ? k * N + j : j * K + k]];
+    z += a * b;
+  }
+  if (epi_has_bias(epi)) z += tab[bias[j]];
+  return apply_act(epi, z);
+}
+
+/* Full product.  y_out (M*N doubles, row-major) and c_out (M*N elements of
+ * out_fmt, row-major) may each be NULL.  nthreads <= 0 uses the OpenMP
+ * default.  Returns 0 on success, -1 on bad arguments, -2 on no memory. */
+int oracle_gemm_epi(int64_t M, int64_t N, int64_t K, int in_fmt, int out_fmt, int la, int lb, int epi,
+                    const void* A, const void* B, const void* bias, double* y_out, void* c_out, int nthreads) {
+  if (check_args(M, N, K, in_fmt, out_fmt, la, lb, epi)) return -1;
+  if (!A || !B || (epi_has_bias(epi) && !bias)) return -1;
+  double* tab = make_table(in_fmt);
+  if (!tab) return -2;
+#ifdef _OPENMP
+  if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+#endif
+  for (int64_t i = 0; i < M; ++i) {
+    for (int64_t j = 0; j < N; ++j) {
+      double y = one_element(tab, (const uint16_t*)A, (const uint16_t*)B, (const uint16_t*)bias, M, N, K, la, lb,
+                             epi, i, j);
+      if (y_out) y_out[i * N + j] = y;
+      if (c_out) store_bits(c_out, out_fmt, i * N + j, oracle_encode(out_fmt, y));
+    }
+  }
+  free(tab);
+  return 0;
+}
+
+/* Selected elements only: for p < count, element (rows[p], cols[p]).
+ * y_out[p] gets the fp64 value, bits_out[p] its rounded encoding. */
+int oracle_gemm_epi_points(int64_t M, int64_t N, int64_t K, int in_fmt, int out_fmt, int la, int lb, int epi,
+                           const void* A, const void* B, const void* bias, int64_t count, const int64_t* rows,
+                           const int64_t* cols, double* y_out, uint32_t* bits_out, int nthreads) {
+  if (check_args(M, N, K, in_fmt, out_fmt, la, lb, epi)) return -1;
+  if (!A || !B || (epi_has_bias(epi) && !bias) || count < 0 || (count && (!rows || !cols))) return -1;
+  for (int64_t p = 0; p < count; ++p)
+    if (rows[p] < 0 || rows[p] >= M || cols[p] < 0 || cols[p] >= N) return -1;
+  double* tab = make_table(in_fmt);
+  if (!tab) return -2;
+#ifdef _OPENMP
+  if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 16) num_threads(nthreads)
+#endif
+  for (int64_t p = 0; p < count; ++p) {
+    double y = one_element(tab, (const uint16_t*)A, (const uint16_t*)B, (const uint16_t*)bias, M, N, K, la, lb, epi,
+                           rows[p], cols[p]);
+    if (y_out) y_out[p] = y;
+    if (bits_out) bits_out[p] = oracle_encode(out_fmt, y);
+  }
+  free(tab);
+  return 0;
+}
+
+/* Threads an OpenMP region of this library uses by default. */
+int oracle_max_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}

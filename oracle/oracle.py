@@ -1,0 +1,150 @@
+"""ctypes front end of the C oracle -- TEST INFRASTRUCTURE ONLY.
+
+Argument marshalling only: every value is computed by ``oracle.c``.  Inputs
+are the raw bit patterns the GPU side also sees (numpy ``uint16`` arrays for
+fp16/bf16), so both sides start from identical bytes.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+# Codes understood by oracle.c (its own numbering; nothing is shared with the
+# GPU library's header).
+FORMATS = {"f16": 0, "bf16": 1, "f32": 2}
+LAYOUTS = {"row": 0, "col": 1}
+EPILOGUES = {"none": 0, "relu": 1, "bias_relu": 2, "bias_gelu": 3, "bias": 4}
+
+_lib = None
+
+
+def lib_path() -> str:
+    return _LIB
+
+
+def build() -> str:
+    """Compile oracle.c with the host C compiler (no HIP involved)."""
+    cmd = [
+        "gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-Wall",
+        "-shared", "-fPIC", _SRC, "-o", _LIB, "-lm",
+    ]
+    subprocess.run(cmd, check=True)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        build()
+    lib = ctypes.CDLL(_LIB)
+    i64, i32, u32, vp, dp = ctypes.c_int64, ctypes.c_int, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_double
+    lib.oracle_decode.argtypes = [i32, u32]
+    lib.oracle_decode.restype = dp
+    lib.oracle_encode.argtypes = [i32, dp]
+    lib.oracle_encode.restype = u32
+    lib.oracle_decode_n.argtypes = [i32, vp, vp, i64]
+    lib.oracle_decode_n.restype = None
+    lib.oracle_encode_n.argtypes = [i32, vp, vp, i64]
+    lib.oracle_encode_n.restype = None
+    lib.oracle_gelu.argtypes = [dp]
+    lib.oracle_gelu.restype = dp
+    lib.oracle_gemm_epi.argtypes = [i64, i64, i64, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, i32]
+    lib.oracle_gemm_epi.restype = i32
+    lib.oracle_gemm_epi_points.argtypes = [i64, i64, i64, i32, i32, i32, i32, i32, vp, vp, vp,
+                                           i64, vp, vp, vp, vp, i32]
+    lib.oracle_gemm_epi_points.restype = i32
+    lib.oracle_max_threads.argtypes = []
+    lib.oracle_max_threads.restype = i32
+    _lib = lib
+    return lib
+
+
+def max_threads() -> int:
+    return int(_load().oracle_max_threads())
+
+
+def decode(fmt: str, bits: int) -> float:
+    return float(_load().oracle_decode(FORMATS[fmt], int(bits)))
+
+
+def encode(fmt: str, x: float) -> int:
+    return int(_load().oracle_encode(FORMATS[fmt], float(x)))
+
+
+def decode_array(fmt: str, bits) -> np.ndarray:
+    """Values (fp64) of an array of bit patterns."""
+    b = np.ascontiguousarray(bits, dtype=np.uint32)
+    out = np.empty(b.shape, np.float64)
+    _load().oracle_decode_n(FORMATS[fmt], _ptr(b), _ptr(out), b.size)
+    return out
+
+
+def encode_array(fmt: str, x) -> np.ndarray:
+    """Bit patterns (uint32) of an fp64 array rounded once to the format."""
+    v = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty(v.shape, np.uint32)
+    _load().oracle_encode_n(FORMATS[fmt], _ptr(v), _ptr(out), v.size)
+    return out
+
+
+def gelu(x: float) -> float:
+    return float(_load().oracle_gelu(float(x)))
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def _bits16(a, name):
+    if a is None:
+        return None
+    a = np.ascontiguousarray(a)
+    if a.dtype != np.uint16:
+        raise TypeError(f"{name}: expected uint16 bit patterns, got {a.dtype}")
+    return a
+
+
+def gemm_epi(A, B, bias, M, N, K, in_dtype, out_dtype, layout_a, layout_b, epilogue,
+             want_y=True, want_c=True, nthreads=0):
+    """Full M x N product.  Returns (y, c): y is fp64 act(z) (row-major M x N),
+    c the rounded output bit patterns (uint16, or uint32 for f32)."""
+    A, B, bias = _bits16(A, "A"), _bits16(B, "B"), _bits16(bias, "bias")
+    if A.size != M * K or B.size != K * N or (bias is not None and bias.size != N):
+        raise ValueError("operand sizes do not match M, N, K")
+    y = np.empty((M, N), np.float64) if want_y else None
+    c = np.empty((M, N), np.uint32 if out_dtype == "f32" else np.uint16) if want_c else None
+    rc = _load().oracle_gemm_epi(M, N, K, FORMATS[in_dtype], FORMATS[out_dtype], LAYOUTS[layout_a],
+                                 LAYOUTS[layout_b], EPILOGUES[epilogue], _ptr(A), _ptr(B), _ptr(bias),
+                                 _ptr(y), _ptr(c), int(nthreads))
+    if rc != 0:
+        raise ValueError(f"oracle_gemm_epi rejected its arguments (rc={rc})")
+    return y, c
+
+
+def gemm_epi_points(A, B, bias, M, N, K, in_dtype, out_dtype, layout_a, layout_b, epilogue,
+                    rows, cols, nthreads=0):
+    """Selected elements (rows[p], cols[p]).  Returns (y, bits) as 1-D arrays."""
+    A, B, bias = _bits16(A, "A"), _bits16(B, "B"), _bits16(bias, "bias")
+    if A.size != M * K or B.size != K * N or (bias is not None and bias.size != N):
+        raise ValueError("operand sizes do not match M, N, K")
+    rows = np.ascontiguousarray(rows, np.int64)
+    cols = np.ascontiguousarray(cols, np.int64)
+    if rows.shape != cols.shape:
+        raise ValueError("rows and cols differ in length")
+    y = np.empty(rows.size, np.float64)
+    bits = np.empty(rows.size, np.uint32)
+    rc = _load().oracle_gemm_epi_points(M, N, K, FORMATS[in_dtype], FORMATS[out_dtype], LAYOUTS[layout_a],
+                                        LAYOUTS[layout_b], EPILOGUES[epilogue], _ptr(A), _ptr(B), _ptr(bias),
+                                        rows.size, _ptr(rows), _ptr(cols), _ptr(y), _ptr(bits), int(nthreads))
+    if rc != 0:
+        raise ValueError(f"oracle_gemm_epi_points rejected its arguments (rc={rc})")
+    return y, bits
