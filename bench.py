@@ -1,0 +1,199 @@
+"""Benchmark: GEMM+epilogue TFLOP/s (% of dense MFMA peak) and skinny-M GB/s
+(% of HBM peak) on one MI355X.
+
+One step = one launch of the library on one batch of synthetic input:
+  * main line: C = GELU_tanh(A.B + bias), bf16 in/out, fp32 accumulate,
+    M = N = K = 8192, A row-major, B column-major (value = TFLOP/s, 2MNK
+    per step);
+  * "skinny": C = A.B + bias, bf16, M = 32, N = K = 8192, B column-major
+    (GB/s of compulsory A + B + bias + C bytes per step).
+Inputs are resident in HBM before timing starts; operand sets are rotated
+across launches so that the 256 MB last-level cache cannot serve B from a
+previous launch.  Timing uses HIP events on the stream the kernels are
+launched on.  The CPU oracle is timed on a bounded sample of the main
+workload as a reported baseline (rank 0, N = 1 only).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only main|skinny]
+                       [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+MAIN = "gemm_bias_gelu_bf16_8192x8192x8192_rm_cm"
+SKINNY = "skinny_gemm_bias_bf16_32x8192x8192_rm_cm"
+
+# MI355X published peaks
+PEAK_BF16_TFLOPS = 2500.0  # dense bf16/fp16 MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def _device_sets(w, n_sets, torch, parity, inputs):
+    """n_sets independent device copies of the workload's operands."""
+    bits = inputs.workload_inputs(w)
+    A0 = parity.to_device(bits["A"], w.in_dtype)
+    B0 = parity.to_device(bits["B"], w.in_dtype)
+    bias0 = parity.to_device(bits["bias"], w.in_dtype) if bits["bias"] is not None else None
+    sets = []
+    for i in range(n_sets):
+        A = A0 if i == 0 else A0.clone()
+        B = B0 if i == 0 else B0.clone()
+        bias = None if bias0 is None else (bias0 if i == 0 else bias0.clone())
+        C = parity.empty_out(w.M * w.N, w.out_dtype)
+        sets.append((A, B, bias, C))
+    torch.cuda.synchronize()
+    return bits, sets
+
+
+def _time_launches(plan, sets, steps, warmup, torch):
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        A, B, bias, C = sets[i % len(sets)]
+        plan.run(A, B, bias, C, stream)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(steps):
+        A, B, bias, C = sets[i % len(sets)]
+        plan.run(A, B, bias, C, stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps  # ms per launch
+
+
+def _cpu_baseline(w, bits):
+    """Oracle rate on a bounded sample of rows of the workload."""
+    import numpy as np
+
+    import oracle
+
+    def run_rows(r):
+        rows = np.repeat(np.arange(r), w.N)
+        cols = np.tile(np.arange(w.N), r)
+        t0 = time.perf_counter()
+        oracle.gemm_epi_points(bits["A"], bits["B"], bits["bias"], w.M, w.N, w.K, w.in_dtype, w.out_dtype,
+                               w.layout_a, w.layout_b, w.epilogue, rows, cols)
+        return time.perf_counter() - t0
+
+    t1 = run_rows(1)
+    rows = int(max(1, min(w.M, round(12.0 / max(t1, 1e-3)))))
+    t = run_rows(rows)
+    flops = 2.0 * rows * w.N * w.K
+    return {
+        "value": flops / t / 1e12,
+        "unit": "TFLOP/s",
+        "cores": oracle.max_threads(),
+        "kind": "oracle",
+        "sample": f"{rows} full output rows of {w.name} ({rows}x{w.N} outputs, K={w.K}), fp64, {t:.1f} s",
+        "seconds": t,
+    }
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--only", choices=["main", "skinny", "both"], default="both")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the hot path is a single-GPU kernel "
+              "(--gpus must be 1)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from epilogue_gemm_amd import binding, inputs
+    from tests import parity
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    binding.load_library()
+    torch.cuda.set_device(0)
+
+    out = {}
+    if args.only in ("main", "both"):
+        w = inputs.WORKLOADS[MAIN]
+        bits, sets = _device_sets(w, 3, torch, parity, inputs)
+        plan = binding.Plan(w.M, w.N, w.K, w.in_dtype, w.out_dtype, w.layout_a, w.layout_b, w.epilogue)
+        ms = _time_launches(plan, sets, args.steps, args.warmup, torch)
+        tflops = w.flops / (ms * 1e-3) / 1e12
+        out["main"] = dict(w=w, bits=bits, ms=ms, value=tflops, kernel=plan.name)
+        plan.close()
+        del sets
+        torch.cuda.empty_cache()
+    if args.only in ("skinny", "both"):
+        w = inputs.WORKLOADS[SKINNY]
+        # 5 sets x 128 MiB of B: more than the 256 MB last-level cache
+        bits_s, sets = _device_sets(w, 5, torch, parity, inputs)
+        plan = binding.Plan(w.M, w.N, w.K, w.in_dtype, w.out_dtype, w.layout_a, w.layout_b, w.epilogue)
+        steps = max(args.steps, 200)
+        ms = _time_launches(plan, sets, steps, max(args.warmup, 20), torch)
+        gbs = w.compulsory_bytes() / (ms * 1e-3) / 1e9
+        out["skinny"] = dict(w=w, ms=ms, value=gbs, kernel=plan.name, steps=steps)
+        plan.close()
+        del sets
+        torch.cuda.empty_cache()
+
+    rec = {}
+    if "main" in out:
+        m = out["main"]
+        w = m["w"]
+        rec = {
+            "metric": "GEMM+epilogue TFLOP/s (% MFMA peak); skinny-M GB/s (% HBM peak), 1 GPU",
+            "value": round(m["value"], 2),
+            "unit": "TFLOP/s",
+            "n_gpus": 1,
+            "steps": args.steps,
+            "warmup": args.warmup,
+            "ms_per_step": round(m["ms"], 4),
+            "higher_is_better": True,
+            "scaling": "weak",
+            "vs_baseline": None,
+            "dtype": "bf16",
+            "data": "synthetic",
+            "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "epilogue": w.epilogue,
+                       "layout_a": w.layout_a, "layout_b": w.layout_b, "kernel": m["kernel"],
+                       "operand_sets_rotated": 3},
+            "roofline": {"bound": "mfma", "achieved": round(m["value"], 2), "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(m["value"] / PEAK_BF16_TFLOPS, 4), "traffic": None},
+        }
+    if "skinny" in out:
+        s = out["skinny"]
+        w = s["w"]
+        sk = {
+            "metric": "skinny-M GB/s (% HBM peak)",
+            "value": round(s["value"], 1),
+            "unit": "GB/s",
+            "ms_per_step": round(s["ms"], 5),
+            "steps": s["steps"],
+            "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "epilogue": w.epilogue,
+                       "kernel": s["kernel"], "operand_sets_rotated": 5,
+                       "compulsory_bytes": w.compulsory_bytes()},
+            "roofline": {"bound": "hbm", "achieved": round(s["value"], 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(s["value"] / PEAK_HBM_GBS, 4), "traffic": None},
+        }
+        if rec:
+            rec["skinny"] = sk
+        else:
+            rec = {**sk, "n_gpus": 1, "warmup": args.warmup, "higher_is_better": True, "scaling": "weak",
+                   "vs_baseline": None, "dtype": "bf16", "data": "synthetic"}
+    if "main" in out and not args.no_cpu_baseline:
+        rec["cpu_baseline"] = _cpu_baseline(out["main"]["w"], out["main"]["bits"])
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,200 @@
+"""Python binding of libgemm_epi.so (include/gemm_epi.h) -- argument
+marshalling only.
+
+The functions below carry the C names and call straight into the library;
+every step of the computation runs in its HIP kernels.  ``Plan`` is a thin
+convenience over them that takes torch CUDA tensors (used only as device
+memory) and torch's current stream.  There is no fallback: if the library
+is missing, loading fails with an error that says how to build it.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgemm_epi.so")
+HEADER = os.path.join(os.path.dirname(_HERE), "include", "gemm_epi.h")
+
+# Enum values of include/gemm_epi.h
+DTYPES = {"f16": 0, "bf16": 1, "f32": 2}
+LAYOUTS = {"row": 0, "col": 1}
+EPILOGUES = {"none": 0, "relu": 1, "bias_relu": 2, "bias_gelu": 3, "bias": 4}
+KERNELS = {"auto": 0, "generic": 1, "tile": 2, "skinny": 3}
+KERNEL_NAMES = {v: k for k, v in KERNELS.items()}
+STATUS = {0: "OK", 1: "ERR_INVALID_ARG", 2: "ERR_UNSUPPORTED", 3: "ERR_HIP", 4: "ERR_NO_MEMORY"}
+OK = 0
+
+
+class GemmEpiError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        msg = f"{fn} returned {gemm_epi_status_string(status)}"
+        if status == 3:
+            msg += f" (hipError_t {gemm_epi_last_hip_error()})"
+        super().__init__(msg)
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libgemm_epi.so once.  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: the HIP library has not been built. "
+            "Run `python -c 'import __graft_entry__ as g; g.build()'` or "
+            "`python epilogue_gemm_amd/build.py` first.")
+    lib = ctypes.CDLL(path)
+    i64, i32, vp, cp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_char_p
+    lib.gemm_epi_plan.argtypes = [ctypes.POINTER(vp), i64, i64, i64, i32, i32, i32, i32, i32]
+    lib.gemm_epi_plan.restype = i32
+    lib.gemm_epi_run.argtypes = [vp, vp, vp, vp, vp, vp]
+    lib.gemm_epi_run.restype = i32
+    lib.gemm_epi_destroy.argtypes = [vp]
+    lib.gemm_epi_destroy.restype = i32
+    lib.gemm_epi_status_string.argtypes = [i32]
+    lib.gemm_epi_status_string.restype = cp
+    lib.gemm_epi_last_hip_error.argtypes = []
+    lib.gemm_epi_last_hip_error.restype = i32
+    lib.gemm_epi_plan_select.argtypes = [vp, i32, i32]
+    lib.gemm_epi_plan_select.restype = i32
+    lib.gemm_epi_num_configs.argtypes = [i32]
+    lib.gemm_epi_num_configs.restype = i32
+    lib.gemm_epi_plan_describe.argtypes = [vp, ctypes.POINTER(i32), ctypes.POINTER(i32)]
+    lib.gemm_epi_plan_describe.restype = cp
+    _lib = lib
+    return lib
+
+
+def header_functions(header: str = HEADER):
+    """Names of the functions include/gemm_epi.h declares."""
+    text = open(header).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gemm_epi_\w+)\s*\(", text)))
+
+
+# ---- the C entry points, same names ----------------------------------------
+
+def gemm_epi_plan(M, N, K, in_dtype, out_dtype, layout_a, layout_b, epilogue) -> int:
+    """Returns the plan handle (an int); raises GemmEpiError on failure."""
+    h = ctypes.c_void_p()
+    st = load_library().gemm_epi_plan(ctypes.byref(h), int(M), int(N), int(K), DTYPES[in_dtype], DTYPES[out_dtype],
+                                      LAYOUTS[layout_a], LAYOUTS[layout_b], EPILOGUES[epilogue])
+    if st != OK:
+        raise GemmEpiError("gemm_epi_plan", st)
+    return h.value
+
+
+def gemm_epi_plan_status(M, N, K, in_dtype, out_dtype, layout_a, layout_b, epilogue, raw=False) -> int:
+    """Status code of gemm_epi_plan for raw (possibly invalid) enum values;
+    destroys the plan if one was made.  For tests of argument validation."""
+    h = ctypes.c_void_p()
+    lib = load_library()
+    if raw:
+        args = (in_dtype, out_dtype, layout_a, layout_b, epilogue)
+    else:
+        args = (DTYPES[in_dtype], DTYPES[out_dtype], LAYOUTS[layout_a], LAYOUTS[layout_b], EPILOGUES[epilogue])
+    st = lib.gemm_epi_plan(ctypes.byref(h), int(M), int(N), int(K), *args)
+    if st == OK:
+        lib.gemm_epi_destroy(h)
+    return st
+
+
+def gemm_epi_run(plan, A_ptr, B_ptr, bias_ptr, C_ptr, stream) -> int:
+    return load_library().gemm_epi_run(plan, A_ptr, B_ptr, bias_ptr, C_ptr, stream)
+
+
+def gemm_epi_destroy(plan) -> int:
+    return load_library().gemm_epi_destroy(plan)
+
+
+def gemm_epi_status_string(status: int) -> str:
+    return load_library().gemm_epi_status_string(int(status)).decode()
+
+
+def gemm_epi_last_hip_error() -> int:
+    return int(load_library().gemm_epi_last_hip_error())
+
+
+def gemm_epi_plan_select(plan, kernel: str, config: int = -1) -> int:
+    return load_library().gemm_epi_plan_select(plan, KERNELS[kernel], int(config))
+
+
+def gemm_epi_num_configs(kernel: str) -> int:
+    return int(load_library().gemm_epi_num_configs(KERNELS[kernel]))
+
+
+def gemm_epi_plan_describe(plan):
+    """(kernel family name, config index, config name)."""
+    k, c = ctypes.c_int(), ctypes.c_int()
+    name = load_library().gemm_epi_plan_describe(plan, ctypes.byref(k), ctypes.byref(c))
+    if name is None:
+        raise ValueError("NULL plan")
+    return KERNEL_NAMES[k.value], c.value, name.decode()
+
+
+# ---- convenience over torch tensors (device memory + stream only) ----------
+
+_TORCH_DTYPE_NAMES = {"float16": "f16", "bfloat16": "bf16", "float32": "f32"}
+
+
+def _dtype_name(t) -> str:
+    return _TORCH_DTYPE_NAMES[str(t.dtype).replace("torch.", "")]
+
+
+class Plan:
+    """A planned problem.  ``run(A, B, bias, C)`` enqueues on torch's current
+    CUDA stream (or the given one) and returns without synchronising."""
+
+    def __init__(self, M, N, K, in_dtype, out_dtype, layout_a="row", layout_b="row", epilogue="none",
+                 kernel: str = "auto", config: int = -1):
+        self.M, self.N, self.K = int(M), int(N), int(K)
+        self.in_dtype, self.out_dtype = in_dtype, out_dtype
+        self.layout_a, self.layout_b, self.epilogue = layout_a, layout_b, epilogue
+        self.handle = gemm_epi_plan(M, N, K, in_dtype, out_dtype, layout_a, layout_b, epilogue)
+        if kernel != "auto":
+            st = gemm_epi_plan_select(self.handle, kernel, config)
+            if st != OK:
+                gemm_epi_destroy(self.handle)
+                self.handle = None
+                raise GemmEpiError("gemm_epi_plan_select", st)
+        self.kernel, self.config, self.name = gemm_epi_plan_describe(self.handle)
+
+    def _check(self, t, name, dtype, numel):
+        if t is None:
+            return None
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name}: expected a contiguous CUDA tensor")
+        if _dtype_name(t) != dtype:
+            raise ValueError(f"{name}: dtype {t.dtype} does not match {dtype}")
+        if t.numel() != numel:
+            raise ValueError(f"{name}: {t.numel()} elements, expected {numel}")
+        return t.data_ptr()
+
+    def run(self, A, B, bias, C, stream=None):
+        import torch
+
+        a = self._check(A, "A", self.in_dtype, self.M * self.K)
+        b = self._check(B, "B", self.in_dtype, self.K * self.N)
+        bi = self._check(bias, "bias", self.in_dtype, self.N)
+        c = self._check(C, "C", self.out_dtype, self.M * self.N)
+        s = (stream or torch.cuda.current_stream()).cuda_stream
+        st = gemm_epi_run(self.handle, a, b, bi, c, s)
+        if st != OK:
+            raise GemmEpiError("gemm_epi_run", st)
+
+    def close(self):
+        if self.handle is not None:
+            gemm_epi_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

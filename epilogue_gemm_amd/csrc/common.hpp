@@ -1,0 +1,123 @@
+// common.hpp -- shared device pieces of the gfx950 GEMM+epilogue kernels:
+// element types, the fp32 epilogue and the output conversion.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/gemm_epi.h"
+
+namespace ge {
+
+typedef _Float16 f16;
+typedef __bf16 bf16;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Arguments every kernel family receives from the host side.
+struct LaunchArgs {
+  const void* A;
+  const void* B;
+  const void* bias;
+  void* C;
+  int M, N, K;
+  int epi;     // gemm_epi_epilogue
+  int la, lb;  // gemm_epi_layout of A and B
+  hipStream_t stream;
+};
+
+// ---------------------------------------------------------------------------
+// 16-bit input element -> fp32
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float to_f32(f16 x) { return (float)x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+
+// ---------------------------------------------------------------------------
+// Epilogue on an fp32 accumulator value z with its column's bias b.
+//   GELU: x / (1 + exp(-1.5957691216 (x + 0.044715 x^3))), the tanh form of
+//   GELU as a logistic (ainew.jp "TileLang で GPU カーネル設計を解説",
+//   section 4 "EPILOGUE FUSION").  exp(u) is evaluated as 2^(u log2 e) with
+//   the hardware exp2 (v_exp_f32) and the quotient with v_rcp_f32; both are
+//   accurate to about one fp32 ulp, far below the 16-bit output spacing.
+//   Large negative x: 2^(+big) = +inf, 1/inf = 0, result -0.  Large
+//   positive x: 2^(-big) = 0, result x.
+// Bias is added first, then the activation (csdn tutorial ch.10
+// sec. 10.8 "GEMM Epilogue 融合").
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float gelu_logistic(float x) {
+  const float u = -1.5957691216f * (x + 0.044715f * x * x * x);
+  const float e = __builtin_amdgcn_exp2f(u * 1.4426950408889634f);
+  return x * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+template <int EPI>
+__device__ __forceinline__ float epilogue(float z, float b) {
+  if constexpr (EPI == GEMM_EPI_NONE) return z;
+  else if constexpr (EPI == GEMM_EPI_RELU) return fmaxf(z, 0.0f);
+  else if constexpr (EPI == GEMM_EPI_BIAS_RELU) return fmaxf(z + b, 0.0f);
+  else if constexpr (EPI == GEMM_EPI_BIAS_GELU) return gelu_logistic(z + b);
+  else return z + b;  // GEMM_EPI_BIAS
+}
+
+template <int EPI>
+constexpr bool epi_has_bias() {
+  return EPI == GEMM_EPI_BIAS_RELU || EPI == GEMM_EPI_BIAS_GELU || EPI == GEMM_EPI_BIAS;
+}
+
+// ---------------------------------------------------------------------------
+// fp32 -> output element, round to nearest even (v_cvt_f16_f32 under the
+// default round-to-nearest mode; v_cvt_pk_bf16_f32 for bf16).
+// ---------------------------------------------------------------------------
+template <typename TOut>
+__device__ __forceinline__ TOut from_f32(float x) {
+  return (TOut)x;
+}
+
+template <typename T>
+__device__ __forceinline__ uint16_t bits16(T x) {
+  return __builtin_bit_cast(uint16_t, x);
+}
+
+// Four consecutive outputs of one row -> one vector store.
+template <typename TOut>
+__device__ __forceinline__ void store4(TOut* p, float v0, float v1, float v2, float v3) {
+  if constexpr (sizeof(TOut) == 4) {
+    *reinterpret_cast<f32x4*>(p) = f32x4{v0, v1, v2, v3};
+  } else {
+    u32x2 w;
+    w.x = (uint32_t)bits16(from_f32<TOut>(v0)) | ((uint32_t)bits16(from_f32<TOut>(v1)) << 16);
+    w.y = (uint32_t)bits16(from_f32<TOut>(v2)) | ((uint32_t)bits16(from_f32<TOut>(v3)) << 16);
+    *reinterpret_cast<u32x2*>(p) = w;
+  }
+}
+
+// Four consecutive 16-bit bias values as fp32.
+template <typename TIn>
+__device__ __forceinline__ f32x4 load_bias4(const TIn* p) {
+  const u32x2 w = *reinterpret_cast<const u32x2*>(p);
+  f32x4 r;
+  r.x = to_f32(__builtin_bit_cast(TIn, (uint16_t)(w.x & 0xffffu)));
+  r.y = to_f32(__builtin_bit_cast(TIn, (uint16_t)(w.x >> 16)));
+  r.z = to_f32(__builtin_bit_cast(TIn, (uint16_t)(w.y & 0xffffu)));
+  r.w = to_f32(__builtin_bit_cast(TIn, (uint16_t)(w.y >> 16)));
+  return r;
+}
+
+// 32x32x16 MFMA, fp32 accumulate, for either 16-bit input format.  Each
+// operand register holds 8 consecutive-in-k elements of one row (first
+// operand) or one column (second operand).
+template <typename TIn>
+__device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
+  if constexpr (__is_same(TIn, f16))
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
+                                                   0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                    0, 0, 0);
+}
+
+}  // namespace ge

@@ -1,0 +1,218 @@
+// gemm_epi.cpp -- host side of the C ABI declared in include/gemm_epi.h:
+// argument validation, kernel-family selection, launch on the caller's
+// stream.  The plan is a small immutable host object; nothing here
+// allocates device memory or synchronises.
+#include <hip/hip_runtime.h>
+
+#include <new>
+
+#include "kernels.hpp"
+
+namespace ge {
+
+// Tile configurations: workgroup tile BM x BN (k-step 64), 4 waves each
+// owning (BM/2) x (BN/2).  Larger tiles reuse each loaded byte more; smaller
+// ones give small problems enough workgroups for 256 CUs.
+static const TileConfig kTile[] = {
+    {256, 256, "tile_256x256x64"},
+    {128, 128, "tile_128x128x64"},
+    {64, 64, "tile_64x64x64"},
+};
+
+int tile_num_configs() { return (int)(sizeof(kTile) / sizeof(kTile[0])); }
+const TileConfig& tile_config(int cfg) { return kTile[cfg]; }
+
+bool tile_supports(int cfg, const Problem& p) {
+  if (cfg < 0 || cfg >= tile_num_configs()) return false;
+  const TileConfig& c = kTile[cfg];
+  return p.M % c.bm == 0 && p.N % c.bn == 0 && p.K % 64 == 0;
+}
+
+int tile_choose(const Problem& p) {
+  // Largest tile that still gives at least one workgroup per CU; else the
+  // smallest tile that fits (most parallelism).
+  int fallback = -1;
+  for (int c = 0; c < tile_num_configs(); ++c) {
+    if (!tile_supports(c, p)) continue;
+    const int64_t tiles = (p.M / kTile[c].bm) * (p.N / kTile[c].bn);
+    if (tiles >= 256) return c;
+    fallback = c;
+  }
+  return fallback;
+}
+
+LaunchFn tile_launcher(int cfg, const Problem& p) {
+  if (p.in_dt == GEMM_EPI_F16) return tile_launcher_f16(cfg, p.out_dt, p.la, p.lb);
+  if (p.in_dt == GEMM_EPI_BF16) return tile_launcher_bf16(cfg, p.out_dt, p.la, p.lb);
+  return nullptr;
+}
+
+}  // namespace ge
+
+struct gemm_epi_plan_s {
+  ge::Problem p;
+  int kernel;  // gemm_epi_kernel actually used for aligned pointers
+  int config;
+  ge::LaunchFn fn;       // chosen family
+  ge::LaunchFn generic;  // fallback for unaligned pointers
+  const char* name;
+};
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+bool valid_enum_args(gemm_epi_dtype in, gemm_epi_dtype out, gemm_epi_layout la, gemm_epi_layout lb,
+                     gemm_epi_epilogue epi) {
+  if (in != GEMM_EPI_F16 && in != GEMM_EPI_BF16) return false;
+  if (out != in && out != GEMM_EPI_F32) return false;
+  if ((la != GEMM_EPI_ROW_MAJOR && la != GEMM_EPI_COL_MAJOR) || (lb != GEMM_EPI_ROW_MAJOR && lb != GEMM_EPI_COL_MAJOR))
+    return false;
+  return epi >= GEMM_EPI_NONE && epi <= GEMM_EPI_BIAS;
+}
+
+bool uses_bias(int epi) { return epi == GEMM_EPI_BIAS_RELU || epi == GEMM_EPI_BIAS_GELU || epi == GEMM_EPI_BIAS; }
+
+// Resolve (kernel, config) for the plan's problem; returns false if that
+// family cannot run it.
+bool resolve(gemm_epi_plan_s* pl, int kernel, int config) {
+  const ge::Problem& p = pl->p;
+  if (kernel == GEMM_EPI_KERNEL_AUTO) {
+    int c = ge::skinny_choose(p);
+    if (c >= 0) return resolve(pl, GEMM_EPI_KERNEL_SKINNY, c);
+    c = ge::tile_choose(p);
+    if (c >= 0) return resolve(pl, GEMM_EPI_KERNEL_TILE, c);
+    return resolve(pl, GEMM_EPI_KERNEL_GENERIC, 0);
+  }
+  if (kernel == GEMM_EPI_KERNEL_GENERIC) {
+    if (config > 0) return false;
+    pl->kernel = kernel;
+    pl->config = 0;
+    pl->fn = pl->generic;
+    pl->name = "generic";
+    return pl->fn != nullptr;
+  }
+  if (kernel == GEMM_EPI_KERNEL_TILE) {
+    if (config < 0) config = ge::tile_choose(p);
+    if (!ge::tile_supports(config, p)) return false;
+    ge::LaunchFn fn = ge::tile_launcher(config, p);
+    if (!fn) return false;
+    pl->kernel = kernel;
+    pl->config = config;
+    pl->fn = fn;
+    pl->name = ge::tile_config(config).name;
+    return true;
+  }
+  if (kernel == GEMM_EPI_KERNEL_SKINNY) {
+    if (config < 0) config = ge::skinny_choose(p);
+    if (!ge::skinny_supports(config, p)) return false;
+    ge::LaunchFn fn = ge::skinny_launcher(config, p);
+    if (!fn) return false;
+    pl->kernel = kernel;
+    pl->config = config;
+    pl->fn = fn;
+    pl->name = ge::skinny_config(config).name;
+    return true;
+  }
+  return false;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+gemm_epi_status gemm_epi_plan(gemm_epi_plan_t* out, int64_t M, int64_t N, int64_t K, gemm_epi_dtype in_dtype,
+                              gemm_epi_dtype out_dtype, gemm_epi_layout layout_a, gemm_epi_layout layout_b,
+                              gemm_epi_epilogue epilogue) {
+  if (!out || M <= 0 || N <= 0 || K <= 0) return GEMM_EPI_ERR_INVALID_ARG;
+  if (!valid_enum_args(in_dtype, out_dtype, layout_a, layout_b, epilogue)) return GEMM_EPI_ERR_INVALID_ARG;
+  const int64_t lim = (int64_t)1 << 31;
+  if (M >= lim || N >= lim || K >= lim || M * K >= lim || K * N >= lim || M * N >= lim)
+    return GEMM_EPI_ERR_UNSUPPORTED;
+  gemm_epi_plan_s* pl = new (std::nothrow) gemm_epi_plan_s();
+  if (!pl) return GEMM_EPI_ERR_NO_MEMORY;
+  pl->p = ge::Problem{M, N, K, (int)in_dtype, (int)out_dtype, (int)layout_a, (int)layout_b, (int)epilogue};
+  pl->generic = ge::generic_launcher(pl->p);
+  if (!pl->generic || !resolve(pl, GEMM_EPI_KERNEL_AUTO, -1)) {
+    delete pl;
+    return GEMM_EPI_ERR_UNSUPPORTED;
+  }
+  *out = pl;
+  return GEMM_EPI_OK;
+}
+
+gemm_epi_status gemm_epi_run(gemm_epi_plan_t plan, const void* A, const void* B, const void* bias, void* C,
+                             void* stream) {
+  if (!plan || !A || !B || !C) return GEMM_EPI_ERR_INVALID_ARG;
+  const bool need_bias = uses_bias(plan->p.epi);
+  if (need_bias != (bias != nullptr)) return GEMM_EPI_ERR_INVALID_ARG;
+  ge::LaunchArgs a;
+  a.A = A;
+  a.B = B;
+  a.bias = bias;
+  a.C = C;
+  a.M = (int)plan->p.M;
+  a.N = (int)plan->p.N;
+  a.K = (int)plan->p.K;
+  a.epi = plan->p.epi;
+  a.la = plan->p.la;
+  a.lb = plan->p.lb;
+  a.stream = (hipStream_t)stream;
+  const bool aligned = aligned16(A) && aligned16(B) && aligned16(C) && (!bias || aligned16(bias));
+  ge::LaunchFn fn = aligned ? plan->fn : plan->generic;
+  const hipError_t e = fn(a);
+  if (e != hipSuccess) {
+    g_last_hip_error = (int)e;
+    return GEMM_EPI_ERR_HIP;
+  }
+  return GEMM_EPI_OK;
+}
+
+gemm_epi_status gemm_epi_destroy(gemm_epi_plan_t plan) {
+  delete plan;
+  return GEMM_EPI_OK;
+}
+
+const char* gemm_epi_status_string(gemm_epi_status status) {
+  switch (status) {
+    case GEMM_EPI_OK: return "GEMM_EPI_OK";
+    case GEMM_EPI_ERR_INVALID_ARG: return "GEMM_EPI_ERR_INVALID_ARG";
+    case GEMM_EPI_ERR_UNSUPPORTED: return "GEMM_EPI_ERR_UNSUPPORTED";
+    case GEMM_EPI_ERR_HIP: return "GEMM_EPI_ERR_HIP";
+    case GEMM_EPI_ERR_NO_MEMORY: return "GEMM_EPI_ERR_NO_MEMORY";
+    default: return "GEMM_EPI_ERR_UNKNOWN";
+  }
+}
+
+int gemm_epi_last_hip_error(void) { return g_last_hip_error; }
+
+gemm_epi_status gemm_epi_plan_select(gemm_epi_plan_t plan, gemm_epi_kernel kernel, int config) {
+  if (!plan) return GEMM_EPI_ERR_INVALID_ARG;
+  if (kernel < GEMM_EPI_KERNEL_AUTO || kernel > GEMM_EPI_KERNEL_SKINNY) return GEMM_EPI_ERR_INVALID_ARG;
+  const int n = gemm_epi_num_configs(kernel);
+  if (config < -1 || (kernel != GEMM_EPI_KERNEL_AUTO && config >= n)) return GEMM_EPI_ERR_INVALID_ARG;
+  gemm_epi_plan_s trial = *plan;
+  if (!resolve(&trial, kernel, kernel == GEMM_EPI_KERNEL_AUTO ? -1 : config)) return GEMM_EPI_ERR_UNSUPPORTED;
+  *plan = trial;
+  return GEMM_EPI_OK;
+}
+
+int gemm_epi_num_configs(gemm_epi_kernel kernel) {
+  switch (kernel) {
+    case GEMM_EPI_KERNEL_GENERIC: return 1;
+    case GEMM_EPI_KERNEL_TILE: return ge::tile_num_configs();
+    case GEMM_EPI_KERNEL_SKINNY: return ge::skinny_num_configs();
+    default: return 0;
+  }
+}
+
+const char* gemm_epi_plan_describe(gemm_epi_plan_t plan, gemm_epi_kernel* kernel, int* config) {
+  if (!plan) return nullptr;
+  if (kernel) *kernel = (gemm_epi_kernel)plan->kernel;
+  if (config) *config = plan->config;
+  return plan->name;
+}
+
+}  // extern "C"

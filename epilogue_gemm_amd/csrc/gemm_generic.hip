@@ -1,0 +1,73 @@
+// gemm_generic.hip -- correctness anchor: one thread per output element,
+// fp32 fused multiply-add over k, the fp32 epilogue, one store.  Handles any
+// M, N, K, either layout of A and B and any pointer alignment.  Slow by
+// design; the plan uses it only where the fast kernels do not apply.
+//
+// A product of two fp16 (11-bit significands) or two bf16 (8-bit) values is
+// exact in fp32, so each fma adds an exact product to the running sum.
+#include "kernels.hpp"
+
+namespace ge {
+namespace {
+
+constexpr int kGenThreadsX = 64;  // along N: a wave reads/writes consecutive columns
+constexpr int kGenThreadsY = 4;   // along M
+
+template <typename TIn, typename TOut, int EPI>
+__global__ __launch_bounds__(256) void gemm_generic_kernel(const TIn* __restrict__ A, const TIn* __restrict__ B,
+                                                           const TIn* __restrict__ bias, TOut* __restrict__ C,
+                                                           int64_t M, int64_t N, int64_t K, int la, int lb) {
+  const int64_t j = (int64_t)blockIdx.x * kGenThreadsX + (threadIdx.x % kGenThreadsX);
+  if (j >= N) return;
+  const int64_t i_step = (int64_t)gridDim.y * kGenThreadsY;
+  for (int64_t i = (int64_t)blockIdx.y * kGenThreadsY + threadIdx.x / kGenThreadsX; i < M; i += i_step) {
+    // element strides of a(i, k) and b(k, j) along k
+    const TIn* pa = la == GEMM_EPI_ROW_MAJOR ? A + i * K : A + i;
+    const int64_t sa = la == GEMM_EPI_ROW_MAJOR ? 1 : M;
+    const TIn* pb = lb == GEMM_EPI_ROW_MAJOR ? B + j : B + j * K;
+    const int64_t sb = lb == GEMM_EPI_ROW_MAJOR ? N : 1;
+    float acc = 0.0f;
+    for (int64_t k = 0; k < K; ++k) acc = __builtin_fmaf(to_f32(pa[k * sa]), to_f32(pb[k * sb]), acc);
+    float b = 0.0f;
+    if constexpr (epi_has_bias<EPI>()) b = to_f32(bias[j]);
+    C[i * N + j] = from_f32<TOut>(epilogue<EPI>(acc, b));
+  }
+}
+
+template <typename TIn, typename TOut, int EPI>
+hipError_t launch_generic(const LaunchArgs& a) {
+  const int64_t gx = ((int64_t)a.N + kGenThreadsX - 1) / kGenThreadsX;
+  int64_t gy = ((int64_t)a.M + kGenThreadsY - 1) / kGenThreadsY;
+  if (gy > 65535) gy = 65535;
+  hipLaunchKernelGGL((gemm_generic_kernel<TIn, TOut, EPI>), dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, a.stream,
+                     (const TIn*)a.A, (const TIn*)a.B, (const TIn*)a.bias, (TOut*)a.C, (int64_t)a.M, (int64_t)a.N,
+                     (int64_t)a.K, a.la, a.lb);
+  return hipGetLastError();
+}
+
+template <typename TIn, typename TOut>
+LaunchFn pick_epi(int epi) {
+  switch (epi) {
+    case GEMM_EPI_NONE: return &launch_generic<TIn, TOut, GEMM_EPI_NONE>;
+    case GEMM_EPI_RELU: return &launch_generic<TIn, TOut, GEMM_EPI_RELU>;
+    case GEMM_EPI_BIAS_RELU: return &launch_generic<TIn, TOut, GEMM_EPI_BIAS_RELU>;
+    case GEMM_EPI_BIAS_GELU: return &launch_generic<TIn, TOut, GEMM_EPI_BIAS_GELU>;
+    case GEMM_EPI_BIAS: return &launch_generic<TIn, TOut, GEMM_EPI_BIAS>;
+    default: return nullptr;
+  }
+}
+
+}  // namespace
+
+LaunchFn generic_launcher(const Problem& p) {
+  if (p.in_dt == GEMM_EPI_F16) {
+    if (p.out_dt == GEMM_EPI_F16) return pick_epi<f16, f16>(p.epi);
+    if (p.out_dt == GEMM_EPI_F32) return pick_epi<f16, float>(p.epi);
+  } else if (p.in_dt == GEMM_EPI_BF16) {
+    if (p.out_dt == GEMM_EPI_BF16) return pick_epi<bf16, bf16>(p.epi);
+    if (p.out_dt == GEMM_EPI_F32) return pick_epi<bf16, float>(p.epi);
+  }
+  return nullptr;
+}
+
+}  // namespace ge

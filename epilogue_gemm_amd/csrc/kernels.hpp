@@ -1,0 +1,46 @@
+// kernels.hpp -- host-side view of the three kernel families: their
+// configuration tables, the divisibility each one needs, and the launch
+// entry each .hip file exports.
+#pragma once
+
+#include "common.hpp"
+
+namespace ge {
+
+using LaunchFn = hipError_t (*)(const LaunchArgs&);
+
+struct Problem {
+  int64_t M, N, K;
+  int in_dt, out_dt, la, lb, epi;
+};
+
+// ---- generic: any shape, layout and alignment -----------------------------
+// Extra LaunchArgs fields it needs are the layouts (passed through `Problem`).
+LaunchFn generic_launcher(const Problem& p);
+
+// ---- tile: LDS-pipelined MFMA kernel --------------------------------------
+struct TileConfig {
+  int bm, bn;  // workgroup tile; bk is 64 for every config
+  const char* name;
+};
+int tile_num_configs();
+const TileConfig& tile_config(int cfg);
+bool tile_supports(int cfg, const Problem& p);
+int tile_choose(const Problem& p);  // -1 when no config fits
+LaunchFn tile_launcher(int cfg, const Problem& p);
+// per input format, one translation unit each
+LaunchFn tile_launcher_f16(int cfg, int out_dt, int la, int lb);
+LaunchFn tile_launcher_bf16(int cfg, int out_dt, int la, int lb);
+
+// ---- skinny: weight-streaming kernel for M <= 32 --------------------------
+struct SkinnyConfig {
+  int waves;  // waves per workgroup; each owns a contiguous K range
+  const char* name;
+};
+int skinny_num_configs();
+const SkinnyConfig& skinny_config(int cfg);
+bool skinny_supports(int cfg, const Problem& p);
+int skinny_choose(const Problem& p);
+LaunchFn skinny_launcher(int cfg, const Problem& p);
+
+}  // namespace ge

@@ -1,0 +1,142 @@
+/*
+ * gemm_epi.h -- C ABI of the MI355X (gfx950) GEMM with a fused epilogue:
+ *
+ *     C = act(A . B [+ bias])        fp16/bf16 inputs, fp32 accumulation
+ *
+ * The operation is the tiled GEMM whose epilogue (bias add, then ReLU or
+ * GELU) runs on the fp32 accumulators before the single store of C:
+ *   - GEMM definition and the fp16/bf16-in, fp32-accumulate, convert-on-output
+ *     data flow: csdn "从零开始学习 TileLang" tutorial, ch.10 "GEMM 矩阵乘法",
+ *     sec. 10.1 and 10.6;
+ *   - epilogue on the accumulator before write-back (bias then ReLU):
+ *     same chapter, sec. 10.8 "GEMM Epilogue 融合";
+ *   - C = ReLU(A @ B): atlascloud.ai "Writing high-performance kernels in
+ *     TileLang", section "Écrivons un GEMM";
+ *   - C = GELU_tanh(A @ B + bias): ainew.jp "TileLang で GPU カーネル設計を解説",
+ *     section 4 "EPILOGUE FUSION";
+ *   - a row-major A with a column-major B and an fp32 C: TileFusion
+ *     "基础GEMM示例" (xdnf.cn repost).
+ *
+ * Plain C: no HIP, torch or C++ types appear here.  Device buffers are plain
+ * device pointers owned by the caller; the stream is a hipStream_t passed as
+ * void* (NULL = the null stream).
+ *
+ * Errors never abort: every call returns a gemm_epi_status.
+ */
+#ifndef GEMM_EPI_H
+#define GEMM_EPI_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element formats.  F32 is an output format only. */
+typedef enum gemm_epi_dtype {
+  GEMM_EPI_F16 = 0,  /* IEEE binary16 */
+  GEMM_EPI_BF16 = 1, /* bfloat16 (top half of binary32) */
+  GEMM_EPI_F32 = 2   /* IEEE binary32 */
+} gemm_epi_dtype;
+
+/* Storage order of an R x C operand: ROW_MAJOR puts (r, c) at r*C + c,
+ * COL_MAJOR at c*R + r.  For B (logical K x N), COL_MAJOR is the N x K
+ * "weight" layout with K contiguous.  C is always row-major M x N. */
+typedef enum gemm_epi_layout { GEMM_EPI_ROW_MAJOR = 0, GEMM_EPI_COL_MAJOR = 1 } gemm_epi_layout;
+
+/* Epilogue applied to the fp32 accumulator z before conversion:
+ *   NONE       C = z
+ *   RELU       C = max(z, 0)
+ *   BIAS_RELU  C = max(z + bias[n], 0)
+ *   BIAS_GELU  C = g(z + bias[n]),  g(x) = x / (1 + exp(-1.5957691216 (x + 0.044715 x^3)))
+ *              (the tanh form of GELU written as a logistic)
+ *   BIAS       C = z + bias[n]
+ * bias has N elements of the input format, broadcast over rows, and is
+ * added before the activation. */
+typedef enum gemm_epi_epilogue {
+  GEMM_EPI_NONE = 0,
+  GEMM_EPI_RELU = 1,
+  GEMM_EPI_BIAS_RELU = 2,
+  GEMM_EPI_BIAS_GELU = 3,
+  GEMM_EPI_BIAS = 4
+} gemm_epi_epilogue;
+
+typedef enum gemm_epi_status {
+  GEMM_EPI_OK = 0,
+  GEMM_EPI_ERR_INVALID_ARG = 1, /* null/ill-formed argument, bad enum, bad size */
+  GEMM_EPI_ERR_UNSUPPORTED = 2, /* well-formed, but no kernel handles it */
+  GEMM_EPI_ERR_HIP = 3,         /* the HIP runtime reported an error (see gemm_epi_last_hip_error) */
+  GEMM_EPI_ERR_NO_MEMORY = 4    /* host allocation of the plan failed */
+} gemm_epi_status;
+
+/* Kernel families.  AUTO lets the plan choose. */
+typedef enum gemm_epi_kernel {
+  GEMM_EPI_KERNEL_AUTO = 0,
+  GEMM_EPI_KERNEL_GENERIC = 1, /* any shape, layout and alignment; correctness anchor */
+  GEMM_EPI_KERNEL_TILE = 2,    /* LDS-pipelined MFMA tile kernel (compute-bound shapes) */
+  GEMM_EPI_KERNEL_SKINNY = 3   /* weight-streaming kernel for M <= 32 (HBM-bound shapes) */
+} gemm_epi_kernel;
+
+typedef struct gemm_epi_plan_s* gemm_epi_plan_t;
+
+/* gemm_epi_plan -- validate a problem and choose its kernel.
+ *
+ * A is M x K in layout_a, B is K x N in layout_b, C is M x N row-major,
+ * all packed (leading dimension = the contiguous extent).
+ * in_dtype in {F16, BF16}; out_dtype in {in_dtype, F32}.
+ * Host only: no device allocation, no launch, no HIP call; allocates the
+ * small host plan object only.  *out is written only on GEMM_EPI_OK.
+ * Errors: INVALID_ARG (out == NULL, M/N/K <= 0, unknown enum, out_dtype
+ * not allowed), UNSUPPORTED (any of M*K, K*N, M*N >= 2^31 elements),
+ * NO_MEMORY. */
+gemm_epi_status gemm_epi_plan(gemm_epi_plan_t* out, int64_t M, int64_t N, int64_t K, gemm_epi_dtype in_dtype,
+                              gemm_epi_dtype out_dtype, gemm_epi_layout layout_a, gemm_epi_layout layout_b,
+                              gemm_epi_epilogue epilogue);
+
+/* gemm_epi_run -- enqueue C = act(A.B [+ bias]) on `stream` and return
+ * without synchronising.
+ *
+ * A, B, bias, C are device pointers owned by the caller, who keeps them
+ * alive until the stream has passed the kernel.  bias must be non-NULL
+ * exactly when the epilogue uses it.  C must not overlap A, B or bias.
+ * A plan is immutable during run, so concurrent runs of one plan on
+ * different streams are safe.  Pointers that are not 16-byte aligned send
+ * the call to the generic kernel.
+ * Errors: INVALID_ARG (plan NULL, a required pointer NULL, bias given
+ * without a bias epilogue), HIP (the launch failed; the code is kept per
+ * thread for gemm_epi_last_hip_error). */
+gemm_epi_status gemm_epi_run(gemm_epi_plan_t plan, const void* A, const void* B, const void* bias, void* C,
+                             void* stream);
+
+/* gemm_epi_destroy -- free the host plan object.  NULL is a no-op (OK).
+ * No device synchronisation: runs already enqueued are unaffected. */
+gemm_epi_status gemm_epi_destroy(gemm_epi_plan_t plan);
+
+/* Static, NUL-terminated name of a status code. */
+const char* gemm_epi_status_string(gemm_epi_status status);
+
+/* hipError_t of the calling thread's last failed HIP call (0 if none). */
+int gemm_epi_last_hip_error(void);
+
+/* gemm_epi_plan_select -- force a kernel family and configuration index
+ * (for tests and tuning).  kernel = AUTO restores the plan's own choice
+ * and ignores config.  Otherwise config indexes that family's table
+ * (0 .. gemm_epi_num_configs-1), and -1 lets the family choose.
+ * Errors: INVALID_ARG (NULL plan, bad enum or index), UNSUPPORTED (the
+ * family cannot run this problem: its shape, layout or divisibility
+ * requirements are not met; the plan is then unchanged). */
+gemm_epi_status gemm_epi_plan_select(gemm_epi_plan_t plan, gemm_epi_kernel kernel, int config);
+
+/* Number of configurations of a kernel family (0 for AUTO or unknown). */
+int gemm_epi_num_configs(gemm_epi_kernel kernel);
+
+/* The kernel family and configuration the plan will launch for 16-byte
+ * aligned pointers; either out pointer may be NULL.  Returns the family's
+ * static name (e.g. "tile_256x256x64"), or NULL for a NULL plan. */
+const char* gemm_epi_plan_describe(gemm_epi_plan_t plan, gemm_epi_kernel* kernel, int* config);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GEMM_EPI_H */

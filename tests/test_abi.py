@@ -1,0 +1,136 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every function include/gemm_epi.h declares, and gemm_epi_plan's validation
+and kernel selection behave as the header documents.  gemm_epi_plan makes
+no HIP call, so all of this runs on a machine without a GPU."""
+import ctypes
+import os
+import subprocess
+
+import pytest
+
+from epilogue_gemm_amd import binding as gb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(gb.LIB_PATH):
+        pytest.fail("libgemm_epi.so is not built (run __graft_entry__.build())")
+    return gb.load_library()
+
+
+def test_exports_every_declared_function(lib):
+    declared = gb.header_functions()
+    assert len(declared) >= 8
+    out = subprocess.run(["nm", "-D", "--defined-only", gb.LIB_PATH], capture_output=True, text=True, check=True)
+    exported = {line.split()[-1] for line in out.stdout.splitlines() if line.strip()}
+    missing = [f for f in declared if f not in exported]
+    assert not missing, missing
+    for f in declared:
+        assert hasattr(lib, f)
+
+
+def test_header_is_plain_c():
+    # the header must compile as C with no HIP or C++ headers
+    src = os.path.join(ROOT, "include", "gemm_epi.h")
+    r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-fsyntax-only", "-x", "c", src], capture_output=True,
+                       text=True)
+    assert r.returncode == 0, r.stderr
+
+
+def test_status_strings(lib):
+    for code, name in gb.STATUS.items():
+        assert gb.gemm_epi_status_string(code) == "GEMM_EPI_" + name
+    assert gb.gemm_epi_status_string(99) == "GEMM_EPI_ERR_UNKNOWN"
+    assert gb.gemm_epi_last_hip_error() == 0
+
+
+def test_plan_rejects_invalid_arguments(lib):
+    ok = dict(M=64, N=64, K=64, in_dtype="f16", out_dtype="f16", layout_a="row", layout_b="row", epilogue="none")
+    assert gb.gemm_epi_plan_status(**ok) == 0
+    for k, v in [("M", 0), ("N", -1), ("K", 0)]:
+        assert gb.gemm_epi_plan_status(**{**ok, k: v}) == 1
+    assert gb.gemm_epi_plan_status(**{**ok, "in_dtype": "f32", "out_dtype": "f32"}) == 1  # f32 input
+    assert gb.gemm_epi_plan_status(**{**ok, "out_dtype": "bf16"}) == 1  # mixed 16-bit formats
+    raw = [0, 0, 0, 0, 0]
+    for pos, bad in [(0, 7), (1, 9), (2, 2), (3, -1), (4, 5)]:
+        args = list(raw)
+        args[pos] = bad
+        assert gb.gemm_epi_plan_status(64, 64, 64, *args, raw=True) == 1
+    # null out pointer
+    assert lib.gemm_epi_plan(None, 64, 64, 64, 0, 0, 0, 0, 0) == 1
+
+
+def test_plan_rejects_oversized(lib):
+    big = 1 << 31
+    assert gb.gemm_epi_plan_status(big, 1, 1, "f16", "f16", "row", "row", "none") == 2
+    assert gb.gemm_epi_plan_status(65536, 32768, 1, "f16", "f16", "row", "row", "none") == 2  # M*N = 2^31
+    assert gb.gemm_epi_plan_status(46340, 46340, 1, "f16", "f16", "row", "row", "none") == 0
+
+
+def test_run_rejects_invalid_arguments_without_touching_the_device(lib):
+    h = gb.gemm_epi_plan(64, 64, 64, "bf16", "bf16", "row", "col", "bias_gelu")
+    try:
+        p = 0x1000
+        assert gb.gemm_epi_run(None, p, p, p, p, None) == 1  # null plan
+        assert gb.gemm_epi_run(h, None, p, p, p, None) == 1  # null A
+        assert gb.gemm_epi_run(h, p, p, None, p, None) == 1  # bias epilogue without bias
+        assert gb.gemm_epi_run(h, p, p, p, None, None) == 1  # null C
+    finally:
+        gb.gemm_epi_destroy(h)
+    h = gb.gemm_epi_plan(64, 64, 64, "f16", "f16", "row", "row", "relu")
+    try:
+        assert gb.gemm_epi_run(h, 0x1000, 0x1000, 0x1000, 0x1000, None) == 1  # bias without a bias epilogue
+    finally:
+        gb.gemm_epi_destroy(h)
+    assert gb.gemm_epi_destroy(None) == 0
+
+
+@pytest.mark.parametrize("M,N,K,la,lb,want_kernel,want_name", [
+    (8192, 8192, 8192, "row", "col", "tile", "tile_256x256x64"),
+    (4096, 4096, 4096, "row", "row", "tile", "tile_256x256x64"),
+    (1024, 1024, 1024, "row", "row", "tile", "tile_64x64x64"),
+    (128, 64, 256, "row", "col", "tile", "tile_64x64x64"),
+    (32, 8192, 8192, "row", "col", "skinny", "skinny_32n_16waves"),
+    (1, 4096, 4096, "row", "col", "skinny", "skinny_32n_16waves"),
+    (32, 8192, 8192, "row", "row", "generic", "generic"),  # small M, N-contiguous B: no fast path yet
+    (37, 53, 29, "row", "row", "generic", "generic"),
+    (256, 256, 100, "col", "row", "generic", "generic"),  # K not a multiple of 64
+])
+def test_auto_selection(lib, M, N, K, la, lb, want_kernel, want_name):
+    h = gb.gemm_epi_plan(M, N, K, "bf16", "bf16", la, lb, "none")
+    try:
+        kern, cfg, name = gb.gemm_epi_plan_describe(h)
+        assert (kern, name) == (want_kernel, want_name)
+    finally:
+        gb.gemm_epi_destroy(h)
+
+
+def test_select_forces_and_validates(lib):
+    h = gb.gemm_epi_plan(512, 512, 256, "f16", "f32", "row", "col", "none")
+    try:
+        assert gb.gemm_epi_num_configs("tile") == 3
+        assert gb.gemm_epi_num_configs("skinny") == 3
+        assert gb.gemm_epi_num_configs("generic") == 1
+        assert gb.gemm_epi_num_configs("auto") == 0
+        for cfg in range(3):
+            assert gb.gemm_epi_plan_select(h, "tile", cfg) == 0
+            assert gb.gemm_epi_plan_describe(h)[:2] == ("tile", cfg)
+        assert gb.gemm_epi_plan_select(h, "generic", 0) == 0
+        assert gb.gemm_epi_plan_describe(h)[0] == "generic"
+        assert gb.gemm_epi_plan_select(h, "skinny", -1) == 2  # M = 512 > 32: unsupported, plan unchanged
+        assert gb.gemm_epi_plan_describe(h)[0] == "generic"
+        assert gb.gemm_epi_plan_select(h, "tile", 3) == 1  # no such config
+        assert lib.gemm_epi_plan_select(ctypes.c_void_p(h), 9, 0) == 1  # bad enum
+        assert gb.gemm_epi_plan_select(h, "auto", -1) == 0
+        assert gb.gemm_epi_plan_describe(h) == ("tile", 2, "tile_64x64x64")  # 64 workgroups beats 16
+    finally:
+        gb.gemm_epi_destroy(h)
+    h = gb.gemm_epi_plan(32, 128, 1024, "bf16", "bf16", "row", "col", "bias")
+    try:
+        assert gb.gemm_epi_plan_describe(h)[:2] == ("skinny", 0)
+        assert gb.gemm_epi_plan_select(h, "skinny", 1) == 0
+        assert gb.gemm_epi_plan_select(h, "tile", -1) == 2  # M = 32 not a multiple of 64
+    finally:
+        gb.gemm_epi_destroy(h)

@@ -1,0 +1,198 @@
+"""Parity of the HIP library (through its C ABI) with the CPU oracle.
+
+  * integer-valued operands: every product and partial sum is an exact
+    small integer in fp32, so for none/ReLU/bias/bias+ReLU the GPU output
+    must equal the oracle's bit for bit, whatever the accumulation order;
+    this pins indexing, layouts, swizzles, pipelining and rasterisation;
+  * N(0,1)-type operands at sizes that span several tiles, and the five
+    workloads at full size in the launch configuration the benchmark
+    times (outputs sampled where the full oracle would take too long):
+    relative Frobenius error <= 1e-3 and max error <= 2e-2 after output
+    rounding (tests/parity.py states the one-ulp tie rule).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from epilogue_gemm_amd import binding as gb
+from epilogue_gemm_amd import inputs
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+EPIS = ["none", "relu", "bias", "bias_relu", "bias_gelu"]
+BITWISE_EPIS = {"none", "relu", "bias", "bias_relu"}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    gb.load_library()
+    torch.cuda.init()
+
+
+def run_gpu(bits, M, N, K, in_dt, out_dt, la, lb, epi, kernel="auto", config=-1, offset=0):
+    """Runs one problem through the library; `offset` shifts every device
+    pointer by that many elements (to test unaligned pointers)."""
+    def dev(b):
+        if b is None:
+            return None
+        t = parity.to_device(np.concatenate([np.zeros(offset, np.uint16), b.reshape(-1)]), in_dt)
+        return t[offset:]
+
+    A, B, bias = dev(bits["A"]), dev(bits["B"]), dev(bits["bias"])
+    Cfull = parity.empty_out(M * N + offset, out_dt)
+    C = Cfull[offset:]
+    C.fill_(float("nan"))
+    plan = gb.Plan(M, N, K, in_dt, out_dt, la, lb, epi, kernel, config)
+    st = gb.gemm_epi_run(plan.handle, A.data_ptr(), B.data_ptr(), bias.data_ptr() if bias is not None else None,
+                         C.data_ptr(), torch.cuda.current_stream().cuda_stream)
+    assert st == 0, gb.gemm_epi_status_string(st)
+    torch.cuda.synchronize()
+    name = plan.name
+    plan.close()
+    return parity.out_bits(C), name
+
+
+def oracle_full(bits, M, N, K, in_dt, out_dt, la, lb, epi):
+    return oracle.gemm_epi(bits["A"], bits["B"], bits["bias"], M, N, K, in_dt, out_dt, la, lb, epi)
+
+
+def check_case(bits, M, N, K, in_dt, out_dt, la, lb, epi, kernel, config, bitwise, offset=0):
+    got, name = run_gpu(bits, M, N, K, in_dt, out_dt, la, lb, epi, kernel, config, offset)
+    y, c = oracle_full(bits, M, N, K, in_dt, out_dt, la, lb, epi)
+    if bitwise:
+        mism = np.count_nonzero(got.reshape(-1) != c.reshape(-1).astype(got.dtype))
+        assert mism == 0, f"{name}: {mism} of {got.size} outputs differ from the oracle bit pattern"
+    else:
+        r = parity.compare(got, c, y, out_dt)
+        assert r["ok"], f"{name}: {r}"
+    return name
+
+
+# ---------------------------------------------------------------------------
+# integer operands: bit-exact
+# ---------------------------------------------------------------------------
+
+TILE_SHAPES = {0: (512, 512, 192), 1: (256, 384, 128), 2: (192, 128, 320)}
+
+
+@pytest.mark.parametrize("config", [0, 1, 2])
+@pytest.mark.parametrize("la,lb", [("row", "col"), ("row", "row"), ("col", "col"), ("col", "row")])
+@pytest.mark.parametrize("in_dt,out_dt", [("f16", "f16"), ("bf16", "bf16"), ("f16", "f32"), ("bf16", "f32")])
+def test_tile_integer_bitexact(config, la, lb, in_dt, out_dt):
+    M, N, K = TILE_SHAPES[config]
+    epis = EPIS if (la, lb) in (("row", "col"), ("row", "row")) else ["bias_relu", "bias_gelu"]
+    for epi in epis:
+        bits = inputs.integer_inputs(M, N, K, in_dt, la, lb, epi.startswith("bias"), seed=config * 7 + len(epi))
+        name = check_case(bits, M, N, K, in_dt, out_dt, la, lb, epi, "tile", config, epi in BITWISE_EPIS)
+        assert name.startswith("tile_")
+
+
+@pytest.mark.parametrize("config", [0, 1, 2])
+@pytest.mark.parametrize("M", [1, 7, 31, 32])
+@pytest.mark.parametrize("in_dt,out_dt", [("bf16", "bf16"), ("f16", "f16"), ("bf16", "f32")])
+def test_skinny_integer_bitexact(config, M, in_dt, out_dt):
+    N, K = 96, 2048
+    for epi in EPIS:
+        bits = inputs.integer_inputs(M, N, K, in_dt, "row", "col", epi.startswith("bias"), seed=M + config)
+        name = check_case(bits, M, N, K, in_dt, out_dt, "row", "col", epi, "skinny", config, epi in BITWISE_EPIS)
+        assert name.startswith("skinny_")
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 1), (2, 8, 4), (37, 53, 29), (65, 130, 200), (3, 700, 5)])
+@pytest.mark.parametrize("la,lb", [("row", "col"), ("row", "row"), ("col", "col"), ("col", "row")])
+def test_generic_integer_bitexact(M, N, K, la, lb):
+    for in_dt, out_dt in [("f16", "f16"), ("bf16", "bf16"), ("bf16", "f32")]:
+        for epi in EPIS:
+            bits = inputs.integer_inputs(M, N, K, in_dt, la, lb, epi.startswith("bias"), seed=M * N + K)
+            check_case(bits, M, N, K, in_dt, out_dt, la, lb, epi, "generic", 0, epi in BITWISE_EPIS)
+
+
+# ---------------------------------------------------------------------------
+# random operands: tolerance
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("kernel,config,M,N,K,la,lb", [
+    ("tile", 0, 768, 1024, 512, "row", "col"),
+    ("tile", 0, 512, 768, 640, "row", "row"),
+    ("tile", 1, 384, 256, 1024, "row", "row"),
+    ("tile", 2, 320, 192, 448, "col", "col"),
+    ("skinny", 0, 32, 512, 4096, "row", "col"),
+    ("skinny", 2, 5, 160, 768, "row", "col"),
+    ("generic", 0, 97, 61, 333, "row", "row"),
+    ("generic", 0, 64, 64, 4096, "col", "col"),
+])
+@pytest.mark.parametrize("in_dt,out_dt,epi", [("bf16", "bf16", "bias_gelu"), ("f16", "f16", "relu"),
+                                              ("f16", "f32", "none"), ("bf16", "bf16", "bias")])
+def test_random_tolerance(kernel, config, M, N, K, la, lb, in_dt, out_dt, epi):
+    bits = inputs.make_inputs(M, N, K, in_dt, la, lb, epi.startswith("bias"), float(np.sqrt(K)), 0.1, seed=M + N)
+    check_case(bits, M, N, K, in_dt, out_dt, la, lb, epi, kernel, config, bitwise=False)
+
+
+def test_unaligned_pointers_use_generic_and_stay_correct():
+    M, N, K = 256, 256, 128
+    bits = inputs.make_inputs(M, N, K, "bf16", "row", "col", True, 11.0, 0.1, seed=5)
+    got_a, name_a = run_gpu(bits, M, N, K, "bf16", "bf16", "row", "col", "bias_gelu")
+    got_u, name_u = run_gpu(bits, M, N, K, "bf16", "bf16", "row", "col", "bias_gelu", offset=1)
+    assert name_a.startswith("tile_")
+    y, c = oracle_full(bits, M, N, K, "bf16", "bf16", "row", "col", "bias_gelu")
+    for got in (got_a, got_u):
+        r = parity.compare(got, c, y, "bf16")
+        assert r["ok"], r
+
+
+def test_run_is_deterministic():
+    M, N, K = 1024, 1024, 512
+    bits = inputs.make_inputs(M, N, K, "bf16", "row", "col", True, 22.0, 0.1, seed=6)
+    a, _ = run_gpu(bits, M, N, K, "bf16", "bf16", "row", "col", "bias_gelu", "tile", 0)
+    b, _ = run_gpu(bits, M, N, K, "bf16", "bf16", "row", "col", "bias_gelu", "tile", 0)
+    assert np.array_equal(a, b)
+
+
+def test_all_tile_configs_agree_on_integers():
+    # every tile configuration and the generic kernel give identical bits
+    M, N, K = 512, 512, 256
+    bits = inputs.integer_inputs(M, N, K, "f16", "row", "row", True, seed=8)
+    ref, _ = run_gpu(bits, M, N, K, "f16", "f16", "row", "row", "bias_relu", "generic", 0)
+    for cfg in range(gb.gemm_epi_num_configs("tile")):
+        got, _ = run_gpu(bits, M, N, K, "f16", "f16", "row", "row", "bias_relu", "tile", cfg)
+        assert np.array_equal(got, ref), cfg
+
+
+# ---------------------------------------------------------------------------
+# the five workloads at full size, auto-selected plan (what the benchmark runs)
+# ---------------------------------------------------------------------------
+
+def _sample_points(M, N, n, seed):
+    rng = np.random.default_rng(seed)
+    rows = rng.integers(0, M, n)
+    cols = rng.integers(0, N, n)
+    # plus one full row and one full column
+    rows = np.concatenate([rows, np.full(N, M // 3), np.arange(M)])
+    cols = np.concatenate([cols, np.arange(N), np.full(M, N // 5)])
+    return rows, cols
+
+
+@pytest.mark.parametrize("name", list(inputs.WORKLOADS))
+def test_workload_full_size(name):
+    w = inputs.WORKLOADS[name]
+    bits = inputs.workload_inputs(w)
+    print(f"[workload] {w.name}", flush=True)
+    got, kname = run_gpu(bits, w.M, w.N, w.K, w.in_dtype, w.out_dtype, w.layout_a, w.layout_b, w.epilogue)
+    got = got.reshape(w.M, w.N)
+    assert kname != "generic"
+    assert np.all(np.isfinite(parity.values(got.reshape(-1), w.out_dtype)))
+    if w.M * w.N * w.K <= 2**31:
+        y, c = oracle_full(bits, w.M, w.N, w.K, w.in_dtype, w.out_dtype, w.layout_a, w.layout_b, w.epilogue)
+        r = parity.compare(got, c, y, w.out_dtype)
+    else:
+        rows, cols = _sample_points(w.M, w.N, 8192, seed=w.seed)
+        y, c = oracle.gemm_epi_points(bits["A"], bits["B"], bits["bias"], w.M, w.N, w.K, w.in_dtype, w.out_dtype,
+                                      w.layout_a, w.layout_b, w.epilogue, rows, cols)
+        c = c.astype(np.uint16 if w.out_dtype != "f32" else np.uint32)
+        r = parity.compare(got[rows, cols], c, y, w.out_dtype)
+    print(f"[workload] {w.name} kernel={kname} {r}", flush=True)
+    assert r["ok"], r
