@@ -105,6 +105,9 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--only", choices=["main", "skinny", "both"], default="both")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="after timing, run a plain 1 GiB device copy (elementwise kernel) three times, so that "
+                         "HBM byte counters can be scaled against a kernel of known traffic")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print("bench.py measures one GPU only: the hot path is a single-GPU kernel "
@@ -145,6 +148,14 @@ def main(argv=None):
         plan.close()
         del sets
         torch.cuda.empty_cache()
+
+    if args.calib_copy:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)  # reads 1 GiB, writes 1 GiB
+        torch.cuda.synchronize()
+        del src, dst
 
     rec = {}
     if "main" in out:

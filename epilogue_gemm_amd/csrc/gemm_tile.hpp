@@ -1,35 +1,43 @@
 // gemm_tile.hpp -- the LDS-pipelined MFMA tile kernel for gfx950.
 //
-// One workgroup (256 threads = 4 waves of 64) computes a BM x BN tile of C.
-// Per k-step of 64:
-//   global -> registers   128-bit loads, coalesced along the operand's
-//                         contiguous index;
-//   registers -> LDS      into the stage not being read, with an XOR swizzle
-//                         of 16-byte chunks so that MFMA operand reads and the
-//                         stores hit distinct banks;
-//   LDS -> MFMA           each wave owns a (BM/2) x (BN/2) sub-tile made of
-//                         32x32 blocks and issues v_mfma_f32_32x32x16_{f16,bf16}
-//                         with fp32 accumulators.
-// Two LDS stages plus one register stage form a three-deep software pipeline:
-// while the waves multiply stage s, the loads for the next-but-one k-step are
-// in flight and the next k-step is being written into stage s^1.  One
-// workgroup barrier per k-step.
+// One workgroup (256 threads = 4 waves of 64) computes a BM x BN tile of C,
+// looping over k in steps of 64.  Both operands are staged in LDS in one
+// layout: rows along M (for A) or N (for B), 64 k values per row, k
+// contiguous, the 16-byte chunks of each row XOR-swizzled.  Each wave owns
+// a (BM/2) x (BN/2) sub-tile made of 32x32 blocks and feeds
+// v_mfma_f32_32x32x16_{f16,bf16} from LDS, accumulating in fp32.
+//
+// Getting a k-step into LDS:
+//   * an operand whose k index is contiguous in memory (A row-major, B
+//     column-major) is copied global -> LDS by 128-bit buffer loads that
+//     write LDS directly (no VGPR round trip, no LDS store instruction);
+//     each wave instruction fills 1 KiB = 8 rows, and each lane fetches the
+//     global chunk that belongs at its LDS position under the swizzle;
+//   * an operand whose M/N index is contiguous (A column-major, B row-major)
+//     is loaded 8 M/N-values wide for several k into registers, transposed
+//     in registers and written k-contiguous.
+//
+// Pipeline: two LDS stages, statically distinct (the loop is unrolled by
+// two) so the compiler can tell a read of one stage from an in-flight
+// direct load into the other.  In k-step kt (tile kt in stage s):
+//   substeps 0..2  multiply, read the next substep's fragments, and for a
+//                  register-staged operand write tile kt+1 into stage s^1
+//                  and refill its registers with tile kt+2;
+//   barrier        after waiting for this wave's direct loads of tile kt+1;
+//   substep 3      multiply, read substep 0 of stage s^1, and issue the
+//                  direct loads of tile kt+2 into stage s, which every wave
+//                  finished reading before the barrier.
+// Every MFMA slot carries an explicit share of the memory instructions;
+// slots are fenced so the issue order is the one written here.
 //
 // After the k loop the epilogue (bias add, then ReLU or GELU) runs on the
 // fp32 accumulators and each lane writes four consecutive outputs of one row
 // with one vector store: the kernel never writes an intermediate tensor.
 // (Tile-level fusion of load -> GEMM -> activation -> store: TileFusion
 // "基础GEMM示例"; epilogue on the fragment before write-back: csdn
-// "从零开始学习 TileLang" ch.10 sec. 10.8; block rasterisation for L2 reuse:
-// atlascloud.ai "Writing high-performance kernels in TileLang", section
-// "Écrivons un GEMM".)
-//
-// Both operands reach LDS in one layout: rows along M (for A) or N (for B),
-// 64 k values per row, k contiguous.  An operand whose k index is contiguous
-// in memory (A row-major, B column-major) is copied 16 bytes at a time.  An
-// operand whose M/N index is contiguous (A column-major, B row-major) is
-// loaded as 8-wide rows along M/N for several k, transposed in registers,
-// and written k-contiguous.
+// "从零开始学习 TileLang" ch.10 sec. 10.8; software pipelining and block
+// rasterisation for L2 reuse: atlascloud.ai "Writing high-performance kernels
+// in TileLang", section "Écrivons un GEMM".)
 //
 // The MFMA is issued with B's fragment as the first operand and A's as the
 // second, so the 32x32 result block arrives transposed: lane l holds
@@ -54,65 +62,92 @@ constexpr int kThreads = 256;
 // (t = 0..7) and get positions c ^ j ^ t, again distinct.
 __device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
 
-template <int R, bool KMAJ>
-struct Loader;
+// Buffer resource over [base, base + bytes): 128-bit raw buffer loads then
+// take one per-lane 32-bit offset plus one wave-uniform offset, so the loop
+// carries no 64-bit addresses.  Offsets at or past `bytes` read as zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
 
-// k-contiguous operand: row r of the tile is X[(r0 + r) * ld + k].
+__device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+// s_waitcnt immediate that waits until at most n vector-memory operations
+// of this wave are outstanding (LDS and export counters unconstrained).
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+// k-contiguous operand, global -> LDS directly.  Row r of the tile is
+// X[(r0 + r) * ld + k].  Instruction i of wave w fills tile rows
+// (4 i + w) * 8 .. +7; lane L writes LDS bytes 16 L .. 16 L + 15 of that
+// KiB, i.e. row (4 i + w) * 8 + L / 8 at chunk position L % 8, so it loads
+// logical chunk (L % 8) ^ swz(row).  Since swz depends on the row only
+// through (L / 8) ^ w ^ 4 (i & 1), two per-lane offsets (even and odd i)
+// cover every instruction; the rest of the offset is wave-uniform.
 template <int R>
-struct Loader<R, true> {
-  static constexpr int CH = R * kBK / 8 / kThreads;  // 16-byte chunks per thread
-  const char* g;
-  int64_t chunk_row_step;  // bytes between this thread's consecutive chunks (32 rows)
-  u32x4 r[CH];
+struct DirectLoader {
+  static constexpr int NI = R / 32;  // wave instructions per wave per k-step
+  __amdgpu_buffer_rsrc_t rsrc;
+  uint32_t voff[2];
+  uint32_t rows64;  // bytes of 64 rows
+  int wave;
 
-  __device__ __forceinline__ Loader(const void* X, int r0, int ld, int tid) {
-    g = (const char*)X + ((int64_t)(r0 + (tid >> 3)) * ld + (tid & 7) * 8) * 2;
-    chunk_row_step = (int64_t)32 * ld * 2;
-  }
-  __device__ __forceinline__ void load(int kt) {
-    const char* p = g + (int64_t)kt * kRowBytes;
+  __device__ __forceinline__ DirectLoader(const void* X, int r0, int rows_total, int ld, int tid, int wave_) {
+    const char* base = (const char*)X + (int64_t)r0 * ld * 2;
+    rsrc = make_rsrc(base, (uint32_t)((int64_t)(rows_total - r0) * ld * 2));
+    wave = wave_;
+    const int lane = tid & 63;
+    const int rl = lane >> 3, pc = lane & 7;
 #pragma unroll
-    for (int i = 0; i < CH; ++i) r[i] = *(const u32x4*)(p + i * chunk_row_step);
-  }
-  __device__ __forceinline__ void store(char* s, int tid) const {
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int row = i * 32 + (tid >> 3);
-      *(u32x4*)(s + row * kRowBytes + (((tid & 7) ^ swz(row)) << 4)) = r[i];
+    for (int p = 0; p < 2; ++p) {
+      const int row = (4 * p + wave) * 8 + rl;
+      voff[p] = (uint32_t)(row * ld * 2 + ((pc ^ rl ^ wave ^ (4 * p)) << 4));
     }
+    rows64 = (uint32_t)(64 * ld * 2);
+  }
+  // Issue instruction i of k-step kt into the operand region `dst` of a stage.
+  __device__ __forceinline__ void issue(char* dst, int kt, int i) const {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr)(dst + (4 * i + wave) * 1024), 16, voff[i & 1],
+                                             (i >> 1) * rows64 + kt * kRowBytes, 0, 0);
   }
 };
 
-// M/N-contiguous operand: row r of the tile (an M or N index) at k is
-// X[k * ld + r0 + r].  Each thread loads KB k-rows of 8 consecutive M/N
-// values and writes, for each of the 8, its KB k-values contiguously.
+// M/N-contiguous operand through registers: row r of the tile (an M or N
+// index) at k is X[k * ld + r0 + r].  Each thread loads KB k-rows of 8
+// consecutive M/N values and writes, for each of the 8, its KB k-values
+// contiguously.
 template <int R>
-struct Loader<R, false> {
+struct RegLoader {
   static constexpr int KB = R / 32;  // k values per thread: 8, 4 or 2
   static constexpr int NG = R / 8;   // 8-wide groups along M/N
   static_assert(KB >= 2 && KB <= 8, "tile extent");
-  const char* g;
-  int64_t kstep;  // bytes between consecutive k rows
+  static constexpr int LOADS = KB;
+  __amdgpu_buffer_rsrc_t rsrc;
+  uint32_t voff;
+  uint32_t kstep;  // bytes between consecutive k rows
   int ng, kg;
   u32x4 r[KB];
 
-  __device__ __forceinline__ Loader(const void* X, int r0, int ld, int tid) {
+  __device__ __forceinline__ RegLoader(const void* X, int r0, int k_total, int ld, int tid) {
     ng = tid % NG;
     kg = tid / NG;
-    kstep = (int64_t)ld * 2;
-    g = (const char*)X + ((int64_t)kg * KB * ld + r0 + ng * 8) * 2;
+    kstep = (uint32_t)(ld * 2);
+    const char* base = (const char*)X + (int64_t)r0 * 2;
+    rsrc = make_rsrc(base, (uint32_t)((int64_t)k_total * ld * 2 - (int64_t)r0 * 2));
+    voff = (uint32_t)(kg * KB * ld * 2 + ng * 16);
   }
   __device__ __forceinline__ void load(int kt) {
-    const char* p = g + (int64_t)kt * kBK * kstep;
 #pragma unroll
-    for (int i = 0; i < KB; ++i) r[i] = *(const u32x4*)(p + i * kstep);
+    for (int i = 0; i < KB; ++i) r[i] = load16(rsrc, voff, (uint32_t)(kt * kBK + i) * kstep);
   }
   // 16-bit element j (0..7) of a 128-bit register
   static __device__ __forceinline__ uint32_t half_of(const u32x4& v, int j) {
     const uint32_t w = v[j >> 1];
     return (j & 1) ? (w >> 16) : (w & 0xffffu);
   }
-  __device__ __forceinline__ void store(char* s, int) const {
+  __device__ __forceinline__ void store(char* s) const {
     const int k0 = kg * KB;
     const int c = k0 >> 3;
     const int inner = (k0 & 7) * 2;
@@ -182,23 +217,38 @@ __global__ __launch_bounds__(kThreads) void gemm_tile_kernel(const TIn* __restri
   constexpr int WM = BM / 2, WN = BN / 2;  // wave sub-tile
   constexpr int TM = WM / 32, TN = WN / 32;
   constexpr int A_BYTES = BM * kRowBytes, B_BYTES = BN * kRowBytes;
-  constexpr int STAGE = A_BYTES + B_BYTES;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+  // One array per operand and stage, so that every access names its stage
+  // statically (and A's stages sit within reach of one 16-bit immediate
+  // offset of each other, as do B's).
+  __shared__ __attribute__((aligned(1024))) char sA0[A_BYTES];
+  __shared__ __attribute__((aligned(1024))) char sA1[A_BYTES];
+  __shared__ __attribute__((aligned(1024))) char sB0[B_BYTES];
+  __shared__ __attribute__((aligned(1024))) char sB1[B_BYTES];
+  struct Stage {
+    char* a;
+    char* b;
+  };
+  const Stage stage0{sA0, sB0}, stage1{sA1, sB1};
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
 
   int tm, tn;
   raster(blockIdx.x, tiles_m, tiles_n, panel, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
 
-  Loader<BM, A_KMAJ> la(A, m0, A_KMAJ ? K : M, tid);
-  Loader<BN, B_KMAJ> lb(B, n0, B_KMAJ ? K : N, tid);
+  // Operand movers: direct (k-contiguous) or register-staged (transposed).
+  // The unused kind of each operand is never called.
+  DirectLoader<BM> da(A, m0, M, K, tid, wave);
+  DirectLoader<BN> db(B, n0, N, K, tid, wave);
+  RegLoader<BM> ra(A, m0, K, M, tid);
+  RegLoader<BN> rb(B, n0, K, N, tid);
 
   // Per-lane LDS read offsets.  Fragment i of a wave's operand covers rows
-  // w0 + 32 i + (lane % 32), logical chunk 2 kk + lane / 32 for k-substep kk.
+  // w0 + 32 i + (lane % 32), logical chunk 2 kk + lane / 32 for k-substep kk;
+  // swz() of those rows is f_lane ^ 4 ((w0 / 32 + i) & 1).
   const int f_lane = (lane & 7) ^ ((lane & 31) >> 3);
   int sw[4][2];
 #pragma unroll
@@ -216,42 +266,128 @@ __global__ __launch_bounds__(kThreads) void gemm_tile_kernel(const TIn* __restri
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
 
+  // fragments of one k-substep, double buffered
+  u32x4 fa[2][TM], fb[2][TN];
+  auto read_frag = [&](const Stage& st, int kk, int f, u32x4 (&xa)[TM], u32x4 (&xb)[TN])
+                       __attribute__((always_inline)) {
+    if (f < TM) xa[f] = *(const u32x4*)(st.a + a_row + f * 32 * kRowBytes + sw[kk][(a_par + f) & 1]);
+    else xb[f - TM] = *(const u32x4*)(st.b + b_row + (f - TM) * 32 * kRowBytes + sw[kk][(b_par + f - TM) & 1]);
+  };
+
+  constexpr int NMF = TM * TN;  // MFMAs per substep
+  constexpr int NDR = TM + TN;  // LDS fragment reads per substep
+  // register loads per k-step (transposed operands)
+  constexpr int REG_LOADS = (A_KMAJ ? 0 : RegLoader<BM>::LOADS) + (B_KMAJ ? 0 : RegLoader<BN>::LOADS);
+  // direct loads per wave per k-step
+  constexpr int NDA = A_KMAJ ? DirectLoader<BM>::NI : 0;
+  constexpr int NDL = NDA + (B_KMAJ ? DirectLoader<BN>::NI : 0);
+
+  // One substep: NMF slots, each one MFMA followed by the memory work placed
+  // in that slot, in program order; nothing moves across a slot boundary.
+  //   fragment reads for the next substep: slots 0 .. NDR-1 (spread when
+  //     NMF < NDR);
+  //   a register-staged operand (substep 0 for A, substep 0 or 1 for B,
+  //     slot 0): write tile kt+1 into `nx`, then reload with tile kt+2;
+  //   direct loads of tile kt+2 (substep 3 only): spread over the slots.
+  auto substep = [&](int sub, const u32x4 (&xa)[TM], const u32x4 (&xb)[TN], const Stage& rd, int rd_kk, bool do_read,
+                     u32x4 (&na)[TM], u32x4 (&nb)[TN], bool do_store, bool do_load, const Stage& nx,
+                     const Stage& dl_dst, bool do_direct, int kt) __attribute__((always_inline)) {
+#pragma unroll
+    for (int slot = 0; slot < NMF; ++slot) {
+      const int i = slot / TN, j = slot % TN;
+      acc[i][j] = mfma32<TIn>(xb[j], xa[i], acc[i][j]);
+      if (do_read) {
+        if (NMF >= NDR) {
+          if (slot < NDR) read_frag(rd, rd_kk, slot, na, nb);
+        } else {
+#pragma unroll
+          for (int f = slot * NDR / NMF; f < (slot + 1) * NDR / NMF; ++f) read_frag(rd, rd_kk, f, na, nb);
+        }
+      }
+      if (sub < 3 && do_store && slot == 0) {
+        if (!A_KMAJ && sub == 0) {
+          ra.store(nx.a);
+          if (do_load) ra.load(kt + 2);
+        }
+        if (!B_KMAJ && sub == (A_KMAJ ? 0 : 1)) {
+          rb.store(nx.b);
+          if (do_load) rb.load(kt + 2);
+        }
+      }
+      if (sub == 3 && do_direct) {
+#pragma unroll
+        for (int d = 0; d < NDL; ++d) {
+          if (d * NMF / NDL == slot) {
+            if (d < NDA) da.issue(dl_dst.a, kt + 2, d);
+            else db.issue(dl_dst.b, kt + 2, d - NDA);
+          }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // k-step kt with tile kt in stage `cur` and stage `nxt` receiving kt + 1.
+  auto kstep = [&](const Stage& cur, const Stage& nxt, int kt, bool more1, bool more2) __attribute__((always_inline)) {
+    substep(0, fa[0], fb[0], cur, 1, true, fa[1], fb[1], more1, more2, nxt, cur, false, kt);
+    substep(1, fa[1], fb[1], cur, 2, true, fa[0], fb[0], more1, more2, nxt, cur, false, kt);
+    substep(2, fa[0], fb[0], cur, 3, true, fa[1], fb[1], more1, more2, nxt, cur, false, kt);
+    // This wave's direct loads of tile kt + 1 are its oldest outstanding
+    // vector-memory operations; the register loads of tile kt + 2 issued in
+    // substeps 0..2 may stay in flight.
+    if (more2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(REG_LOADS));
+    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    __syncthreads();
+    substep(3, fa[1], fb[1], nxt, 0, more1, fa[0], fb[0], false, false, nxt, cur, more2, kt);
+  };
+
+  // Prologue: tile 0 into stage 0, tile 1 on its way into stage 1.
   const int KT = K / kBK;
-  la.load(0);
-  lb.load(0);
-  la.store(smem, tid);
-  lb.store(smem + A_BYTES, tid);
+#pragma unroll
+  for (int d = 0; d < NDL; ++d) {
+    if (d < NDA) da.issue(stage0.a, 0, d);
+    else db.issue(stage0.b, 0, d - NDA);
+  }
+  if constexpr (!A_KMAJ) {
+    ra.load(0);
+    ra.store(stage0.a);
+  }
+  if constexpr (!B_KMAJ) {
+    rb.load(0);
+    rb.store(stage0.b);
+  }
   if (KT > 1) {
-    la.load(1);
-    lb.load(1);
+#pragma unroll
+    for (int d = 0; d < NDL; ++d) {
+      if (d < NDA) da.issue(stage1.a, 1, d);
+      else db.issue(stage1.b, 1, d - NDA);
+    }
+    if constexpr (!A_KMAJ) ra.load(1);
+    if constexpr (!B_KMAJ) rb.load(1);
+    // tile 0 complete; tile 1's loads may stay in flight
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(NDL + REG_LOADS));
+  } else {
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   }
   __syncthreads();
+#pragma unroll
+  for (int f = 0; f < NDR; ++f) read_frag(stage0, 0, f, fa[0], fb[0]);
 
-  for (int kt = 0; kt < KT; ++kt) {
-    const char* sa = smem + (kt & 1) * STAGE;
-    const char* sb = sa + A_BYTES;
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      u32x4 af[TM], bf[TN];
-#pragma unroll
-      for (int i = 0; i < TM; ++i) af[i] = *(const u32x4*)(sa + a_row + i * 32 * kRowBytes + sw[kk][(a_par + i) & 1]);
-#pragma unroll
-      for (int j = 0; j < TN; ++j) bf[j] = *(const u32x4*)(sb + b_row + j * 32 * kRowBytes + sw[kk][(b_par + j) & 1]);
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = mfma32<TIn>(bf[j], af[i], acc[i][j]);
-    }
-    if (kt + 1 < KT) {
-      char* na = smem + ((kt + 1) & 1) * STAGE;
-      la.store(na, tid);
-      lb.store(na + A_BYTES, tid);
-      if (kt + 2 < KT) {
-        la.load(kt + 2);
-        lb.load(kt + 2);
-      }
-    }
-    __syncthreads();
+  int kt = 0;
+  for (; kt + 3 < KT; kt += 2) {
+    kstep(stage0, stage1, kt, true, true);
+    kstep(stage1, stage0, kt + 1, true, true);
+  }
+  // 1, 2 or 3 k-steps remain, the first one in stage 0
+  if (KT - kt == 3) {
+    kstep(stage0, stage1, kt, true, true);
+    kstep(stage1, stage0, kt + 1, true, false);
+    kstep(stage0, stage1, kt + 2, false, false);
+  } else if (KT - kt == 2) {
+    kstep(stage0, stage1, kt, true, false);
+    kstep(stage1, stage0, kt + 1, false, false);
+  } else {
+    kstep(stage0, stage1, kt, false, false);
   }
 
   const int m_w = m0 + wm * WM, n_w = n0 + wn * WN;
@@ -285,5 +421,4 @@ LaunchFn pick_layout(int la, int lb) {
 }
 
 }  // namespace tile
-
 }  // namespace ge
