@@ -35,6 +35,41 @@ SKINNY = "skinny_gemm_bias_bf16_32x8192x8192_rm_cm"
 PEAK_BF16_TFLOPS = 2500.0  # dense bf16/fp16 MFMA
 PEAK_HBM_GBS = 8000.0
 
+CSRC = os.path.join(ROOT, "epilogue_gemm_amd", "csrc")
+# sources that define each kernel family's device code and launch shape
+_FAMILY_SOURCES = {
+    "tile": ["common.hpp", "kernels.hpp", "gemm_tile.hpp", "gemm_tile_bf16.hip", "gemm_tile_f16.hip", "gemm_epi.cpp"],
+    "skinny": ["common.hpp", "kernels.hpp", "gemm_skinny.hip", "gemm_epi.cpp"],
+}
+
+
+def kernel_source_sha(family: str) -> str:
+    """sha256 over the sources of one kernel family (detects a kernel changed
+    since its HBM counters were taken)."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in _FAMILY_SOURCES[family]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(family: str, kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    summary of this kernel and workload (profiles/*.txt, copy-calibrated), or
+    None when there is none or the kernel's sources changed since."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}__{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        for line in fh:
+            if line.startswith("machine-readable:"):
+                kv = dict(t.split("=", 1) for t in line.split()[1:])
+                if kv.get("src_sha256") == kernel_source_sha(family):
+                    return int(float(kv["traffic_bytes"]))
+    return None
+
 
 def _device_sets(w, n_sets, torch, parity, inputs):
     """n_sets independent device copies of the workload's operands."""
@@ -178,7 +213,8 @@ def main(argv=None):
                        "layout_a": w.layout_a, "layout_b": w.layout_b, "kernel": m["kernel"],
                        "operand_sets_rotated": 3},
             "roofline": {"bound": "mfma", "achieved": round(m["value"], 2), "peak": PEAK_BF16_TFLOPS,
-                         "unit": "TFLOP/s", "frac": round(m["value"] / PEAK_BF16_TFLOPS, 4), "traffic": None},
+                         "unit": "TFLOP/s", "frac": round(m["value"] / PEAK_BF16_TFLOPS, 4),
+                         "traffic": measured_traffic("tile", m["kernel"], w.name)},
         }
     if "skinny" in out:
         s = out["skinny"]
@@ -193,7 +229,8 @@ def main(argv=None):
                        "kernel": s["kernel"], "operand_sets_rotated": 5,
                        "compulsory_bytes": w.compulsory_bytes()},
             "roofline": {"bound": "hbm", "achieved": round(s["value"], 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": round(s["value"] / PEAK_HBM_GBS, 4), "traffic": None},
+                         "frac": round(s["value"] / PEAK_HBM_GBS, 4),
+                         "traffic": measured_traffic("skinny", s["kernel"], w.name)},
         }
         if rec:
             rec["skinny"] = sk
