@@ -75,10 +75,6 @@ __device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t voff,
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
-// s_waitcnt immediate that waits until at most n vector-memory operations
-// of this wave are outstanding (LDS and export counters unconstrained).
-constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
-
 // k-contiguous operand, global -> LDS directly.  Row r of the tile is
 // X[(r0 + r) * ld + k].  Instruction i of wave w fills tile rows
 // (4 i + w) * 8 .. +7; lane L writes LDS bytes 16 L .. 16 L + 15 of that

@@ -34,7 +34,8 @@ LaunchFn tile_launcher_bf16(int cfg, int out_dt, int la, int lb);
 
 // ---- skinny: weight-streaming kernel for M <= 32 --------------------------
 struct SkinnyConfig {
-  int waves;  // waves per workgroup; each owns a contiguous K range
+  int waves;   // waves per workgroup; each owns a contiguous K range
+  int stages;  // k-chunks of 64 each wave keeps in flight (LDS ring depth)
   const char* name;
 };
 int skinny_num_configs();

@@ -91,12 +91,18 @@ def test_tile_integer_bitexact(config, la, lb, in_dt, out_dt):
         assert name.startswith("tile_")
 
 
-@pytest.mark.parametrize("config", [0, 1, 2])
+# (waves x stages x 64) k granularity of each skinny configuration, in order
+SKINNY_GRAN = [2048, 2048, 2048, 1024, 1024, 512, 256, 64]
+
+
+@pytest.mark.parametrize("config", range(len(SKINNY_GRAN)))
 @pytest.mark.parametrize("M", [1, 7, 31, 32])
 @pytest.mark.parametrize("in_dt,out_dt", [("bf16", "bf16"), ("f16", "f16"), ("bf16", "f32")])
 def test_skinny_integer_bitexact(config, M, in_dt, out_dt):
-    N, K = 96, 2048
-    for epi in EPIS:
+    # one and several ring turns per wave
+    N = 96
+    cases = [(SKINNY_GRAN[config], epi) for epi in EPIS] + [(3 * SKINNY_GRAN[config], "bias_relu")]
+    for K, epi in cases:
         bits = inputs.integer_inputs(M, N, K, in_dt, "row", "col", epi.startswith("bias"), seed=M + config)
         name = check_case(bits, M, N, K, in_dt, out_dt, "row", "col", epi, "skinny", config, epi in BITWISE_EPIS)
         assert name.startswith("skinny_")
@@ -121,7 +127,8 @@ def test_generic_integer_bitexact(M, N, K, la, lb):
     ("tile", 1, 384, 256, 1024, "row", "row"),
     ("tile", 2, 320, 192, 448, "col", "col"),
     ("skinny", 0, 32, 512, 4096, "row", "col"),
-    ("skinny", 2, 5, 160, 768, "row", "col"),
+    ("skinny", 6, 5, 160, 768, "row", "col"),
+    ("skinny", 1, 17, 256, 6144, "row", "col"),
     ("generic", 0, 97, 61, 333, "row", "row"),
     ("generic", 0, 64, 64, 4096, "col", "col"),
 ])
