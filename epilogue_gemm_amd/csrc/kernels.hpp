@@ -34,8 +34,10 @@ LaunchFn tile_launcher_bf16(int cfg, int out_dt, int la, int lb);
 
 // ---- skinny: weight-streaming kernel for M <= 32 --------------------------
 struct SkinnyConfig {
-  int waves;   // waves per workgroup; each owns a contiguous K range
-  int stages;  // k-chunks of 64 each wave keeps in flight (LDS ring depth)
+  int waves;   // waves per workgroup
+  int stages;  // LDS ring slots: chunks in flight + the one being multiplied
+  int kc;      // k-values per chunk
+  int a_lds;   // 1: A's chunk is staged in LDS too (else read into registers)
   const char* name;
 };
 int skinny_num_configs();

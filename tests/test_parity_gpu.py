@@ -91,8 +91,8 @@ def test_tile_integer_bitexact(config, la, lb, in_dt, out_dt):
         assert name.startswith("tile_")
 
 
-# (waves x stages x 64) k granularity of each skinny configuration, in order
-SKINNY_GRAN = [2048, 2048, 2048, 1024, 1024, 512, 256, 64]
+# (k per chunk x ring slots) k granularity of each skinny configuration, in order
+SKINNY_GRAN = [1024, 1024, 1024, 1024, 2048, 1024, 512, 256]
 
 
 @pytest.mark.parametrize("config", range(len(SKINNY_GRAN)))
@@ -127,8 +127,10 @@ def test_generic_integer_bitexact(M, N, K, la, lb):
     ("tile", 1, 384, 256, 1024, "row", "row"),
     ("tile", 2, 320, 192, 448, "col", "col"),
     ("skinny", 0, 32, 512, 4096, "row", "col"),
-    ("skinny", 6, 5, 160, 768, "row", "col"),
-    ("skinny", 1, 17, 256, 6144, "row", "col"),
+    ("skinny", 7, 5, 160, 768, "row", "col"),
+    ("skinny", 0, 17, 256, 6144, "row", "col"),
+    ("skinny", 2, 32, 96, 3072, "row", "col"),
+    ("skinny", 4, 3, 64, 6144, "row", "col"),
     ("generic", 0, 97, 61, 333, "row", "row"),
     ("generic", 0, 64, 64, 4096, "col", "col"),
 ])
