@@ -25,7 +25,7 @@ const TileConfig& tile_config(int cfg) { return kTile[cfg]; }
 bool tile_supports(int cfg, const Problem& p) {
   if (cfg < 0 || cfg >= tile_num_configs()) return false;
   const TileConfig& c = kTile[cfg];
-  return p.M % c.bm == 0 && p.N % c.bn == 0 && p.K % 64 == 0;
+  return p.M % c.bm == 0 && p.N % c.bn == 0 && p.K % 64 == 0 && p.K >= 128;
 }
 
 int tile_choose(const Problem& p) {
@@ -42,8 +42,9 @@ int tile_choose(const Problem& p) {
 }
 
 LaunchFn tile_launcher(int cfg, const Problem& p) {
-  if (p.in_dt == GEMM_EPI_F16) return tile_launcher_f16(cfg, p.out_dt, p.la, p.lb);
-  if (p.in_dt == GEMM_EPI_BF16) return tile_launcher_bf16(cfg, p.out_dt, p.la, p.lb);
+  const bool f32 = p.out_dt == GEMM_EPI_F32;
+  if (p.in_dt == GEMM_EPI_F16) return (f32 ? tile_launcher_f16_f32 : tile_launcher_f16_f16)(cfg, p.la, p.lb, p.epi);
+  if (p.in_dt == GEMM_EPI_BF16) return (f32 ? tile_launcher_bf16_f32 : tile_launcher_bf16_bf16)(cfg, p.la, p.lb, p.epi);
   return nullptr;
 }
 

@@ -178,37 +178,90 @@ __device__ __forceinline__ void raster(int bid, int tiles_m, int tiles_n, int pa
   tn = r / rows;
 }
 
-template <int BM, int BN, typename TIn, typename TOut, int EPI>
-__device__ __forceinline__ void write_tile(const f32x16 (&acc)[BM / 64][BN / 64], const TIn* __restrict__ bias,
-                                          TOut* __restrict__ C, int N, int m_w, int n_w, int lane) {
-  constexpr int TM = BM / 64, TN = BN / 64;
-  const int m_l = lane & 31;
-  const int n_l = 4 * (lane >> 5);
+// Epilogue of one wave's WM x WN sub-tile: bias, activation and conversion
+// on the accumulators, then one coalesced store of each output.
+//
+// The MFMA layout gives lane l four consecutive columns of one row per
+// register quad, which as a store would touch 32 rows per instruction.  So
+// each 32-row band of the sub-tile is first written to a private LDS
+// staging area in row-major order (16-byte chunks XOR-swizzled by row to
+// spread the banks), then read back 16 bytes per lane along rows and stored:
+// one wave instruction covers whole row segments of the band.  Bands are
+// processed one after another so that few values are live at a time.
+template <int WM, int WN, typename TIn, typename TOut, int EPI>
+__device__ __forceinline__ void write_tile(const f32x16 (&acc)[WM / 32][WN / 32], const TIn* __restrict__ bias,
+                                          TOut* __restrict__ C, int N, int m_w, int n_w, int lane, char* stage) {
+  constexpr int TM = WM / 32, TN = WN / 32;
+  constexpr int OSZ = (int)sizeof(TOut);
+  constexpr int CPR = WN * OSZ / 16;           // 16-byte chunks per staged row
+  constexpr int SWM = (CPR < 16 ? CPR : 16) - 1;  // swizzle mask
+  constexpr int RPI = 64 / CPR;                // rows per store instruction
+  const int m_l = lane & 31, h = lane >> 5;
+
+  // bias of this lane's 16 columns in each 32-column block, kept packed
+  u32x2 bq[TN][4];
 #pragma unroll
-  for (int j = 0; j < TN; ++j) {
-    f32x4 b[4];
+  for (int j = 0; j < TN; ++j)
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      if constexpr (epi_has_bias<EPI>()) b[q] = load_bias4<TIn>(bias + n_w + j * 32 + 8 * q + n_l);
-      else b[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (epi_has_bias<EPI>()) bq[j][q] = *(const u32x2*)(bias + n_w + j * 32 + 8 * q + 4 * h);
+      else bq[j][q] = u32x2{0u, 0u};
     }
+
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      TOut* row = C + (int64_t)(m_w + i * 32 + m_l) * N + n_w + j * 32 + n_l;
+  for (int i = 0; i < TM; ++i) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        store4<TOut>(row + 8 * q, epilogue<EPI>(acc[i][j][4 * q + 0], b[q].x),
-                     epilogue<EPI>(acc[i][j][4 * q + 1], b[q].y), epilogue<EPI>(acc[i][j][4 * q + 2], b[q].z),
-                     epilogue<EPI>(acc[i][j][4 * q + 3], b[q].w));
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float b = 0.0f;
+          if constexpr (epi_has_bias<EPI>()) {
+            const uint32_t w = bq[j][q][e >> 1];
+            b = to_f32(__builtin_bit_cast(TIn, (uint16_t)((e & 1) ? (w >> 16) : (w & 0xffffu))));
+          }
+          v[e] = epilogue<EPI>(acc[i][j][4 * q + e], b);
+        }
+        // columns j*32 + 8q + 4h .. +3 of row m_l
+        if constexpr (OSZ == 4) {
+          const int c = 8 * j + 2 * q + h;
+          *(f32x4*)(stage + m_l * (WN * 4) + ((c ^ (m_l & SWM)) << 4)) = f32x4{v[0], v[1], v[2], v[3]};
+        } else {
+          const int c = 4 * j + q;
+          u32x2 w;
+          w.x = (uint32_t)bits16(from_f32<TOut>(v[0])) | ((uint32_t)bits16(from_f32<TOut>(v[1])) << 16);
+          w.y = (uint32_t)bits16(from_f32<TOut>(v[2])) | ((uint32_t)bits16(from_f32<TOut>(v[3])) << 16);
+          *(u32x2*)(stage + m_l * (WN * 2) + ((c ^ (m_l & SWM)) << 4) + 8 * h) = w;
+        }
       }
     }
+    // read back along rows: lane -> (row r, chunk c), store 16 bytes
+#pragma unroll
+    for (int t = 0; t < 32 / RPI; ++t) {
+      const int r = t * RPI + lane / CPR, c = lane % CPR;
+      const u32x4 d = *(const u32x4*)(stage + r * (WN * OSZ) + ((c ^ (r & SWM)) << 4));
+      *(u32x4*)((char*)(C + (int64_t)(m_w + i * 32 + r) * N + n_w) + c * 16) = d;
+    }
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-template <int BM, int BN, typename TIn, typename TOut, bool A_KMAJ, bool B_KMAJ>
+// Workgroup barrier for the k loop.  Each wave first waits until at most
+// VM of its own vector-memory operations are outstanding (its direct loads
+// of the next tile are then in LDS) and its LDS writes are done; unlike
+// __syncthreads(), loads issued later may stay in flight.
+template <int VM>
+__device__ __forceinline__ void kloop_barrier() {
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(VM) & ~(15 << 8));  // vmcnt(VM) lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+}
+
+template <int BM, int BN, typename TIn, typename TOut, bool A_KMAJ, bool B_KMAJ, int EPI>
 __global__ __launch_bounds__(kThreads) void gemm_tile_kernel(const TIn* __restrict__ A, const TIn* __restrict__ B,
                                                              const TIn* __restrict__ bias, TOut* __restrict__ C,
-                                                             int M, int N, int K, int epi, int tiles_m, int tiles_n,
+                                                             int M, int N, int K, int tiles_m, int tiles_n,
                                                              int panel) {
   constexpr int WM = BM / 2, WN = BN / 2;  // wave sub-tile
   constexpr int TM = WM / 32, TN = WN / 32;
@@ -310,7 +363,7 @@ __global__ __launch_bounds__(kThreads) void gemm_tile_kernel(const TIn* __restri
           if (do_load) rb.load(kt + 2);
         }
       }
-      if (sub == 3 && do_direct) {
+      if constexpr (NDL > 0) if (sub == 3 && do_direct) {
 #pragma unroll
         for (int d = 0; d < NDL; ++d) {
           if (d * NMF / NDL == slot) {
@@ -331,89 +384,108 @@ __global__ __launch_bounds__(kThreads) void gemm_tile_kernel(const TIn* __restri
     // This wave's direct loads of tile kt + 1 are its oldest outstanding
     // vector-memory operations; the register loads of tile kt + 2 issued in
     // substeps 0..2 may stay in flight.
-    if (more2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(REG_LOADS));
-    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-    __syncthreads();
+    if (more2) kloop_barrier<REG_LOADS>();
+    else kloop_barrier<0>();
+    __builtin_amdgcn_sched_barrier(0);
     substep(3, fa[1], fb[1], nxt, 0, more1, fa[0], fb[0], false, false, nxt, cur, more2, kt);
   };
 
-  // Prologue: tile 0 into stage 0, tile 1 on its way into stage 1.
+  // Tile t lives in stage (t + KT) % 2, so that the last two tiles are
+  // always in stages 0 and 1 and the k loop ends with two peeled k-steps
+  // and no other branches (one straight path keeps the accumulators in
+  // place).  KT >= 2 (checked on the host).
   const int KT = K / kBK;
-#pragma unroll
-  for (int d = 0; d < NDL; ++d) {
-    if (d < NDA) da.issue(stage0.a, 0, d);
-    else db.issue(stage0.b, 0, d - NDA);
-  }
-  if constexpr (!A_KMAJ) {
-    ra.load(0);
-    ra.store(stage0.a);
-  }
-  if constexpr (!B_KMAJ) {
-    rb.load(0);
-    rb.store(stage0.b);
-  }
-  if (KT > 1) {
+  auto prologue = [&](const Stage& s_first, const Stage& s_second) __attribute__((always_inline)) {
 #pragma unroll
     for (int d = 0; d < NDL; ++d) {
-      if (d < NDA) da.issue(stage1.a, 1, d);
-      else db.issue(stage1.b, 1, d - NDA);
+      if (d < NDA) da.issue(s_first.a, 0, d);
+      else db.issue(s_first.b, 0, d - NDA);
+    }
+    if constexpr (!A_KMAJ) {
+      ra.load(0);
+      ra.store(s_first.a);
+    }
+    if constexpr (!B_KMAJ) {
+      rb.load(0);
+      rb.store(s_first.b);
+    }
+#pragma unroll
+    for (int d = 0; d < NDL; ++d) {
+      if (d < NDA) da.issue(s_second.a, 1, d);
+      else db.issue(s_second.b, 1, d - NDA);
     }
     if constexpr (!A_KMAJ) ra.load(1);
     if constexpr (!B_KMAJ) rb.load(1);
     // tile 0 complete; tile 1's loads may stay in flight
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(NDL + REG_LOADS));
-  } else {
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-  }
-  __syncthreads();
+    __syncthreads();
 #pragma unroll
-  for (int f = 0; f < NDR; ++f) read_frag(stage0, 0, f, fa[0], fb[0]);
+    for (int f = 0; f < NDR; ++f) read_frag(s_first, 0, f, fa[0], fb[0]);
+  };
 
   int kt = 0;
-  for (; kt + 3 < KT; kt += 2) {
+  if (KT & 1) {
+    prologue(stage1, stage0);
+    kstep(stage1, stage0, 0, true, true);
+    kt = 1;
+  } else {
+    prologue(stage0, stage1);
+  }
+  for (; kt + 4 <= KT; kt += 2) {
     kstep(stage0, stage1, kt, true, true);
     kstep(stage1, stage0, kt + 1, true, true);
   }
-  // 1, 2 or 3 k-steps remain, the first one in stage 0
-  if (KT - kt == 3) {
-    kstep(stage0, stage1, kt, true, true);
-    kstep(stage1, stage0, kt + 1, true, false);
-    kstep(stage0, stage1, kt + 2, false, false);
-  } else if (KT - kt == 2) {
-    kstep(stage0, stage1, kt, true, false);
-    kstep(stage1, stage0, kt + 1, false, false);
-  } else {
-    kstep(stage0, stage1, kt, false, false);
-  }
+  kstep(stage0, stage1, kt, true, false);
+  kstep(stage1, stage0, kt + 1, false, false);
 
-  const int m_w = m0 + wm * WM, n_w = n0 + wn * WN;
-  switch (epi) {
-    case GEMM_EPI_NONE: write_tile<BM, BN, TIn, TOut, GEMM_EPI_NONE>(acc, bias, C, N, m_w, n_w, lane); break;
-    case GEMM_EPI_RELU: write_tile<BM, BN, TIn, TOut, GEMM_EPI_RELU>(acc, bias, C, N, m_w, n_w, lane); break;
-    case GEMM_EPI_BIAS_RELU: write_tile<BM, BN, TIn, TOut, GEMM_EPI_BIAS_RELU>(acc, bias, C, N, m_w, n_w, lane); break;
-    case GEMM_EPI_BIAS_GELU: write_tile<BM, BN, TIn, TOut, GEMM_EPI_BIAS_GELU>(acc, bias, C, N, m_w, n_w, lane); break;
-    default: write_tile<BM, BN, TIn, TOut, GEMM_EPI_BIAS>(acc, bias, C, N, m_w, n_w, lane); break;
-  }
+  // Every wave is done with the operand stages: reuse them as the staging
+  // areas of the epilogue, one per wave.
+  __syncthreads();
+  char* const stage_w = wave == 0 ? sA0 : wave == 1 ? sA1 : wave == 2 ? sB0 : sB1;
+  write_tile<WM, WN, TIn, TOut, EPI>(acc, bias, C, N, m0 + wm * WM, n0 + wn * WN, lane, stage_w);
 }
 
 // Host launch of one instantiation.
-template <int BM, int BN, typename TIn, typename TOut, bool A_KMAJ, bool B_KMAJ>
+template <int BM, int BN, typename TIn, typename TOut, bool A_KMAJ, bool B_KMAJ, int EPI>
 hipError_t launch(const LaunchArgs& a) {
   const int tiles_m = a.M / BM, tiles_n = a.N / BN;
   const int panel = tiles_m < 4 ? tiles_m : 4;
-  hipLaunchKernelGGL((gemm_tile_kernel<BM, BN, TIn, TOut, A_KMAJ, B_KMAJ>), dim3(tiles_m * tiles_n), dim3(kThreads), 0,
-                     a.stream, (const TIn*)a.A, (const TIn*)a.B, (const TIn*)a.bias, (TOut*)a.C, a.M, a.N, a.K, a.epi,
-                     tiles_m, tiles_n, panel);
+  hipLaunchKernelGGL((gemm_tile_kernel<BM, BN, TIn, TOut, A_KMAJ, B_KMAJ, EPI>), dim3(tiles_m * tiles_n),
+                     dim3(kThreads), 0, a.stream, (const TIn*)a.A, (const TIn*)a.B, (const TIn*)a.bias, (TOut*)a.C,
+                     a.M, a.N, a.K, tiles_m, tiles_n, panel);
   return hipGetLastError();
 }
 
+template <int BM, int BN, typename TIn, typename TOut, bool A_KMAJ, bool B_KMAJ>
+LaunchFn pick_epi(int epi) {
+  switch (epi) {
+    case GEMM_EPI_NONE: return &launch<BM, BN, TIn, TOut, A_KMAJ, B_KMAJ, GEMM_EPI_NONE>;
+    case GEMM_EPI_RELU: return &launch<BM, BN, TIn, TOut, A_KMAJ, B_KMAJ, GEMM_EPI_RELU>;
+    case GEMM_EPI_BIAS_RELU: return &launch<BM, BN, TIn, TOut, A_KMAJ, B_KMAJ, GEMM_EPI_BIAS_RELU>;
+    case GEMM_EPI_BIAS_GELU: return &launch<BM, BN, TIn, TOut, A_KMAJ, B_KMAJ, GEMM_EPI_BIAS_GELU>;
+    case GEMM_EPI_BIAS: return &launch<BM, BN, TIn, TOut, A_KMAJ, B_KMAJ, GEMM_EPI_BIAS>;
+    default: return nullptr;
+  }
+}
+
 template <int BM, int BN, typename TIn, typename TOut>
-LaunchFn pick_layout(int la, int lb) {
+LaunchFn pick_layout(int la, int lb, int epi) {
   const bool ak = la == GEMM_EPI_ROW_MAJOR, bk = lb == GEMM_EPI_COL_MAJOR;
-  if (ak && bk) return &launch<BM, BN, TIn, TOut, true, true>;
-  if (ak && !bk) return &launch<BM, BN, TIn, TOut, true, false>;
-  if (!ak && bk) return &launch<BM, BN, TIn, TOut, false, true>;
-  return &launch<BM, BN, TIn, TOut, false, false>;
+  if (ak && bk) return pick_epi<BM, BN, TIn, TOut, true, true>(epi);
+  if (ak && !bk) return pick_epi<BM, BN, TIn, TOut, true, false>(epi);
+  if (!ak && bk) return pick_epi<BM, BN, TIn, TOut, false, true>(epi);
+  return pick_epi<BM, BN, TIn, TOut, false, false>(epi);
+}
+
+// All configurations for one input and output format.
+template <typename TIn, typename TOut>
+LaunchFn pick_config(int cfg, int la, int lb, int epi) {
+  switch (cfg) {
+    case 0: return pick_layout<256, 256, TIn, TOut>(la, lb, epi);
+    case 1: return pick_layout<128, 128, TIn, TOut>(la, lb, epi);
+    case 2: return pick_layout<64, 64, TIn, TOut>(la, lb, epi);
+    default: return nullptr;
+  }
 }
 
 }  // namespace tile

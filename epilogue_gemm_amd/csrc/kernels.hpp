@@ -28,9 +28,11 @@ const TileConfig& tile_config(int cfg);
 bool tile_supports(int cfg, const Problem& p);
 int tile_choose(const Problem& p);  // -1 when no config fits
 LaunchFn tile_launcher(int cfg, const Problem& p);
-// per input format, one translation unit each
-LaunchFn tile_launcher_f16(int cfg, int out_dt, int la, int lb);
-LaunchFn tile_launcher_bf16(int cfg, int out_dt, int la, int lb);
+// one translation unit per (input, output) format pair
+LaunchFn tile_launcher_f16_f16(int cfg, int la, int lb, int epi);
+LaunchFn tile_launcher_f16_f32(int cfg, int la, int lb, int epi);
+LaunchFn tile_launcher_bf16_bf16(int cfg, int la, int lb, int epi);
+LaunchFn tile_launcher_bf16_f32(int cfg, int la, int lb, int epi);
 
 // ---- skinny: weight-streaming kernel for M <= 32 --------------------------
 struct SkinnyConfig {
