@@ -10,13 +10,15 @@
 
 namespace ge {
 
-// Tile configurations: workgroup tile BM x BN (k-step 64), 4 waves each
-// owning (BM/2) x (BN/2).  Larger tiles reuse each loaded byte more; smaller
-// ones give small problems enough workgroups for 256 CUs.
+// Tile configurations: workgroup tile BM x BN (k-step 64) and its waves,
+// each owning (BM/2) x (BN/(waves/2)).  Larger tiles reuse each loaded byte
+// more; smaller ones give small problems enough workgroups for 256 CUs;
+// 8 waves put two on each SIMD so one can multiply while the other waits.
 static const TileConfig kTile[] = {
-    {256, 256, "tile_256x256x64"},
-    {128, 128, "tile_128x128x64"},
-    {64, 64, "tile_64x64x64"},
+    {256, 256, 4, "tile_256x256x64"},
+    {128, 128, 4, "tile_128x128x64"},
+    {64, 64, 4, "tile_64x64x64"},
+    {256, 256, 8, "tile_256x256x64_8w"},
 };
 
 int tile_num_configs() { return (int)(sizeof(kTile) / sizeof(kTile[0])); }
@@ -30,9 +32,10 @@ bool tile_supports(int cfg, const Problem& p) {
 
 int tile_choose(const Problem& p) {
   // Largest tile that still gives at least one workgroup per CU; else the
-  // smallest tile that fits (most parallelism).
+  // smallest tile that fits (most parallelism).  Only the 4-wave
+  // configurations are candidates (the 8-wave one is selected explicitly).
   int fallback = -1;
-  for (int c = 0; c < tile_num_configs(); ++c) {
+  for (int c = 0; c < 3; ++c) {
     if (!tile_supports(c, p)) continue;
     const int64_t tiles = (p.M / kTile[c].bm) * (p.N / kTile[c].bn);
     if (tiles >= 256) return c;

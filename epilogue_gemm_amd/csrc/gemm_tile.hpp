@@ -52,7 +52,6 @@ namespace tile {
 
 constexpr int kBK = 64;             // k extent of one stage
 constexpr int kRowBytes = kBK * 2;  // one LDS row: 64 16-bit elements
-constexpr int kThreads = 256;
 
 // 16-byte chunk c of LDS row r is stored at chunk position c ^ swz(r).
 // Operand reads: the 16 lanes of a quarter-wave read 16 consecutive rows at
@@ -76,17 +75,19 @@ __device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t voff,
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
 // k-contiguous operand, global -> LDS directly.  Row r of the tile is
-// X[(r0 + r) * ld + k].  Instruction i of wave w fills tile rows
-// (4 i + w) * 8 .. +7; lane L writes LDS bytes 16 L .. 16 L + 15 of that
-// KiB, i.e. row (4 i + w) * 8 + L / 8 at chunk position L % 8, so it loads
-// logical chunk (L % 8) ^ swz(row).  Since swz depends on the row only
-// through (L / 8) ^ w ^ 4 (i & 1), two per-lane offsets (even and odd i)
-// cover every instruction; the rest of the offset is wave-uniform.
-template <int R>
+// X[(r0 + r) * ld + k].  Instruction i of wave w (of NW) fills tile rows
+// (NW i + w) * 8 .. +7; lane L writes LDS bytes 16 L .. 16 L + 15 of that
+// KiB, i.e. row (NW i + w) * 8 + L / 8 at chunk position L % 8, so it loads
+// logical chunk (L % 8) ^ swz(row).  swz depends on the row only through
+// L / 8 and (NW i + w) % 8, which takes NV = 8 / NW values as i varies, so NV
+// per-lane offsets cover every instruction; the rest is wave-uniform.
+template <int R, int NW>
 struct DirectLoader {
-  static constexpr int NI = R / 32;  // wave instructions per wave per k-step
+  static constexpr int NI = R / (8 * NW);  // wave instructions per wave per k-step
+  static constexpr int NV = 8 / NW;
+  static_assert(NV >= 1 && NV <= 2, "4 or 8 waves");
   __amdgpu_buffer_rsrc_t rsrc;
-  uint32_t voff[2];
+  uint32_t voff[2];  // fixed extent: an NW-dependent one left host kernel stubs undefined
   uint32_t rows64;  // bytes of 64 rows
   int wave;
 
@@ -97,16 +98,16 @@ struct DirectLoader {
     const int lane = tid & 63;
     const int rl = lane >> 3, pc = lane & 7;
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const int row = (4 * p + wave) * 8 + rl;
-      voff[p] = (uint32_t)(row * ld * 2 + ((pc ^ rl ^ wave ^ (4 * p)) << 4));
+    for (int p = 0; p < NV; ++p) {
+      const int row = (NW * p + wave) * 8 + rl;
+      voff[p] = (uint32_t)(row * ld * 2 + ((pc ^ swz(row)) << 4));
     }
     rows64 = (uint32_t)(64 * ld * 2);
   }
   // Issue instruction i of k-step kt into the operand region `dst` of a stage.
   __device__ __forceinline__ void issue(char* dst, int kt, int i) const {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr)(dst + (4 * i + wave) * 1024), 16, voff[i & 1],
-                                             (i >> 1) * rows64 + kt * kRowBytes, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr)(dst + (NW * i + wave) * 1024), 16, voff[i % NV],
+                                             (i / NV) * rows64 + kt * kRowBytes, 0, 0);
   }
 };
 
@@ -114,9 +115,9 @@ struct DirectLoader {
 // index) at k is X[k * ld + r0 + r].  Each thread loads KB k-rows of 8
 // consecutive M/N values and writes, for each of the 8, its KB k-values
 // contiguously.
-template <int R>
+template <int R, int NT>
 struct RegLoader {
-  static constexpr int KB = R / 32;  // k values per thread: 8, 4 or 2
+  static constexpr int KB = R * 8 / NT;  // k values per thread: 8, 4 or 2
   static constexpr int NG = R / 8;   // 8-wide groups along M/N
   static_assert(KB >= 2 && KB <= 8, "tile extent");
   static constexpr int LOADS = KB;
@@ -258,12 +259,14 @@ __device__ __forceinline__ void kloop_barrier() {
   __builtin_amdgcn_s_barrier();
 }
 
-template <int BM, int BN, typename TIn, typename TOut, bool A_KMAJ, bool B_KMAJ, int EPI>
-__global__ __launch_bounds__(kThreads) void gemm_tile_kernel(const TIn* __restrict__ A, const TIn* __restrict__ B,
+template <int BM, int BN, int NW, typename TIn, typename TOut, bool A_KMAJ, bool B_KMAJ, int EPI>
+__global__ __launch_bounds__(NW * 64) void gemm_tile_kernel(const TIn* __restrict__ A, const TIn* __restrict__ B,
                                                              const TIn* __restrict__ bias, TOut* __restrict__ C,
                                                              int M, int N, int K, int tiles_m, int tiles_n,
                                                              int panel) {
-  constexpr int WM = BM / 2, WN = BN / 2;  // wave sub-tile
+  // NW waves in a 2 x (NW / 2) grid, each owning a WM x WN sub-tile
+  constexpr int NT = NW * 64;
+  constexpr int WM = BM / 2, WN = BN / (NW / 2);
   constexpr int TM = WM / 32, TN = WN / 32;
   constexpr int A_BYTES = BM * kRowBytes, B_BYTES = BN * kRowBytes;
   // One array per operand and stage, so that every access names its stage
@@ -282,7 +285,7 @@ __global__ __launch_bounds__(kThreads) void gemm_tile_kernel(const TIn* __restri
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / (NW / 2), wn = wave % (NW / 2);
 
   int tm, tn;
   raster(blockIdx.x, tiles_m, tiles_n, panel, tm, tn);
@@ -290,10 +293,10 @@ __global__ __launch_bounds__(kThreads) void gemm_tile_kernel(const TIn* __restri
 
   // Operand movers: direct (k-contiguous) or register-staged (transposed).
   // The unused kind of each operand is never called.
-  DirectLoader<BM> da(A, m0, M, K, tid, wave);
-  DirectLoader<BN> db(B, n0, N, K, tid, wave);
-  RegLoader<BM> ra(A, m0, K, M, tid);
-  RegLoader<BN> rb(B, n0, K, N, tid);
+  DirectLoader<BM, NW> da(A, m0, M, K, tid, wave);
+  DirectLoader<BN, NW> db(B, n0, N, K, tid, wave);
+  RegLoader<BM, NT> ra(A, m0, K, M, tid);
+  RegLoader<BN, NT> rb(B, n0, K, N, tid);
 
   // Per-lane LDS read offsets.  Fragment i of a wave's operand covers rows
   // w0 + 32 i + (lane % 32), logical chunk 2 kk + lane / 32 for k-substep kk;
@@ -326,10 +329,10 @@ __global__ __launch_bounds__(kThreads) void gemm_tile_kernel(const TIn* __restri
   constexpr int NMF = TM * TN;  // MFMAs per substep
   constexpr int NDR = TM + TN;  // LDS fragment reads per substep
   // register loads per k-step (transposed operands)
-  constexpr int REG_LOADS = (A_KMAJ ? 0 : RegLoader<BM>::LOADS) + (B_KMAJ ? 0 : RegLoader<BN>::LOADS);
+  constexpr int REG_LOADS = (A_KMAJ ? 0 : RegLoader<BM, NT>::LOADS) + (B_KMAJ ? 0 : RegLoader<BN, NT>::LOADS);
   // direct loads per wave per k-step
-  constexpr int NDA = A_KMAJ ? DirectLoader<BM>::NI : 0;
-  constexpr int NDL = NDA + (B_KMAJ ? DirectLoader<BN>::NI : 0);
+  constexpr int NDA = A_KMAJ ? DirectLoader<BM, NW>::NI : 0;
+  constexpr int NDL = NDA + (B_KMAJ ? DirectLoader<BN, NW>::NI : 0);
 
   // One substep: NMF slots, each one MFMA followed by the memory work placed
   // in that slot, in program order; nothing moves across a slot boundary.
@@ -441,49 +444,54 @@ __global__ __launch_bounds__(kThreads) void gemm_tile_kernel(const TIn* __restri
   // Every wave is done with the operand stages: reuse them as the staging
   // areas of the epilogue, one per wave.
   __syncthreads();
-  char* const stage_w = wave == 0 ? sA0 : wave == 1 ? sA1 : wave == 2 ? sB0 : sB1;
+  // (wave w uses part w / 4 of stage array w % 4; BM == BN for every
+  // configuration, and a part holds one staged band)
+  static_assert(BM == BN && 32 * WN * sizeof(TOut) <= (size_t)A_BYTES / (NW / 4), "staging area");
+  char* const stage_w = (wave % 4 == 0 ? sA0 : wave % 4 == 1 ? sA1 : wave % 4 == 2 ? sB0 : sB1) +
+                        (wave / 4) * (A_BYTES / (NW / 4));
   write_tile<WM, WN, TIn, TOut, EPI>(acc, bias, C, N, m0 + wm * WM, n0 + wn * WN, lane, stage_w);
 }
 
 // Host launch of one instantiation.
-template <int BM, int BN, typename TIn, typename TOut, bool A_KMAJ, bool B_KMAJ, int EPI>
+template <int BM, int BN, int NW, typename TIn, typename TOut, bool A_KMAJ, bool B_KMAJ, int EPI>
 hipError_t launch(const LaunchArgs& a) {
   const int tiles_m = a.M / BM, tiles_n = a.N / BN;
   const int panel = tiles_m < 4 ? tiles_m : 4;
-  hipLaunchKernelGGL((gemm_tile_kernel<BM, BN, TIn, TOut, A_KMAJ, B_KMAJ, EPI>), dim3(tiles_m * tiles_n),
-                     dim3(kThreads), 0, a.stream, (const TIn*)a.A, (const TIn*)a.B, (const TIn*)a.bias, (TOut*)a.C,
+  hipLaunchKernelGGL((gemm_tile_kernel<BM, BN, NW, TIn, TOut, A_KMAJ, B_KMAJ, EPI>), dim3(tiles_m * tiles_n),
+                     dim3(NW * 64), 0, a.stream, (const TIn*)a.A, (const TIn*)a.B, (const TIn*)a.bias, (TOut*)a.C,
                      a.M, a.N, a.K, tiles_m, tiles_n, panel);
   return hipGetLastError();
 }
 
-template <int BM, int BN, typename TIn, typename TOut, bool A_KMAJ, bool B_KMAJ>
+template <int BM, int BN, int NW, typename TIn, typename TOut, bool A_KMAJ, bool B_KMAJ>
 LaunchFn pick_epi(int epi) {
   switch (epi) {
-    case GEMM_EPI_NONE: return &launch<BM, BN, TIn, TOut, A_KMAJ, B_KMAJ, GEMM_EPI_NONE>;
-    case GEMM_EPI_RELU: return &launch<BM, BN, TIn, TOut, A_KMAJ, B_KMAJ, GEMM_EPI_RELU>;
-    case GEMM_EPI_BIAS_RELU: return &launch<BM, BN, TIn, TOut, A_KMAJ, B_KMAJ, GEMM_EPI_BIAS_RELU>;
-    case GEMM_EPI_BIAS_GELU: return &launch<BM, BN, TIn, TOut, A_KMAJ, B_KMAJ, GEMM_EPI_BIAS_GELU>;
-    case GEMM_EPI_BIAS: return &launch<BM, BN, TIn, TOut, A_KMAJ, B_KMAJ, GEMM_EPI_BIAS>;
+    case GEMM_EPI_NONE: return &launch<BM, BN, NW, TIn, TOut, A_KMAJ, B_KMAJ, GEMM_EPI_NONE>;
+    case GEMM_EPI_RELU: return &launch<BM, BN, NW, TIn, TOut, A_KMAJ, B_KMAJ, GEMM_EPI_RELU>;
+    case GEMM_EPI_BIAS_RELU: return &launch<BM, BN, NW, TIn, TOut, A_KMAJ, B_KMAJ, GEMM_EPI_BIAS_RELU>;
+    case GEMM_EPI_BIAS_GELU: return &launch<BM, BN, NW, TIn, TOut, A_KMAJ, B_KMAJ, GEMM_EPI_BIAS_GELU>;
+    case GEMM_EPI_BIAS: return &launch<BM, BN, NW, TIn, TOut, A_KMAJ, B_KMAJ, GEMM_EPI_BIAS>;
     default: return nullptr;
   }
 }
 
-template <int BM, int BN, typename TIn, typename TOut>
+template <int BM, int BN, int NW, typename TIn, typename TOut>
 LaunchFn pick_layout(int la, int lb, int epi) {
   const bool ak = la == GEMM_EPI_ROW_MAJOR, bk = lb == GEMM_EPI_COL_MAJOR;
-  if (ak && bk) return pick_epi<BM, BN, TIn, TOut, true, true>(epi);
-  if (ak && !bk) return pick_epi<BM, BN, TIn, TOut, true, false>(epi);
-  if (!ak && bk) return pick_epi<BM, BN, TIn, TOut, false, true>(epi);
-  return pick_epi<BM, BN, TIn, TOut, false, false>(epi);
+  if (ak && bk) return pick_epi<BM, BN, NW, TIn, TOut, true, true>(epi);
+  if (ak && !bk) return pick_epi<BM, BN, NW, TIn, TOut, true, false>(epi);
+  if (!ak && bk) return pick_epi<BM, BN, NW, TIn, TOut, false, true>(epi);
+  return pick_epi<BM, BN, NW, TIn, TOut, false, false>(epi);
 }
 
 // All configurations for one input and output format.
 template <typename TIn, typename TOut>
 LaunchFn pick_config(int cfg, int la, int lb, int epi) {
   switch (cfg) {
-    case 0: return pick_layout<256, 256, TIn, TOut>(la, lb, epi);
-    case 1: return pick_layout<128, 128, TIn, TOut>(la, lb, epi);
-    case 2: return pick_layout<64, 64, TIn, TOut>(la, lb, epi);
+    case 0: return pick_layout<256, 256, 4, TIn, TOut>(la, lb, epi);
+    case 1: return pick_layout<128, 128, 4, TIn, TOut>(la, lb, epi);
+    case 2: return pick_layout<64, 64, 4, TIn, TOut>(la, lb, epi);
+    case 3: return pick_layout<256, 256, 8, TIn, TOut>(la, lb, epi);
     default: return nullptr;
   }
 }

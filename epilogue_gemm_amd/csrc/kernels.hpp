@@ -21,6 +21,7 @@ LaunchFn generic_launcher(const Problem& p);
 // ---- tile: LDS-pipelined MFMA kernel --------------------------------------
 struct TileConfig {
   int bm, bn;  // workgroup tile; bk is 64 for every config
+  int waves;   // waves per workgroup
   const char* name;
 };
 int tile_num_configs();

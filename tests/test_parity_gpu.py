@@ -76,10 +76,10 @@ def check_case(bits, M, N, K, in_dt, out_dt, la, lb, epi, kernel, config, bitwis
 # integer operands: bit-exact
 # ---------------------------------------------------------------------------
 
-TILE_SHAPES = {0: (512, 512, 192), 1: (256, 384, 128), 2: (192, 128, 320)}
+TILE_SHAPES = {0: (512, 512, 192), 1: (256, 384, 128), 2: (192, 128, 320), 3: (768, 512, 256)}
 
 
-@pytest.mark.parametrize("config", [0, 1, 2])
+@pytest.mark.parametrize("config", [0, 1, 2, 3])
 @pytest.mark.parametrize("la,lb", [("row", "col"), ("row", "row"), ("col", "col"), ("col", "row")])
 @pytest.mark.parametrize("in_dt,out_dt", [("f16", "f16"), ("bf16", "bf16"), ("f16", "f32"), ("bf16", "f32")])
 def test_tile_integer_bitexact(config, la, lb, in_dt, out_dt):
@@ -124,6 +124,8 @@ def test_generic_integer_bitexact(M, N, K, la, lb):
 @pytest.mark.parametrize("kernel,config,M,N,K,la,lb", [
     ("tile", 0, 768, 1024, 512, "row", "col"),
     ("tile", 0, 512, 768, 640, "row", "row"),
+    ("tile", 3, 512, 1024, 704, "row", "col"),
+    ("tile", 3, 768, 512, 384, "row", "row"),
     ("tile", 1, 384, 256, 1024, "row", "row"),
     ("tile", 2, 320, 192, 448, "col", "col"),
     ("skinny", 0, 32, 512, 4096, "row", "col"),
