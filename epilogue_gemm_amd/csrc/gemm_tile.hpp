@@ -484,17 +484,5 @@ LaunchFn pick_layout(int la, int lb, int epi) {
   return pick_epi<BM, BN, NW, TIn, TOut, false, false>(epi);
 }
 
-// All configurations for one input and output format.
-template <typename TIn, typename TOut>
-LaunchFn pick_config(int cfg, int la, int lb, int epi) {
-  switch (cfg) {
-    case 0: return pick_layout<256, 256, 4, TIn, TOut>(la, lb, epi);
-    case 1: return pick_layout<128, 128, 4, TIn, TOut>(la, lb, epi);
-    case 2: return pick_layout<64, 64, 4, TIn, TOut>(la, lb, epi);
-    case 3: return pick_layout<256, 256, 8, TIn, TOut>(la, lb, epi);
-    default: return nullptr;
-  }
-}
-
 }  // namespace tile
 }  // namespace ge

@@ -1,6 +1,6 @@
 // gemm_tile_bf16_bf16.hip -- tile-kernel instantiations for bf16 inputs and bf16 output
 // (one translation unit per format pair, so they compile in parallel).
-#include "gemm_tile.hpp"
+#include "tile_dispatch.hpp"
 
 namespace ge {
 

@@ -1,6 +1,6 @@
 // gemm_tile_bf16_f32.hip -- tile-kernel instantiations for bf16 inputs and f32 output
 // (one translation unit per format pair, so they compile in parallel).
-#include "gemm_tile.hpp"
+#include "tile_dispatch.hpp"
 
 namespace ge {
 

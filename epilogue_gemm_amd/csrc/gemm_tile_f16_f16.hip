@@ -1,6 +1,6 @@
 // gemm_tile_f16_f16.hip -- tile-kernel instantiations for f16 inputs and f16 output
 // (one translation unit per format pair, so they compile in parallel).
-#include "gemm_tile.hpp"
+#include "tile_dispatch.hpp"
 
 namespace ge {
 
