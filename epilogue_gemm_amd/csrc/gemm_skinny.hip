@@ -22,19 +22,24 @@
 //     count), so that concurrent workgroups read different k offsets: when
 //     all of them read the same offset of their rows at once, the traffic
 //     bunches on a subset of the HBM channels and the rate drops by a third;
-//   - the ring has P slots: while chunk c is multiplied, chunks c+1 ..
+//   - A's chunk (at most 32 rows x KC, the same for every workgroup and
+//     so served by L2) is copied the same way into a second ring, with the
+//     same slot and swizzle;
+//   - the rings have P slots: while chunk c is multiplied, chunks c+1 ..
 //     c+P-1 are in flight.  One workgroup barrier per chunk, after each
 //     wave has waited for its own loads of chunk c (s_waitcnt vmcnt), makes
 //     the slot complete; it also proves every wave has finished chunk c-1,
-//     whose slot then receives chunk c+P-1;
+//     whose slot then receives chunk c+P-1.  Chunk c sits in slot
+//     (c + off) % P with off chosen so that the last P chunks fill slots
+//     0 .. P-1: any chunk count of at least P runs with every slot index a
+//     compile-time constant;
 //   - inside a chunk, wave w multiplies its own KC/NW k-values:
-//     v_mfma_f32_32x32x16 with B's rows as the first operand (from LDS) and
-//     A's rows as the second (A is at most 32 x K and the same for every
-//     workgroup, so it is read from L2 straight into operand registers,
-//     issued with the chunk's B loads).  Lane l then holds the outputs
+//     v_mfma_f32_32x32x16 with B's rows as the first operand and A's rows
+//     as the second, both from LDS.  Lane l then holds the outputs
 //     (m = l % 32, n = 8 (v / 4) + 4 (l / 32) + v % 4) of accumulator v;
 //   - the NW partial 32x32 blocks are summed through LDS in wave order,
-//     then bias, activation, conversion and one store per output.
+//     then bias, activation and conversion, and each thread writes four
+//     consecutive outputs of a row with one vector store.
 //
 // Within each 16-k MFMA step lane half h takes k = 8h .. 8h + 7 of both
 // operands, so every product pairs matching k.
@@ -80,7 +85,7 @@ __device__ __forceinline__ void arrive() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <typename TIn, typename TOut, int NW, int P, int KC, bool A_LDS, int EPI>
+template <typename TIn, typename TOut, int NW, int P, int KC, int EPI>
 __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const TIn* __restrict__ A, const TIn* __restrict__ B,
                                                               const TIn* __restrict__ bias, TOut* __restrict__ C,
                                                               int M, int N, int K) {
@@ -88,14 +93,14 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const TIn* __restr
   constexpr int SLOT = 32 * RB;         // one ring slot: 32 rows of B
   constexpr int MF = KC / 16 / NW;      // MFMAs per wave per chunk
   constexpr int ND = SLOT / 1024 / NW;  // direct-load instructions per wave per chunk
-  // vector-memory operations per wave per chunk
-  constexpr int OPS = ND + (A_LDS ? ND : MF);
+  // vector-memory operations per wave per chunk (B's and A's)
+  constexpr int OPS = 2 * ND;
   static_assert(MF >= 1 && ND >= 1 && RB >= 256 && RB <= 1024 && P >= 2, "chunk shape");
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n0 = blockIdx.x * 32;
-  const int nchunks = K / KC;  // a multiple of P (checked on the host)
+  const int nchunks = K / KC;  // at least P (checked on the host)
 
   // Workgroup b walks the chunks starting at chunk b (mod the count): at
   // any moment the workgroups read at spread-out k offsets of their rows
@@ -106,9 +111,9 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const TIn* __restr
 
   char* slot[P];
   ring_slots<SLOT, P>(slot, std::make_integer_sequence<int, P>{});
-  // A's chunk (32 rows x KC, rows past M zero) when it is staged in LDS
-  char* slot_a[A_LDS ? P : 1];
-  if constexpr (A_LDS) ring_slots<SLOT, P>(slot_a, std::make_integer_sequence<int, P>{}, std::integral_constant<int, P>{});
+  // A's chunk: 32 rows x KC, rows past M zero
+  char* slot_a[P];
+  ring_slots<SLOT, P>(slot_a, std::make_integer_sequence<int, P>{}, std::integral_constant<int, P>{});
 
   // B: rows n0 .. n0 + 31.  Wave instruction t (wave w issues t = w ND + d)
   // fills LDS bytes [1024 t, 1024 t + 1024) of the slot: lane L lands at
@@ -117,10 +122,10 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const TIn* __restr
   // lane fetches global chunk p ^ (r % 16) of its row segment.
   const uint32_t row_bytes = (uint32_t)K * 2u;
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(B + (int64_t)n0 * K, 32u * row_bytes);
-  // A's chunk, when staged in LDS, uses the same mapping, but with the whole
-  // row offset in the per-lane part: the buffer's range check covers only
-  // that part, and it is what turns rows past M into zeros.
-  uint32_t vb[ND], sb[ND], vas[A_LDS ? ND : 1];
+  // A's chunk uses the same mapping, but with the whole row offset in the
+  // per-lane part: the buffer's range check covers only that part, and it
+  // is what turns rows past M into zeros.
+  uint32_t vb[ND], sb[ND], vas[ND];
 #pragma unroll
   for (int d = 0; d < ND; ++d) {
     const int t = wave * ND + d;
@@ -129,21 +134,19 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const TIn* __restr
     const int r0 = (1024 * t) / RB;  // first row of the instruction (wave-uniform)
     vb[d] = (uint32_t)(r - r0) * row_bytes + (uint32_t)((p ^ (r & 15)) << 4);
     sb[d] = (uint32_t)r0 * row_bytes;
-    if constexpr (A_LDS) vas[d] = (uint32_t)r * row_bytes + (uint32_t)((p ^ (r & 15)) << 4);
+    vas[d] = (uint32_t)r * row_bytes + (uint32_t)((p ^ (r & 15)) << 4);
   }
 
   // A: rows past M read as zero (outside the buffer resource).  Wave w's
   // k-values of a chunk are [16 MF w, 16 MF (w + 1)).
   const int r = lane & 31, h = lane >> 5;
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(A, (uint32_t)M * row_bytes);
-  const uint32_t va = (uint32_t)r * row_bytes + (uint32_t)(wave * MF * 16 + 8 * h) * 2u;
 
   // B fragment of MFMA q: row r, global chunk g = 2 (w MF + q) + h.
   int rd[MF];
 #pragma unroll
   for (int q = 0; q < MF; ++q) rd[q] = r * RB + (((2 * (wave * MF + q) + h) ^ (r & 15)) << 4);
 
-  u32x4 a[A_LDS ? 1 : P][MF];
   f32x16 acc = f32x16{};
 
   auto issue = [&](int j, int c) __attribute__((always_inline)) {
@@ -151,43 +154,62 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const TIn* __restr
 #pragma unroll
     for (int d = 0; d < ND; ++d)
       load_lds16(rb, slot[j] + (wave * ND + d) * 1024, vb[d], sb[d] + kb);
-    if constexpr (A_LDS) {
 #pragma unroll
-      for (int d = 0; d < ND; ++d) load_lds16(ra, slot_a[j] + (wave * ND + d) * 1024, vas[d], kb);
-    } else {
-#pragma unroll
-      for (int q = 0; q < MF; ++q)
-        a[j][q] =
-            __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, (int)va, (int)(kb + 32u * q), 0));
-    }
+    for (int d = 0; d < ND; ++d) load_lds16(ra, slot_a[j] + (wave * ND + d) * 1024, vas[d], kb);
   };
   auto compute = [&](int j) __attribute__((always_inline)) {
     u32x4 b[MF];
 #pragma unroll
     for (int q = 0; q < MF; ++q) b[q] = *(const u32x4*)(slot[j] + rd[q]);
-    if constexpr (A_LDS) {
-      // A's slot has B's layout: lane (m, h) reads row m at B's positions
-      u32x4 x[MF];
+    // A's slot has B's layout: lane (m, h) reads row m at B's positions
+    u32x4 x[MF];
 #pragma unroll
-      for (int q = 0; q < MF; ++q) x[q] = *(const u32x4*)(slot_a[j] + rd[q]);
+    for (int q = 0; q < MF; ++q) x[q] = *(const u32x4*)(slot_a[j] + rd[q]);
 #pragma unroll
-      for (int q = 0; q < MF; ++q) acc = mfma32<TIn>(b[q], x[q], acc);
-    } else {
-#pragma unroll
-      for (int q = 0; q < MF; ++q) acc = mfma32<TIn>(b[q], a[j][q], acc);
-    }
+    for (int q = 0; q < MF; ++q) acc = mfma32<TIn>(b[q], x[q], acc);
   };
-  // This thread's bias value (every output it writes is in column
-  // n0 + tid % 32), loaded now so that its latency hides behind the stream.
-  float bias_v = 0.0f;
-  if constexpr (epi_has_bias<EPI>()) bias_v = to_f32(bias[n0 + (tid & 31)]);
+  // Output stage: output group t (0 .. 255) is (m = t / 8, n0 + 4 (t % 8)
+  // .. +3), taken by threads t, t + 64 NW, ...; every group of a thread has
+  // the same columns, whose bias values are loaded now so that the latency
+  // hides behind the stream.
+  const int oq = tid & 7;
+  u32x2 bias_q = u32x2{0u, 0u};
+  if constexpr (epi_has_bias<EPI>())
+    if (tid < 256) bias_q = *(const u32x2*)(bias + n0 + 4 * oq);
   __builtin_amdgcn_sched_barrier(0);
 
+  // Chunk c lives in slot (c + off) % P, so that the last P chunks sit in
+  // slots 0 .. P-1 in order whatever the chunk count; every slot index
+  // below is a compile-time constant.
+  const int off = (P - nchunks % P) % P;
   // chunks 0 .. P-2 in flight
-#pragma unroll
-  for (int j = 0; j + 1 < P; ++j) issue(j, j);
+  static_for<P>([&](auto oc) __attribute__((always_inline)) {
+    constexpr int o = decltype(oc)::value;
+    if (off == o) {
+      static_for<P - 1>([&](auto jc) __attribute__((always_inline)) {
+        constexpr int j = decltype(jc)::value;
+        issue((j + o) % P, j);
+      });
+    }
+  });
 
+  // One chunk: wait for it (and prove every wave is past the previous
+  // one), refill the slot just freed with the chunk P-1 ahead, multiply.
   int c0 = 0;
+  // head: the first nchunks % P chunks, in slots off .. P-1
+  static_for<P>([&](auto sc) __attribute__((always_inline)) {
+    constexpr int s = decltype(sc)::value;
+    if constexpr (s > 0) {
+      if (off != 0 && s >= off) {
+        arrive<OPS * (P - 2)>();
+        issue((s + P - 1) % P, c0 + P - 1);
+        compute(s);
+        __builtin_amdgcn_sched_barrier(0);
+        ++c0;
+      }
+    }
+  });
+  // whole turns of the ring
   for (; c0 + P < nchunks; c0 += P) {
     static_for<P>([&](auto jc) __attribute__((always_inline)) {
       constexpr int j = decltype(jc)::value;
@@ -210,72 +232,94 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const TIn* __restr
     __builtin_amdgcn_sched_barrier(0);
   });
 
-  // Partial sums of the NW waves through LDS (slot 0, when large enough, is
-  // free once every wave is past the barrier below), summed in wave order.
+  // Partial sums of the NW waves through LDS: once every wave is past the
+  // barrier below the ring is free, and wave w's 4 KiB record goes to byte
+  // 4096 w of the ring (spanning slots in order).  Lane l stores its 16
+  // values as four 16-byte chunks, chunk c at position c ^ ((l >> 2) & 3)
+  // of its 64 bytes, so each 16-lane group of a write covers 16 distinct
+  // bank groups.
+  static_assert(NW * 4096 <= P * SLOT && SLOT % 4096 == 0, "reduction records");
+  auto record = [&](int w) __attribute__((always_inline)) -> char* {
+    char* r = slot[0];
+    static_for<P>([&](auto jc) __attribute__((always_inline)) {
+      constexpr int j = decltype(jc)::value;
+      if (w * 4096 / SLOT == j) r = slot[j] + (w * 4096) % SLOT;
+    });
+    return r;
+  };
   __syncthreads();
-  float* red;
-  if constexpr (SLOT >= NW * 4096) red = (float*)slot[0];
-  else red = (float*)ring_slot<2 * P, NW * 4096>();
+  {
+    char* rec = record(wave) + lane * 64;
+    const int sw = (lane >> 2) & 3;
 #pragma unroll
-  for (int v = 0; v < 16; ++v) red[(wave * 16 + v) * 64 + lane] = acc[v];
+    for (int c = 0; c < 4; ++c)
+      *(f32x4*)(rec + ((c ^ sw) << 4)) = f32x4{acc[4 * c], acc[4 * c + 1], acc[4 * c + 2], acc[4 * c + 3]};
+  }
   __syncthreads();
 
-  // output (m, n_local), consecutive threads -> consecutive columns; the
-  // column n0 + tid % 32 is the same in every pass
-  for (int o = tid; o < 32 * 32; o += NW * 64) {
-    const int nl = o & 31, m = o >> 5;
-    if (m >= M) continue;
-    const int src_lane = m + 32 * ((nl >> 2) & 1);
-    const int v = (nl >> 3) * 4 + (nl & 3);
-    float z = 0.0f;
+  // Output (m, n0 + 4q + e), q = t % 8: accumulator v = 4 (q / 2) + e of
+  // lane m + 32 (q % 2) in every wave's record, summed in wave order; then
+  // bias, activation, conversion and one vector store of four outputs.
+  for (int t = tid; t < 256; t += NW * 64) {
+    const int om = t >> 3;
+    if (om >= M) break;
+    const int L = om + 32 * (oq & 1), c = oq >> 1;
+    f32x4 z = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int w = 0; w < NW; ++w) z += red[(w * 16 + v) * 64 + src_lane];
-    C[(int64_t)m * N + n0 + nl] = from_f32<TOut>(epilogue<EPI>(z, bias_v));
+    for (int w = 0; w < NW; ++w) z += *(const f32x4*)(record(w) + L * 64 + ((c ^ ((L >> 2) & 3)) << 4));
+    float v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float b = 0.0f;
+      if constexpr (epi_has_bias<EPI>())
+        b = to_f32(__builtin_bit_cast(TIn, (uint16_t)((e & 1) ? (bias_q[e >> 1] >> 16) : (bias_q[e >> 1] & 0xffffu))));
+      v[e] = epilogue<EPI>(z[e], b);
+    }
+    store4<TOut>(C + (int64_t)om * N + n0 + 4 * oq, v[0], v[1], v[2], v[3]);
   }
 }
 
-template <typename TIn, typename TOut, int NW, int P, int KC, bool A_LDS, int EPI>
+template <typename TIn, typename TOut, int NW, int P, int KC, int EPI>
 hipError_t launch_skinny(const LaunchArgs& a) {
-  hipLaunchKernelGGL((gemm_skinny_kernel<TIn, TOut, NW, P, KC, A_LDS, EPI>), dim3(a.N / 32), dim3(NW * 64), 0, a.stream,
+  hipLaunchKernelGGL((gemm_skinny_kernel<TIn, TOut, NW, P, KC, EPI>), dim3(a.N / 32), dim3(NW * 64), 0, a.stream,
                      (const TIn*)a.A, (const TIn*)a.B, (const TIn*)a.bias, (TOut*)a.C, a.M, a.N, a.K);
   return hipGetLastError();
 }
 
-template <typename TIn, typename TOut, int NW, int P, int KC, bool A_LDS>
+template <typename TIn, typename TOut, int NW, int P, int KC>
 LaunchFn pick_epi(int epi) {
   switch (epi) {
-    case GEMM_EPI_NONE: return &launch_skinny<TIn, TOut, NW, P, KC, A_LDS, GEMM_EPI_NONE>;
-    case GEMM_EPI_RELU: return &launch_skinny<TIn, TOut, NW, P, KC, A_LDS, GEMM_EPI_RELU>;
-    case GEMM_EPI_BIAS_RELU: return &launch_skinny<TIn, TOut, NW, P, KC, A_LDS, GEMM_EPI_BIAS_RELU>;
-    case GEMM_EPI_BIAS_GELU: return &launch_skinny<TIn, TOut, NW, P, KC, A_LDS, GEMM_EPI_BIAS_GELU>;
-    case GEMM_EPI_BIAS: return &launch_skinny<TIn, TOut, NW, P, KC, A_LDS, GEMM_EPI_BIAS>;
+    case GEMM_EPI_NONE: return &launch_skinny<TIn, TOut, NW, P, KC, GEMM_EPI_NONE>;
+    case GEMM_EPI_RELU: return &launch_skinny<TIn, TOut, NW, P, KC, GEMM_EPI_RELU>;
+    case GEMM_EPI_BIAS_RELU: return &launch_skinny<TIn, TOut, NW, P, KC, GEMM_EPI_BIAS_RELU>;
+    case GEMM_EPI_BIAS_GELU: return &launch_skinny<TIn, TOut, NW, P, KC, GEMM_EPI_BIAS_GELU>;
+    case GEMM_EPI_BIAS: return &launch_skinny<TIn, TOut, NW, P, KC, GEMM_EPI_BIAS>;
     default: return nullptr;
   }
 }
 
-template <int NW, int P, int KC, bool A_LDS>
+template <int NW, int P, int KC>
 LaunchFn pick_types(const Problem& p) {
   if (p.in_dt == GEMM_EPI_F16) {
-    if (p.out_dt == GEMM_EPI_F16) return pick_epi<f16, f16, NW, P, KC, A_LDS>(p.epi);
-    if (p.out_dt == GEMM_EPI_F32) return pick_epi<f16, float, NW, P, KC, A_LDS>(p.epi);
+    if (p.out_dt == GEMM_EPI_F16) return pick_epi<f16, f16, NW, P, KC>(p.epi);
+    if (p.out_dt == GEMM_EPI_F32) return pick_epi<f16, float, NW, P, KC>(p.epi);
   } else if (p.in_dt == GEMM_EPI_BF16) {
-    if (p.out_dt == GEMM_EPI_BF16) return pick_epi<bf16, bf16, NW, P, KC, A_LDS>(p.epi);
-    if (p.out_dt == GEMM_EPI_F32) return pick_epi<bf16, float, NW, P, KC, A_LDS>(p.epi);
+    if (p.out_dt == GEMM_EPI_BF16) return pick_epi<bf16, bf16, NW, P, KC>(p.epi);
+    if (p.out_dt == GEMM_EPI_F32) return pick_epi<bf16, float, NW, P, KC>(p.epi);
   }
   return nullptr;
 }
 
-// In order of preference; the plan takes the first one whose k granularity
-// (KC * P) divides K.  LDS ring = P x 32 rows x 2 KC bytes.
+// In order of preference; the plan takes the first one whose chunk divides
+// K into at least P chunks.  LDS: B and A rings, each P x 32 rows x 2 KC
+// bytes.
 const SkinnyConfig kSkinny[] = {
-    {4, 4, 256, 1, "skinny_32n_4w_4x256k_al"},   // B + A rings 64 + 64 KiB, 512-byte row segments
-    {8, 4, 256, 1, "skinny_32n_8w_4x256k_al"},   // same ring, more waves
-    {4, 8, 128, 1, "skinny_32n_4w_8x128k_al"},   // 64 + 64 KiB, 256-byte row segments, 7 chunks in flight
-    {8, 2, 512, 1, "skinny_32n_8w_2x512k_al"},   // 64 + 64 KiB, 1 KiB row segments
-    {8, 4, 512, 0, "skinny_32n_8w_4x512k"},      // B ring 128 KiB; A read into registers
-    {8, 4, 256, 0, "skinny_32n_8w_4x256k"},      // 64 KiB
-    {4, 2, 256, 0, "skinny_32n_4w_2x256k"},      // 32 KiB
-    {2, 2, 128, 0, "skinny_32n_2w_2x128k"},      // 16 KiB, 256-byte row segments; any K divisible by 256
+    {8, 5, 256, "skinny_32n_8w_5x256k"},  // 80 + 80 KiB: four chunks of 512-byte row segments in flight
+    {8, 4, 256, "skinny_32n_8w_4x256k"},  // 64 + 64 KiB
+    {4, 4, 256, "skinny_32n_4w_4x256k"},  // 64 + 64 KiB, fewer waves
+    {4, 8, 128, "skinny_32n_4w_8x128k"},  // 64 + 64 KiB, 256-byte row segments, seven chunks in flight
+    {4, 2, 256, "skinny_32n_4w_2x256k"},  // 32 + 32 KiB: K down to 512
+    {2, 2, 128, "skinny_32n_2w_2x128k"},  // 16 + 16 KiB: K down to 256
 };
 
 }  // namespace
@@ -285,10 +329,11 @@ const SkinnyConfig& skinny_config(int cfg) { return kSkinny[cfg]; }
 
 bool skinny_supports(int cfg, const Problem& p) {
   if (cfg < 0 || cfg >= skinny_num_configs()) return false;
-  const int64_t gran = (int64_t)kSkinny[cfg].kc * kSkinny[cfg].stages;
-  // 32 rows of B and all of A must be addressable by one buffer resource
+  // K in whole chunks, at least one turn of the ring; 32 rows of B and all
+  // of A must be addressable by one buffer resource
+  const SkinnyConfig& c = kSkinny[cfg];
   return p.M >= 1 && p.M <= 32 && p.la == GEMM_EPI_ROW_MAJOR && p.lb == GEMM_EPI_COL_MAJOR && p.N % 32 == 0 &&
-         p.K % gran == 0 && 32 * p.K * 2 < ((int64_t)1 << 32);
+         p.K % c.kc == 0 && p.K / c.kc >= c.stages && 32 * p.K * 2 < ((int64_t)1 << 32);
 }
 
 int skinny_choose(const Problem& p) {
@@ -299,14 +344,12 @@ int skinny_choose(const Problem& p) {
 
 LaunchFn skinny_launcher(int cfg, const Problem& p) {
   switch (cfg) {
-    case 0: return pick_types<4, 4, 256, true>(p);
-    case 1: return pick_types<8, 4, 256, true>(p);
-    case 2: return pick_types<4, 8, 128, true>(p);
-    case 3: return pick_types<8, 2, 512, true>(p);
-    case 4: return pick_types<8, 4, 512, false>(p);
-    case 5: return pick_types<8, 4, 256, false>(p);
-    case 6: return pick_types<4, 2, 256, false>(p);
-    case 7: return pick_types<2, 2, 128, false>(p);
+    case 0: return pick_types<8, 5, 256>(p);
+    case 1: return pick_types<8, 4, 256>(p);
+    case 2: return pick_types<4, 4, 256>(p);
+    case 3: return pick_types<4, 8, 128>(p);
+    case 4: return pick_types<4, 2, 256>(p);
+    case 5: return pick_types<2, 2, 128>(p);
     default: return nullptr;
   }
 }

@@ -42,7 +42,6 @@ struct SkinnyConfig {
   int waves;   // waves per workgroup
   int stages;  // LDS ring slots: chunks in flight + the one being multiplied
   int kc;      // k-values per chunk
-  int a_lds;   // 1: A's chunk is staged in LDS too (else read into registers)
   const char* name;
 };
 int skinny_num_configs();

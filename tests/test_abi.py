@@ -92,9 +92,9 @@ def test_run_rejects_invalid_arguments_without_touching_the_device(lib):
     (4096, 4096, 4096, "row", "row", "tile", "tile_256x256x64"),
     (1024, 1024, 1024, "row", "row", "tile", "tile_64x64x64"),
     (128, 64, 256, "row", "col", "tile", "tile_64x64x64"),
-    (32, 8192, 8192, "row", "col", "skinny", "skinny_32n_4w_4x256k_al"),
-    (1, 4096, 4096, "row", "col", "skinny", "skinny_32n_4w_4x256k_al"),
-    (32, 4096, 768, "row", "col", "skinny", "skinny_32n_2w_2x128k"),  # k granularity 256
+    (32, 8192, 8192, "row", "col", "skinny", "skinny_32n_8w_5x256k"),
+    (1, 4096, 4096, "row", "col", "skinny", "skinny_32n_8w_5x256k"),
+    (32, 4096, 768, "row", "col", "skinny", "skinny_32n_4w_2x256k"),  # three chunks of 256
     (32, 4096, 192, "row", "col", "generic", "generic"),
     (32, 8192, 8192, "row", "row", "generic", "generic"),  # small M, N-contiguous B: no fast path yet
     (37, 53, 29, "row", "row", "generic", "generic"),
@@ -113,7 +113,7 @@ def test_select_forces_and_validates(lib):
     h = gb.gemm_epi_plan(512, 512, 256, "f16", "f32", "row", "col", "none")
     try:
         assert gb.gemm_epi_num_configs("tile") == 6
-        assert gb.gemm_epi_num_configs("skinny") == 8
+        assert gb.gemm_epi_num_configs("skinny") == 6
         assert gb.gemm_epi_num_configs("generic") == 1
         assert gb.gemm_epi_num_configs("auto") == 0
         for cfg in range(4):
@@ -134,22 +134,24 @@ def test_select_forces_and_validates(lib):
         gb.gemm_epi_destroy(h)
     h = gb.gemm_epi_plan(32, 128, 1024, "bf16", "bf16", "row", "col", "bias")
     try:
-        assert gb.gemm_epi_plan_describe(h)[:2] == ("skinny", 0)  # first config whose k granularity divides K
-        assert gb.gemm_epi_plan_select(h, "skinny", 4) == 2  # 4 chunks of 512 do not divide 1024
-        assert gb.gemm_epi_plan_select(h, "skinny", 5) == 0
+        assert gb.gemm_epi_plan_describe(h)[:2] == ("skinny", 1)  # first config that fits
+        assert gb.gemm_epi_plan_select(h, "skinny", 0) == 2  # four chunks of 256 do not fill five slots
+        assert gb.gemm_epi_plan_select(h, "skinny", 3) == 0
         assert gb.gemm_epi_plan_select(h, "tile", -1) == 2  # M = 32 not a multiple of 64
     finally:
         gb.gemm_epi_destroy(h)
 
 
-# (k per chunk x ring slots) k granularity of each skinny configuration, in order
-SKINNY_GRAN = [1024, 1024, 1024, 1024, 2048, 1024, 512, 256]
+# (k per chunk, ring slots) of each skinny configuration, in order: K must
+# be whole chunks, at least one per slot
+SKINNY_CHUNKS = [(256, 5), (256, 4), (256, 4), (128, 8), (256, 2), (128, 2)]
 
 
 def test_skinny_k_granularity(lib):
-    assert gb.gemm_epi_num_configs("skinny") == len(SKINNY_GRAN)
-    for cfg, g in enumerate(SKINNY_GRAN):
-        for K, ok in ((g, True), (g + 128, False)):
+    assert gb.gemm_epi_num_configs("skinny") == len(SKINNY_CHUNKS)
+    for cfg, (kc, slots) in enumerate(SKINNY_CHUNKS):
+        for K, ok in ((kc * slots, True), (kc * (slots + 1), True), (kc * (slots - 1), False),
+                      (kc * slots + 64, False)):
             h = gb.gemm_epi_plan(32, 64, K, "bf16", "bf16", "row", "col", "none")
             try:
                 assert (gb.gemm_epi_plan_select(h, "skinny", cfg) == 0) == ok, (cfg, K)

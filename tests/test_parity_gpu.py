@@ -106,17 +106,19 @@ def test_ring_integer_bitexact(config, M, N, K, in_dt, out_dt):
         assert name.startswith("ring_")
 
 
-# (k per chunk x ring slots) k granularity of each skinny configuration, in order
-SKINNY_GRAN = [1024, 1024, 1024, 1024, 2048, 1024, 512, 256]
+# (k per chunk, ring slots) of each skinny configuration, in order
+SKINNY_CHUNKS = [(256, 5), (256, 4), (256, 4), (128, 8), (256, 2), (128, 2)]
 
 
-@pytest.mark.parametrize("config", range(len(SKINNY_GRAN)))
+@pytest.mark.parametrize("config", range(len(SKINNY_CHUNKS)))
 @pytest.mark.parametrize("M", [1, 7, 31, 32])
 @pytest.mark.parametrize("in_dt,out_dt", [("bf16", "bf16"), ("f16", "f16"), ("bf16", "f32")])
 def test_skinny_integer_bitexact(config, M, in_dt, out_dt):
-    # one and several ring turns per wave
+    # one ring turn; then chunk counts that leave a head of one and of
+    # P - 1 chunks before the whole turns
     N = 96
-    cases = [(SKINNY_GRAN[config], epi) for epi in EPIS] + [(3 * SKINNY_GRAN[config], "bias_relu")]
+    kc, slots = SKINNY_CHUNKS[config]
+    cases = [(kc * slots, epi) for epi in EPIS] + [(kc * (2 * slots + 1), "bias_relu"), (kc * (2 * slots - 1), "bias")]
     for K, epi in cases:
         bits = inputs.integer_inputs(M, N, K, in_dt, "row", "col", epi.startswith("bias"), seed=M + config)
         name = check_case(bits, M, N, K, in_dt, out_dt, "row", "col", epi, "skinny", config, epi in BITWISE_EPIS)
@@ -146,10 +148,13 @@ def test_generic_integer_bitexact(M, N, K, la, lb):
     ("tile", 1, 384, 256, 1024, "row", "row"),
     ("tile", 2, 320, 192, 448, "col", "col"),
     ("skinny", 0, 32, 512, 4096, "row", "col"),
-    ("skinny", 7, 5, 160, 768, "row", "col"),
+    ("skinny", 5, 5, 160, 768, "row", "col"),
     ("skinny", 0, 17, 256, 6144, "row", "col"),
-    ("skinny", 2, 32, 96, 3072, "row", "col"),
-    ("skinny", 4, 3, 64, 6144, "row", "col"),
+    ("skinny", 3, 32, 96, 3072, "row", "col"),
+    ("skinny", 1, 3, 64, 6144, "row", "col"),
+    ("skinny", 0, 32, 256, 8192, "row", "col"),
+    ("skinny", 2, 11, 128, 4352, "row", "col"),
+    ("skinny", 4, 29, 64, 1792, "row", "col"),
     ("generic", 0, 97, 61, 333, "row", "row"),
     ("generic", 0, 64, 64, 4096, "col", "col"),
 ])
