@@ -58,17 +58,20 @@ __device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
 // Epilogue on an fp32 accumulator value z with its column's bias b.
 //   GELU: x / (1 + exp(-1.5957691216 (x + 0.044715 x^3))), the tanh form of
 //   GELU as a logistic (ainew.jp "TileLang で GPU カーネル設計を解説",
-//   section 4 "EPILOGUE FUSION").  exp(u) is evaluated as 2^(u log2 e) with
-//   the hardware exp2 (v_exp_f32) and the quotient with v_rcp_f32; both are
-//   accurate to about one fp32 ulp, far below the 16-bit output spacing.
-//   Large negative x: 2^(+big) = +inf, 1/inf = 0, result -0.  Large
-//   positive x: 2^(-big) = 0, result x.
+//   section 4 "EPILOGUE FUSION").  The exponent is regrouped as
+//   x (c1 + c2 x^2) with log2 e folded into c1 = -1.5957691216 log2 e and
+//   c2 = -1.5957691216 * 0.044715 log2 e, so that exp is the hardware exp2
+//   (v_exp_f32) of one product and the quotient is v_rcp_f32: seven
+//   operations, each accurate to about one fp32 ulp, far below the 16-bit
+//   output spacing.  Large negative x: 2^(+big) = +inf, 1/inf = 0, result
+//   -0.  Large positive x: 2^(-big) = 0, result x.
 // Bias is added first, then the activation (csdn tutorial ch.10
 // sec. 10.8 "GEMM Epilogue 融合").
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float gelu_logistic(float x) {
-  const float u = -1.5957691216f * (x + 0.044715f * x * x * x);
-  const float e = __builtin_amdgcn_exp2f(u * 1.4426950408889634f);
+  constexpr float c1 = (float)(-1.5957691216 * 1.4426950408889634);
+  constexpr float c2 = (float)(-1.5957691216 * 0.044715 * 1.4426950408889634);
+  const float e = __builtin_amdgcn_exp2f(x * __builtin_fmaf(c2, x * x, c1));
   return x * __builtin_amdgcn_rcpf(1.0f + e);
 }
 

@@ -22,8 +22,6 @@ LaunchFn generic_launcher(const Problem& p);
 struct TileConfig {
   int bm, bn;  // workgroup tile
   int waves;   // waves per workgroup
-  int ring;    // 1: four-slot ring of 32-deep k-steps (k-contiguous A and B
-               // only, K a multiple of 128); 0: two 64-deep stages
   const char* name;
 };
 int tile_num_configs();

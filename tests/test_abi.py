@@ -88,8 +88,9 @@ def test_run_rejects_invalid_arguments_without_touching_the_device(lib):
 
 
 @pytest.mark.parametrize("M,N,K,la,lb,want_kernel,want_name", [
-    (8192, 8192, 8192, "row", "col", "tile", "tile_256x256x64"),
+    (8192, 8192, 8192, "row", "col", "tile", "tile_256x256x64_8w"),
     (4096, 4096, 4096, "row", "row", "tile", "tile_256x256x64"),
+    (4096, 4096, 4096, "row", "col", "tile", "tile_256x256x64_8w"),
     (1024, 1024, 1024, "row", "row", "tile", "tile_64x64x64"),
     (128, 64, 256, "row", "col", "tile", "tile_64x64x64"),
     (32, 8192, 8192, "row", "col", "skinny", "skinny_32n_8w_5x256k"),
@@ -112,21 +113,18 @@ def test_auto_selection(lib, M, N, K, la, lb, want_kernel, want_name):
 def test_select_forces_and_validates(lib):
     h = gb.gemm_epi_plan(512, 512, 256, "f16", "f32", "row", "col", "none")
     try:
-        assert gb.gemm_epi_num_configs("tile") == 6
+        assert gb.gemm_epi_num_configs("tile") == 4
         assert gb.gemm_epi_num_configs("skinny") == 6
         assert gb.gemm_epi_num_configs("generic") == 1
         assert gb.gemm_epi_num_configs("auto") == 0
         for cfg in range(4):
             assert gb.gemm_epi_plan_select(h, "tile", cfg) == 0
             assert gb.gemm_epi_plan_describe(h)[:2] == ("tile", cfg)
-        for cfg in (4, 5):  # ring kernels: K = 256 is a multiple of 128, A row- and B column-major
-            assert gb.gemm_epi_plan_select(h, "tile", cfg) == 0
-            assert gb.gemm_epi_plan_describe(h)[:2] == ("tile", cfg)
         assert gb.gemm_epi_plan_select(h, "generic", 0) == 0
         assert gb.gemm_epi_plan_describe(h)[0] == "generic"
         assert gb.gemm_epi_plan_select(h, "skinny", -1) == 2  # M = 512 > 32: unsupported, plan unchanged
         assert gb.gemm_epi_plan_describe(h)[0] == "generic"
-        assert gb.gemm_epi_plan_select(h, "tile", 6) == 1  # no such config
+        assert gb.gemm_epi_plan_select(h, "tile", 4) == 1  # no such config
         assert lib.gemm_epi_plan_select(ctypes.c_void_p(h), 9, 0) == 1  # bad enum
         assert gb.gemm_epi_plan_select(h, "auto", -1) == 0
         assert gb.gemm_epi_plan_describe(h) == ("tile", 2, "tile_64x64x64")  # 64 workgroups beats 16
