@@ -38,7 +38,7 @@ PEAK_HBM_GBS = 8000.0
 CSRC = os.path.join(ROOT, "epilogue_gemm_amd", "csrc")
 # sources that define each kernel family's device code and launch shape
 _FAMILY_SOURCES = {
-    "tile": ["common.hpp", "kernels.hpp", "gemm_tile.hpp", "gemm_tile_bf16_bf16.hip", "gemm_tile_bf16_f32.hip",
+    "tile": ["common.hpp", "kernels.hpp", "gemm_tile.hpp", "tile_dispatch.hpp", "gemm_tile_bf16_bf16.hip", "gemm_tile_bf16_f32.hip",
              "gemm_tile_f16_f16.hip", "gemm_tile_f16_f32.hip", "gemm_epi.cpp"],
     "skinny": ["common.hpp", "kernels.hpp", "gemm_skinny.hip", "gemm_epi.cpp"],
 }
@@ -138,7 +138,7 @@ def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--only", choices=["main", "skinny", "both"], default="both")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
