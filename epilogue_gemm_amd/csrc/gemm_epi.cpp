@@ -14,14 +14,11 @@ namespace ge {
 // each owning (BM/2) x (BN/(waves/2)).  Larger tiles reuse each loaded byte
 // more; smaller ones give small problems enough workgroups for 256 CUs;
 // 8 waves put two on each SIMD so one can multiply while the other waits.
-// The ping-pong configuration splits its 8 waves into two groups that take
-// turns multiplying and moving data (k-contiguous operands only).
 static const TileConfig kTile[] = {
-    {256, 256, 4, 0, "tile_256x256x64"},
-    {128, 128, 4, 0, "tile_128x128x64"},
-    {64, 64, 4, 0, "tile_64x64x64"},
-    {256, 256, 8, 0, "tile_256x256x64_8w"},
-    {256, 256, 8, 1, "tile_256x256x64_pp"},
+    {256, 256, 4, "tile_256x256x64"},
+    {128, 128, 4, "tile_128x128x64"},
+    {64, 64, 4, "tile_64x64x64"},
+    {256, 256, 8, "tile_256x256x64_8w"},
 };
 
 int tile_num_configs() { return (int)(sizeof(kTile) / sizeof(kTile[0])); }
@@ -30,7 +27,6 @@ const TileConfig& tile_config(int cfg) { return kTile[cfg]; }
 bool tile_supports(int cfg, const Problem& p) {
   if (cfg < 0 || cfg >= tile_num_configs()) return false;
   const TileConfig& c = kTile[cfg];
-  if (c.kcontig && (p.la != GEMM_EPI_ROW_MAJOR || p.lb != GEMM_EPI_COL_MAJOR || p.K % 128 != 0)) return false;
   return p.M % c.bm == 0 && p.N % c.bn == 0 && p.K % 64 == 0 && p.K >= 128;
 }
 

@@ -22,7 +22,6 @@ LaunchFn generic_launcher(const Problem& p);
 struct TileConfig {
   int bm, bn;  // workgroup tile
   int waves;   // waves per workgroup
-  int kcontig;  // 1: A row-major and B column-major only
   const char* name;
 };
 int tile_num_configs();

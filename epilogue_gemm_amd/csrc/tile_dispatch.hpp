@@ -2,7 +2,7 @@
 // output format, in the order of the host-side table (gemm_epi.cpp).
 #pragma once
 
-#include "gemm_pingpong.hpp"
+#include "gemm_tile.hpp"
 
 namespace ge {
 namespace tile {
@@ -14,7 +14,6 @@ LaunchFn pick_config(int cfg, int la, int lb, int epi) {
     case 1: return pick_layout<128, 128, 4, TIn, TOut>(la, lb, epi);
     case 2: return pick_layout<64, 64, 4, TIn, TOut>(la, lb, epi);
     case 3: return pick_layout<256, 256, 8, TIn, TOut>(la, lb, epi);
-    case 4: return pingpong::pick<TIn, TOut>(la, lb, epi);
     default: return nullptr;
   }
 }

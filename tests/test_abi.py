@@ -113,18 +113,18 @@ def test_auto_selection(lib, M, N, K, la, lb, want_kernel, want_name):
 def test_select_forces_and_validates(lib):
     h = gb.gemm_epi_plan(512, 512, 256, "f16", "f32", "row", "col", "none")
     try:
-        assert gb.gemm_epi_num_configs("tile") == 5
+        assert gb.gemm_epi_num_configs("tile") == 4
         assert gb.gemm_epi_num_configs("skinny") == 6
         assert gb.gemm_epi_num_configs("generic") == 1
         assert gb.gemm_epi_num_configs("auto") == 0
-        for cfg in range(5):  # the ping-pong one too: A row-, B column-major, K = 256
+        for cfg in range(4):
             assert gb.gemm_epi_plan_select(h, "tile", cfg) == 0
             assert gb.gemm_epi_plan_describe(h)[:2] == ("tile", cfg)
         assert gb.gemm_epi_plan_select(h, "generic", 0) == 0
         assert gb.gemm_epi_plan_describe(h)[0] == "generic"
         assert gb.gemm_epi_plan_select(h, "skinny", -1) == 2  # M = 512 > 32: unsupported, plan unchanged
         assert gb.gemm_epi_plan_describe(h)[0] == "generic"
-        assert gb.gemm_epi_plan_select(h, "tile", 5) == 1  # no such config
+        assert gb.gemm_epi_plan_select(h, "tile", 4) == 1  # no such config
         assert lib.gemm_epi_plan_select(ctypes.c_void_p(h), 9, 0) == 1  # bad enum
         assert gb.gemm_epi_plan_select(h, "auto", -1) == 0
         assert gb.gemm_epi_plan_describe(h) == ("tile", 2, "tile_64x64x64")  # 64 workgroups beats 16
