@@ -77,12 +77,16 @@ __device__ __forceinline__ void ring_slots(char* (&s)[P], std::integer_sequence<
 // once each wave has at most PENDING of its own memory operations
 // outstanding and all waves have met; the barrier also orders every wave's
 // reads of the previous slot before the loads that overwrite it.
+// (The empty asm statements with a memory clobber keep the compiler from
+// moving LDS accesses across the barrier, which orders no memory for it.)
 template <int PENDING>
 __device__ __forceinline__ void arrive() {
+  asm volatile("" ::: "memory");
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(PENDING));
   __builtin_amdgcn_sched_barrier(0);
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
 }
 
 template <typename TIn, typename TOut, int NW, int P, int KC, int EPI>

@@ -253,10 +253,16 @@ __device__ __forceinline__ void write_tile(const f32x16 (&acc)[WM / 32][WN / 32]
 // VM of its own vector-memory operations are outstanding (its direct loads
 // of the next tile are then in LDS) and its LDS writes are done; unlike
 // __syncthreads(), loads issued later may stay in flight.
+// The empty asm statements with a memory clobber keep the compiler from
+// moving any memory access across the barrier (the barrier builtin itself
+// orders no memory for the compiler, and other waves' accesses are what it
+// synchronises).
 template <int VM>
 __device__ __forceinline__ void kloop_barrier() {
+  asm volatile("" ::: "memory");
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(VM) & ~(15 << 8));  // vmcnt(VM) lgkmcnt(0)
   __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 template <int BM, int BN, int NW, typename TIn, typename TOut, bool A_KMAJ, bool B_KMAJ, int EPI>
