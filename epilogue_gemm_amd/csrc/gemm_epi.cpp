@@ -26,8 +26,13 @@ const TileConfig& tile_config(int cfg) { return kTile[cfg]; }
 
 bool tile_supports(int cfg, const Problem& p) {
   if (cfg < 0 || cfg >= tile_num_configs()) return false;
+  // M and N need not be tile multiples (the last tile row or column is
+  // shifted back to end at M or N), but must hold one tile; rows of every
+  // operand and of C must stay 16-byte aligned (N % 8; M % 8 when A is
+  // column-major), and K must be whole k-steps.
   const TileConfig& c = kTile[cfg];
-  return p.M % c.bm == 0 && p.N % c.bn == 0 && p.K % 64 == 0 && p.K >= 128;
+  return p.M >= c.bm && p.N >= c.bn && p.N % 8 == 0 && (p.la == GEMM_EPI_ROW_MAJOR || p.M % 8 == 0) &&
+         p.K % 64 == 0 && p.K >= 128;
 }
 
 int tile_choose(const Problem& p) {
@@ -40,7 +45,7 @@ int tile_choose(const Problem& p) {
   int fallback = -1;
   for (int c = 0; c < 3; ++c) {
     if (!tile_supports(c, p)) continue;
-    const int64_t tiles = (p.M / kTile[c].bm) * (p.N / kTile[c].bn);
+    const int64_t tiles = ((p.M + kTile[c].bm - 1) / kTile[c].bm) * ((p.N + kTile[c].bn - 1) / kTile[c].bn);
     if (tiles >= 256) {
       fallback = c;
       break;

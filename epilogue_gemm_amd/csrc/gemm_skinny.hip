@@ -9,7 +9,8 @@
 //
 //   - a workgroup owns 32 consecutive output columns n and all of K, so
 //     there is no reduction across workgroups and bias and activation are
-//     applied exactly once;
+//     applied exactly once (when N % 32 != 0 the last workgroup's columns
+//     overlap its neighbour's, which it rewrites with identical values);
 //   - K is walked in chunks of KC values.  A chunk of B is 32 rows x KC
 //     k-values, and every row segment of it (2 KC bytes) is contiguous in
 //     memory: the NW waves copy it into one LDS ring slot with 128-bit
@@ -103,7 +104,10 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const TIn* __restr
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int n0 = blockIdx.x * 32;
+  // When N % 32 != 0 the last workgroup's columns are shifted back to end
+  // at N: it recomputes (and rewrites, with identical values) some of its
+  // neighbour's columns, and no access leaves B, bias or C.
+  const int n0 = min((int)blockIdx.x * 32, N - 32);
   const int nchunks = K / KC;  // at least P (checked on the host)
 
   // Workgroup b walks the chunks starting at chunk b (mod the count): at
@@ -285,7 +289,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const TIn* __restr
 
 template <typename TIn, typename TOut, int NW, int P, int KC, int EPI>
 hipError_t launch_skinny(const LaunchArgs& a) {
-  hipLaunchKernelGGL((gemm_skinny_kernel<TIn, TOut, NW, P, KC, EPI>), dim3(a.N / 32), dim3(NW * 64), 0, a.stream,
+  hipLaunchKernelGGL((gemm_skinny_kernel<TIn, TOut, NW, P, KC, EPI>), dim3((a.N + 31) / 32), dim3(NW * 64), 0, a.stream,
                      (const TIn*)a.A, (const TIn*)a.B, (const TIn*)a.bias, (TOut*)a.C, a.M, a.N, a.K);
   return hipGetLastError();
 }
@@ -336,7 +340,7 @@ bool skinny_supports(int cfg, const Problem& p) {
   // K in whole chunks, at least one turn of the ring; 32 rows of B and all
   // of A must be addressable by one buffer resource
   const SkinnyConfig& c = kSkinny[cfg];
-  return p.M >= 1 && p.M <= 32 && p.la == GEMM_EPI_ROW_MAJOR && p.lb == GEMM_EPI_COL_MAJOR && p.N % 32 == 0 &&
+  return p.M >= 1 && p.M <= 32 && p.la == GEMM_EPI_ROW_MAJOR && p.lb == GEMM_EPI_COL_MAJOR && p.N >= 32 && p.N % 8 == 0 &&
          p.K % c.kc == 0 && p.K / c.kc >= c.stages && 32 * p.K * 2 < ((int64_t)1 << 32);
 }
 

@@ -295,7 +295,11 @@ __global__ __launch_bounds__(NW * 64) void gemm_tile_kernel(const TIn* __restric
 
   int tm, tn;
   raster(blockIdx.x, tiles_m, tiles_n, panel, tm, tn);
-  const int m0 = tm * BM, n0 = tn * BN;
+  // When M or N is not a tile multiple, the last tile row or column is
+  // shifted back to end at M or N: it recomputes (and rewrites, with
+  // identical values) part of its neighbour, and no access leaves A, B,
+  // bias or C.
+  const int m0 = min(tm * BM, M - BM), n0 = min(tn * BN, N - BN);
 
   // Operand movers: direct (k-contiguous) or register-staged (transposed).
   // The unused kind of each operand is never called.
@@ -461,7 +465,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_tile_kernel(const TIn* __restric
 // Host launch of one instantiation.
 template <int BM, int BN, int NW, typename TIn, typename TOut, bool A_KMAJ, bool B_KMAJ, int EPI>
 hipError_t launch(const LaunchArgs& a) {
-  const int tiles_m = a.M / BM, tiles_n = a.N / BN;
+  const int tiles_m = (a.M + BM - 1) / BM, tiles_n = (a.N + BN - 1) / BN;
   const int panel = tiles_m < 4 ? tiles_m : 4;
   hipLaunchKernelGGL((gemm_tile_kernel<BM, BN, NW, TIn, TOut, A_KMAJ, B_KMAJ, EPI>), dim3(tiles_m * tiles_n),
                      dim3(NW * 64), 0, a.stream, (const TIn*)a.A, (const TIn*)a.B, (const TIn*)a.bias, (TOut*)a.C,

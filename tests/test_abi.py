@@ -96,8 +96,14 @@ def test_run_rejects_invalid_arguments_without_touching_the_device(lib):
     (32, 8192, 8192, "row", "col", "skinny", "skinny_32n_8w_5x256k"),
     (1, 4096, 4096, "row", "col", "skinny", "skinny_32n_8w_5x256k"),
     (32, 4096, 768, "row", "col", "skinny", "skinny_32n_4w_2x256k"),  # three chunks of 256
-    (32, 4096, 192, "row", "col", "generic", "generic"),
+    (32, 4096, 192, "row", "col", "generic", "generic"),  # K too short for a skinny ring, M for a tile
     (32, 8192, 8192, "row", "row", "generic", "generic"),  # small M, N-contiguous B: no fast path yet
+    (2000, 8200, 4096, "row", "col", "tile", "tile_256x256x64_8w"),  # last tile row and column shifted back
+    (1000, 1000, 1024, "row", "col", "tile", "tile_64x64x64"),  # 16 x 16 edge-tiled 64 x 64 tiles
+    (3000, 2000, 4096, "row", "row", "tile", "tile_128x128x64"),  # 24 x 16 tiles of 128
+    (1000, 1000, 1024, "col", "col", "tile", "tile_64x64x64"),
+    (1001, 1000, 1024, "col", "col", "generic", "generic"),  # column-major A needs M % 8
+    (1000, 1004, 1024, "row", "col", "generic", "generic"),  # N % 8
     (37, 53, 29, "row", "row", "generic", "generic"),
     (256, 256, 100, "col", "row", "generic", "generic"),  # K not a multiple of 64
 ])
@@ -135,7 +141,7 @@ def test_select_forces_and_validates(lib):
         assert gb.gemm_epi_plan_describe(h)[:2] == ("skinny", 1)  # first config that fits
         assert gb.gemm_epi_plan_select(h, "skinny", 0) == 2  # four chunks of 256 do not fill five slots
         assert gb.gemm_epi_plan_select(h, "skinny", 3) == 0
-        assert gb.gemm_epi_plan_select(h, "tile", -1) == 2  # M = 32 not a multiple of 64
+        assert gb.gemm_epi_plan_select(h, "tile", -1) == 2  # M = 32 holds no 64 x 64 tile
     finally:
         gb.gemm_epi_destroy(h)
 

@@ -91,6 +91,33 @@ def test_tile_integer_bitexact(config, la, lb, in_dt, out_dt):
         assert name.startswith("tile_")
 
 
+# M and N that are not tile multiples: the last tile row and column are
+# shifted back to end at M and N and overlap their neighbours
+TILE_EDGE_SHAPES = {0: (264, 520, 192), 1: (200, 136, 128), 2: (72, 200, 256), 3: (304, 264, 128)}
+
+
+@pytest.mark.parametrize("config", [0, 1, 2, 3])
+@pytest.mark.parametrize("la,lb", [("row", "col"), ("row", "row"), ("col", "col"), ("col", "row")])
+@pytest.mark.parametrize("in_dt,out_dt", [("bf16", "bf16"), ("f16", "f32")])
+def test_tile_edge_integer_bitexact(config, la, lb, in_dt, out_dt):
+    M, N, K = TILE_EDGE_SHAPES[config]
+    for epi in ("relu", "bias_relu"):
+        bits = inputs.integer_inputs(M, N, K, in_dt, la, lb, epi.startswith("bias"), seed=config * 11 + len(epi))
+        name = check_case(bits, M, N, K, in_dt, out_dt, la, lb, epi, "tile", config, True)
+        assert name.startswith("tile_")
+
+
+@pytest.mark.parametrize("M", [1, 32])
+@pytest.mark.parametrize("N", [40, 1000])
+def test_skinny_edge_integer_bitexact(M, N):
+    # N % 32 != 0: the last workgroup's columns are shifted back to end at N
+    K = 1280
+    for in_dt, out_dt, epi in (("bf16", "bf16", "bias_relu"), ("f16", "f32", "bias")):
+        bits = inputs.integer_inputs(M, N, K, in_dt, "row", "col", True, seed=M + N)
+        name = check_case(bits, M, N, K, in_dt, out_dt, "row", "col", epi, "auto", -1, True)
+        assert name.startswith("skinny_")
+
+
 # (k per chunk, ring slots) of each skinny configuration, in order
 SKINNY_CHUNKS = [(256, 5), (256, 4), (256, 4), (128, 8), (256, 2), (128, 2)]
 
@@ -128,6 +155,8 @@ def test_generic_integer_bitexact(M, N, K, la, lb):
     ("tile", 0, 512, 768, 640, "row", "row"),
     ("tile", 3, 512, 1024, 704, "row", "col"),
     ("tile", 3, 768, 512, 384, "row", "row"),
+    ("tile", 3, 1000, 1000, 1024, "row", "col"),
+    ("tile", 2, 1000, 1000, 1024, "col", "row"),
     ("tile", 1, 384, 256, 1024, "row", "row"),
     ("tile", 2, 320, 192, 448, "col", "col"),
     ("skinny", 0, 32, 512, 4096, "row", "col"),
