@@ -55,6 +55,10 @@ def load_library(path: str = LIB_PATH):
     lib.gemm_epi_plan.restype = i32
     lib.gemm_epi_run.argtypes = [vp, vp, vp, vp, vp, vp]
     lib.gemm_epi_run.restype = i32
+    lib.gemm_epi_workspace_size.argtypes = [vp]
+    lib.gemm_epi_workspace_size.restype = ctypes.c_size_t
+    lib.gemm_epi_run_ws.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.gemm_epi_run_ws.restype = i32
     lib.gemm_epi_destroy.argtypes = [vp]
     lib.gemm_epi_destroy.restype = i32
     lib.gemm_epi_status_string.argtypes = [i32]
@@ -107,6 +111,14 @@ def gemm_epi_plan_status(M, N, K, in_dtype, out_dtype, layout_a, layout_b, epilo
 
 def gemm_epi_run(plan, A_ptr, B_ptr, bias_ptr, C_ptr, stream) -> int:
     return load_library().gemm_epi_run(plan, A_ptr, B_ptr, bias_ptr, C_ptr, stream)
+
+
+def gemm_epi_workspace_size(plan) -> int:
+    return int(load_library().gemm_epi_workspace_size(plan))
+
+
+def gemm_epi_run_ws(plan, A_ptr, B_ptr, bias_ptr, C_ptr, ws_ptr, ws_bytes, stream) -> int:
+    return load_library().gemm_epi_run_ws(plan, A_ptr, B_ptr, bias_ptr, C_ptr, ws_ptr, int(ws_bytes), stream)
 
 
 def gemm_epi_destroy(plan) -> int:
@@ -176,7 +188,14 @@ class Plan:
             raise ValueError(f"{name}: {t.numel()} elements, expected {numel}")
         return t.data_ptr()
 
-    def run(self, A, B, bias, C, stream=None):
+    @property
+    def workspace_size(self) -> int:
+        """Bytes of workspace that let ``run`` split K (0: never splits)."""
+        return gemm_epi_workspace_size(self.handle)
+
+    def run(self, A, B, bias, C, stream=None, workspace=None):
+        """``workspace``: an optional zero-filled uint8 CUDA tensor of at least
+        ``workspace_size`` bytes (left zero-filled by every completed run)."""
         import torch
 
         a = self._check(A, "A", self.in_dtype, self.M * self.K)
@@ -184,9 +203,17 @@ class Plan:
         bi = self._check(bias, "bias", self.in_dtype, self.N)
         c = self._check(C, "C", self.out_dtype, self.M * self.N)
         s = (stream or torch.cuda.current_stream()).cuda_stream
-        st = gemm_epi_run(self.handle, a, b, bi, c, s)
+        if workspace is None:
+            st = gemm_epi_run(self.handle, a, b, bi, c, s)
+            fn = "gemm_epi_run"
+        else:
+            if not workspace.is_cuda or not workspace.is_contiguous():
+                raise ValueError("workspace: expected a contiguous CUDA tensor")
+            nbytes = workspace.numel() * workspace.element_size()
+            st = gemm_epi_run_ws(self.handle, a, b, bi, c, workspace.data_ptr(), nbytes, s)
+            fn = "gemm_epi_run_ws"
         if st != OK:
-            raise GemmEpiError("gemm_epi_run", st)
+            raise GemmEpiError(fn, st)
 
     def close(self):
         if self.handle is not None:

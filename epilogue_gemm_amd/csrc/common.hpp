@@ -46,6 +46,11 @@ struct LaunchArgs {
   int epi;     // gemm_epi_epilogue
   int la, lb;  // gemm_epi_layout of A and B
   hipStream_t stream;
+  // split-K skinny launches only: caller workspace (partials, then
+  // arrival counters; zero-filled before first use, left zeroed) and the
+  // number of K splits (1: no split, no workspace)
+  void* workspace;
+  int split;
 };
 
 // ---------------------------------------------------------------------------

@@ -71,6 +71,7 @@ struct gemm_epi_plan_s {
   ge::LaunchFn fn;       // chosen family
   ge::LaunchFn generic;  // fallback for unaligned pointers
   const char* name;
+  int split;  // K splits of a skinny plan when run with a workspace (1: none)
 };
 
 namespace {
@@ -105,6 +106,7 @@ bool resolve(gemm_epi_plan_s* pl, int kernel, int config) {
     pl->config = 0;
     pl->fn = pl->generic;
     pl->name = "generic";
+    pl->split = 1;
     return pl->fn != nullptr;
   }
   if (kernel == GEMM_EPI_KERNEL_TILE) {
@@ -116,6 +118,7 @@ bool resolve(gemm_epi_plan_s* pl, int kernel, int config) {
     pl->config = config;
     pl->fn = fn;
     pl->name = ge::tile_config(config).name;
+    pl->split = 1;
     return true;
   }
   if (kernel == GEMM_EPI_KERNEL_SKINNY) {
@@ -127,12 +130,55 @@ bool resolve(gemm_epi_plan_s* pl, int kernel, int config) {
     pl->config = config;
     pl->fn = fn;
     pl->name = ge::skinny_config(config).name;
+    pl->split = ge::skinny_split(config, p);
     return true;
   }
   return false;
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Workspace of a split-K skinny run: one fp32 32 x 32 partial block per
+// (column block, split), then one arrival counter per column block.
+size_t workspace_bytes(const gemm_epi_plan_s* pl) {
+  if (pl->kernel != GEMM_EPI_KERNEL_SKINNY || pl->split <= 1) return 0;
+  const size_t nblocks = (size_t)((pl->p.N + 31) / 32);
+  return nblocks * (size_t)pl->split * 4096 + ((nblocks * 4 + 255) & ~(size_t)255);
+}
+
+gemm_epi_status launch(gemm_epi_plan_t plan, const void* A, const void* B, const void* bias, void* C,
+                       void* workspace, size_t ws_bytes, void* stream) {
+  if (!plan || !A || !B || !C) return GEMM_EPI_ERR_INVALID_ARG;
+  const bool need_bias = uses_bias(plan->p.epi);
+  if (need_bias != (bias != nullptr)) return GEMM_EPI_ERR_INVALID_ARG;
+  ge::LaunchArgs a;
+  a.A = A;
+  a.B = B;
+  a.bias = bias;
+  a.C = C;
+  a.M = (int)plan->p.M;
+  a.N = (int)plan->p.N;
+  a.K = (int)plan->p.K;
+  a.epi = plan->p.epi;
+  a.la = plan->p.la;
+  a.lb = plan->p.lb;
+  a.stream = (hipStream_t)stream;
+  a.workspace = nullptr;
+  a.split = 1;
+  const bool aligned = aligned16(A) && aligned16(B) && aligned16(C) && (!bias || aligned16(bias));
+  const size_t need = workspace_bytes(plan);
+  if (aligned && need > 0 && workspace && aligned16(workspace) && ws_bytes >= need) {
+    a.workspace = workspace;
+    a.split = plan->split;
+  }
+  ge::LaunchFn fn = aligned ? plan->fn : plan->generic;
+  const hipError_t e = fn(a);
+  if (e != hipSuccess) {
+    g_last_hip_error = (int)e;
+    return GEMM_EPI_ERR_HIP;
+  }
+  return GEMM_EPI_OK;
+}
 
 }  // namespace
 
@@ -160,29 +206,14 @@ gemm_epi_status gemm_epi_plan(gemm_epi_plan_t* out, int64_t M, int64_t N, int64_
 
 gemm_epi_status gemm_epi_run(gemm_epi_plan_t plan, const void* A, const void* B, const void* bias, void* C,
                              void* stream) {
-  if (!plan || !A || !B || !C) return GEMM_EPI_ERR_INVALID_ARG;
-  const bool need_bias = uses_bias(plan->p.epi);
-  if (need_bias != (bias != nullptr)) return GEMM_EPI_ERR_INVALID_ARG;
-  ge::LaunchArgs a;
-  a.A = A;
-  a.B = B;
-  a.bias = bias;
-  a.C = C;
-  a.M = (int)plan->p.M;
-  a.N = (int)plan->p.N;
-  a.K = (int)plan->p.K;
-  a.epi = plan->p.epi;
-  a.la = plan->p.la;
-  a.lb = plan->p.lb;
-  a.stream = (hipStream_t)stream;
-  const bool aligned = aligned16(A) && aligned16(B) && aligned16(C) && (!bias || aligned16(bias));
-  ge::LaunchFn fn = aligned ? plan->fn : plan->generic;
-  const hipError_t e = fn(a);
-  if (e != hipSuccess) {
-    g_last_hip_error = (int)e;
-    return GEMM_EPI_ERR_HIP;
-  }
-  return GEMM_EPI_OK;
+  return launch(plan, A, B, bias, C, nullptr, 0, stream);
+}
+
+size_t gemm_epi_workspace_size(gemm_epi_plan_t plan) { return plan ? workspace_bytes(plan) : 0; }
+
+gemm_epi_status gemm_epi_run_ws(gemm_epi_plan_t plan, const void* A, const void* B, const void* bias, void* C,
+                                void* workspace, size_t workspace_bytes_given, void* stream) {
+  return launch(plan, A, B, bias, C, workspace, workspace_bytes_given, stream);
 }
 
 gemm_epi_status gemm_epi_destroy(gemm_epi_plan_t plan) {

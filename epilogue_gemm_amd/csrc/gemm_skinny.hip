@@ -93,7 +93,8 @@ __device__ __forceinline__ void arrive() {
 template <typename TIn, typename TOut, int NW, int P, int KC, int EPI>
 __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const TIn* __restrict__ A, const TIn* __restrict__ B,
                                                               const TIn* __restrict__ bias, TOut* __restrict__ C,
-                                                              int M, int N, int K) {
+                                                              int M, int N, int K, float* __restrict__ part,
+                                                              unsigned* __restrict__ arrivals) {
   constexpr int RB = KC * 2;            // bytes of one row segment of a chunk
   constexpr int SLOT = 32 * RB;         // one ring slot: 32 rows of B
   constexpr int MF = KC / 16 / NW;      // MFMAs per wave per chunk
@@ -108,7 +109,11 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const TIn* __restr
   // at N: it recomputes (and rewrites, with identical values) some of its
   // neighbour's columns, and no access leaves B, bias or C.
   const int n0 = min((int)blockIdx.x * 32, N - 32);
-  const int nchunks = K / KC;  // at least P (checked on the host)
+  // Split K (part != NULL): workgroup (b, s) of the gridDim.y splits takes
+  // chunks [s n, (s + 1) n) of column block b, n = K / KC / splits.
+  const int nsplit = (int)gridDim.y, split = (int)blockIdx.y;
+  const int nchunks = K / KC / nsplit;  // at least P (checked on the host)
+  const int cbase = split * nchunks;
 
   // Workgroup b walks the chunks starting at chunk b (mod the count): at
   // any moment the workgroups read at spread-out k offsets of their rows
@@ -158,7 +163,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const TIn* __restr
   f32x16 acc = f32x16{};
 
   auto issue = [&](int j, int c) __attribute__((always_inline)) {
-    const uint32_t kb = (uint32_t)((c + rot) % nchunks) * RB;
+    const uint32_t kb = (uint32_t)((c + rot) % nchunks + cbase) * RB;
 #pragma unroll
     for (int d = 0; d < ND; ++d)
       load_lds16(rb, slot[j] + (wave * ND + d) * 1024, vb[d], sb[d] + kb);
@@ -268,13 +273,72 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const TIn* __restr
   // Output (m, n0 + 4q + e), q = t % 8: accumulator v = 4 (q / 2) + e of
   // lane m + 32 (q % 2) in every wave's record, summed in wave order; then
   // bias, activation, conversion and one vector store of four outputs.
-  for (int t = tid; t < 256; t += NW * 64) {
-    const int om = t >> 3;
-    if (om >= M) break;
+  auto block_sum = [&](int om) __attribute__((always_inline)) -> f32x4 {
     const int L = om + 32 * (oq & 1), c = oq >> 1;
     f32x4 z = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int w = 0; w < NW; ++w) z += *(const f32x4*)(record(w) + L * 64 + ((c ^ ((L >> 2) & 3)) << 4));
+    return z;
+  };
+  if (part != nullptr) {
+    // Split K: store this workgroup's fp32 partial block (row-major 32 x 32
+    // at part + 1024 (b splits + s)), then count the arrival.  The
+    // workgroup that arrives last for its column block sums the splits'
+    // partials in split order (the result does not depend on which one is
+    // last), applies the epilogue, writes C and re-arms the counter for
+    // the next run.
+    //
+    // Visibility across XCDs without whole-cache maintenance (a release
+    // fence would write back, and an acquire fence invalidate, the XCD's
+    // entire L2 -- which also evicts A, shared by every workgroup): the
+    // partials, the counter and the partial reads are agent-scope atomic
+    // accesses, which go to the device-coherent level; every thread waits
+    // for its partial stores to complete before the workgroup barrier that
+    // precedes the count, and the reads are issued only after the count
+    // has returned.
+    float* mine = part + (size_t)(blockIdx.x * nsplit + split) * 1024;
+    for (int t = tid; t < 256; t += NW * 64) {
+      const int om = t >> 3;
+      if (om >= M) break;
+      const f32x4 z = block_sum(om);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        __hip_atomic_store(mine + om * 32 + 4 * oq + e, z[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    __syncthreads();
+    // (the flag lives in A's first ring slot, unused since the k loop)
+    int* is_last = (int*)slot_a[0];
+    if (tid == 0)
+      *is_last = __hip_atomic_fetch_add(arrivals + blockIdx.x, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                 (unsigned)(nsplit - 1);
+    __syncthreads();
+    if (!*is_last) return;
+    const float* blk = part + (size_t)blockIdx.x * nsplit * 1024;
+    for (int t = tid; t < 256; t += NW * 64) {
+      const int om = t >> 3;
+      if (om >= M) break;
+      float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      for (int s = 0; s < nsplit; ++s)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          v[e] += __hip_atomic_load(blk + s * 1024 + om * 32 + 4 * oq + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float b = 0.0f;
+        if constexpr (epi_has_bias<EPI>())
+          b = to_f32(__builtin_bit_cast(TIn, (uint16_t)((e & 1) ? (bias_q[e >> 1] >> 16) : (bias_q[e >> 1] & 0xffffu))));
+        v[e] = epilogue<EPI>(v[e], b);
+      }
+      store4<TOut>(C + (int64_t)om * N + n0 + 4 * oq, v[0], v[1], v[2], v[3]);
+    }
+    if (tid == 0) __hip_atomic_store(arrivals + blockIdx.x, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
+  for (int t = tid; t < 256; t += NW * 64) {
+    const int om = t >> 3;
+    if (om >= M) break;
+    const f32x4 z = block_sum(om);
     float v[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -289,8 +353,14 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const TIn* __restr
 
 template <typename TIn, typename TOut, int NW, int P, int KC, int EPI>
 hipError_t launch_skinny(const LaunchArgs& a) {
-  hipLaunchKernelGGL((gemm_skinny_kernel<TIn, TOut, NW, P, KC, EPI>), dim3((a.N + 31) / 32), dim3(NW * 64), 0, a.stream,
-                     (const TIn*)a.A, (const TIn*)a.B, (const TIn*)a.bias, (TOut*)a.C, a.M, a.N, a.K);
+  // split K when the caller gave a workspace: partial blocks, then one
+  // arrival counter per column block
+  const int nblocks = (a.N + 31) / 32;
+  float* part = a.split > 1 ? (float*)a.workspace : nullptr;
+  unsigned* arrivals = a.split > 1 ? (unsigned*)((char*)a.workspace + (size_t)nblocks * a.split * 4096) : nullptr;
+  hipLaunchKernelGGL((gemm_skinny_kernel<TIn, TOut, NW, P, KC, EPI>), dim3(nblocks, a.split > 1 ? a.split : 1),
+                     dim3(NW * 64), 0, a.stream, (const TIn*)a.A, (const TIn*)a.B, (const TIn*)a.bias, (TOut*)a.C,
+                     a.M, a.N, a.K, part, arrivals);
   return hipGetLastError();
 }
 
@@ -342,6 +412,14 @@ bool skinny_supports(int cfg, const Problem& p) {
   const SkinnyConfig& c = kSkinny[cfg];
   return p.M >= 1 && p.M <= 32 && p.la == GEMM_EPI_ROW_MAJOR && p.lb == GEMM_EPI_COL_MAJOR && p.N >= 32 && p.N % 8 == 0 &&
          p.K % c.kc == 0 && p.K / c.kc >= c.stages && 32 * p.K * 2 < ((int64_t)1 << 32);
+}
+
+int skinny_split(int cfg, const Problem& p) {
+  const SkinnyConfig& c = kSkinny[cfg];
+  const int64_t nblocks = (p.N + 31) / 32, chunks = p.K / c.kc;
+  int s = 1;
+  while (nblocks * s < 256 && chunks % (2 * s) == 0 && chunks / (2 * s) >= c.stages && s < 16) s *= 2;
+  return s;
 }
 
 int skinny_choose(const Problem& p) {

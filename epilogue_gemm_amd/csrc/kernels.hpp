@@ -46,6 +46,10 @@ int skinny_num_configs();
 const SkinnyConfig& skinny_config(int cfg);
 bool skinny_supports(int cfg, const Problem& p);
 int skinny_choose(const Problem& p);
+// K splits for configuration cfg when a workspace is given: doubled while
+// the grid has fewer than 256 workgroups and every split keeps at least
+// one chunk per ring slot (1: no split)
+int skinny_split(int cfg, const Problem& p);
 LaunchFn skinny_launcher(int cfg, const Problem& p);
 
 }  // namespace ge

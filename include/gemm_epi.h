@@ -26,6 +26,7 @@
 #ifndef GEMM_EPI_H
 #define GEMM_EPI_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -107,6 +108,33 @@ gemm_epi_status gemm_epi_plan(gemm_epi_plan_t* out, int64_t M, int64_t N, int64_
  * thread for gemm_epi_last_hip_error). */
 gemm_epi_status gemm_epi_run(gemm_epi_plan_t plan, const void* A, const void* B, const void* bias, void* C,
                              void* stream);
+
+/* gemm_epi_workspace_size -- bytes of device workspace that let
+ * gemm_epi_run_ws split K across workgroups (0: this plan never splits).
+ *
+ * Only skinny plans (M <= 32) whose N gives fewer than 256 column blocks
+ * of 32 split: a decode-like product with a narrow weight, e.g. one GPU's
+ * column shard of a larger one, would otherwise leave most CUs idle.
+ * (Split-K as the remedy when one block's share of the work is too large:
+ * csdn "从零开始学习 TileLang", ch.17 "常见性能问题", sec. 17.1.)
+ * Host only.  0 for a NULL plan. */
+size_t gemm_epi_workspace_size(gemm_epi_plan_t plan);
+
+/* gemm_epi_run_ws -- gemm_epi_run with a caller-owned device workspace.
+ *
+ * When workspace_bytes >= gemm_epi_workspace_size(plan) > 0 and every
+ * pointer (workspace included) is 16-byte aligned, K is split into
+ * several ranges, each workgroup stores an fp32 partial block into the
+ * workspace, and the last workgroup of each column block to finish sums
+ * the partials in split order (so the result does not depend on timing),
+ * applies the epilogue and writes C.  Otherwise this is gemm_epi_run and
+ * the workspace is not touched.
+ * The workspace must be zero-filled once before its first use; every run
+ * that completes leaves it zero-filled again.  Runs that share a workspace
+ * must not overlap in time (same stream, or ordered by events); the plan
+ * itself is still read-only.  Same errors as gemm_epi_run. */
+gemm_epi_status gemm_epi_run_ws(gemm_epi_plan_t plan, const void* A, const void* B, const void* bias, void* C,
+                                void* workspace, size_t workspace_bytes, void* stream);
 
 /* gemm_epi_destroy -- free the host plan object.  NULL is a no-op (OK).
  * No device synchronisation: runs already enqueued are unaffected. */

@@ -161,3 +161,25 @@ def test_skinny_k_granularity(lib):
                 assert (gb.gemm_epi_plan_select(h, "skinny", cfg) == 0) == ok, (cfg, K)
             finally:
                 gb.gemm_epi_destroy(h)
+
+
+def test_workspace_size(lib):
+    # skinny plans with fewer than 256 column blocks of 32 split K when given
+    # a workspace: one 4 KiB fp32 partial per (block, split), then one
+    # counter per block (rounded to 256 bytes)
+    h = gb.gemm_epi_plan(32, 1024, 8192, "bf16", "bf16", "row", "col", "bias")
+    try:
+        assert gb.gemm_epi_plan_describe(h)[:2] == ("skinny", 0)
+        assert gb.gemm_epi_workspace_size(h) == 32 * 4 * 4096 + 256  # 32 chunks of 256, 4 splits of 8
+    finally:
+        gb.gemm_epi_destroy(h)
+    for args in ((32, 8192, 8192, "bf16", "bf16", "row", "col", "bias"),   # 256 blocks already
+                 (8192, 8192, 8192, "bf16", "bf16", "row", "col", "bias_gelu"),
+                 (37, 53, 29, "f16", "f16", "row", "row", "none")):
+        h = gb.gemm_epi_plan(*args)
+        try:
+            assert gb.gemm_epi_workspace_size(h) == 0, args
+        finally:
+            gb.gemm_epi_destroy(h)
+    assert lib.gemm_epi_workspace_size(None) == 0
+    assert lib.gemm_epi_run_ws(None, None, None, None, None, None, 0, None) == 1  # INVALID_ARG

@@ -118,6 +118,53 @@ def test_skinny_edge_integer_bitexact(M, N):
         assert name.startswith("skinny_")
 
 
+# split K: narrow N with a workspace; the last workgroup of each column
+# block sums the partials in split order
+@pytest.mark.parametrize("M,N,K", [(32, 1024, 8192), (7, 96, 4096), (1, 40, 2560)])
+def test_skinny_split_integer_bitexact(M, N, K):
+    for in_dt, out_dt, epi in (("bf16", "bf16", "bias_relu"), ("f16", "f32", "none")):
+        bits = inputs.integer_inputs(M, N, K, in_dt, "row", "col", epi.startswith("bias"), seed=N + K)
+        plan = gb.Plan(M, N, K, in_dt, out_dt, "row", "col", epi)
+        assert plan.kernel == "skinny" and plan.workspace_size > 0
+        ws = torch.zeros(plan.workspace_size, dtype=torch.uint8, device="cuda")
+        A = parity.to_device(bits["A"], in_dt)
+        B = parity.to_device(bits["B"], in_dt)
+        bias = parity.to_device(bits["bias"], in_dt) if bits["bias"] is not None else None
+        y, c = oracle_full(bits, M, N, K, in_dt, out_dt, "row", "col", epi)
+        for rep in range(2):  # the second run relies on the first leaving the counters at zero
+            C = parity.empty_out(M * N, out_dt)
+            C.fill_(float("nan"))
+            plan.run(A, B, bias, C, workspace=ws)
+            torch.cuda.synchronize()
+            got = parity.out_bits(C)
+            mism = np.count_nonzero(got.reshape(-1) != c.reshape(-1).astype(got.dtype))
+            assert mism == 0, (rep, epi, mism)
+        counters = ws[-256:].cpu().numpy()
+        assert not counters.any()
+        plan.close()
+
+
+def test_skinny_split_random_and_fallback():
+    M, N, K = 32, 1024, 8192
+    bits = inputs.make_inputs(M, N, K, "bf16", "row", "col", True, float(np.sqrt(K)), 0.1, seed=12)
+    plan = gb.Plan(M, N, K, "bf16", "bf16", "row", "col", "bias")
+    A, B = parity.to_device(bits["A"], "bf16"), parity.to_device(bits["B"], "bf16")
+    bias = parity.to_device(bits["bias"], "bf16")
+    y, c = oracle_full(bits, M, N, K, "bf16", "bf16", "row", "col", "bias")
+    outs = []
+    for ws in (torch.zeros(plan.workspace_size, dtype=torch.uint8, device="cuda"),
+               torch.zeros(plan.workspace_size - 16, dtype=torch.uint8, device="cuda"),  # too small: no split
+               None):
+        C = parity.empty_out(M * N, "bf16")
+        plan.run(A, B, bias, C, workspace=ws)
+        torch.cuda.synchronize()
+        r = parity.compare(parity.out_bits(C), c, y, "bf16")
+        assert r["ok"], r
+        outs.append(parity.out_bits(C))
+    assert np.array_equal(outs[1], outs[2])  # the fallback is the unsplit kernel
+    plan.close()
+
+
 # (k per chunk, ring slots) of each skinny configuration, in order
 SKINNY_CHUNKS = [(256, 5), (256, 4), (256, 4), (128, 8), (256, 2), (128, 2)]
 
