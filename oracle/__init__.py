@@ -1,4 +1,4 @@
-"""CPU oracle for C = act(A.B [+ bias]) -- TEST INFRASTRUCTURE ONLY.
+"""CPU oracle for C = act(s * A.B [+ bias]) [+ r] -- TEST INFRASTRUCTURE ONLY.
 
 Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
 import this package.  The GPU library and its Python binding never import,
@@ -19,4 +19,5 @@ from .oracle import (  # noqa: F401
     gemm_epi,
     gemm_epi_points,
     max_threads,
+    silu,
 )

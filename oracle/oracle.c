@@ -9,9 +9,18 @@
  *
  * What it computes (one definition, written out):
  *
- *   z[i][j] = sum_{k<K} a(i,k) * b(k,j)   (+ bias[j] when the epilogue has a bias)
- *   y[i][j] = act(z[i][j])
+ *   z[i][j] = s[j] * sum_{k<K} a(i,k) * b(k,j)   (+ bias[j] when the epilogue has a bias)
+ *   y[i][j] = act(z[i][j])   (+ r[i][j] when a residual is given)
  *   C[i][j] = round_to_nearest_even(y[i][j], output format)
+ *
+ *   s[j] (an optional fp32 per-column scale, 1 when absent) and r[i][j] (an
+ *   optional M x N row-major residual in the output format, 0 when absent)
+ *   are the further epilogue fusions the csdn tutorial lists (ch.10 sec. 10.7
+ *   "GEMM + other epilogue", and the operator table that pairs norms with
+ *   residual fusion).  The pages give no formula for them; the reading taken
+ *   is the common one: the scale multiplies the product before the bias (a
+ *   per-output-channel dequantisation factor), the residual is added after
+ *   the activation, once, before the single rounding.
  *
  *   - The GEMM is the textbook sum over k (TileLang tutorial on csdn,
  *     ch.10 "GEMM 矩阵乘法" sec. 10.1 definition and sec. 10.2 triple loop;
@@ -24,6 +33,8 @@
  *     "TileLang で GPU カーネル設計を解説", section 4 "EPILOGUE FUSION").
  *   - ReLU(x) = max(x, 0) (atlascloud.ai "Writing high-performance kernels
  *     in TileLang", section "Écrivons un GEMM").
+ *   - SiLU(x) = x / (1 + exp(-x)) = x * sigmoid(x), the activation taken for
+ *     the tutorial's "other epilogues" (csdn ch.10 sec. 10.7).
  *   - GELU is the tanh form written as a logistic: x / (1 + exp(-c1*(x + c2*x^3)))
  *     with c1 = 1.5957691216 and c2 = 0.044715 as printed in ainew.jp
  *     section 4; the page's bullet between the last two factors is read as
@@ -60,6 +71,8 @@
 #define ORC_EPI_BIAS_RELU 2
 #define ORC_EPI_BIAS_GELU 3
 #define ORC_EPI_BIAS 4
+#define ORC_EPI_SILU 5
+#define ORC_EPI_BIAS_SILU 6
 
 /* mantissa bits, exponent bits of each format */
 static int fmt_mant(int fmt) { return fmt == ORC_F16 ? 10 : fmt == ORC_BF16 ? 7 : 23; }
@@ -132,6 +145,9 @@ void oracle_encode_n(int fmt, const double* x, uint32_t* out, int64_t n) {
 /* GELU, tanh approximation in its logistic form, constants as printed. */
 double oracle_gelu(double x) { return x / (1.0 + exp(-1.5957691216 * (x + 0.044715 * x * x * x))); }
 
+/* SiLU: x times the logistic sigmoid of x. */
+double oracle_silu(double x) { return x / (1.0 + exp(-x)); }
+
 /* Activation applied to z (bias already added). */
 static double apply_act(int epi, double z) {
   switch (epi) {
@@ -140,16 +156,25 @@ static double apply_act(int epi, double z) {
     return z > 0.0 ? z : 0.0;
   case ORC_EPI_BIAS_GELU:
     return oracle_gelu(z);
+  case ORC_EPI_SILU:
+  case ORC_EPI_BIAS_SILU:
+    return oracle_silu(z);
   default:
     return z;
   }
 }
 
-static int epi_has_bias(int epi) { return epi == ORC_EPI_BIAS_RELU || epi == ORC_EPI_BIAS_GELU || epi == ORC_EPI_BIAS; }
+static int epi_has_bias(int epi) {
+  return epi == ORC_EPI_BIAS_RELU || epi == ORC_EPI_BIAS_GELU || epi == ORC_EPI_BIAS || epi == ORC_EPI_BIAS_SILU;
+}
 
 static void store_bits(void* p, int fmt, int64_t idx, uint32_t v) {
   if (fmt == ORC_F32) ((uint32_t*)p)[idx] = v;
   else ((uint16_t*)p)[idx] = (uint16_t)v;
+}
+
+static uint32_t load_bits(const void* p, int fmt, int64_t idx) {
+  return fmt == ORC_F32 ? ((const uint32_t*)p)[idx] : ((const uint16_t*)p)[idx];
 }
 
 /* Decoding table for a 16-bit input format: table[bits] = value. */
@@ -165,30 +190,45 @@ static int check_args(int64_t M, int64_t N, int64_t K, int in_fmt, int out_fmt, 
   if (in_fmt != ORC_F16 && in_fmt != ORC_BF16) return -1;
   if (out_fmt != in_fmt && out_fmt != ORC_F32) return -1;
   if ((la != ORC_ROW && la != ORC_COL) || (lb != ORC_ROW && lb != ORC_COL)) return -1;
-  if (epi < ORC_EPI_NONE || epi > ORC_EPI_BIAS) return -1;
+  if (epi < ORC_EPI_NONE || epi > ORC_EPI_BIAS_SILU) return -1;
   return 0;
 }
 
-/* One output element: y = act(sum_k a(i,k) b(k,j) [+ bias_j]) in fp64. */
+/* Optional epilogue operands: per-column fp32 scale (N bit patterns) and a
+ * residual (M x N row-major, output format).  Either may be NULL. */
+typedef struct {
+  const uint32_t* scale;
+  const void* residual;
+  int out_fmt;
+} extras_t;
+
+/* One output element: y = act(s_j * sum_k a(i,k) b(k,j) [+ bias_j]) [+ r_ij] in fp64. */
 static double one_element(const double* tab, const uint16_t* A, const uint16_t* B, const uint16_t* bias,
-                          int64_t M, int64_t N, int64_t K, int la, int lb, int epi, int64_t i, int64_t j) {
+                          const extras_t* ex, int64_t M, int64_t N, int64_t K, int la, int lb, int epi, int64_t i,
+                          int64_t j) {
   double z = 0.0;
   for (int64_t k = 0; k < K; ++k) {
     double a = tab[A[la == ORC_ROW ? i * K + k : k * M + i]];
     double b = tab[B[lb == ORC_ROW ? k * N + j : j * K + k]];
     z += a * b;
   }
+  if (ex->scale) z *= oracle_decode(ORC_F32, ex->scale[j]);
   if (epi_has_bias(epi)) z += tab[bias[j]];
-  return apply_act(epi, z);
+  double y = apply_act(epi, z);
+  if (ex->residual) y += oracle_decode(ex->out_fmt, load_bits(ex->residual, ex->out_fmt, i * N + j));
+  return y;
 }
 
-/* Full product.  y_out (M*N doubles, row-major) and c_out (M*N elements of
- * out_fmt, row-major) may each be NULL.  nthreads <= 0 uses the OpenMP
- * default.  Returns 0 on success, -1 on bad arguments, -2 on no memory. */
-int oracle_gemm_epi(int64_t M, int64_t N, int64_t K, int in_fmt, int out_fmt, int la, int lb, int epi,
-                    const void* A, const void* B, const void* bias, double* y_out, void* c_out, int nthreads) {
+/* Full product.  scale and residual are optional (NULL: absent).  y_out
+ * (M*N doubles, row-major) and c_out (M*N elements of out_fmt, row-major)
+ * may each be NULL.  nthreads <= 0 uses the OpenMP default.  Returns 0 on
+ * success, -1 on bad arguments, -2 on no memory. */
+int oracle_gemm_epi_ex(int64_t M, int64_t N, int64_t K, int in_fmt, int out_fmt, int la, int lb, int epi,
+                       const void* A, const void* B, const void* bias, const uint32_t* scale, const void* residual,
+                       double* y_out, void* c_out, int nthreads) {
   if (check_args(M, N, K, in_fmt, out_fmt, la, lb, epi)) return -1;
   if (!A || !B || (epi_has_bias(epi) && !bias)) return -1;
+  const extras_t ex = {scale, residual, out_fmt};
   double* tab = make_table(in_fmt);
   if (!tab) return -2;
 #ifdef _OPENMP
@@ -197,8 +237,8 @@ int oracle_gemm_epi(int64_t M, int64_t N, int64_t K, int in_fmt, int out_fmt, in
 #endif
   for (int64_t i = 0; i < M; ++i) {
     for (int64_t j = 0; j < N; ++j) {
-      double y = one_element(tab, (const uint16_t*)A, (const uint16_t*)B, (const uint16_t*)bias, M, N, K, la, lb,
-                             epi, i, j);
+      double y = one_element(tab, (const uint16_t*)A, (const uint16_t*)B, (const uint16_t*)bias, &ex, M, N, K, la,
+                             lb, epi, i, j);
       if (y_out) y_out[i * N + j] = y;
       if (c_out) store_bits(c_out, out_fmt, i * N + j, oracle_encode(out_fmt, y));
     }
@@ -207,15 +247,22 @@ int oracle_gemm_epi(int64_t M, int64_t N, int64_t K, int in_fmt, int out_fmt, in
   return 0;
 }
 
+int oracle_gemm_epi(int64_t M, int64_t N, int64_t K, int in_fmt, int out_fmt, int la, int lb, int epi,
+                    const void* A, const void* B, const void* bias, double* y_out, void* c_out, int nthreads) {
+  return oracle_gemm_epi_ex(M, N, K, in_fmt, out_fmt, la, lb, epi, A, B, bias, NULL, NULL, y_out, c_out, nthreads);
+}
+
 /* Selected elements only: for p < count, element (rows[p], cols[p]).
  * y_out[p] gets the fp64 value, bits_out[p] its rounded encoding. */
-int oracle_gemm_epi_points(int64_t M, int64_t N, int64_t K, int in_fmt, int out_fmt, int la, int lb, int epi,
-                           const void* A, const void* B, const void* bias, int64_t count, const int64_t* rows,
-                           const int64_t* cols, double* y_out, uint32_t* bits_out, int nthreads) {
+int oracle_gemm_epi_points_ex(int64_t M, int64_t N, int64_t K, int in_fmt, int out_fmt, int la, int lb, int epi,
+                              const void* A, const void* B, const void* bias, const uint32_t* scale,
+                              const void* residual, int64_t count, const int64_t* rows, const int64_t* cols,
+                              double* y_out, uint32_t* bits_out, int nthreads) {
   if (check_args(M, N, K, in_fmt, out_fmt, la, lb, epi)) return -1;
   if (!A || !B || (epi_has_bias(epi) && !bias) || count < 0 || (count && (!rows || !cols))) return -1;
   for (int64_t p = 0; p < count; ++p)
     if (rows[p] < 0 || rows[p] >= M || cols[p] < 0 || cols[p] >= N) return -1;
+  const extras_t ex = {scale, residual, out_fmt};
   double* tab = make_table(in_fmt);
   if (!tab) return -2;
 #ifdef _OPENMP
@@ -223,13 +270,20 @@ int oracle_gemm_epi_points(int64_t M, int64_t N, int64_t K, int in_fmt, int out_
 #pragma omp parallel for schedule(dynamic, 16) num_threads(nthreads)
 #endif
   for (int64_t p = 0; p < count; ++p) {
-    double y = one_element(tab, (const uint16_t*)A, (const uint16_t*)B, (const uint16_t*)bias, M, N, K, la, lb, epi,
-                           rows[p], cols[p]);
+    double y = one_element(tab, (const uint16_t*)A, (const uint16_t*)B, (const uint16_t*)bias, &ex, M, N, K, la, lb,
+                           epi, rows[p], cols[p]);
     if (y_out) y_out[p] = y;
     if (bits_out) bits_out[p] = oracle_encode(out_fmt, y);
   }
   free(tab);
   return 0;
+}
+
+int oracle_gemm_epi_points(int64_t M, int64_t N, int64_t K, int in_fmt, int out_fmt, int la, int lb, int epi,
+                           const void* A, const void* B, const void* bias, int64_t count, const int64_t* rows,
+                           const int64_t* cols, double* y_out, uint32_t* bits_out, int nthreads) {
+  return oracle_gemm_epi_points_ex(M, N, K, in_fmt, out_fmt, la, lb, epi, A, B, bias, NULL, NULL, count, rows, cols,
+                                   y_out, bits_out, nthreads);
 }
 
 /* Threads an OpenMP region of this library uses by default. */

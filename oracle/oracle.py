@@ -20,7 +20,7 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 # GPU library's header).
 FORMATS = {"f16": 0, "bf16": 1, "f32": 2}
 LAYOUTS = {"row": 0, "col": 1}
-EPILOGUES = {"none": 0, "relu": 1, "bias_relu": 2, "bias_gelu": 3, "bias": 4}
+EPILOGUES = {"none": 0, "relu": 1, "bias_relu": 2, "bias_gelu": 3, "bias": 4, "silu": 5, "bias_silu": 6}
 
 _lib = None
 
@@ -57,11 +57,13 @@ def _load():
     lib.oracle_encode_n.restype = None
     lib.oracle_gelu.argtypes = [dp]
     lib.oracle_gelu.restype = dp
-    lib.oracle_gemm_epi.argtypes = [i64, i64, i64, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, i32]
-    lib.oracle_gemm_epi.restype = i32
-    lib.oracle_gemm_epi_points.argtypes = [i64, i64, i64, i32, i32, i32, i32, i32, vp, vp, vp,
-                                           i64, vp, vp, vp, vp, i32]
-    lib.oracle_gemm_epi_points.restype = i32
+    lib.oracle_silu.argtypes = [dp]
+    lib.oracle_silu.restype = dp
+    lib.oracle_gemm_epi_ex.argtypes = [i64, i64, i64, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, i32]
+    lib.oracle_gemm_epi_ex.restype = i32
+    lib.oracle_gemm_epi_points_ex.argtypes = [i64, i64, i64, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp,
+                                              i64, vp, vp, vp, vp, i32]
+    lib.oracle_gemm_epi_points_ex.restype = i32
     lib.oracle_max_threads.argtypes = []
     lib.oracle_max_threads.restype = i32
     _lib = lib
@@ -100,6 +102,10 @@ def gelu(x: float) -> float:
     return float(_load().oracle_gelu(float(x)))
 
 
+def silu(x: float) -> float:
+    return float(_load().oracle_silu(float(x)))
+
+
 def _ptr(a):
     return None if a is None else a.ctypes.data
 
@@ -113,38 +119,63 @@ def _bits16(a, name):
     return a
 
 
+def _extras(scale, residual, M, N, out_dtype):
+    """Optional epilogue operands as the arrays oracle.c reads: the fp32 column
+    scale as uint32 bit patterns (N), the residual as output-format bit
+    patterns (M x N row-major)."""
+    if scale is not None:
+        scale = np.ascontiguousarray(scale)
+        if scale.dtype == np.float32:
+            scale = scale.view(np.uint32)
+        if scale.dtype != np.uint32 or scale.size != N:
+            raise ValueError("scale: expected N float32 values (or their uint32 bit patterns)")
+    if residual is not None:
+        residual = np.ascontiguousarray(residual)
+        want = np.uint32 if out_dtype == "f32" else np.uint16
+        if residual.dtype == np.float32 and out_dtype == "f32":
+            residual = residual.view(np.uint32)
+        if residual.dtype != want or residual.size != M * N:
+            raise ValueError(f"residual: expected M*N {want.__name__} bit patterns of the output format")
+    return scale, residual
+
+
 def gemm_epi(A, B, bias, M, N, K, in_dtype, out_dtype, layout_a, layout_b, epilogue,
-             want_y=True, want_c=True, nthreads=0):
-    """Full M x N product.  Returns (y, c): y is fp64 act(z) (row-major M x N),
-    c the rounded output bit patterns (uint16, or uint32 for f32)."""
+             want_y=True, want_c=True, nthreads=0, scale=None, residual=None):
+    """Full M x N product.  Returns (y, c): y is fp64 act(s * A.B [+ bias]) [+ r]
+    (row-major M x N), c the rounded output bit patterns (uint16, or uint32
+    for f32).  scale (N fp32) and residual (M x N, output format) are
+    optional."""
     A, B, bias = _bits16(A, "A"), _bits16(B, "B"), _bits16(bias, "bias")
     if A.size != M * K or B.size != K * N or (bias is not None and bias.size != N):
         raise ValueError("operand sizes do not match M, N, K")
+    scale, residual = _extras(scale, residual, M, N, out_dtype)
     y = np.empty((M, N), np.float64) if want_y else None
     c = np.empty((M, N), np.uint32 if out_dtype == "f32" else np.uint16) if want_c else None
-    rc = _load().oracle_gemm_epi(M, N, K, FORMATS[in_dtype], FORMATS[out_dtype], LAYOUTS[layout_a],
-                                 LAYOUTS[layout_b], EPILOGUES[epilogue], _ptr(A), _ptr(B), _ptr(bias),
-                                 _ptr(y), _ptr(c), int(nthreads))
+    rc = _load().oracle_gemm_epi_ex(M, N, K, FORMATS[in_dtype], FORMATS[out_dtype], LAYOUTS[layout_a],
+                                    LAYOUTS[layout_b], EPILOGUES[epilogue], _ptr(A), _ptr(B), _ptr(bias),
+                                    _ptr(scale), _ptr(residual), _ptr(y), _ptr(c), int(nthreads))
     if rc != 0:
         raise ValueError(f"oracle_gemm_epi rejected its arguments (rc={rc})")
     return y, c
 
 
 def gemm_epi_points(A, B, bias, M, N, K, in_dtype, out_dtype, layout_a, layout_b, epilogue,
-                    rows, cols, nthreads=0):
+                    rows, cols, nthreads=0, scale=None, residual=None):
     """Selected elements (rows[p], cols[p]).  Returns (y, bits) as 1-D arrays."""
     A, B, bias = _bits16(A, "A"), _bits16(B, "B"), _bits16(bias, "bias")
     if A.size != M * K or B.size != K * N or (bias is not None and bias.size != N):
         raise ValueError("operand sizes do not match M, N, K")
+    scale, residual = _extras(scale, residual, M, N, out_dtype)
     rows = np.ascontiguousarray(rows, np.int64)
     cols = np.ascontiguousarray(cols, np.int64)
     if rows.shape != cols.shape:
         raise ValueError("rows and cols differ in length")
     y = np.empty(rows.size, np.float64)
     bits = np.empty(rows.size, np.uint32)
-    rc = _load().oracle_gemm_epi_points(M, N, K, FORMATS[in_dtype], FORMATS[out_dtype], LAYOUTS[layout_a],
-                                        LAYOUTS[layout_b], EPILOGUES[epilogue], _ptr(A), _ptr(B), _ptr(bias),
-                                        rows.size, _ptr(rows), _ptr(cols), _ptr(y), _ptr(bits), int(nthreads))
+    rc = _load().oracle_gemm_epi_points_ex(M, N, K, FORMATS[in_dtype], FORMATS[out_dtype], LAYOUTS[layout_a],
+                                           LAYOUTS[layout_b], EPILOGUES[epilogue], _ptr(A), _ptr(B), _ptr(bias),
+                                           _ptr(scale), _ptr(residual), rows.size, _ptr(rows), _ptr(cols), _ptr(y),
+                                           _ptr(bits), int(nthreads))
     if rc != 0:
         raise ValueError(f"oracle_gemm_epi_points rejected its arguments (rc={rc})")
     return y, bits

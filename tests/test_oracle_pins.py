@@ -373,3 +373,138 @@ def test_rejects_bad_arguments():
         oracle.gemm_epi(A, A, None, 2, 2, 2, "f16", "f16", "row", "row", "bias")  # missing bias
     with pytest.raises(ValueError):
         oracle.gemm_epi(A, A, None, 2, 3, 2, "f16", "f16", "row", "row", "none")  # size mismatch
+
+
+# --------------------------------------------------------------------------
+# further epilogues: SiLU, per-column scale, residual
+# --------------------------------------------------------------------------
+
+def test_silu_vs_torch_and_closed_forms():
+    x = np.linspace(-30.0, 30.0, 6001)
+    got = np.array([oracle.silu(v) for v in x])
+    # torch's float64 SiLU (a library routine)
+    ref = torch.nn.functional.silu(torch.from_numpy(x)).numpy()
+    assert np.allclose(got, ref, rtol=1e-14, atol=1e-300)
+    # x * sigmoid(x) = (x / 2) (1 + tanh(x / 2)): a different transcendental
+    # (which cancels for x << 0, hence the absolute term)
+    alt = 0.5 * x * (1.0 + np.tanh(0.5 * x))
+    assert np.allclose(got, alt, rtol=1e-13, atol=1e-13)
+    # silu(x) - silu(-x) = x (sigmoid(x) + sigmoid(-x) = 1); slope 1/2 at 0
+    neg = np.array([oracle.silu(-v) for v in x])
+    assert np.allclose(got - neg, x, rtol=1e-14, atol=1e-14)
+    assert oracle.silu(0.0) == 0.0
+    assert oracle.silu(1e-8) == pytest.approx(0.5e-8, rel=1e-7)
+    assert oracle.silu(40.0) == 40.0
+    assert oracle.silu(-800.0) == 0.0
+    # its minimum is at x = -1.2784645 with value -0.2784645 (the root of
+    # 1 + x (1 - sigmoid(x)) = 0, where silu(x) = -(1 + x))
+    xs = np.linspace(-1.3, -1.25, 5001)
+    v = np.array([oracle.silu(t) for t in xs])
+    assert xs[np.argmin(v)] == pytest.approx(-1.2784645, abs=2e-5)
+    assert v.min() == pytest.approx(-0.2784645, abs=1e-6)
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+@pytest.mark.parametrize("K", [1, 64, 4096])
+def test_all_ones_with_scale_and_residual(fmt, K):
+    M, N = 3, 5
+    one = _bits_of([1.0], fmt)[0]
+    A = np.full(M * K, one, np.uint16)
+    B = np.full(K * N, one, np.uint16)
+    s = np.array([0.5, -2.0, 0.25, 3.0, 1.0], np.float32)
+    bias = _bits_of([1.0, 0.5, -3.0, -1.0, 0.0], fmt)
+    bv = _values(bias, fmt)
+    r_vals = np.arange(M * N, dtype=np.float64).reshape(M, N) - 6.0
+    r = oracle.encode_array("f32", r_vals)
+    # the scale multiplies the product, then the bias is added
+    y, _ = oracle.gemm_epi(A, B, bias, M, N, K, fmt, "f32", "row", "col", "bias", scale=s)
+    assert np.array_equal(y, np.broadcast_to(s * K + bv, (M, N)))
+    # ...then the activation, then the residual
+    y, _ = oracle.gemm_epi(A, B, bias, M, N, K, fmt, "f32", "row", "col", "bias_relu", scale=s, residual=r)
+    assert np.array_equal(y, np.maximum(s * K + bv, 0.0) + r_vals)
+    y, _ = oracle.gemm_epi(A, B, None, M, N, K, fmt, "f32", "row", "col", "relu", residual=r)
+    assert np.array_equal(y, K + r_vals)
+    y, _ = oracle.gemm_epi(A, B, bias, M, N, K, fmt, "f32", "row", "row", "bias_silu", scale=s)
+    want = np.array([oracle.silu(s[j] * K + bv[j]) for j in range(N)])
+    assert np.array_equal(y, np.broadcast_to(want, (M, N)))
+    y, _ = oracle.gemm_epi(A, B, None, M, N, K, fmt, "f32", "row", "row", "silu")
+    assert np.all(y == oracle.silu(float(K)))
+    # residual in a 16-bit output format
+    r16 = _bits_of(r_vals.reshape(-1), fmt)
+    y, c = oracle.gemm_epi(A, B, None, M, N, K, fmt, fmt, "row", "col", "none", residual=r16)
+    assert np.array_equal(y, K + _values(r16, fmt).reshape(M, N))
+    assert np.array_equal(c.reshape(-1), oracle.encode_array(fmt, y.reshape(-1)).astype(np.uint16))
+
+
+def _exact_reference_ex(a_vals, b_vals, bias_vals, scale, resid, epilogue):
+    """Exact rational act(s * A.B + bias) + r for the piecewise-linear epilogues."""
+    z = _exact_reference(a_vals, b_vals, None, "none")
+    M, N = len(z), len(z[0])
+    out = []
+    for i in range(M):
+        row = []
+        for j in range(N):
+            v = z[i][j] * Fraction(float(scale[j]))
+            if epilogue in ("bias", "bias_relu"):
+                v += Fraction(float(bias_vals[j]))
+            if epilogue in ("relu", "bias_relu"):
+                v = max(v, Fraction(0))
+            row.append(v + Fraction(float(resid[i, j])))
+        out.append(row)
+    return out
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+@pytest.mark.parametrize("shape", [(2, 8, 4), (3, 5, 7), (5, 7, 3)])
+@pytest.mark.parametrize("epilogue", ["none", "relu", "bias", "bias_relu"])
+def test_brute_force_exact_scale_residual(fmt, shape, epilogue):
+    M, N, K = shape
+    rng = np.random.default_rng(M * 1000 + N * 10 + K)
+    a = _values(_bits_of(rng.standard_normal((M, K)) * 3, fmt), fmt).reshape(M, K)
+    b = _values(_bits_of(rng.standard_normal((K, N)), fmt), fmt).reshape(K, N)
+    bias = _values(_bits_of(rng.standard_normal(N), fmt), fmt)
+    scale = rng.standard_normal(N).astype(np.float32)
+    resid = _values(_bits_of(rng.standard_normal(M * N), "f32").astype(np.uint32), "f32").reshape(M, N)
+    exact = _exact_reference_ex(a, b, bias, scale, resid, epilogue)
+    bias_bits = _bits_of(bias, fmt) if epilogue.startswith("bias") else None
+    y, c = oracle.gemm_epi(_bits_of(a, fmt), np.ascontiguousarray(_bits_of(b, fmt).reshape(K, N).T), bias_bits,
+                           M, N, K, fmt, "f32", "row", "col", epilogue, scale=scale,
+                           residual=oracle.encode_array("f32", resid.reshape(-1)))
+    for i in range(M):
+        for j in range(N):
+            mag = float(sum(abs(Fraction(float(a[i, k])) * Fraction(float(b[k, j]))) for k in range(K)))
+            mag = mag * abs(float(scale[j])) + abs(float(bias[j])) + abs(float(resid[i, j]))
+            assert abs(y[i, j] - float(exact[i][j])) <= 8 * 2.0**-52 * max(mag, 1e-300), (i, j)
+
+
+def test_silu_matches_torch_on_a_product():
+    fmt, M, N, K = "bf16", 29, 41, 96
+    rng = np.random.default_rng(12)
+    a_bits = _bits_of(rng.standard_normal((M, K)), fmt).reshape(M, K)
+    b_bits = _bits_of(rng.standard_normal((K, N)) / 8, fmt).reshape(K, N)
+    bias_bits = _bits_of(rng.standard_normal(N) * 0.1, fmt)
+    scale = (rng.random(N) + 0.5).astype(np.float32)
+    r_bits = _bits_of(rng.standard_normal(M * N), fmt)
+    a = torch.from_numpy(_values(a_bits, fmt).reshape(M, K))
+    b = torch.from_numpy(_values(b_bits, fmt).reshape(K, N))
+    ref = torch.nn.functional.silu((a @ b) * torch.from_numpy(scale.astype(np.float64))
+                                   + torch.from_numpy(_values(bias_bits, fmt)))
+    ref = ref + torch.from_numpy(_values(r_bits, fmt).reshape(M, N))
+    y, _ = oracle.gemm_epi(a_bits, b_bits, bias_bits, M, N, K, fmt, fmt, "row", "row", "bias_silu", scale=scale,
+                           residual=r_bits)
+    assert np.allclose(y, ref.numpy(), rtol=1e-12, atol=1e-12)
+    # the points entry computes the same values
+    rows, cols = rng.integers(0, M, 50), rng.integers(0, N, 50)
+    py, _ = oracle.gemm_epi_points(a_bits, b_bits, bias_bits, M, N, K, fmt, fmt, "row", "row", "bias_silu", rows,
+                                   cols, scale=scale, residual=r_bits)
+    assert np.array_equal(py, y[rows, cols])
+
+
+def test_rejects_bad_extras():
+    A = np.zeros(4, np.uint16)
+    with pytest.raises(ValueError):
+        oracle.gemm_epi(A, A, None, 2, 2, 2, "f16", "f16", "row", "row", "none", scale=np.ones(3, np.float32))
+    with pytest.raises(ValueError):
+        oracle.gemm_epi(A, A, None, 2, 2, 2, "f16", "f16", "row", "row", "none", residual=np.zeros(4, np.uint32))
+    with pytest.raises(ValueError):
+        oracle.gemm_epi(A, A, None, 2, 2, 2, "f16", "f16", "row", "row", "bias_silu")  # missing bias
