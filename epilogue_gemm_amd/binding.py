@@ -20,11 +20,16 @@ HEADER = os.path.join(os.path.dirname(_HERE), "include", "gemm_epi.h")
 # Enum values of include/gemm_epi.h
 DTYPES = {"f16": 0, "bf16": 1, "f32": 2}
 LAYOUTS = {"row": 0, "col": 1}
-EPILOGUES = {"none": 0, "relu": 1, "bias_relu": 2, "bias_gelu": 3, "bias": 4}
+EPILOGUES = {"none": 0, "relu": 1, "bias_relu": 2, "bias_gelu": 3, "bias": 4, "silu": 5, "bias_silu": 6}
 KERNELS = {"auto": 0, "generic": 1, "tile": 2, "skinny": 3}
 KERNEL_NAMES = {v: k for k, v in KERNELS.items()}
 STATUS = {0: "OK", 1: "ERR_INVALID_ARG", 2: "ERR_UNSUPPORTED", 3: "ERR_HIP", 4: "ERR_NO_MEMORY"}
 OK = 0
+
+
+class Extras(ctypes.Structure):
+    """struct gemm_epi_extras: optional column scale and residual pointers."""
+    _fields_ = [("col_scale", ctypes.c_void_p), ("residual", ctypes.c_void_p)]
 
 
 class GemmEpiError(RuntimeError):
@@ -59,6 +64,8 @@ def load_library(path: str = LIB_PATH):
     lib.gemm_epi_workspace_size.restype = ctypes.c_size_t
     lib.gemm_epi_run_ws.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.gemm_epi_run_ws.restype = i32
+    lib.gemm_epi_run_ex.argtypes = [vp, vp, vp, vp, ctypes.POINTER(Extras), vp, vp, ctypes.c_size_t, vp]
+    lib.gemm_epi_run_ex.restype = i32
     lib.gemm_epi_destroy.argtypes = [vp]
     lib.gemm_epi_destroy.restype = i32
     lib.gemm_epi_status_string.argtypes = [i32]
@@ -119,6 +126,14 @@ def gemm_epi_workspace_size(plan) -> int:
 
 def gemm_epi_run_ws(plan, A_ptr, B_ptr, bias_ptr, C_ptr, ws_ptr, ws_bytes, stream) -> int:
     return load_library().gemm_epi_run_ws(plan, A_ptr, B_ptr, bias_ptr, C_ptr, ws_ptr, int(ws_bytes), stream)
+
+
+def gemm_epi_run_ex(plan, A_ptr, B_ptr, bias_ptr, scale_ptr, residual_ptr, C_ptr, ws_ptr, ws_bytes, stream,
+                    extras_null=False) -> int:
+    """extras_null passes a NULL gemm_epi_extras pointer (scale_ptr and
+    residual_ptr are then ignored)."""
+    ex = None if extras_null else ctypes.byref(Extras(scale_ptr, residual_ptr))
+    return load_library().gemm_epi_run_ex(plan, A_ptr, B_ptr, bias_ptr, ex, C_ptr, ws_ptr, int(ws_bytes), stream)
 
 
 def gemm_epi_destroy(plan) -> int:
@@ -193,9 +208,12 @@ class Plan:
         """Bytes of workspace that let ``run`` split K (0: never splits)."""
         return gemm_epi_workspace_size(self.handle)
 
-    def run(self, A, B, bias, C, stream=None, workspace=None):
+    def run(self, A, B, bias, C, stream=None, workspace=None, scale=None, residual=None):
         """``workspace``: an optional zero-filled uint8 CUDA tensor of at least
-        ``workspace_size`` bytes (left zero-filled by every completed run)."""
+        ``workspace_size`` bytes (left zero-filled by every completed run).
+        ``scale``: optional fp32 per-column factors (N); ``residual``:
+        optional M x N tensor of the output format, added after the
+        activation (must not overlap C)."""
         import torch
 
         a = self._check(A, "A", self.in_dtype, self.M * self.K)
@@ -203,6 +221,18 @@ class Plan:
         bi = self._check(bias, "bias", self.in_dtype, self.N)
         c = self._check(C, "C", self.out_dtype, self.M * self.N)
         s = (stream or torch.cuda.current_stream()).cuda_stream
+        if scale is not None or residual is not None:
+            sc = self._check(scale, "scale", "f32", self.N)
+            r = self._check(residual, "residual", self.out_dtype, self.M * self.N)
+            ws, nbytes = None, 0
+            if workspace is not None:
+                if not workspace.is_cuda or not workspace.is_contiguous():
+                    raise ValueError("workspace: expected a contiguous CUDA tensor")
+                ws, nbytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+            st = gemm_epi_run_ex(self.handle, a, b, bi, sc, r, c, ws, nbytes, s)
+            if st != OK:
+                raise GemmEpiError("gemm_epi_run_ex", st)
+            return
         if workspace is None:
             st = gemm_epi_run(self.handle, a, b, bi, c, s)
             fn = "gemm_epi_run"

@@ -51,6 +51,10 @@ struct LaunchArgs {
   // number of K splits (1: no split, no workspace)
   void* workspace;
   int split;
+  // optional epilogue operands (nullptr: absent): fp32 column scale (N)
+  // and residual (M x N row-major, output format)
+  const float* scale;
+  const void* residual;
 };
 
 // ---------------------------------------------------------------------------
@@ -58,6 +62,11 @@ struct LaunchArgs {
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float to_f32(f16 x) { return (float)x; }
 __device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+// an output element (16-bit or fp32) -> fp32
+template <typename T>
+__device__ __forceinline__ float out_to_f32(T x) {
+  return (float)x;
+}
 
 // ---------------------------------------------------------------------------
 // Epilogue on an fp32 accumulator value z with its column's bias b.
@@ -80,18 +89,39 @@ __device__ __forceinline__ float gelu_logistic(float x) {
   return x * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
+// SiLU(x) = x / (1 + exp(-x)): exp as v_exp_f32 of -x log2 e, the quotient
+// as v_rcp_f32.  Large negative x: 1/inf = 0, result -0; large positive x:
+// result x.
+__device__ __forceinline__ float silu_logistic(float x) {
+  constexpr float c = (float)(-1.4426950408889634);
+  return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x * c));
+}
+
 template <int EPI>
 __device__ __forceinline__ float epilogue(float z, float b) {
   if constexpr (EPI == GEMM_EPI_NONE) return z;
   else if constexpr (EPI == GEMM_EPI_RELU) return fmaxf(z, 0.0f);
   else if constexpr (EPI == GEMM_EPI_BIAS_RELU) return fmaxf(z + b, 0.0f);
   else if constexpr (EPI == GEMM_EPI_BIAS_GELU) return gelu_logistic(z + b);
+  else if constexpr (EPI == GEMM_EPI_SILU) return silu_logistic(z);
+  else if constexpr (EPI == GEMM_EPI_BIAS_SILU) return silu_logistic(z + b);
   else return z + b;  // GEMM_EPI_BIAS
 }
 
 template <int EPI>
 constexpr bool epi_has_bias() {
-  return EPI == GEMM_EPI_BIAS_RELU || EPI == GEMM_EPI_BIAS_GELU || EPI == GEMM_EPI_BIAS;
+  return EPI == GEMM_EPI_BIAS_RELU || EPI == GEMM_EPI_BIAS_GELU || EPI == GEMM_EPI_BIAS || EPI == GEMM_EPI_BIAS_SILU;
+}
+
+// The optional operands around the activation: act(s z + b) + r.  `scale`
+// and `res` are uniform across the launch, so the tests are scalar
+// branches.
+template <int EPI>
+__device__ __forceinline__ float epilogue_ex(float z, float b, bool has_scale, float s, bool has_res, float r) {
+  if (has_scale) z *= s;
+  float v = epilogue<EPI>(z, b);
+  if (has_res) v += r;
+  return v;
 }
 
 // ---------------------------------------------------------------------------
@@ -118,6 +148,23 @@ __device__ __forceinline__ void store4(TOut* p, float v0, float v1, float v2, fl
     w.x = (uint32_t)bits16(from_f32<TOut>(v0)) | ((uint32_t)bits16(from_f32<TOut>(v1)) << 16);
     w.y = (uint32_t)bits16(from_f32<TOut>(v2)) | ((uint32_t)bits16(from_f32<TOut>(v3)) << 16);
     *reinterpret_cast<u32x2*>(p) = w;
+  }
+}
+
+// Four consecutive elements (fp32, or 16-bit) as fp32; p 8-byte aligned
+// (16-bit) or 16-byte aligned (fp32).
+template <typename T>
+__device__ __forceinline__ f32x4 load4(const T* p) {
+  if constexpr (sizeof(T) == 4) {
+    return *reinterpret_cast<const f32x4*>(p);
+  } else {
+    const u32x2 w = *reinterpret_cast<const u32x2*>(p);
+    f32x4 r;
+    r.x = to_f32(__builtin_bit_cast(T, (uint16_t)(w.x & 0xffffu)));
+    r.y = to_f32(__builtin_bit_cast(T, (uint16_t)(w.x >> 16)));
+    r.z = to_f32(__builtin_bit_cast(T, (uint16_t)(w.y & 0xffffu)));
+    r.w = to_f32(__builtin_bit_cast(T, (uint16_t)(w.y >> 16)));
+    return r;
   }
 }
 

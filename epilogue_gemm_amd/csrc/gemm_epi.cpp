@@ -84,10 +84,12 @@ bool valid_enum_args(gemm_epi_dtype in, gemm_epi_dtype out, gemm_epi_layout la, 
   if (out != in && out != GEMM_EPI_F32) return false;
   if ((la != GEMM_EPI_ROW_MAJOR && la != GEMM_EPI_COL_MAJOR) || (lb != GEMM_EPI_ROW_MAJOR && lb != GEMM_EPI_COL_MAJOR))
     return false;
-  return epi >= GEMM_EPI_NONE && epi <= GEMM_EPI_BIAS;
+  return epi >= GEMM_EPI_NONE && epi <= GEMM_EPI_BIAS_SILU;
 }
 
-bool uses_bias(int epi) { return epi == GEMM_EPI_BIAS_RELU || epi == GEMM_EPI_BIAS_GELU || epi == GEMM_EPI_BIAS; }
+bool uses_bias(int epi) {
+  return epi == GEMM_EPI_BIAS_RELU || epi == GEMM_EPI_BIAS_GELU || epi == GEMM_EPI_BIAS || epi == GEMM_EPI_BIAS_SILU;
+}
 
 // Resolve (kernel, config) for the plan's problem; returns false if that
 // family cannot run it.
@@ -146,11 +148,19 @@ size_t workspace_bytes(const gemm_epi_plan_s* pl) {
   return nblocks * (size_t)pl->split * 4096 + ((nblocks * 4 + 255) & ~(size_t)255);
 }
 
-gemm_epi_status launch(gemm_epi_plan_t plan, const void* A, const void* B, const void* bias, void* C,
-                       void* workspace, size_t ws_bytes, void* stream) {
+gemm_epi_status launch(gemm_epi_plan_t plan, const void* A, const void* B, const void* bias,
+                       const gemm_epi_extras* extras, void* C, void* workspace, size_t ws_bytes, void* stream) {
   if (!plan || !A || !B || !C) return GEMM_EPI_ERR_INVALID_ARG;
   const bool need_bias = uses_bias(plan->p.epi);
   if (need_bias != (bias != nullptr)) return GEMM_EPI_ERR_INVALID_ARG;
+  const float* scale = extras ? extras->col_scale : nullptr;
+  const void* residual = extras ? extras->residual : nullptr;
+  if (residual) {
+    // the residual must not overlap C (edge tiles write some outputs twice)
+    const uintptr_t bytes = (uintptr_t)(plan->p.M * plan->p.N) * (plan->p.out_dt == GEMM_EPI_F32 ? 4u : 2u);
+    const uintptr_t r0 = (uintptr_t)residual, c0 = (uintptr_t)C;
+    if (r0 < c0 + bytes && c0 < r0 + bytes) return GEMM_EPI_ERR_INVALID_ARG;
+  }
   ge::LaunchArgs a;
   a.A = A;
   a.B = B;
@@ -165,7 +175,10 @@ gemm_epi_status launch(gemm_epi_plan_t plan, const void* A, const void* B, const
   a.stream = (hipStream_t)stream;
   a.workspace = nullptr;
   a.split = 1;
-  const bool aligned = aligned16(A) && aligned16(B) && aligned16(C) && (!bias || aligned16(bias));
+  a.scale = scale;
+  a.residual = residual;
+  const bool aligned = aligned16(A) && aligned16(B) && aligned16(C) && (!bias || aligned16(bias)) &&
+                       (!scale || aligned16(scale)) && (!residual || aligned16(residual));
   const size_t need = workspace_bytes(plan);
   if (aligned && need > 0 && workspace && aligned16(workspace) && ws_bytes >= need) {
     a.workspace = workspace;
@@ -206,14 +219,20 @@ gemm_epi_status gemm_epi_plan(gemm_epi_plan_t* out, int64_t M, int64_t N, int64_
 
 gemm_epi_status gemm_epi_run(gemm_epi_plan_t plan, const void* A, const void* B, const void* bias, void* C,
                              void* stream) {
-  return launch(plan, A, B, bias, C, nullptr, 0, stream);
+  return launch(plan, A, B, bias, nullptr, C, nullptr, 0, stream);
 }
 
 size_t gemm_epi_workspace_size(gemm_epi_plan_t plan) { return plan ? workspace_bytes(plan) : 0; }
 
 gemm_epi_status gemm_epi_run_ws(gemm_epi_plan_t plan, const void* A, const void* B, const void* bias, void* C,
                                 void* workspace, size_t workspace_bytes_given, void* stream) {
-  return launch(plan, A, B, bias, C, workspace, workspace_bytes_given, stream);
+  return launch(plan, A, B, bias, nullptr, C, workspace, workspace_bytes_given, stream);
+}
+
+gemm_epi_status gemm_epi_run_ex(gemm_epi_plan_t plan, const void* A, const void* B, const void* bias,
+                                const gemm_epi_extras* extras, void* C, void* workspace, size_t workspace_bytes_given,
+                                void* stream) {
+  return launch(plan, A, B, bias, extras, C, workspace, workspace_bytes_given, stream);
 }
 
 gemm_epi_status gemm_epi_destroy(gemm_epi_plan_t plan) {

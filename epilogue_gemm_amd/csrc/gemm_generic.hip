@@ -16,7 +16,9 @@ constexpr int kGenThreadsY = 4;   // along M
 template <typename TIn, typename TOut, int EPI>
 __global__ __launch_bounds__(256) void gemm_generic_kernel(const TIn* __restrict__ A, const TIn* __restrict__ B,
                                                            const TIn* __restrict__ bias, TOut* __restrict__ C,
-                                                           int64_t M, int64_t N, int64_t K, int la, int lb) {
+                                                           int64_t M, int64_t N, int64_t K, int la, int lb,
+                                                           const float* __restrict__ scale,
+                                                           const TOut* __restrict__ res) {
   const int64_t j = (int64_t)blockIdx.x * kGenThreadsX + (threadIdx.x % kGenThreadsX);
   if (j >= N) return;
   const int64_t i_step = (int64_t)gridDim.y * kGenThreadsY;
@@ -30,7 +32,9 @@ __global__ __launch_bounds__(256) void gemm_generic_kernel(const TIn* __restrict
     for (int64_t k = 0; k < K; ++k) acc = __builtin_fmaf(to_f32(pa[k * sa]), to_f32(pb[k * sb]), acc);
     float b = 0.0f;
     if constexpr (epi_has_bias<EPI>()) b = to_f32(bias[j]);
-    C[i * N + j] = from_f32<TOut>(epilogue<EPI>(acc, b));
+    const float s = scale ? scale[j] : 1.0f;
+    const float r = res ? out_to_f32(res[i * N + j]) : 0.0f;
+    C[i * N + j] = from_f32<TOut>(epilogue_ex<EPI>(acc, b, scale != nullptr, s, res != nullptr, r));
   }
 }
 
@@ -41,7 +45,7 @@ hipError_t launch_generic(const LaunchArgs& a) {
   if (gy > 65535) gy = 65535;
   hipLaunchKernelGGL((gemm_generic_kernel<TIn, TOut, EPI>), dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, a.stream,
                      (const TIn*)a.A, (const TIn*)a.B, (const TIn*)a.bias, (TOut*)a.C, (int64_t)a.M, (int64_t)a.N,
-                     (int64_t)a.K, a.la, a.lb);
+                     (int64_t)a.K, a.la, a.lb, a.scale, (const TOut*)a.residual);
   return hipGetLastError();
 }
 
@@ -53,6 +57,8 @@ LaunchFn pick_epi(int epi) {
     case GEMM_EPI_BIAS_RELU: return &launch_generic<TIn, TOut, GEMM_EPI_BIAS_RELU>;
     case GEMM_EPI_BIAS_GELU: return &launch_generic<TIn, TOut, GEMM_EPI_BIAS_GELU>;
     case GEMM_EPI_BIAS: return &launch_generic<TIn, TOut, GEMM_EPI_BIAS>;
+    case GEMM_EPI_SILU: return &launch_generic<TIn, TOut, GEMM_EPI_SILU>;
+    case GEMM_EPI_BIAS_SILU: return &launch_generic<TIn, TOut, GEMM_EPI_BIAS_SILU>;
     default: return nullptr;
   }
 }

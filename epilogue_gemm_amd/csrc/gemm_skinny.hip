@@ -94,7 +94,9 @@ template <typename TIn, typename TOut, int NW, int P, int KC, int EPI>
 __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const TIn* __restrict__ A, const TIn* __restrict__ B,
                                                               const TIn* __restrict__ bias, TOut* __restrict__ C,
                                                               int M, int N, int K, float* __restrict__ part,
-                                                              unsigned* __restrict__ arrivals) {
+                                                              unsigned* __restrict__ arrivals,
+                                                              const float* __restrict__ scale,
+                                                              const TOut* __restrict__ res) {
   constexpr int RB = KC * 2;            // bytes of one row segment of a chunk
   constexpr int SLOT = 32 * RB;         // one ring slot: 32 rows of B
   constexpr int MF = KC / 16 / NW;      // MFMAs per wave per chunk
@@ -272,13 +274,30 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const TIn* __restr
 
   // Output (m, n0 + 4q + e), q = t % 8: accumulator v = 4 (q / 2) + e of
   // lane m + 32 (q % 2) in every wave's record, summed in wave order; then
-  // bias, activation, conversion and one vector store of four outputs.
+  // finish() below.
   auto block_sum = [&](int om) __attribute__((always_inline)) -> f32x4 {
     const int L = om + 32 * (oq & 1), c = oq >> 1;
     f32x4 z = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int w = 0; w < NW; ++w) z += *(const f32x4*)(record(w) + L * 64 + ((c ^ ((L >> 2) & 3)) << 4));
     return z;
+  };
+  // Column scale, bias, activation, residual, conversion and one vector
+  // store of outputs (om, n0 + 4 oq .. + 3).
+  auto finish = [&](int om, f32x4 z) __attribute__((always_inline)) {
+    const int n = n0 + 4 * oq;
+    f32x4 sc = f32x4{1.0f, 1.0f, 1.0f, 1.0f}, r = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    if (scale) sc = *(const f32x4*)(scale + n);
+    if (res) r = load4<TOut>(res + (int64_t)om * N + n);
+    float v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float b = 0.0f;
+      if constexpr (epi_has_bias<EPI>())
+        b = to_f32(__builtin_bit_cast(TIn, (uint16_t)((e & 1) ? (bias_q[e >> 1] >> 16) : (bias_q[e >> 1] & 0xffffu))));
+      v[e] = epilogue_ex<EPI>(z[e], b, scale != nullptr, sc[e], res != nullptr, r[e]);
+    }
+    store4<TOut>(C + (int64_t)om * N + n, v[0], v[1], v[2], v[3]);
   };
   if (part != nullptr) {
     // Split K: store this workgroup's fp32 partial block (row-major 32 x 32
@@ -318,19 +337,12 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const TIn* __restr
     for (int t = tid; t < 256; t += NW * 64) {
       const int om = t >> 3;
       if (om >= M) break;
-      float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      f32x4 z = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
       for (int s = 0; s < nsplit; ++s)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          v[e] += __hip_atomic_load(blk + s * 1024 + om * 32 + 4 * oq + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float b = 0.0f;
-        if constexpr (epi_has_bias<EPI>())
-          b = to_f32(__builtin_bit_cast(TIn, (uint16_t)((e & 1) ? (bias_q[e >> 1] >> 16) : (bias_q[e >> 1] & 0xffffu))));
-        v[e] = epilogue<EPI>(v[e], b);
-      }
-      store4<TOut>(C + (int64_t)om * N + n0 + 4 * oq, v[0], v[1], v[2], v[3]);
+          z[e] += __hip_atomic_load(blk + s * 1024 + om * 32 + 4 * oq + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      finish(om, z);
     }
     if (tid == 0) __hip_atomic_store(arrivals + blockIdx.x, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return;
@@ -338,16 +350,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const TIn* __restr
   for (int t = tid; t < 256; t += NW * 64) {
     const int om = t >> 3;
     if (om >= M) break;
-    const f32x4 z = block_sum(om);
-    float v[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      float b = 0.0f;
-      if constexpr (epi_has_bias<EPI>())
-        b = to_f32(__builtin_bit_cast(TIn, (uint16_t)((e & 1) ? (bias_q[e >> 1] >> 16) : (bias_q[e >> 1] & 0xffffu))));
-      v[e] = epilogue<EPI>(z[e], b);
-    }
-    store4<TOut>(C + (int64_t)om * N + n0 + 4 * oq, v[0], v[1], v[2], v[3]);
+    finish(om, block_sum(om));
   }
 }
 
@@ -360,7 +363,7 @@ hipError_t launch_skinny(const LaunchArgs& a) {
   unsigned* arrivals = a.split > 1 ? (unsigned*)((char*)a.workspace + (size_t)nblocks * a.split * 4096) : nullptr;
   hipLaunchKernelGGL((gemm_skinny_kernel<TIn, TOut, NW, P, KC, EPI>), dim3(nblocks, a.split > 1 ? a.split : 1),
                      dim3(NW * 64), 0, a.stream, (const TIn*)a.A, (const TIn*)a.B, (const TIn*)a.bias, (TOut*)a.C,
-                     a.M, a.N, a.K, part, arrivals);
+                     a.M, a.N, a.K, part, arrivals, a.scale, (const TOut*)a.residual);
   return hipGetLastError();
 }
 
@@ -372,6 +375,8 @@ LaunchFn pick_epi(int epi) {
     case GEMM_EPI_BIAS_RELU: return &launch_skinny<TIn, TOut, NW, P, KC, GEMM_EPI_BIAS_RELU>;
     case GEMM_EPI_BIAS_GELU: return &launch_skinny<TIn, TOut, NW, P, KC, GEMM_EPI_BIAS_GELU>;
     case GEMM_EPI_BIAS: return &launch_skinny<TIn, TOut, NW, P, KC, GEMM_EPI_BIAS>;
+    case GEMM_EPI_SILU: return &launch_skinny<TIn, TOut, NW, P, KC, GEMM_EPI_SILU>;
+    case GEMM_EPI_BIAS_SILU: return &launch_skinny<TIn, TOut, NW, P, KC, GEMM_EPI_BIAS_SILU>;
     default: return nullptr;
   }
 }

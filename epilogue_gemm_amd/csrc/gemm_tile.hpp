@@ -189,9 +189,10 @@ __device__ __forceinline__ void raster(int bid, int tiles_m, int tiles_n, int pa
 // spread the banks), then read back 16 bytes per lane along rows and stored:
 // one wave instruction covers whole row segments of the band.  Bands are
 // processed one after another so that few values are live at a time.
-template <int WM, int WN, typename TIn, typename TOut, int EPI>
+template <int WM, int WN, typename TIn, typename TOut, int EPI, bool EXTRAS>
 __device__ __forceinline__ void write_tile(const f32x16 (&acc)[WM / 32][WN / 32], const TIn* __restrict__ bias,
-                                          TOut* __restrict__ C, int N, int m_w, int n_w, int lane, char* stage) {
+                                          TOut* __restrict__ C, int N, int m_w, int n_w, int lane, char* stage,
+                                          const float* __restrict__ scale, const TOut* __restrict__ res) {
   constexpr int TM = WM / 32, TN = WN / 32;
   constexpr int OSZ = (int)sizeof(TOut);
   constexpr int CPR = WN * OSZ / 16;           // 16-byte chunks per staged row
@@ -215,6 +216,13 @@ __device__ __forceinline__ void write_tile(const f32x16 (&acc)[WM / 32][WN / 32]
     for (int j = 0; j < TN; ++j) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
+        // optional column scale and residual of these four outputs
+        const int col = n_w + j * 32 + 8 * q + 4 * h;
+        f32x4 sc = f32x4{1.0f, 1.0f, 1.0f, 1.0f}, r = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        if constexpr (EXTRAS) {
+          if (scale) sc = *(const f32x4*)(scale + col);
+          if (res) r = load4<TOut>(res + (int64_t)(m_w + i * 32 + m_l) * N + col);
+        }
         float v[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -223,7 +231,8 @@ __device__ __forceinline__ void write_tile(const f32x16 (&acc)[WM / 32][WN / 32]
             const uint32_t w = bq[j][q][e >> 1];
             b = to_f32(__builtin_bit_cast(TIn, (uint16_t)((e & 1) ? (w >> 16) : (w & 0xffffu))));
           }
-          v[e] = epilogue<EPI>(acc[i][j][4 * q + e], b);
+          v[e] = epilogue_ex<EPI>(acc[i][j][4 * q + e], b, EXTRAS && scale != nullptr, sc[e], EXTRAS && res != nullptr,
+                                  r[e]);
         }
         // columns j*32 + 8q + 4h .. +3 of row m_l
         if constexpr (OSZ == 4) {
@@ -269,7 +278,8 @@ template <int BM, int BN, int NW, typename TIn, typename TOut, bool A_KMAJ, bool
 __global__ __launch_bounds__(NW * 64) void gemm_tile_kernel(const TIn* __restrict__ A, const TIn* __restrict__ B,
                                                              const TIn* __restrict__ bias, TOut* __restrict__ C,
                                                              int M, int N, int K, int tiles_m, int tiles_n,
-                                                             int panel) {
+                                                             int panel, const float* __restrict__ scale,
+                                                             const TOut* __restrict__ res) {
   // NW waves in a 2 x (NW / 2) grid, each owning a WM x WN sub-tile
   constexpr int NT = NW * 64;
   constexpr int WM = BM / 2, WN = BN / (NW / 2);
@@ -459,7 +469,13 @@ __global__ __launch_bounds__(NW * 64) void gemm_tile_kernel(const TIn* __restric
   static_assert(BM == BN && 32 * WN * sizeof(TOut) <= (size_t)A_BYTES / (NW / 4), "staging area");
   char* const stage_w = (wave % 4 == 0 ? sA0 : wave % 4 == 1 ? sA1 : wave % 4 == 2 ? sB0 : sB1) +
                         (wave / 4) * (A_BYTES / (NW / 4));
-  write_tile<WM, WN, TIn, TOut, EPI>(acc, bias, C, N, m0 + wm * WM, n0 + wn * WN, lane, stage_w);
+  // (the optional column scale and residual get their own copy of the
+  // epilogue, so that the plain one carries no tests for them)
+  if (scale != nullptr || res != nullptr)
+    write_tile<WM, WN, TIn, TOut, EPI, true>(acc, bias, C, N, m0 + wm * WM, n0 + wn * WN, lane, stage_w, scale, res);
+  else
+    write_tile<WM, WN, TIn, TOut, EPI, false>(acc, bias, C, N, m0 + wm * WM, n0 + wn * WN, lane, stage_w, nullptr,
+                                              nullptr);
 }
 
 // Host launch of one instantiation.
@@ -469,7 +485,7 @@ hipError_t launch(const LaunchArgs& a) {
   const int panel = tiles_m < 4 ? tiles_m : 4;
   hipLaunchKernelGGL((gemm_tile_kernel<BM, BN, NW, TIn, TOut, A_KMAJ, B_KMAJ, EPI>), dim3(tiles_m * tiles_n),
                      dim3(NW * 64), 0, a.stream, (const TIn*)a.A, (const TIn*)a.B, (const TIn*)a.bias, (TOut*)a.C,
-                     a.M, a.N, a.K, tiles_m, tiles_n, panel);
+                     a.M, a.N, a.K, tiles_m, tiles_n, panel, a.scale, (const TOut*)a.residual);
   return hipGetLastError();
 }
 
@@ -481,6 +497,8 @@ LaunchFn pick_epi(int epi) {
     case GEMM_EPI_BIAS_RELU: return &launch<BM, BN, NW, TIn, TOut, A_KMAJ, B_KMAJ, GEMM_EPI_BIAS_RELU>;
     case GEMM_EPI_BIAS_GELU: return &launch<BM, BN, NW, TIn, TOut, A_KMAJ, B_KMAJ, GEMM_EPI_BIAS_GELU>;
     case GEMM_EPI_BIAS: return &launch<BM, BN, NW, TIn, TOut, A_KMAJ, B_KMAJ, GEMM_EPI_BIAS>;
+    case GEMM_EPI_SILU: return &launch<BM, BN, NW, TIn, TOut, A_KMAJ, B_KMAJ, GEMM_EPI_SILU>;
+    case GEMM_EPI_BIAS_SILU: return &launch<BM, BN, NW, TIn, TOut, A_KMAJ, B_KMAJ, GEMM_EPI_BIAS_SILU>;
     default: return nullptr;
   }
 }

@@ -39,14 +39,14 @@ class Workload:
     out_dtype: str  # "f16" | "bf16" | "f32"
     layout_a: str  # "row" | "col"
     layout_b: str  # "row" | "col"
-    epilogue: str  # "none" | "relu" | "bias_relu" | "bias_gelu" | "bias"
+    epilogue: str  # "none" | "relu" | "bias_relu" | "bias_gelu" | "bias" | "silu" | "bias_silu"
     b_div: float  # B ~ N(0,1) / b_div
     bias_std: float  # bias ~ N(0, bias_std^2)
     seed: int
 
     @property
     def has_bias(self) -> bool:
-        return self.epilogue in ("bias_relu", "bias_gelu", "bias")
+        return self.epilogue.startswith("bias")
 
     @property
     def flops(self) -> int:
@@ -141,3 +141,28 @@ def integer_inputs(M: int, N: int, K: int, in_dtype: str, layout_a: str, layout_
         "B": to_bits(b),
         "bias": to_bits(bias.to(dt)) if bias is not None else None,
     }
+
+
+def extras_inputs(M: int, N: int, out_dtype: str, seed: int, integer: bool = False):
+    """Optional epilogue operands: dict(scale=float32 array of N, residual=bit
+    patterns of an M x N row-major array in the output format: uint16 for
+    f16/bf16, uint32 for f32).
+
+    Random (integer=False): scale ~ U(0.5, 1.5), residual ~ N(0, 1).
+    Integer (integer=True): scale from {-2, -1, -0.5, 0.5, 1, 2} and residual
+    integers in [-8, 8], so that with integer operands every fp32 step of the
+    epilogue is exact."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed) + 7919)
+    if integer:
+        choices = torch.tensor([-2.0, -1.0, -0.5, 0.5, 1.0, 2.0])
+        scale = choices[torch.randint(0, 6, (N,), generator=g)]
+        resid = torch.randint(-8, 9, (M, N), generator=g).to(torch.float32)
+    else:
+        scale = torch.rand(N, generator=g, dtype=torch.float32) + 0.5
+        resid = torch.randn(M, N, generator=g, dtype=torch.float32)
+    if out_dtype == "f32":
+        rbits = resid.contiguous().view(torch.int32).numpy().view(np.uint32).copy()
+    else:
+        rbits = to_bits(resid.to(_TORCH_DT[out_dtype]))
+    return {"scale": scale.numpy().astype(np.float32), "residual": rbits.reshape(-1)}

@@ -1,7 +1,7 @@
 /*
  * gemm_epi.h -- C ABI of the MI355X (gfx950) GEMM with a fused epilogue:
  *
- *     C = act(A . B [+ bias])        fp16/bf16 inputs, fp32 accumulation
+ *     C = act(s . (A . B) [+ bias]) [+ R]     fp16/bf16 inputs, fp32 accumulation
  *
  * The operation is the tiled GEMM whose epilogue (bias add, then ReLU or
  * GELU) runs on the fp32 accumulators before the single store of C:
@@ -15,7 +15,12 @@
  *   - C = GELU_tanh(A @ B + bias): ainew.jp "TileLang で GPU カーネル設計を解説",
  *     section 4 "EPILOGUE FUSION";
  *   - a row-major A with a column-major B and an fp32 C: TileFusion
- *     "基础GEMM示例" (xdnf.cn repost).
+ *     "基础GEMM示例" (xdnf.cn repost);
+ *   - further epilogue fusions (another activation, a quantisation scale,
+ *     a residual): csdn tutorial ch.10 sec. 10.7 (where hand-written GEMMs
+ *     pay: GEMM with bias, activation, quantisation and other epilogues)
+ *     and its operator table (residual fusion); the pages give no formula,
+ *     the forms below are the common ones.
  *
  * Plain C: no HIP, torch or C++ types appear here.  Device buffers are plain
  * device pointers owned by the caller; the stream is a hipStream_t passed as
@@ -52,14 +57,20 @@ typedef enum gemm_epi_layout { GEMM_EPI_ROW_MAJOR = 0, GEMM_EPI_COL_MAJOR = 1 } 
  *   BIAS_GELU  C = g(z + bias[n]),  g(x) = x / (1 + exp(-1.5957691216 (x + 0.044715 x^3)))
  *              (the tanh form of GELU written as a logistic)
  *   BIAS       C = z + bias[n]
+ *   SILU       C = z / (1 + exp(-z))            (x times the logistic sigmoid)
+ *   BIAS_SILU  C = silu(z + bias[n])
  * bias has N elements of the input format, broadcast over rows, and is
- * added before the activation. */
+ * added before the activation.  gemm_epi_run_ex adds an optional column
+ * scale (applied to z before the bias) and residual (added after the
+ * activation). */
 typedef enum gemm_epi_epilogue {
   GEMM_EPI_NONE = 0,
   GEMM_EPI_RELU = 1,
   GEMM_EPI_BIAS_RELU = 2,
   GEMM_EPI_BIAS_GELU = 3,
-  GEMM_EPI_BIAS = 4
+  GEMM_EPI_BIAS = 4,
+  GEMM_EPI_SILU = 5,
+  GEMM_EPI_BIAS_SILU = 6
 } gemm_epi_epilogue;
 
 typedef enum gemm_epi_status {
@@ -135,6 +146,32 @@ size_t gemm_epi_workspace_size(gemm_epi_plan_t plan);
  * itself is still read-only.  Same errors as gemm_epi_run. */
 gemm_epi_status gemm_epi_run_ws(gemm_epi_plan_t plan, const void* A, const void* B, const void* bias, void* C,
                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* Optional epilogue operands of gemm_epi_run_ex.  With them the output is
+ *
+ *     C[m][n] = act(col_scale[n] * (A.B)[m][n] + bias[n]) + residual[m][n]
+ *
+ * computed in fp32 and rounded once.
+ *   col_scale  N fp32 values (a per-output-column factor such as a weight
+ *              dequantisation scale), or NULL for 1.
+ *   residual   M x N row-major elements of the output format, or NULL for
+ *              0.  It must not overlap C: where M or N is not a multiple of
+ *              a tile, neighbouring workgroups compute some outputs twice,
+ *              and an in-place residual would then be added twice. */
+typedef struct gemm_epi_extras {
+  const float* col_scale;
+  const void* residual;
+} gemm_epi_extras;
+
+/* gemm_epi_run_ex -- gemm_epi_run_ws with the optional epilogue operands of
+ * gemm_epi_extras.  extras == NULL, or both of its pointers NULL, is exactly
+ * gemm_epi_run_ws (workspace may be NULL with workspace_bytes 0).  A
+ * col_scale or residual that is not 16-byte aligned sends the call to the
+ * generic kernel, like any other unaligned pointer.  Same errors as
+ * gemm_epi_run; INVALID_ARG also when residual overlaps C. */
+gemm_epi_status gemm_epi_run_ex(gemm_epi_plan_t plan, const void* A, const void* B, const void* bias,
+                                const gemm_epi_extras* extras, void* C, void* workspace, size_t workspace_bytes,
+                                void* stream);
 
 /* gemm_epi_destroy -- free the host plan object.  NULL is a no-op (OK).
  * No device synchronisation: runs already enqueued are unaffected. */

@@ -25,6 +25,14 @@ def to_device(bits: np.ndarray, dtype: str, device="cuda"):
     return t.view(_TORCH_DT[dtype]).to(device)
 
 
+def to_device_out(bits: np.ndarray, dtype: str, device="cuda"):
+    """Output-format bit patterns (uint16, or uint32 for f32) -> device tensor."""
+    if dtype == "f32":
+        t = torch.from_numpy(np.ascontiguousarray(bits).astype(np.uint32).view(np.int32).reshape(-1).copy())
+        return t.view(torch.float32).to(device)
+    return to_device(np.asarray(bits).astype(np.uint16), dtype, device)
+
+
 def empty_out(n: int, dtype: str, device="cuda"):
     return torch.empty(n, dtype=_TORCH_DT[dtype], device=device)
 

@@ -54,7 +54,7 @@ def test_plan_rejects_invalid_arguments(lib):
     assert gb.gemm_epi_plan_status(**{**ok, "in_dtype": "f32", "out_dtype": "f32"}) == 1  # f32 input
     assert gb.gemm_epi_plan_status(**{**ok, "out_dtype": "bf16"}) == 1  # mixed 16-bit formats
     raw = [0, 0, 0, 0, 0]
-    for pos, bad in [(0, 7), (1, 9), (2, 2), (3, -1), (4, 5)]:
+    for pos, bad in [(0, 7), (1, 9), (2, 2), (3, -1), (4, 7), (4, -1)]:
         args = list(raw)
         args[pos] = bad
         assert gb.gemm_epi_plan_status(64, 64, 64, *args, raw=True) == 1
@@ -85,6 +85,30 @@ def test_run_rejects_invalid_arguments_without_touching_the_device(lib):
     finally:
         gb.gemm_epi_destroy(h)
     assert gb.gemm_epi_destroy(None) == 0
+
+
+def test_run_ex_rejects_invalid_arguments_without_touching_the_device(lib):
+    M, N = 64, 64
+    h = gb.gemm_epi_plan(M, N, 64, "bf16", "bf16", "row", "col", "bias_silu")
+    try:
+        p, c = 0x10000, 0x100000
+        nbytes = M * N * 2
+        # no plan / missing bias / bias without a bias epilogue
+        assert gb.gemm_epi_run_ex(None, p, p, p, 0, 0, c, None, 0, None) == 1
+        assert gb.gemm_epi_run_ex(h, p, p, None, 0, 0, c, None, 0, None) == 1
+        # a residual overlapping C (same start, inside, straddling the end)
+        for r in (c, c + 64, c + nbytes - 2, c - nbytes + 2):
+            assert gb.gemm_epi_run_ex(h, p, p, p, None, r, c, None, 0, None) == 1, hex(r)
+    finally:
+        gb.gemm_epi_destroy(h)
+    h = gb.gemm_epi_plan(M, N, 64, "f16", "f32", "row", "row", "silu")
+    try:
+        c = 0x100000
+        # fp32 output: the residual spans 4 bytes per element
+        assert gb.gemm_epi_run_ex(h, 0x1000, 0x1000, None, None, c + M * N * 4 - 4, c, None, 0, None) == 1
+        assert gb.gemm_epi_run_ex(h, 0x1000, 0x1000, 0x1000, None, None, c, None, 0, None) == 1  # bias given
+    finally:
+        gb.gemm_epi_destroy(h)
 
 
 @pytest.mark.parametrize("M,N,K,la,lb,want_kernel,want_name", [
