@@ -11,7 +11,19 @@
  *
  *   z[i][j] = s[j] * sum_{k<K} a(i,k) * b(k,j)   (+ bias[j] when the epilogue has a bias)
  *   y[i][j] = act(z[i][j])   (+ r[i][j] when a residual is given)
- *   C[i][j] = round_to_nearest_even(y[i][j], output format)
+ *   C[i][j] = round_to_nearest_even(q * y[i][j], output format)
+ *
+ *   q is an optional fp32 output scale (1 when absent).  Output formats:
+ *   the input format, fp32, or FP8 E4M3 (the quantised output the tutorial
+ *   names as a fusion, ch.10 sec. 10.7 and the "GEMM + quantisation"
+ *   list of its closing chapter).  E4M3 follows the OCP 8-bit floating
+ *   point definition: 1 sign, 4 exponent (bias 7), 3 fraction bits, no
+ *   infinities, S.1111.111 the only NaN, largest finite 448.  Encoding to
+ *   E4M3 saturates: |q y| >= 448 gives +-448.  Its rounding decision is
+ *   taken from q y rounded to fp32 first (round to nearest even), then
+ *   rounded to nearest even in E4M3 -- the precision in which a GPU kernel
+ *   that works in fp32 decides the code; a residual is not defined for
+ *   FP8 output.
  *
  *   s[j] (an optional fp32 per-column scale, 1 when absent) and r[i][j] (an
  *   optional M x N row-major residual in the output format, 0 when absent)
@@ -62,6 +74,7 @@
 #define ORC_F16 0
 #define ORC_BF16 1
 #define ORC_F32 2
+#define ORC_FP8 3 /* OCP FP8 E4M3 */
 
 #define ORC_ROW 0
 #define ORC_COL 1
@@ -129,9 +142,53 @@ static uint32_t encode_bits(double x, int mant, int expb) {
   return sbit | ((uint32_t)(E + bias) << mant) | ((uint32_t)n - (1u << mant));
 }
 
-double oracle_decode(int fmt, uint32_t bits) { return decode_bits(bits, fmt_mant(fmt), fmt_expb(fmt)); }
+/* E4M3 value of a byte: sign, exponent e (bias 7), fraction f; e = 0 is
+ * subnormal (f * 2^-9); S.1111.111 is NaN; no infinities. */
+static double decode_e4m3(uint32_t bits) {
+  uint32_t sign = (bits >> 7) & 1u, e = (bits >> 3) & 15u, f = bits & 7u;
+  if (e == 15u && f == 7u) return NAN;
+  double v = e == 0 ? ldexp((double)f, -9) : ldexp((double)(8u + f), (int)e - 10);
+  return sign ? -v : v;
+}
 
-uint32_t oracle_encode(int fmt, double x) { return encode_bits(x, fmt_mant(fmt), fmt_expb(fmt)); }
+/* E4M3 code of x: round to nearest even, saturating at +-448; NaN gives
+ * 0x7F. */
+static uint32_t encode_e4m3(double x) {
+  if (isnan(x)) return 0x7Fu;
+  uint32_t sbit = signbit(x) ? 0x80u : 0u;
+  double a = fabs(x);
+  if (a >= 448.0) return sbit | 0x7Eu; /* saturate (also +-inf) */
+  if (a == 0.0) return sbit;
+  int e2;
+  frexp(a, &e2);
+  int E = e2 - 1;      /* a in [2^E, 2^(E+1)) */
+  if (E < -6) E = -6;  /* subnormals share the spacing 2^-9 */
+  double n = nearbyint(ldexp(a, 3 - E)); /* a / 2^(E-3), ties to even */
+  if (n >= 16.0) {     /* carried into the next binade */
+    n = ldexp(n, -1);
+    E += 1;
+  }
+  if (n < 8.0) return sbit | (uint32_t)n; /* subnormal (E == -6) */
+  /* a < 448 rounds to at most 448 = 2^8 * 1.75: never the NaN code */
+  return sbit | ((uint32_t)(E + 7) << 3) | ((uint32_t)n - 8u);
+}
+
+double oracle_decode(int fmt, uint32_t bits) {
+  if (fmt == ORC_FP8) return decode_e4m3(bits);
+  return decode_bits(bits, fmt_mant(fmt), fmt_expb(fmt));
+}
+
+uint32_t oracle_encode(int fmt, double x) {
+  if (fmt == ORC_FP8) return encode_e4m3(x);
+  return encode_bits(x, fmt_mant(fmt), fmt_expb(fmt));
+}
+
+/* Output code of y: one RNE to a 16- or 32-bit format; for E4M3, RNE to
+ * fp32 first, then RNE (saturating) to E4M3. */
+static uint32_t encode_out(int fmt, double y) {
+  if (fmt == ORC_FP8) return encode_e4m3(oracle_decode(ORC_F32, oracle_encode(ORC_F32, y)));
+  return oracle_encode(fmt, y);
+}
 
 /* Element-wise forms of the two conversions above, for n values. */
 void oracle_decode_n(int fmt, const uint32_t* bits, double* out, int64_t n) {
@@ -170,6 +227,7 @@ static int epi_has_bias(int epi) {
 
 static void store_bits(void* p, int fmt, int64_t idx, uint32_t v) {
   if (fmt == ORC_F32) ((uint32_t*)p)[idx] = v;
+  else if (fmt == ORC_FP8) ((uint8_t*)p)[idx] = (uint8_t)v;
   else ((uint16_t*)p)[idx] = (uint16_t)v;
 }
 
@@ -188,17 +246,19 @@ static double* make_table(int fmt) {
 static int check_args(int64_t M, int64_t N, int64_t K, int in_fmt, int out_fmt, int la, int lb, int epi) {
   if (M <= 0 || N <= 0 || K <= 0) return -1;
   if (in_fmt != ORC_F16 && in_fmt != ORC_BF16) return -1;
-  if (out_fmt != in_fmt && out_fmt != ORC_F32) return -1;
+  if (out_fmt != in_fmt && out_fmt != ORC_F32 && out_fmt != ORC_FP8) return -1;
   if ((la != ORC_ROW && la != ORC_COL) || (lb != ORC_ROW && lb != ORC_COL)) return -1;
   if (epi < ORC_EPI_NONE || epi > ORC_EPI_BIAS_SILU) return -1;
   return 0;
 }
 
-/* Optional epilogue operands: per-column fp32 scale (N bit patterns) and a
- * residual (M x N row-major, output format).  Either may be NULL. */
+/* Optional epilogue operands: per-column fp32 scale (N bit patterns), a
+ * residual (M x N row-major, output format) and the fp32 output scale (one
+ * bit pattern).  Each may be NULL. */
 typedef struct {
   const uint32_t* scale;
   const void* residual;
+  const uint32_t* out_scale;
   int out_fmt;
 } extras_t;
 
@@ -216,6 +276,7 @@ static double one_element(const double* tab, const uint16_t* A, const uint16_t* 
   if (epi_has_bias(epi)) z += tab[bias[j]];
   double y = apply_act(epi, z);
   if (ex->residual) y += oracle_decode(ex->out_fmt, load_bits(ex->residual, ex->out_fmt, i * N + j));
+  if (ex->out_scale) y *= oracle_decode(ORC_F32, ex->out_scale[0]);
   return y;
 }
 
@@ -225,10 +286,11 @@ static double one_element(const double* tab, const uint16_t* A, const uint16_t* 
  * success, -1 on bad arguments, -2 on no memory. */
 int oracle_gemm_epi_ex(int64_t M, int64_t N, int64_t K, int in_fmt, int out_fmt, int la, int lb, int epi,
                        const void* A, const void* B, const void* bias, const uint32_t* scale, const void* residual,
-                       double* y_out, void* c_out, int nthreads) {
+                       const uint32_t* out_scale, double* y_out, void* c_out, int nthreads) {
   if (check_args(M, N, K, in_fmt, out_fmt, la, lb, epi)) return -1;
   if (!A || !B || (epi_has_bias(epi) && !bias)) return -1;
-  const extras_t ex = {scale, residual, out_fmt};
+  if (residual && out_fmt == ORC_FP8) return -1;
+  const extras_t ex = {scale, residual, out_scale, out_fmt};
   double* tab = make_table(in_fmt);
   if (!tab) return -2;
 #ifdef _OPENMP
@@ -240,7 +302,7 @@ int oracle_gemm_epi_ex(int64_t M, int64_t N, int64_t K, int in_fmt, int out_fmt,
       double y = one_element(tab, (const uint16_t*)A, (const uint16_t*)B, (const uint16_t*)bias, &ex, M, N, K, la,
                              lb, epi, i, j);
       if (y_out) y_out[i * N + j] = y;
-      if (c_out) store_bits(c_out, out_fmt, i * N + j, oracle_encode(out_fmt, y));
+      if (c_out) store_bits(c_out, out_fmt, i * N + j, encode_out(out_fmt, y));
     }
   }
   free(tab);
@@ -249,20 +311,22 @@ int oracle_gemm_epi_ex(int64_t M, int64_t N, int64_t K, int in_fmt, int out_fmt,
 
 int oracle_gemm_epi(int64_t M, int64_t N, int64_t K, int in_fmt, int out_fmt, int la, int lb, int epi,
                     const void* A, const void* B, const void* bias, double* y_out, void* c_out, int nthreads) {
-  return oracle_gemm_epi_ex(M, N, K, in_fmt, out_fmt, la, lb, epi, A, B, bias, NULL, NULL, y_out, c_out, nthreads);
+  return oracle_gemm_epi_ex(M, N, K, in_fmt, out_fmt, la, lb, epi, A, B, bias, NULL, NULL, NULL, y_out, c_out,
+                            nthreads);
 }
 
 /* Selected elements only: for p < count, element (rows[p], cols[p]).
  * y_out[p] gets the fp64 value, bits_out[p] its rounded encoding. */
 int oracle_gemm_epi_points_ex(int64_t M, int64_t N, int64_t K, int in_fmt, int out_fmt, int la, int lb, int epi,
                               const void* A, const void* B, const void* bias, const uint32_t* scale,
-                              const void* residual, int64_t count, const int64_t* rows, const int64_t* cols,
-                              double* y_out, uint32_t* bits_out, int nthreads) {
+                              const void* residual, const uint32_t* out_scale, int64_t count, const int64_t* rows,
+                              const int64_t* cols, double* y_out, uint32_t* bits_out, int nthreads) {
   if (check_args(M, N, K, in_fmt, out_fmt, la, lb, epi)) return -1;
   if (!A || !B || (epi_has_bias(epi) && !bias) || count < 0 || (count && (!rows || !cols))) return -1;
+  if (residual && out_fmt == ORC_FP8) return -1;
   for (int64_t p = 0; p < count; ++p)
     if (rows[p] < 0 || rows[p] >= M || cols[p] < 0 || cols[p] >= N) return -1;
-  const extras_t ex = {scale, residual, out_fmt};
+  const extras_t ex = {scale, residual, out_scale, out_fmt};
   double* tab = make_table(in_fmt);
   if (!tab) return -2;
 #ifdef _OPENMP
@@ -273,7 +337,7 @@ int oracle_gemm_epi_points_ex(int64_t M, int64_t N, int64_t K, int in_fmt, int o
     double y = one_element(tab, (const uint16_t*)A, (const uint16_t*)B, (const uint16_t*)bias, &ex, M, N, K, la, lb,
                            epi, rows[p], cols[p]);
     if (y_out) y_out[p] = y;
-    if (bits_out) bits_out[p] = oracle_encode(out_fmt, y);
+    if (bits_out) bits_out[p] = encode_out(out_fmt, y);
   }
   free(tab);
   return 0;
@@ -282,8 +346,8 @@ int oracle_gemm_epi_points_ex(int64_t M, int64_t N, int64_t K, int in_fmt, int o
 int oracle_gemm_epi_points(int64_t M, int64_t N, int64_t K, int in_fmt, int out_fmt, int la, int lb, int epi,
                            const void* A, const void* B, const void* bias, int64_t count, const int64_t* rows,
                            const int64_t* cols, double* y_out, uint32_t* bits_out, int nthreads) {
-  return oracle_gemm_epi_points_ex(M, N, K, in_fmt, out_fmt, la, lb, epi, A, B, bias, NULL, NULL, count, rows, cols,
-                                   y_out, bits_out, nthreads);
+  return oracle_gemm_epi_points_ex(M, N, K, in_fmt, out_fmt, la, lb, epi, A, B, bias, NULL, NULL, NULL, count, rows,
+                                   cols, y_out, bits_out, nthreads);
 }
 
 /* Threads an OpenMP region of this library uses by default. */

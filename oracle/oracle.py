@@ -18,7 +18,7 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 
 # Codes understood by oracle.c (its own numbering; nothing is shared with the
 # GPU library's header).
-FORMATS = {"f16": 0, "bf16": 1, "f32": 2}
+FORMATS = {"f16": 0, "bf16": 1, "f32": 2, "fp8": 3}
 LAYOUTS = {"row": 0, "col": 1}
 EPILOGUES = {"none": 0, "relu": 1, "bias_relu": 2, "bias_gelu": 3, "bias": 4, "silu": 5, "bias_silu": 6}
 
@@ -59,9 +59,9 @@ def _load():
     lib.oracle_gelu.restype = dp
     lib.oracle_silu.argtypes = [dp]
     lib.oracle_silu.restype = dp
-    lib.oracle_gemm_epi_ex.argtypes = [i64, i64, i64, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, i32]
+    lib.oracle_gemm_epi_ex.argtypes = [i64, i64, i64, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, i32]
     lib.oracle_gemm_epi_ex.restype = i32
-    lib.oracle_gemm_epi_points_ex.argtypes = [i64, i64, i64, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp,
+    lib.oracle_gemm_epi_points_ex.argtypes = [i64, i64, i64, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp,
                                               i64, vp, vp, vp, vp, i32]
     lib.oracle_gemm_epi_points_ex.restype = i32
     lib.oracle_max_threads.argtypes = []
@@ -119,10 +119,15 @@ def _bits16(a, name):
     return a
 
 
-def _extras(scale, residual, M, N, out_dtype):
+_OUT_NP = {"f16": np.uint16, "bf16": np.uint16, "f32": np.uint32, "fp8": np.uint8}
+
+
+def _extras(scale, residual, M, N, out_dtype, out_scale=None):
     """Optional epilogue operands as the arrays oracle.c reads: the fp32 column
     scale as uint32 bit patterns (N), the residual as output-format bit
-    patterns (M x N row-major)."""
+    patterns (M x N row-major), the fp32 output scale as one bit pattern."""
+    if out_scale is not None:
+        out_scale = np.array([out_scale], np.float32).view(np.uint32)
     if scale is not None:
         scale = np.ascontiguousarray(scale)
         if scale.dtype == np.float32:
@@ -130,42 +135,45 @@ def _extras(scale, residual, M, N, out_dtype):
         if scale.dtype != np.uint32 or scale.size != N:
             raise ValueError("scale: expected N float32 values (or their uint32 bit patterns)")
     if residual is not None:
+        if out_dtype == "fp8":
+            raise ValueError("residual: not defined for fp8 output")
         residual = np.ascontiguousarray(residual)
         want = np.uint32 if out_dtype == "f32" else np.uint16
         if residual.dtype == np.float32 and out_dtype == "f32":
             residual = residual.view(np.uint32)
         if residual.dtype != want or residual.size != M * N:
             raise ValueError(f"residual: expected M*N {want.__name__} bit patterns of the output format")
-    return scale, residual
+    return scale, residual, out_scale
 
 
 def gemm_epi(A, B, bias, M, N, K, in_dtype, out_dtype, layout_a, layout_b, epilogue,
-             want_y=True, want_c=True, nthreads=0, scale=None, residual=None):
-    """Full M x N product.  Returns (y, c): y is fp64 act(s * A.B [+ bias]) [+ r]
-    (row-major M x N), c the rounded output bit patterns (uint16, or uint32
-    for f32).  scale (N fp32) and residual (M x N, output format) are
-    optional."""
+             want_y=True, want_c=True, nthreads=0, scale=None, residual=None, out_scale=None):
+    """Full M x N product.  Returns (y, c): y is fp64 q * (act(s * A.B [+ bias])
+    [+ r]) (row-major M x N), the value that is rounded; c the output bit
+    patterns (uint16; uint32 for f32; uint8 for fp8).  scale (N fp32),
+    residual (M x N, output format; not for fp8) and out_scale (q, an fp32
+    scalar) are optional."""
     A, B, bias = _bits16(A, "A"), _bits16(B, "B"), _bits16(bias, "bias")
     if A.size != M * K or B.size != K * N or (bias is not None and bias.size != N):
         raise ValueError("operand sizes do not match M, N, K")
-    scale, residual = _extras(scale, residual, M, N, out_dtype)
+    scale, residual, out_scale = _extras(scale, residual, M, N, out_dtype, out_scale)
     y = np.empty((M, N), np.float64) if want_y else None
-    c = np.empty((M, N), np.uint32 if out_dtype == "f32" else np.uint16) if want_c else None
+    c = np.empty((M, N), _OUT_NP[out_dtype]) if want_c else None
     rc = _load().oracle_gemm_epi_ex(M, N, K, FORMATS[in_dtype], FORMATS[out_dtype], LAYOUTS[layout_a],
                                     LAYOUTS[layout_b], EPILOGUES[epilogue], _ptr(A), _ptr(B), _ptr(bias),
-                                    _ptr(scale), _ptr(residual), _ptr(y), _ptr(c), int(nthreads))
+                                    _ptr(scale), _ptr(residual), _ptr(out_scale), _ptr(y), _ptr(c), int(nthreads))
     if rc != 0:
         raise ValueError(f"oracle_gemm_epi rejected its arguments (rc={rc})")
     return y, c
 
 
 def gemm_epi_points(A, B, bias, M, N, K, in_dtype, out_dtype, layout_a, layout_b, epilogue,
-                    rows, cols, nthreads=0, scale=None, residual=None):
+                    rows, cols, nthreads=0, scale=None, residual=None, out_scale=None):
     """Selected elements (rows[p], cols[p]).  Returns (y, bits) as 1-D arrays."""
     A, B, bias = _bits16(A, "A"), _bits16(B, "B"), _bits16(bias, "bias")
     if A.size != M * K or B.size != K * N or (bias is not None and bias.size != N):
         raise ValueError("operand sizes do not match M, N, K")
-    scale, residual = _extras(scale, residual, M, N, out_dtype)
+    scale, residual, out_scale = _extras(scale, residual, M, N, out_dtype, out_scale)
     rows = np.ascontiguousarray(rows, np.int64)
     cols = np.ascontiguousarray(cols, np.int64)
     if rows.shape != cols.shape:
@@ -174,8 +182,8 @@ def gemm_epi_points(A, B, bias, M, N, K, in_dtype, out_dtype, layout_a, layout_b
     bits = np.empty(rows.size, np.uint32)
     rc = _load().oracle_gemm_epi_points_ex(M, N, K, FORMATS[in_dtype], FORMATS[out_dtype], LAYOUTS[layout_a],
                                            LAYOUTS[layout_b], EPILOGUES[epilogue], _ptr(A), _ptr(B), _ptr(bias),
-                                           _ptr(scale), _ptr(residual), rows.size, _ptr(rows), _ptr(cols), _ptr(y),
-                                           _ptr(bits), int(nthreads))
+                                           _ptr(scale), _ptr(residual), _ptr(out_scale), rows.size, _ptr(rows),
+                                           _ptr(cols), _ptr(y), _ptr(bits), int(nthreads))
     if rc != 0:
         raise ValueError(f"oracle_gemm_epi_points rejected its arguments (rc={rc})")
     return y, bits

@@ -508,3 +508,108 @@ def test_rejects_bad_extras():
         oracle.gemm_epi(A, A, None, 2, 2, 2, "f16", "f16", "row", "row", "none", residual=np.zeros(4, np.uint32))
     with pytest.raises(ValueError):
         oracle.gemm_epi(A, A, None, 2, 2, 2, "f16", "f16", "row", "row", "bias_silu")  # missing bias
+
+
+# --------------------------------------------------------------------------
+# FP8 E4M3 output (OCP 8-bit floating point, E4M3 variant) and output scale
+# --------------------------------------------------------------------------
+
+def _torch_e4m3_values(codes):
+    t = torch.from_numpy(np.asarray(codes, np.uint8).copy()).view(torch.float8_e4m3fn)
+    return t.to(torch.float64).numpy()
+
+
+def test_decode_fp8_exhaustive_vs_torch():
+    codes = np.arange(256, dtype=np.uint32)
+    got = oracle.decode_array("fp8", codes)
+    ref = _torch_e4m3_values(codes)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert nan.sum() == 2  # S.1111.111 only
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert oracle.decode("fp8", 0x7E) == 448.0 and oracle.decode("fp8", 0x01) == 2.0**-9
+    assert oracle.decode("fp8", 0x08) == 2.0**-6 and oracle.decode("fp8", 0xB8) == -1.0
+
+
+def test_encode_fp8_vs_torch_in_range():
+    # torch's fp32 -> e4m3fn conversion is round-to-nearest-even; inside the
+    # finite range it must agree with the oracle on fp32-representable values
+    rng = np.random.default_rng(17)
+    x = np.concatenate([rng.standard_normal(200000) * 40, rng.standard_normal(50000) * 0.01,
+                        np.ldexp(rng.random(20000), rng.integers(-12, 9, 20000))])
+    x = x.astype(np.float32)
+    x = x[np.abs(x) < 448]
+    got = oracle.encode_array("fp8", x.astype(np.float64)).astype(np.uint8)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(got, ref)
+
+
+def test_encode_fp8_ties_and_saturation():
+    enc = lambda v: oracle.encode("fp8", v)  # noqa: E731
+    # ties to even in the normal range: 1 + 1/16 between 1 and 1.125 -> 1;
+    # 1 + 3/16 between 1.125 and 1.25 -> 1.25
+    assert enc(1.0 + 1 / 16) == 0x38 and enc(1.0 + 3 / 16) == 0x3A
+    assert enc(1.0 + 1 / 16 + 2.0**-30) == 0x39  # just above the tie
+    # subnormal ties: half the smallest step rounds to 0, 1.5 steps to 2 steps
+    assert enc(2.0**-10) == 0x00 and enc(3 * 2.0**-10) == 0x02 and enc(-(2.0**-10)) == 0x80
+    # carry out of the subnormal range into the first normal binade
+    assert enc(7.5 * 2.0**-9) == 0x08
+    # saturation at +-448 (no infinities in E4M3), NaN stays NaN
+    for v, code in ((448.0, 0x7E), (460.0, 0x7E), (464.0, 0x7E), (1e30, 0x7E), (math.inf, 0x7E),
+                    (-500.0, 0xFE), (-math.inf, 0xFE), (416.0, 0x7D), (432.0, 0x7E)):
+        assert enc(v) == code, (v, hex(enc(v)))
+    assert enc(math.nan) == 0x7F
+    # every finite code is its own encoding
+    for c in range(256):
+        v = oracle.decode("fp8", c)
+        if not math.isnan(v):
+            assert enc(v) == c, c
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+def test_fp8_output_all_ones_and_out_scale(fmt):
+    M, N = 2, 3
+    one = _bits_of([1.0], fmt)[0]
+    for K, q, want in ((64, None, 64.0), (256, None, 256.0), (1024, None, 448.0), (1024, 0.25, 256.0),
+                       (96, 1.0, 96.0), (100, 1.0, 96.0), (104, 1.0, 104.0), (9, 0.5, 4.5)):
+        A = np.full(M * K, one, np.uint16)
+        B = np.full(K * N, one, np.uint16)
+        y, c = oracle.gemm_epi(A, B, None, M, N, K, fmt, "fp8", "row", "col", "none", out_scale=q)
+        assert c.dtype == np.uint8
+        assert np.all(oracle.decode_array("fp8", c.reshape(-1).astype(np.uint32)) == want), (K, q)
+        assert np.all(y == K * (q if q is not None else 1.0))
+    # 100 lies between the codes for 96 and 104 (spacing 8): ties to even -> 96;
+    # and the output scale multiplies after the activation, for any format
+    A = np.full(M * 8, one, np.uint16)
+    B = np.full(8 * N, one, np.uint16)
+    bias = _bits_of([1.0, -20.0, 0.5], fmt)
+    y, c = oracle.gemm_epi(A, B, bias, M, N, 8, fmt, "f32", "row", "col", "bias_relu", out_scale=-2.0)
+    assert np.array_equal(y, np.broadcast_to(-2.0 * np.maximum(8.0 + _values(bias, fmt), 0.0), (M, N)))
+
+
+def test_fp8_rounding_decided_from_fp32():
+    # a value just above an E4M3 tie in fp64 that rounds onto the tie in fp32
+    # is decided from the fp32 value: ties to even
+    fmt, M, N, K = "f16", 1, 1, 2
+    a = _bits_of([1.0, 1.0], fmt)
+    # 1 + 1/16 + 2^-20 (an fp16 subnormal addend): exact in fp32, above the tie
+    b = _bits_of([1.0 + 1 / 16, 2.0**-20], fmt)
+    y, c = oracle.gemm_epi(a, b, None, M, N, K, fmt, "fp8", "row", "row", "none")
+    assert y[0, 0] == 1.0 + 1 / 16 + 2.0**-20
+    assert c[0, 0] == 0x39
+    # 1 + 1/16 + 2^-24 is half an fp32 ulp above the tie: fp32 rounds it to
+    # the tie (even), and the tie goes to even in E4M3
+    b = _bits_of([1.0 + 1 / 16, 2.0**-24], fmt)
+    y, c = oracle.gemm_epi(a, b, None, M, N, K, fmt, "fp8", "row", "row", "none")
+    assert y[0, 0] == 1.0 + 1 / 16 + 2.0**-24
+    assert c[0, 0] == 0x38
+    bf = _bits_of([1.0 + 1 / 16, 2.0**-30], "bf16")
+    y, c = oracle.gemm_epi(_bits_of([1.0, 1.0], "bf16"), bf, None, M, N, K, "bf16", "fp8", "row", "row", "none")
+    assert y[0, 0] == 1.0 + 1 / 16 + 2.0**-30
+    assert c[0, 0] == 0x38  # fp32 rounds 1 + 1/16 + 2^-30 onto the tie, which goes to even
+
+
+def test_fp8_rejects_residual():
+    A = np.zeros(4, np.uint16)
+    with pytest.raises(ValueError):
+        oracle.gemm_epi(A, A, None, 2, 2, 2, "f16", "fp8", "row", "row", "none", residual=np.zeros(4, np.uint8))
