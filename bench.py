@@ -89,18 +89,27 @@ def _device_sets(w, n_sets, torch, parity, inputs):
     return bits, sets
 
 
-def _time_launches(plan, sets, steps, warmup, torch):
+def _time_launches(plan, sets, steps, warmup, torch, extras=None):
+    """ms per launch over `steps` launches rotating through `sets`; `extras`
+    (optional) is a list, per set, of (column scale, residual) tensors."""
     stream = torch.cuda.current_stream()
-    for i in range(warmup):
+
+    def launch(i):
         A, B, bias, C = sets[i % len(sets)]
-        plan.run(A, B, bias, C, stream)
+        if extras is None:
+            plan.run(A, B, bias, C, stream)
+        else:
+            sc, res = extras[i % len(sets)]
+            plan.run(A, B, bias, C, stream, scale=sc, residual=res)
+
+    for i in range(warmup):
+        launch(i)
     torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     start.record(stream)
     for i in range(steps):
-        A, B, bias, C = sets[i % len(sets)]
-        plan.run(A, B, bias, C, stream)
+        launch(i)
     end.record(stream)
     torch.cuda.synchronize()
     return start.elapsed_time(end) / steps  # ms per launch
@@ -170,6 +179,42 @@ def main(argv=None):
         tflops = w.flops / (ms * 1e-3) / 1e12
         out["main"] = dict(w=w, bits=bits, ms=ms, value=tflops, kernel=plan.name)
         plan.close()
+        # the further epilogues on the same shape and operands (reported, not
+        # the headline): bias+SiLU, and bias+GELU with a column scale and a
+        # residual (one residual per operand set, none overlapping C)
+        variants = []
+        ex = inputs.extras_inputs(w.M, w.N, w.out_dtype, seed=w.seed)
+        scale = torch.from_numpy(ex["scale"]).cuda()
+        res0 = parity.to_device_out(ex["residual"], w.out_dtype)
+        extras = [(scale, res0 if i == 0 else res0.clone()) for i in range(len(sets))]
+        vsteps = min(args.steps, 50)
+        for epi, with_extras in (("bias_silu", False), ("bias_gelu", True)):
+            p = binding.Plan(w.M, w.N, w.K, w.in_dtype, w.out_dtype, w.layout_a, w.layout_b, epi)
+            vms = _time_launches(p, sets, vsteps, max(args.warmup // 2, 5), torch, extras if with_extras else None)
+            variants.append({"epilogue": epi, "out_dtype": w.out_dtype, "col_scale": with_extras,
+                             "residual": with_extras, "out_scale": False, "kernel": p.name,
+                             "ms_per_step": round(vms, 4), "TFLOP/s": round(w.flops / (vms * 1e-3) / 1e12, 1),
+                             "steps": vsteps})
+            p.close()
+        # quantised output: bias+GELU, then the output scale and FP8 E4M3
+        del extras, res0
+        sets8 = [(A, B, bias, parity.empty_out(w.M * w.N, "fp8")) for A, B, bias, _ in sets]
+        q = torch.tensor([ex["out_scale"]], dtype=torch.float32, device="cuda")
+        p = binding.Plan(w.M, w.N, w.K, w.in_dtype, "fp8", w.layout_a, w.layout_b, "bias_gelu")
+        stream = torch.cuda.current_stream()
+
+        class _Q:  # runs the plan with the output scale
+            name = p.name
+
+            def run(self, A, B, bias, C, s):
+                p.run(A, B, bias, C, s, out_scale=q)
+        vms = _time_launches(_Q(), sets8, vsteps, max(args.warmup // 2, 5), torch)
+        variants.append({"epilogue": "bias_gelu", "out_dtype": "fp8", "col_scale": False, "residual": False,
+                         "out_scale": True, "kernel": p.name, "ms_per_step": round(vms, 4),
+                         "TFLOP/s": round(w.flops / (vms * 1e-3) / 1e12, 1), "steps": vsteps})
+        p.close()
+        del sets8, stream
+        out["main"]["variants"] = variants
         del sets
         torch.cuda.empty_cache()
     if args.only in ("skinny", "both"):
@@ -216,6 +261,7 @@ def main(argv=None):
             "roofline": {"bound": "mfma", "achieved": round(m["value"], 2), "peak": PEAK_BF16_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(m["value"] / PEAK_BF16_TFLOPS, 4),
                          "traffic": measured_traffic("tile", m["kernel"], w.name)},
+            "epilogue_variants": m.get("variants", []),
         }
     if "skinny" in out:
         s = out["skinny"]

@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libgemm_epi.so")
 HEADER = os.path.join(os.path.dirname(_HERE), "include", "gemm_epi.h")
 
 # Enum values of include/gemm_epi.h
-DTYPES = {"f16": 0, "bf16": 1, "f32": 2}
+DTYPES = {"f16": 0, "bf16": 1, "f32": 2, "fp8": 3}
 LAYOUTS = {"row": 0, "col": 1}
 EPILOGUES = {"none": 0, "relu": 1, "bias_relu": 2, "bias_gelu": 3, "bias": 4, "silu": 5, "bias_silu": 6}
 KERNELS = {"auto": 0, "generic": 1, "tile": 2, "skinny": 3}
@@ -28,8 +28,9 @@ OK = 0
 
 
 class Extras(ctypes.Structure):
-    """struct gemm_epi_extras: optional column scale and residual pointers."""
-    _fields_ = [("col_scale", ctypes.c_void_p), ("residual", ctypes.c_void_p)]
+    """struct gemm_epi_extras: optional column scale, residual and output
+    scale pointers."""
+    _fields_ = [("col_scale", ctypes.c_void_p), ("residual", ctypes.c_void_p), ("out_scale", ctypes.c_void_p)]
 
 
 class GemmEpiError(RuntimeError):
@@ -129,10 +130,10 @@ def gemm_epi_run_ws(plan, A_ptr, B_ptr, bias_ptr, C_ptr, ws_ptr, ws_bytes, strea
 
 
 def gemm_epi_run_ex(plan, A_ptr, B_ptr, bias_ptr, scale_ptr, residual_ptr, C_ptr, ws_ptr, ws_bytes, stream,
-                    extras_null=False) -> int:
-    """extras_null passes a NULL gemm_epi_extras pointer (scale_ptr and
-    residual_ptr are then ignored)."""
-    ex = None if extras_null else ctypes.byref(Extras(scale_ptr, residual_ptr))
+                    extras_null=False, out_scale_ptr=None) -> int:
+    """extras_null passes a NULL gemm_epi_extras pointer (the three extras
+    pointers are then ignored)."""
+    ex = None if extras_null else ctypes.byref(Extras(scale_ptr, residual_ptr, out_scale_ptr))
     return load_library().gemm_epi_run_ex(plan, A_ptr, B_ptr, bias_ptr, ex, C_ptr, ws_ptr, int(ws_bytes), stream)
 
 
@@ -167,7 +168,7 @@ def gemm_epi_plan_describe(plan):
 
 # ---- convenience over torch tensors (device memory + stream only) ----------
 
-_TORCH_DTYPE_NAMES = {"float16": "f16", "bfloat16": "bf16", "float32": "f32"}
+_TORCH_DTYPE_NAMES = {"float16": "f16", "bfloat16": "bf16", "float32": "f32", "float8_e4m3fn": "fp8"}
 
 
 def _dtype_name(t) -> str:
@@ -208,12 +209,14 @@ class Plan:
         """Bytes of workspace that let ``run`` split K (0: never splits)."""
         return gemm_epi_workspace_size(self.handle)
 
-    def run(self, A, B, bias, C, stream=None, workspace=None, scale=None, residual=None):
+    def run(self, A, B, bias, C, stream=None, workspace=None, scale=None, residual=None, out_scale=None):
         """``workspace``: an optional zero-filled uint8 CUDA tensor of at least
         ``workspace_size`` bytes (left zero-filled by every completed run).
         ``scale``: optional fp32 per-column factors (N); ``residual``:
         optional M x N tensor of the output format, added after the
-        activation (must not overlap C)."""
+        activation (must not overlap C); ``out_scale``: optional one-element
+        fp32 CUDA tensor multiplying the final value (the quantisation
+        scale of an fp8 output)."""
         import torch
 
         a = self._check(A, "A", self.in_dtype, self.M * self.K)
@@ -221,15 +224,16 @@ class Plan:
         bi = self._check(bias, "bias", self.in_dtype, self.N)
         c = self._check(C, "C", self.out_dtype, self.M * self.N)
         s = (stream or torch.cuda.current_stream()).cuda_stream
-        if scale is not None or residual is not None:
+        if scale is not None or residual is not None or out_scale is not None:
             sc = self._check(scale, "scale", "f32", self.N)
             r = self._check(residual, "residual", self.out_dtype, self.M * self.N)
+            q = self._check(out_scale, "out_scale", "f32", 1)
             ws, nbytes = None, 0
             if workspace is not None:
                 if not workspace.is_cuda or not workspace.is_contiguous():
                     raise ValueError("workspace: expected a contiguous CUDA tensor")
                 ws, nbytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
-            st = gemm_epi_run_ex(self.handle, a, b, bi, sc, r, c, ws, nbytes, s)
+            st = gemm_epi_run_ex(self.handle, a, b, bi, sc, r, c, ws, nbytes, s, out_scale_ptr=q)
             if st != OK:
                 raise GemmEpiError("gemm_epi_run_ex", st)
             return

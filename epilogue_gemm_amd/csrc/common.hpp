@@ -21,6 +21,12 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// FP8 E4M3 output element (OCP 8-bit floating point: bias 7, no
+// infinities, largest finite 448), as gfx950's v_cvt_pk_fp8_f32 writes it.
+struct fp8e4m3 {
+  uint8_t bits;
+};
+
 // f(std::integral_constant<int, I>{}) for I = 0 .. N-1, so that I is a
 // compile-time constant inside f (for immediates such as s_waitcnt counts).
 template <typename F, int... I>
@@ -51,10 +57,12 @@ struct LaunchArgs {
   // number of K splits (1: no split, no workspace)
   void* workspace;
   int split;
-  // optional epilogue operands (nullptr: absent): fp32 column scale (N)
-  // and residual (M x N row-major, output format)
+  // optional epilogue operands (nullptr: absent): fp32 column scale (N),
+  // residual (M x N row-major, output format) and fp32 output scale (one
+  // value, read by every thread)
   const float* scale;
   const void* residual;
+  const float* out_scale;
 };
 
 // ---------------------------------------------------------------------------
@@ -62,10 +70,11 @@ struct LaunchArgs {
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float to_f32(f16 x) { return (float)x; }
 __device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
-// an output element (16-bit or fp32) -> fp32
+// an output element (16-bit, fp32 or E4M3) -> fp32
 template <typename T>
 __device__ __forceinline__ float out_to_f32(T x) {
-  return (float)x;
+  if constexpr (__is_same(T, fp8e4m3)) return __builtin_amdgcn_cvt_f32_fp8((int)x.bits, 0);
+  else return (float)x;
 }
 
 // ---------------------------------------------------------------------------
@@ -113,14 +122,15 @@ constexpr bool epi_has_bias() {
   return EPI == GEMM_EPI_BIAS_RELU || EPI == GEMM_EPI_BIAS_GELU || EPI == GEMM_EPI_BIAS || EPI == GEMM_EPI_BIAS_SILU;
 }
 
-// The optional operands around the activation: act(s z + b) + r.  `scale`
-// and `res` are uniform across the launch, so the tests are scalar
-// branches.
+// The optional operands around the activation: q (act(s z + b) + r).  The
+// flags are uniform across the launch, so the tests are scalar branches.
 template <int EPI>
-__device__ __forceinline__ float epilogue_ex(float z, float b, bool has_scale, float s, bool has_res, float r) {
+__device__ __forceinline__ float epilogue_ex(float z, float b, bool has_scale, float s, bool has_res, float r,
+                                             bool has_q, float q) {
   if (has_scale) z *= s;
   float v = epilogue<EPI>(z, b);
   if (has_res) v += r;
+  if (has_q) v *= q;
   return v;
 }
 
@@ -133,6 +143,22 @@ __device__ __forceinline__ TOut from_f32(float x) {
   return (TOut)x;
 }
 
+// E4M3 saturates: clamp to +-448 first (a NaN passes through both
+// comparisons unchanged), then v_cvt_pk_fp8_f32 rounds to nearest even.
+__device__ __forceinline__ float sat_e4m3(float x) { return x > 448.0f ? 448.0f : (x < -448.0f ? -448.0f : x); }
+
+template <>
+__device__ __forceinline__ fp8e4m3 from_f32<fp8e4m3>(float x) {
+  const float c = sat_e4m3(x);
+  return fp8e4m3{(uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(c, c, 0, false) & 0xff)};
+}
+
+// Four E4M3 codes of v0..v3, byte i = v_i.
+__device__ __forceinline__ uint32_t pack4_e4m3(float v0, float v1, float v2, float v3) {
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(sat_e4m3(v0), sat_e4m3(v1), 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(sat_e4m3(v2), sat_e4m3(v3), lo, true);
+}
+
 template <typename T>
 __device__ __forceinline__ uint16_t bits16(T x) {
   return __builtin_bit_cast(uint16_t, x);
@@ -141,7 +167,9 @@ __device__ __forceinline__ uint16_t bits16(T x) {
 // Four consecutive outputs of one row -> one vector store.
 template <typename TOut>
 __device__ __forceinline__ void store4(TOut* p, float v0, float v1, float v2, float v3) {
-  if constexpr (sizeof(TOut) == 4) {
+  if constexpr (sizeof(TOut) == 1) {
+    *reinterpret_cast<uint32_t*>(p) = pack4_e4m3(v0, v1, v2, v3);
+  } else if constexpr (sizeof(TOut) == 4) {
     *reinterpret_cast<f32x4*>(p) = f32x4{v0, v1, v2, v3};
   } else {
     u32x2 w;
@@ -151,11 +179,15 @@ __device__ __forceinline__ void store4(TOut* p, float v0, float v1, float v2, fl
   }
 }
 
-// Four consecutive elements (fp32, or 16-bit) as fp32; p 8-byte aligned
-// (16-bit) or 16-byte aligned (fp32).
+// Four consecutive elements (fp32, 16-bit or E4M3) as fp32; p 16-, 8- or
+// 4-byte aligned respectively.
 template <typename T>
 __device__ __forceinline__ f32x4 load4(const T* p) {
-  if constexpr (sizeof(T) == 4) {
+  if constexpr (sizeof(T) == 1) {
+    const int w = *reinterpret_cast<const int*>(p);
+    return f32x4{__builtin_amdgcn_cvt_f32_fp8(w, 0), __builtin_amdgcn_cvt_f32_fp8(w, 1),
+                 __builtin_amdgcn_cvt_f32_fp8(w, 2), __builtin_amdgcn_cvt_f32_fp8(w, 3)};
+  } else if constexpr (sizeof(T) == 4) {
     return *reinterpret_cast<const f32x4*>(p);
   } else {
     const u32x2 w = *reinterpret_cast<const u32x2*>(p);

@@ -28,10 +28,11 @@ bool tile_supports(int cfg, const Problem& p) {
   if (cfg < 0 || cfg >= tile_num_configs()) return false;
   // M and N need not be tile multiples (the last tile row or column is
   // shifted back to end at M or N), but must hold one tile; rows of every
-  // operand and of C must stay 16-byte aligned (N % 8; M % 8 when A is
-  // column-major), and K must be whole k-steps.
+  // operand and of C must stay 16-byte aligned (N % 8, N % 16 for 1-byte
+  // E4M3 output; M % 8 when A is column-major), and K must be whole k-steps.
   const TileConfig& c = kTile[cfg];
-  return p.M >= c.bm && p.N >= c.bn && p.N % 8 == 0 && (p.la == GEMM_EPI_ROW_MAJOR || p.M % 8 == 0) &&
+  const int n_align = p.out_dt == GEMM_EPI_FP8_E4M3 ? 16 : 8;
+  return p.M >= c.bm && p.N >= c.bn && p.N % n_align == 0 && (p.la == GEMM_EPI_ROW_MAJOR || p.M % 8 == 0) &&
          p.K % 64 == 0 && p.K >= 128;
 }
 
@@ -56,9 +57,12 @@ int tile_choose(const Problem& p) {
 }
 
 LaunchFn tile_launcher(int cfg, const Problem& p) {
-  const bool f32 = p.out_dt == GEMM_EPI_F32;
-  if (p.in_dt == GEMM_EPI_F16) return (f32 ? tile_launcher_f16_f32 : tile_launcher_f16_f16)(cfg, p.la, p.lb, p.epi);
-  if (p.in_dt == GEMM_EPI_BF16) return (f32 ? tile_launcher_bf16_f32 : tile_launcher_bf16_bf16)(cfg, p.la, p.lb, p.epi);
+  const bool f32 = p.out_dt == GEMM_EPI_F32, fp8 = p.out_dt == GEMM_EPI_FP8_E4M3;
+  if (p.in_dt == GEMM_EPI_F16)
+    return (fp8 ? tile_launcher_f16_fp8 : f32 ? tile_launcher_f16_f32 : tile_launcher_f16_f16)(cfg, p.la, p.lb, p.epi);
+  if (p.in_dt == GEMM_EPI_BF16)
+    return (fp8 ? tile_launcher_bf16_fp8 : f32 ? tile_launcher_bf16_f32 : tile_launcher_bf16_bf16)(cfg, p.la, p.lb,
+                                                                                                  p.epi);
   return nullptr;
 }
 
@@ -81,7 +85,7 @@ thread_local int g_last_hip_error = 0;
 bool valid_enum_args(gemm_epi_dtype in, gemm_epi_dtype out, gemm_epi_layout la, gemm_epi_layout lb,
                      gemm_epi_epilogue epi) {
   if (in != GEMM_EPI_F16 && in != GEMM_EPI_BF16) return false;
-  if (out != in && out != GEMM_EPI_F32) return false;
+  if (out != in && out != GEMM_EPI_F32 && out != GEMM_EPI_FP8_E4M3) return false;
   if ((la != GEMM_EPI_ROW_MAJOR && la != GEMM_EPI_COL_MAJOR) || (lb != GEMM_EPI_ROW_MAJOR && lb != GEMM_EPI_COL_MAJOR))
     return false;
   return epi >= GEMM_EPI_NONE && epi <= GEMM_EPI_BIAS_SILU;
@@ -155,8 +159,11 @@ gemm_epi_status launch(gemm_epi_plan_t plan, const void* A, const void* B, const
   if (need_bias != (bias != nullptr)) return GEMM_EPI_ERR_INVALID_ARG;
   const float* scale = extras ? extras->col_scale : nullptr;
   const void* residual = extras ? extras->residual : nullptr;
+  const float* out_scale = extras ? extras->out_scale : nullptr;
   if (residual) {
-    // the residual must not overlap C (edge tiles write some outputs twice)
+    // no residual for a quantised output; and it must not overlap C (edge
+    // tiles write some outputs twice)
+    if (plan->p.out_dt == GEMM_EPI_FP8_E4M3) return GEMM_EPI_ERR_INVALID_ARG;
     const uintptr_t bytes = (uintptr_t)(plan->p.M * plan->p.N) * (plan->p.out_dt == GEMM_EPI_F32 ? 4u : 2u);
     const uintptr_t r0 = (uintptr_t)residual, c0 = (uintptr_t)C;
     if (r0 < c0 + bytes && c0 < r0 + bytes) return GEMM_EPI_ERR_INVALID_ARG;
@@ -177,6 +184,7 @@ gemm_epi_status launch(gemm_epi_plan_t plan, const void* A, const void* B, const
   a.split = 1;
   a.scale = scale;
   a.residual = residual;
+  a.out_scale = out_scale;
   const bool aligned = aligned16(A) && aligned16(B) && aligned16(C) && (!bias || aligned16(bias)) &&
                        (!scale || aligned16(scale)) && (!residual || aligned16(residual));
   const size_t need = workspace_bytes(plan);

@@ -18,7 +18,8 @@ __global__ __launch_bounds__(256) void gemm_generic_kernel(const TIn* __restrict
                                                            const TIn* __restrict__ bias, TOut* __restrict__ C,
                                                            int64_t M, int64_t N, int64_t K, int la, int lb,
                                                            const float* __restrict__ scale,
-                                                           const TOut* __restrict__ res) {
+                                                           const TOut* __restrict__ res,
+                                                           const float* __restrict__ out_scale) {
   const int64_t j = (int64_t)blockIdx.x * kGenThreadsX + (threadIdx.x % kGenThreadsX);
   if (j >= N) return;
   const int64_t i_step = (int64_t)gridDim.y * kGenThreadsY;
@@ -34,7 +35,8 @@ __global__ __launch_bounds__(256) void gemm_generic_kernel(const TIn* __restrict
     if constexpr (epi_has_bias<EPI>()) b = to_f32(bias[j]);
     const float s = scale ? scale[j] : 1.0f;
     const float r = res ? out_to_f32(res[i * N + j]) : 0.0f;
-    C[i * N + j] = from_f32<TOut>(epilogue_ex<EPI>(acc, b, scale != nullptr, s, res != nullptr, r));
+    const float os = out_scale ? *out_scale : 1.0f;
+    C[i * N + j] = from_f32<TOut>(epilogue_ex<EPI>(acc, b, scale != nullptr, s, res != nullptr, r, out_scale != nullptr, os));
   }
 }
 
@@ -45,7 +47,7 @@ hipError_t launch_generic(const LaunchArgs& a) {
   if (gy > 65535) gy = 65535;
   hipLaunchKernelGGL((gemm_generic_kernel<TIn, TOut, EPI>), dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, a.stream,
                      (const TIn*)a.A, (const TIn*)a.B, (const TIn*)a.bias, (TOut*)a.C, (int64_t)a.M, (int64_t)a.N,
-                     (int64_t)a.K, a.la, a.lb, a.scale, (const TOut*)a.residual);
+                     (int64_t)a.K, a.la, a.lb, a.scale, (const TOut*)a.residual, a.out_scale);
   return hipGetLastError();
 }
 
@@ -69,9 +71,11 @@ LaunchFn generic_launcher(const Problem& p) {
   if (p.in_dt == GEMM_EPI_F16) {
     if (p.out_dt == GEMM_EPI_F16) return pick_epi<f16, f16>(p.epi);
     if (p.out_dt == GEMM_EPI_F32) return pick_epi<f16, float>(p.epi);
+    if (p.out_dt == GEMM_EPI_FP8_E4M3) return pick_epi<f16, fp8e4m3>(p.epi);
   } else if (p.in_dt == GEMM_EPI_BF16) {
     if (p.out_dt == GEMM_EPI_BF16) return pick_epi<bf16, bf16>(p.epi);
     if (p.out_dt == GEMM_EPI_F32) return pick_epi<bf16, float>(p.epi);
+    if (p.out_dt == GEMM_EPI_FP8_E4M3) return pick_epi<bf16, fp8e4m3>(p.epi);
   }
   return nullptr;
 }

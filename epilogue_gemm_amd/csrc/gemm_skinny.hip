@@ -96,7 +96,8 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const TIn* __restr
                                                               int M, int N, int K, float* __restrict__ part,
                                                               unsigned* __restrict__ arrivals,
                                                               const float* __restrict__ scale,
-                                                              const TOut* __restrict__ res) {
+                                                              const TOut* __restrict__ res,
+                                                              const float* __restrict__ out_scale) {
   constexpr int RB = KC * 2;            // bytes of one row segment of a chunk
   constexpr int SLOT = 32 * RB;         // one ring slot: 32 rows of B
   constexpr int MF = KC / 16 / NW;      // MFMAs per wave per chunk
@@ -282,20 +283,21 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const TIn* __restr
     for (int w = 0; w < NW; ++w) z += *(const f32x4*)(record(w) + L * 64 + ((c ^ ((L >> 2) & 3)) << 4));
     return z;
   };
-  // Column scale, bias, activation, residual, conversion and one vector
-  // store of outputs (om, n0 + 4 oq .. + 3).
+  // Column scale, bias, activation, residual, output scale, conversion and
+  // one vector store of outputs (om, n0 + 4 oq .. + 3).
   auto finish = [&](int om, f32x4 z) __attribute__((always_inline)) {
     const int n = n0 + 4 * oq;
     f32x4 sc = f32x4{1.0f, 1.0f, 1.0f, 1.0f}, r = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     if (scale) sc = *(const f32x4*)(scale + n);
     if (res) r = load4<TOut>(res + (int64_t)om * N + n);
+    const float os = out_scale ? *out_scale : 1.0f;
     float v[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       float b = 0.0f;
       if constexpr (epi_has_bias<EPI>())
         b = to_f32(__builtin_bit_cast(TIn, (uint16_t)((e & 1) ? (bias_q[e >> 1] >> 16) : (bias_q[e >> 1] & 0xffffu))));
-      v[e] = epilogue_ex<EPI>(z[e], b, scale != nullptr, sc[e], res != nullptr, r[e]);
+      v[e] = epilogue_ex<EPI>(z[e], b, scale != nullptr, sc[e], res != nullptr, r[e], out_scale != nullptr, os);
     }
     store4<TOut>(C + (int64_t)om * N + n, v[0], v[1], v[2], v[3]);
   };
@@ -363,7 +365,7 @@ hipError_t launch_skinny(const LaunchArgs& a) {
   unsigned* arrivals = a.split > 1 ? (unsigned*)((char*)a.workspace + (size_t)nblocks * a.split * 4096) : nullptr;
   hipLaunchKernelGGL((gemm_skinny_kernel<TIn, TOut, NW, P, KC, EPI>), dim3(nblocks, a.split > 1 ? a.split : 1),
                      dim3(NW * 64), 0, a.stream, (const TIn*)a.A, (const TIn*)a.B, (const TIn*)a.bias, (TOut*)a.C,
-                     a.M, a.N, a.K, part, arrivals, a.scale, (const TOut*)a.residual);
+                     a.M, a.N, a.K, part, arrivals, a.scale, (const TOut*)a.residual, a.out_scale);
   return hipGetLastError();
 }
 
@@ -386,9 +388,11 @@ LaunchFn pick_types(const Problem& p) {
   if (p.in_dt == GEMM_EPI_F16) {
     if (p.out_dt == GEMM_EPI_F16) return pick_epi<f16, f16, NW, P, KC>(p.epi);
     if (p.out_dt == GEMM_EPI_F32) return pick_epi<f16, float, NW, P, KC>(p.epi);
+    if (p.out_dt == GEMM_EPI_FP8_E4M3) return pick_epi<f16, fp8e4m3, NW, P, KC>(p.epi);
   } else if (p.in_dt == GEMM_EPI_BF16) {
     if (p.out_dt == GEMM_EPI_BF16) return pick_epi<bf16, bf16, NW, P, KC>(p.epi);
     if (p.out_dt == GEMM_EPI_F32) return pick_epi<bf16, float, NW, P, KC>(p.epi);
+    if (p.out_dt == GEMM_EPI_FP8_E4M3) return pick_epi<bf16, fp8e4m3, NW, P, KC>(p.epi);
   }
   return nullptr;
 }

@@ -192,13 +192,16 @@ __device__ __forceinline__ void raster(int bid, int tiles_m, int tiles_n, int pa
 template <int WM, int WN, typename TIn, typename TOut, int EPI, bool EXTRAS>
 __device__ __forceinline__ void write_tile(const f32x16 (&acc)[WM / 32][WN / 32], const TIn* __restrict__ bias,
                                           TOut* __restrict__ C, int N, int m_w, int n_w, int lane, char* stage,
-                                          const float* __restrict__ scale, const TOut* __restrict__ res) {
+                                          const float* __restrict__ scale, const TOut* __restrict__ res,
+                                          const float* __restrict__ out_scale) {
   constexpr int TM = WM / 32, TN = WN / 32;
   constexpr int OSZ = (int)sizeof(TOut);
   constexpr int CPR = WN * OSZ / 16;           // 16-byte chunks per staged row
   constexpr int SWM = (CPR < 16 ? CPR : 16) - 1;  // swizzle mask
   constexpr int RPI = 64 / CPR;                // rows per store instruction
   const int m_l = lane & 31, h = lane >> 5;
+  const bool has_os = EXTRAS && out_scale != nullptr;
+  const float os = has_os ? *out_scale : 1.0f;
 
   // bias of this lane's 16 columns in each 32-column block, kept packed
   u32x2 bq[TN][4];
@@ -232,10 +235,14 @@ __device__ __forceinline__ void write_tile(const f32x16 (&acc)[WM / 32][WN / 32]
             b = to_f32(__builtin_bit_cast(TIn, (uint16_t)((e & 1) ? (w >> 16) : (w & 0xffffu))));
           }
           v[e] = epilogue_ex<EPI>(acc[i][j][4 * q + e], b, EXTRAS && scale != nullptr, sc[e], EXTRAS && res != nullptr,
-                                  r[e]);
+                                  r[e], has_os, os);
         }
         // columns j*32 + 8q + 4h .. +3 of row m_l
-        if constexpr (OSZ == 4) {
+        if constexpr (OSZ == 1) {
+          const int c = 2 * j + (q >> 1);
+          *(uint32_t*)(stage + m_l * WN + ((c ^ (m_l & SWM)) << 4) + 8 * (q & 1) + 4 * h) =
+              pack4_e4m3(v[0], v[1], v[2], v[3]);
+        } else if constexpr (OSZ == 4) {
           const int c = 8 * j + 2 * q + h;
           *(f32x4*)(stage + m_l * (WN * 4) + ((c ^ (m_l & SWM)) << 4)) = f32x4{v[0], v[1], v[2], v[3]};
         } else {
@@ -279,7 +286,8 @@ __global__ __launch_bounds__(NW * 64) void gemm_tile_kernel(const TIn* __restric
                                                              const TIn* __restrict__ bias, TOut* __restrict__ C,
                                                              int M, int N, int K, int tiles_m, int tiles_n,
                                                              int panel, const float* __restrict__ scale,
-                                                             const TOut* __restrict__ res) {
+                                                             const TOut* __restrict__ res,
+                                                             const float* __restrict__ out_scale) {
   // NW waves in a 2 x (NW / 2) grid, each owning a WM x WN sub-tile
   constexpr int NT = NW * 64;
   constexpr int WM = BM / 2, WN = BN / (NW / 2);
@@ -469,13 +477,14 @@ __global__ __launch_bounds__(NW * 64) void gemm_tile_kernel(const TIn* __restric
   static_assert(BM == BN && 32 * WN * sizeof(TOut) <= (size_t)A_BYTES / (NW / 4), "staging area");
   char* const stage_w = (wave % 4 == 0 ? sA0 : wave % 4 == 1 ? sA1 : wave % 4 == 2 ? sB0 : sB1) +
                         (wave / 4) * (A_BYTES / (NW / 4));
-  // (the optional column scale and residual get their own copy of the
-  // epilogue, so that the plain one carries no tests for them)
-  if (scale != nullptr || res != nullptr)
-    write_tile<WM, WN, TIn, TOut, EPI, true>(acc, bias, C, N, m0 + wm * WM, n0 + wn * WN, lane, stage_w, scale, res);
+  // (the optional column scale, residual and output scale get their own
+  // copy of the epilogue, so that the plain one carries no tests for them)
+  if (scale != nullptr || res != nullptr || out_scale != nullptr)
+    write_tile<WM, WN, TIn, TOut, EPI, true>(acc, bias, C, N, m0 + wm * WM, n0 + wn * WN, lane, stage_w, scale, res,
+                                             out_scale);
   else
     write_tile<WM, WN, TIn, TOut, EPI, false>(acc, bias, C, N, m0 + wm * WM, n0 + wn * WN, lane, stage_w, nullptr,
-                                              nullptr);
+                                              nullptr, nullptr);
 }
 
 // Host launch of one instantiation.
@@ -485,7 +494,7 @@ hipError_t launch(const LaunchArgs& a) {
   const int panel = tiles_m < 4 ? tiles_m : 4;
   hipLaunchKernelGGL((gemm_tile_kernel<BM, BN, NW, TIn, TOut, A_KMAJ, B_KMAJ, EPI>), dim3(tiles_m * tiles_n),
                      dim3(NW * 64), 0, a.stream, (const TIn*)a.A, (const TIn*)a.B, (const TIn*)a.bias, (TOut*)a.C,
-                     a.M, a.N, a.K, tiles_m, tiles_n, panel, a.scale, (const TOut*)a.residual);
+                     a.M, a.N, a.K, tiles_m, tiles_n, panel, a.scale, (const TOut*)a.residual, a.out_scale);
   return hipGetLastError();
 }
 

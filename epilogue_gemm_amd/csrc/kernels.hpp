@@ -34,6 +34,8 @@ LaunchFn tile_launcher_f16_f16(int cfg, int la, int lb, int epi);
 LaunchFn tile_launcher_f16_f32(int cfg, int la, int lb, int epi);
 LaunchFn tile_launcher_bf16_bf16(int cfg, int la, int lb, int epi);
 LaunchFn tile_launcher_bf16_f32(int cfg, int la, int lb, int epi);
+LaunchFn tile_launcher_f16_fp8(int cfg, int la, int lb, int epi);
+LaunchFn tile_launcher_bf16_fp8(int cfg, int la, int lb, int epi);
 
 // ---- skinny: weight-streaming kernel for M <= 32 --------------------------
 struct SkinnyConfig {

@@ -145,24 +145,30 @@ def integer_inputs(M: int, N: int, K: int, in_dtype: str, layout_a: str, layout_
 
 def extras_inputs(M: int, N: int, out_dtype: str, seed: int, integer: bool = False):
     """Optional epilogue operands: dict(scale=float32 array of N, residual=bit
-    patterns of an M x N row-major array in the output format: uint16 for
-    f16/bf16, uint32 for f32).
+    patterns of an M x N row-major array in the output format (uint16 for
+    f16/bf16, uint32 for f32; None for fp8, which takes no residual),
+    out_scale=a float).
 
-    Random (integer=False): scale ~ U(0.5, 1.5), residual ~ N(0, 1).
-    Integer (integer=True): scale from {-2, -1, -0.5, 0.5, 1, 2} and residual
-    integers in [-8, 8], so that with integer operands every fp32 step of the
-    epilogue is exact."""
+    Random (integer=False): scale ~ U(0.5, 1.5), residual ~ N(0, 1),
+    out_scale 2^u with u ~ U(-1, 3) rounded to an integer.
+    Integer (integer=True): scale from {-2, -1, -0.5, 0.5, 1, 2}, residual
+    integers in [-8, 8] and out_scale from {0.25, 0.5, 1, 2}, so that with
+    integer operands every fp32 step of the epilogue is exact."""
     g = torch.Generator(device="cpu")
     g.manual_seed(int(seed) + 7919)
     if integer:
         choices = torch.tensor([-2.0, -1.0, -0.5, 0.5, 1.0, 2.0])
         scale = choices[torch.randint(0, 6, (N,), generator=g)]
         resid = torch.randint(-8, 9, (M, N), generator=g).to(torch.float32)
+        out_scale = float([0.25, 0.5, 1.0, 2.0][int(torch.randint(0, 4, (1,), generator=g))])
     else:
         scale = torch.rand(N, generator=g, dtype=torch.float32) + 0.5
         resid = torch.randn(M, N, generator=g, dtype=torch.float32)
-    if out_dtype == "f32":
-        rbits = resid.contiguous().view(torch.int32).numpy().view(np.uint32).copy()
+        out_scale = float(2.0 ** int(torch.randint(-1, 4, (1,), generator=g)))
+    if out_dtype == "fp8":
+        rbits = None
+    elif out_dtype == "f32":
+        rbits = resid.contiguous().view(torch.int32).numpy().view(np.uint32).copy().reshape(-1)
     else:
-        rbits = to_bits(resid.to(_TORCH_DT[out_dtype]))
-    return {"scale": scale.numpy().astype(np.float32), "residual": rbits.reshape(-1)}
+        rbits = to_bits(resid.to(_TORCH_DT[out_dtype])).reshape(-1)
+    return {"scale": scale.numpy().astype(np.float32), "residual": rbits, "out_scale": out_scale}

@@ -38,11 +38,16 @@
 extern "C" {
 #endif
 
-/* Element formats.  F32 is an output format only. */
+/* Element formats.  F32 and FP8_E4M3 are output formats only.  FP8_E4M3 is
+ * the OCP 8-bit floating-point E4M3 format (bias 7, no infinities, largest
+ * finite 448): the quantised output the tutorial lists among the fusions
+ * (csdn ch.10 sec. 10.7, "GEMM + quantisation").  Conversion to it
+ * saturates at +-448 and rounds to nearest even. */
 typedef enum gemm_epi_dtype {
-  GEMM_EPI_F16 = 0,  /* IEEE binary16 */
-  GEMM_EPI_BF16 = 1, /* bfloat16 (top half of binary32) */
-  GEMM_EPI_F32 = 2   /* IEEE binary32 */
+  GEMM_EPI_F16 = 0,      /* IEEE binary16 */
+  GEMM_EPI_BF16 = 1,     /* bfloat16 (top half of binary32) */
+  GEMM_EPI_F32 = 2,      /* IEEE binary32 */
+  GEMM_EPI_FP8_E4M3 = 3  /* OCP FP8 E4M3, one byte */
 } gemm_epi_dtype;
 
 /* Storage order of an R x C operand: ROW_MAJOR puts (r, c) at r*C + c,
@@ -95,7 +100,7 @@ typedef struct gemm_epi_plan_s* gemm_epi_plan_t;
  *
  * A is M x K in layout_a, B is K x N in layout_b, C is M x N row-major,
  * all packed (leading dimension = the contiguous extent).
- * in_dtype in {F16, BF16}; out_dtype in {in_dtype, F32}.
+ * in_dtype in {F16, BF16}; out_dtype in {in_dtype, F32, FP8_E4M3}.
  * Host only: no device allocation, no launch, no HIP call; allocates the
  * small host plan object only.  *out is written only on GEMM_EPI_OK.
  * Errors: INVALID_ARG (out == NULL, M/N/K <= 0, unknown enum, out_dtype
@@ -149,7 +154,7 @@ gemm_epi_status gemm_epi_run_ws(gemm_epi_plan_t plan, const void* A, const void*
 
 /* Optional epilogue operands of gemm_epi_run_ex.  With them the output is
  *
- *     C[m][n] = act(col_scale[n] * (A.B)[m][n] + bias[n]) + residual[m][n]
+ *     C[m][n] = out_scale * (act(col_scale[n] * (A.B)[m][n] + bias[n]) + residual[m][n])
  *
  * computed in fp32 and rounded once.
  *   col_scale  N fp32 values (a per-output-column factor such as a weight
@@ -157,10 +162,14 @@ gemm_epi_status gemm_epi_run_ws(gemm_epi_plan_t plan, const void* A, const void*
  *   residual   M x N row-major elements of the output format, or NULL for
  *              0.  It must not overlap C: where M or N is not a multiple of
  *              a tile, neighbouring workgroups compute some outputs twice,
- *              and an in-place residual would then be added twice. */
+ *              and an in-place residual would then be added twice.  Not
+ *              allowed with FP8_E4M3 output.
+ *   out_scale  one fp32 value in device memory (the quantisation scale of
+ *              an FP8_E4M3 output, or any final factor), or NULL for 1. */
 typedef struct gemm_epi_extras {
   const float* col_scale;
   const void* residual;
+  const float* out_scale;
 } gemm_epi_extras;
 
 /* gemm_epi_run_ex -- gemm_epi_run_ws with the optional epilogue operands of
@@ -168,7 +177,8 @@ typedef struct gemm_epi_extras {
  * gemm_epi_run_ws (workspace may be NULL with workspace_bytes 0).  A
  * col_scale or residual that is not 16-byte aligned sends the call to the
  * generic kernel, like any other unaligned pointer.  Same errors as
- * gemm_epi_run; INVALID_ARG also when residual overlaps C. */
+ * gemm_epi_run; INVALID_ARG also when residual overlaps C or the output is
+ * FP8_E4M3. */
 gemm_epi_status gemm_epi_run_ex(gemm_epi_plan_t plan, const void* A, const void* B, const void* bias,
                                 const gemm_epi_extras* extras, void* C, void* workspace, size_t workspace_bytes,
                                 void* stream);

@@ -53,8 +53,10 @@ def test_plan_rejects_invalid_arguments(lib):
         assert gb.gemm_epi_plan_status(**{**ok, k: v}) == 1
     assert gb.gemm_epi_plan_status(**{**ok, "in_dtype": "f32", "out_dtype": "f32"}) == 1  # f32 input
     assert gb.gemm_epi_plan_status(**{**ok, "out_dtype": "bf16"}) == 1  # mixed 16-bit formats
+    assert gb.gemm_epi_plan_status(**{**ok, "out_dtype": "fp8"}) == 0  # quantised output
+    assert gb.gemm_epi_plan_status(**{**ok, "in_dtype": "fp8", "out_dtype": "fp8"}) == 1  # fp8 input
     raw = [0, 0, 0, 0, 0]
-    for pos, bad in [(0, 7), (1, 9), (2, 2), (3, -1), (4, 7), (4, -1)]:
+    for pos, bad in [(0, 7), (0, 3), (1, 9), (2, 2), (3, -1), (4, 7), (4, -1)]:
         args = list(raw)
         args[pos] = bad
         assert gb.gemm_epi_plan_status(64, 64, 64, *args, raw=True) == 1
@@ -109,6 +111,21 @@ def test_run_ex_rejects_invalid_arguments_without_touching_the_device(lib):
         assert gb.gemm_epi_run_ex(h, 0x1000, 0x1000, 0x1000, None, None, c, None, 0, None) == 1  # bias given
     finally:
         gb.gemm_epi_destroy(h)
+    h = gb.gemm_epi_plan(M, N, 64, "bf16", "fp8", "row", "col", "none")
+    try:
+        # no residual for a quantised output, wherever it lies
+        assert gb.gemm_epi_run_ex(h, 0x1000, 0x1000, None, None, 0x900000, 0x100000, None, 0, None) == 1
+    finally:
+        gb.gemm_epi_destroy(h)
+
+
+def test_fp8_output_needs_16_columns_in_tile_kernels(lib):
+    for N, want in ((528, "tile"), (520, "generic")):
+        h = gb.gemm_epi_plan(1024, N, 256, "bf16", "fp8", "row", "col", "none")
+        try:
+            assert gb.gemm_epi_plan_describe(h)[0] == want, N
+        finally:
+            gb.gemm_epi_destroy(h)
 
 
 @pytest.mark.parametrize("M,N,K,la,lb,want_kernel,want_name", [
