@@ -67,6 +67,16 @@ def load_library(path: str = LIB_PATH):
     lib.gemm_epi_run_ws.restype = i32
     lib.gemm_epi_run_ex.argtypes = [vp, vp, vp, vp, ctypes.POINTER(Extras), vp, vp, ctypes.c_size_t, vp]
     lib.gemm_epi_run_ex.restype = i32
+    lib.gemm_epi_tune.argtypes = [vp, vp, vp, vp, vp, i32, i32, vp, ctypes.POINTER(ctypes.c_float)]
+    lib.gemm_epi_tune.restype = i32
+    lib.gemm_epi_tuning_save.argtypes = [cp]
+    lib.gemm_epi_tuning_save.restype = i32
+    lib.gemm_epi_tuning_load.argtypes = [cp]
+    lib.gemm_epi_tuning_load.restype = i32
+    lib.gemm_epi_tuning_clear.argtypes = []
+    lib.gemm_epi_tuning_clear.restype = None
+    lib.gemm_epi_tuning_size.argtypes = []
+    lib.gemm_epi_tuning_size.restype = i32
     lib.gemm_epi_destroy.argtypes = [vp]
     lib.gemm_epi_destroy.restype = i32
     lib.gemm_epi_status_string.argtypes = [i32]
@@ -135,6 +145,33 @@ def gemm_epi_run_ex(plan, A_ptr, B_ptr, bias_ptr, scale_ptr, residual_ptr, C_ptr
     pointers are then ignored)."""
     ex = None if extras_null else ctypes.byref(Extras(scale_ptr, residual_ptr, out_scale_ptr))
     return load_library().gemm_epi_run_ex(plan, A_ptr, B_ptr, bias_ptr, ex, C_ptr, ws_ptr, int(ws_bytes), stream)
+
+
+TUNE_COLD = 1
+
+
+def gemm_epi_tune(plan, A_ptr, B_ptr, bias_ptr, C_ptr, iters, stream, flags=0):
+    """Returns (status, best microseconds per launch)."""
+    us = ctypes.c_float(0.0)
+    st = load_library().gemm_epi_tune(plan, A_ptr, B_ptr, bias_ptr, C_ptr, int(iters), int(flags), stream,
+                                      ctypes.byref(us))
+    return st, float(us.value)
+
+
+def gemm_epi_tuning_save(path: str) -> int:
+    return load_library().gemm_epi_tuning_save(None if path is None else str(path).encode())
+
+
+def gemm_epi_tuning_load(path: str) -> int:
+    return load_library().gemm_epi_tuning_load(None if path is None else str(path).encode())
+
+
+def gemm_epi_tuning_clear() -> None:
+    load_library().gemm_epi_tuning_clear()
+
+
+def gemm_epi_tuning_size() -> int:
+    return int(load_library().gemm_epi_tuning_size())
 
 
 def gemm_epi_destroy(plan) -> int:
@@ -248,6 +285,24 @@ class Plan:
             fn = "gemm_epi_run_ws"
         if st != OK:
             raise GemmEpiError(fn, st)
+
+    def tune(self, A, B, bias, C, iters=10, stream=None, cold=False) -> float:
+        """Measure every configuration that can run this problem on these
+        buffers and keep the fastest (also recorded in the tuning table).
+        ``cold``: evict the caches before every timed launch.  Returns the
+        winner's mean microseconds per launch; synchronises the stream."""
+        import torch
+
+        a = self._check(A, "A", self.in_dtype, self.M * self.K)
+        b = self._check(B, "B", self.in_dtype, self.K * self.N)
+        bi = self._check(bias, "bias", self.in_dtype, self.N)
+        c = self._check(C, "C", self.out_dtype, self.M * self.N)
+        s = (stream or torch.cuda.current_stream()).cuda_stream
+        st, us = gemm_epi_tune(self.handle, a, b, bi, c, iters, s, TUNE_COLD if cold else 0)
+        if st != OK:
+            raise GemmEpiError("gemm_epi_tune", st)
+        self.kernel, self.config, self.name = gemm_epi_plan_describe(self.handle)
+        return us
 
     def close(self):
         if self.handle is not None:

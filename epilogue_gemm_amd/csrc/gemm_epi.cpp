@@ -100,6 +100,15 @@ bool uses_bias(int epi) {
 bool resolve(gemm_epi_plan_s* pl, int kernel, int config) {
   const ge::Problem& p = pl->p;
   if (kernel == GEMM_EPI_KERNEL_AUTO) {
+    // a measured choice for this exact problem comes first
+    int tk, tc;
+    if (ge::tuning_lookup(p, &tk, &tc) && tk != GEMM_EPI_KERNEL_AUTO) {
+      gemm_epi_plan_s trial = *pl;
+      if (resolve(&trial, tk, tc)) {
+        *pl = trial;
+        return true;
+      }
+    }
     int c = ge::skinny_choose(p);
     if (c >= 0) return resolve(pl, GEMM_EPI_KERNEL_SKINNY, c);
     c = ge::tile_choose(p);
@@ -241,6 +250,97 @@ gemm_epi_status gemm_epi_run_ex(gemm_epi_plan_t plan, const void* A, const void*
                                 const gemm_epi_extras* extras, void* C, void* workspace, size_t workspace_bytes_given,
                                 void* stream) {
   return launch(plan, A, B, bias, extras, C, workspace, workspace_bytes_given, stream);
+}
+
+gemm_epi_status gemm_epi_tune(gemm_epi_plan_t plan, const void* A, const void* B, const void* bias, void* C,
+                              int iters, int flags, void* stream, float* best_us) {
+  if (!plan || !A || !B || !C || iters <= 0 || (flags & ~GEMM_EPI_TUNE_COLD)) return GEMM_EPI_ERR_INVALID_ARG;
+  if (uses_bias(plan->p.epi) != (bias != nullptr)) return GEMM_EPI_ERR_INVALID_ARG;
+  if (!aligned16(A) || !aligned16(B) || !aligned16(C) || (bias && !aligned16(bias))) return GEMM_EPI_ERR_INVALID_ARG;
+  // candidates: every configuration of the fast families that can run the
+  // problem; the generic kernel only when none can
+  struct Cand {
+    int kernel, config;
+  };
+  Cand cands[64];
+  int nc = 0;
+  for (int k : {GEMM_EPI_KERNEL_TILE, GEMM_EPI_KERNEL_SKINNY}) {
+    const int n = gemm_epi_num_configs((gemm_epi_kernel)k);
+    for (int c = 0; c < n && nc < 64; ++c) {
+      gemm_epi_plan_s trial = *plan;
+      if (resolve(&trial, k, c)) cands[nc++] = Cand{k, c};
+    }
+  }
+  if (nc == 0) cands[nc++] = Cand{GEMM_EPI_KERNEL_GENERIC, 0};
+  const hipStream_t s = (hipStream_t)stream;
+  const bool cold = (flags & GEMM_EPI_TUNE_COLD) != 0;
+  void* scratch = nullptr;
+  if (cold && hipMalloc(&scratch, ge::kFlushBytes) != hipSuccess) {
+    (void)hipGetLastError();
+    return GEMM_EPI_ERR_NO_MEMORY;
+  }
+  hipEvent_t ev[2] = {nullptr, nullptr};
+  hipError_t e = hipEventCreate(&ev[0]);
+  if (e == hipSuccess) e = hipEventCreate(&ev[1]);
+  int best = -1;
+  float best_t = 0.0f;
+  for (int i = 0; i < nc && e == hipSuccess; ++i) {
+    gemm_epi_plan_s trial = *plan;
+    resolve(&trial, cands[i].kernel, cands[i].config);
+    ge::LaunchArgs a{};
+    a.A = A;
+    a.B = B;
+    a.bias = bias;
+    a.C = C;
+    a.M = (int)trial.p.M;
+    a.N = (int)trial.p.N;
+    a.K = (int)trial.p.K;
+    a.epi = trial.p.epi;
+    a.la = trial.p.la;
+    a.lb = trial.p.lb;
+    a.stream = s;
+    a.split = 1;
+    for (int w = 0; w < 2 && e == hipSuccess; ++w) e = trial.fn(a);  // warm-up
+    float ms = 0.0f;
+    if (!cold) {
+      if (e == hipSuccess) e = hipEventRecord(ev[0], s);
+      for (int r = 0; r < iters && e == hipSuccess; ++r) e = trial.fn(a);
+      if (e == hipSuccess) e = hipEventRecord(ev[1], s);
+      if (e == hipSuccess) e = hipEventSynchronize(ev[1]);
+      if (e == hipSuccess) e = hipEventElapsedTime(&ms, ev[0], ev[1]);
+    } else {
+      for (int r = 0; r < iters && e == hipSuccess; ++r) {
+        e = ge::flush_caches(scratch, s);
+        if (e == hipSuccess) e = hipEventRecord(ev[0], s);
+        if (e == hipSuccess) e = trial.fn(a);
+        if (e == hipSuccess) e = hipEventRecord(ev[1], s);
+        if (e == hipSuccess) e = hipEventSynchronize(ev[1]);
+        float one = 0.0f;
+        if (e == hipSuccess) e = hipEventElapsedTime(&one, ev[0], ev[1]);
+        ms += one;
+      }
+    }
+    if (e == hipSuccess && (best < 0 || ms < best_t)) {
+      best = i;
+      best_t = ms;
+    }
+  }
+  for (hipEvent_t x : ev)
+    if (x) (void)hipEventDestroy(x);
+  if (scratch) {
+    const hipError_t f = hipStreamSynchronize(s);
+    if (e == hipSuccess) e = f;
+    (void)hipFree(scratch);
+  }
+  if (e != hipSuccess) {
+    g_last_hip_error = (int)e;
+    return GEMM_EPI_ERR_HIP;
+  }
+  const float us = best_t * 1000.0f / (float)iters;
+  resolve(plan, cands[best].kernel, cands[best].config);
+  ge::tuning_record(plan->p, cands[best].kernel, cands[best].config, us);
+  if (best_us) *best_us = us;
+  return GEMM_EPI_OK;
 }
 
 gemm_epi_status gemm_epi_destroy(gemm_epi_plan_t plan) {

@@ -103,6 +103,8 @@ typedef struct gemm_epi_plan_s* gemm_epi_plan_t;
  * in_dtype in {F16, BF16}; out_dtype in {in_dtype, F32, FP8_E4M3}.
  * Host only: no device allocation, no launch, no HIP call; allocates the
  * small host plan object only.  *out is written only on GEMM_EPI_OK.
+ * The kernel is the tuning table's entry for this problem when there is one
+ * that can run it (gemm_epi_tune), else the static rule.
  * Errors: INVALID_ARG (out == NULL, M/N/K <= 0, unknown enum, out_dtype
  * not allowed), UNSUPPORTED (any of M*K, K*N, M*N >= 2^31 elements),
  * NO_MEMORY. */
@@ -183,6 +185,55 @@ gemm_epi_status gemm_epi_run_ex(gemm_epi_plan_t plan, const void* A, const void*
                                 const gemm_epi_extras* extras, void* C, void* workspace, size_t workspace_bytes,
                                 void* stream);
 
+/* Flags of gemm_epi_tune. */
+#define GEMM_EPI_TUNE_COLD 1 /* evict the caches before every timed launch */
+
+/* gemm_epi_tune -- measure every kernel configuration that can run the
+ * plan's problem and make the fastest the plan's choice.
+ *
+ * The search runs on the GPU itself, on the caller's buffers and stream
+ * (C is overwritten with the problem's result; the split-K workspace and
+ * the extras are not used): each candidate is launched twice to warm up,
+ * then `iters` times, and the mean time per launch decides.  Without
+ * flags the timed launches run back to back between two events, so
+ * operands that fit in the 256 MB last-level cache stay there; with
+ * GEMM_EPI_TUNE_COLD every timed launch follows a kernel that writes a
+ * 512 MiB scratch buffer (allocated and freed by this call) and is timed
+ * by its own pair of events -- the condition of a weight streamed once per
+ * step, which decides among HBM-bound configurations.  Candidates are the tile and skinny configurations the problem
+ * meets (the generic kernel only when none does).  The choice is also
+ * recorded in the process-wide tuning table, which every later
+ * gemm_epi_plan of the same problem (shape, formats, layouts, epilogue)
+ * consults before its static rule; the table can be saved to and loaded
+ * from a text file.  (Search on the target, save the configuration, use it
+ * online: csdn "从零开始学习 TileLang", ch.18 "自动调优", sec. 18.1, 18.3.)
+ * Synchronises `stream`.  best_us (may be NULL) receives the winner's mean
+ * microseconds per launch.
+ * Errors: INVALID_ARG (NULL plan or buffer, iters <= 0, unknown flags,
+ * bias given or missing for the epilogue, a buffer not 16-byte aligned),
+ * NO_MEMORY (the cold-cache scratch buffer), HIP. */
+gemm_epi_status gemm_epi_tune(gemm_epi_plan_t plan, const void* A, const void* B, const void* bias, void* C,
+                              int iters, int flags, void* stream, float* best_us);
+
+/* gemm_epi_tuning_save -- write the tuning table to a text file, one entry
+ * per line: M N K in_dtype out_dtype layout_a layout_b epilogue kernel
+ * config microseconds (enum values of this header; '#' starts a comment).
+ * Host only.  INVALID_ARG if the path is NULL or cannot be written. */
+gemm_epi_status gemm_epi_tuning_save(const char* path);
+
+/* gemm_epi_tuning_load -- merge the entries of such a file into the table
+ * (an entry replaces one of the same problem).  Host only.  INVALID_ARG if
+ * the path is NULL or unreadable, or any line is malformed or out of range;
+ * the table is then unchanged.  An entry whose configuration cannot run its
+ * problem is ignored when a plan consults it. */
+gemm_epi_status gemm_epi_tuning_load(const char* path);
+
+/* Remove every entry of the tuning table. */
+void gemm_epi_tuning_clear(void);
+
+/* Number of entries in the tuning table. */
+int gemm_epi_tuning_size(void);
+
 /* gemm_epi_destroy -- free the host plan object.  NULL is a no-op (OK).
  * No device synchronisation: runs already enqueued are unaffected. */
 gemm_epi_status gemm_epi_destroy(gemm_epi_plan_t plan);
@@ -195,6 +246,7 @@ int gemm_epi_last_hip_error(void);
 
 /* gemm_epi_plan_select -- force a kernel family and configuration index
  * (for tests and tuning).  kernel = AUTO restores the plan's own choice
+ * (the tuning table's entry, else the static rule)
  * and ignores config.  Otherwise config indexes that family's table
  * (0 .. gemm_epi_num_configs-1), and -1 lets the family choose.
  * Errors: INVALID_ARG (NULL plan, bad enum or index), UNSUPPORTED (the

@@ -224,3 +224,92 @@ def test_workspace_size(lib):
             gb.gemm_epi_destroy(h)
     assert lib.gemm_epi_workspace_size(None) == 0
     assert lib.gemm_epi_run_ws(None, None, None, None, None, None, 0, None) == 1  # INVALID_ARG
+
+
+# --------------------------------------------------------------------------
+# tuning table: file format, merge, and the plan's use of it (host only)
+# --------------------------------------------------------------------------
+
+def _describe(*args):
+    h = gb.gemm_epi_plan(*args)
+    try:
+        return gb.gemm_epi_plan_describe(h)
+    finally:
+        gb.gemm_epi_destroy(h)
+
+
+def test_tuning_table_drives_the_plan(lib, tmp_path):
+    gb.gemm_epi_tuning_clear()
+    args = (1024, 1024, 1024, "f16", "f16", "row", "row", "relu")
+    assert _describe(*args)[:2] == ("tile", 2)  # static rule: 64 x 64 fills the CUs
+    f = tmp_path / "t.txt"
+    f.write_text("# a comment\n\n1024 1024 1024 0 0 0 0 1 2 1 12.5  # tile config 1\n")
+    assert gb.gemm_epi_tuning_load(f) == 0 and gb.gemm_epi_tuning_size() == 1
+    assert _describe(*args)[:2] == ("tile", 1)
+    assert _describe(1024, 1024, 1024, "f16", "f16", "row", "row", "none")[:2] == ("tile", 2)  # other epilogue
+    # plan_select(AUTO) restores the tuned choice
+    h = gb.gemm_epi_plan(*args)
+    try:
+        assert gb.gemm_epi_plan_select(h, "generic", 0) == 0
+        assert gb.gemm_epi_plan_select(h, "auto", -1) == 0
+        assert gb.gemm_epi_plan_describe(h)[:2] == ("tile", 1)
+    finally:
+        gb.gemm_epi_destroy(h)
+    # save -> clear -> load round trip
+    g = tmp_path / "saved.txt"
+    assert gb.gemm_epi_tuning_save(g) == 0
+    gb.gemm_epi_tuning_clear()
+    assert gb.gemm_epi_tuning_size() == 0 and _describe(*args)[:2] == ("tile", 2)
+    assert gb.gemm_epi_tuning_load(g) == 0 and _describe(*args)[:2] == ("tile", 1)
+    lines = [l for l in g.read_text().splitlines() if l and not l.startswith("#")]
+    assert lines == ["1024 1024 1024 0 0 0 0 1 2 1 12.500"]
+    gb.gemm_epi_tuning_clear()
+
+
+def test_tuning_entry_that_cannot_run_is_ignored(lib, tmp_path):
+    gb.gemm_epi_tuning_clear()
+    f = tmp_path / "t.txt"
+    # skinny for M = 1024, and tile config 0 (256 x 256) for a 64 x 64 problem
+    f.write_text("1024 1024 1024 0 0 0 1 0 3 0 1.0\n64 64 256 1 1 0 1 0 2 0 1.0\n")
+    assert gb.gemm_epi_tuning_load(f) == 0 and gb.gemm_epi_tuning_size() == 2
+    assert _describe(1024, 1024, 1024, "f16", "f16", "row", "col", "none")[0] == "tile"
+    assert _describe(64, 64, 256, "bf16", "bf16", "row", "col", "none")[:2] == ("tile", 2)
+    gb.gemm_epi_tuning_clear()
+
+
+@pytest.mark.parametrize("text", [
+    "1024 1024 1024 0 0 0 0 1 2 1\n",             # missing field
+    "1024 1024 1024 0 0 0 0 1 2 1 3.0 7\n",       # extra field
+    "1024 1024 0 0 0 0 0 1 2 1 3.0\n",            # K = 0
+    "1024 1024 1024 0 5 0 0 1 2 1 3.0\n",         # bad format
+    "1024 1024 1024 0 0 0 0 9 2 1 3.0\n",         # bad epilogue
+    "1024 1024 1024 0 0 0 0 1 0 1 3.0\n",         # kernel AUTO is not a choice
+    "1024 1024 1024 0 0 0 0 1 2 -1 3.0\n",        # negative config
+    "garbage\n",
+])
+def test_tuning_load_rejects_malformed_files(lib, tmp_path, text):
+    gb.gemm_epi_tuning_clear()
+    ok = tmp_path / "ok.txt"
+    ok.write_text("512 512 512 1 1 0 1 3 2 3 9.0\n")
+    assert gb.gemm_epi_tuning_load(ok) == 0
+    f = tmp_path / "bad.txt"
+    f.write_text("256 256 256 0 0 0 0 0 2 2 1.0\n" + text)
+    assert gb.gemm_epi_tuning_load(f) == 1
+    assert gb.gemm_epi_tuning_size() == 1  # unchanged: nothing from the bad file
+    assert gb.gemm_epi_tuning_load(tmp_path / "missing.txt") == 1
+    assert gb.gemm_epi_tuning_load(None) == 1 and gb.gemm_epi_tuning_save(None) == 1
+    gb.gemm_epi_tuning_clear()
+
+
+def test_tune_rejects_invalid_arguments_without_touching_the_device(lib):
+    h = gb.gemm_epi_plan(256, 256, 128, "bf16", "bf16", "row", "col", "bias")
+    try:
+        p = 0x10000
+        assert gb.gemm_epi_tune(None, p, p, p, p, 5, None)[0] == 1
+        assert gb.gemm_epi_tune(h, p, p, None, p, 5, None)[0] == 1  # bias missing
+        assert gb.gemm_epi_tune(h, p, p, p, p, 0, None)[0] == 1  # iters
+        assert gb.gemm_epi_tune(h, p + 2, p, p, p, 5, None)[0] == 1  # unaligned
+        assert gb.gemm_epi_tune(h, p, p, p, p, 5, None, flags=2)[0] == 1  # unknown flag
+    finally:
+        gb.gemm_epi_destroy(h)
+    assert gb.gemm_epi_tuning_size() == 0
