@@ -59,6 +59,8 @@ def load_library(path: str = LIB_PATH):
     i64, i32, vp, cp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_char_p
     lib.gemm_epi_plan.argtypes = [ctypes.POINTER(vp), i64, i64, i64, i32, i32, i32, i32, i32]
     lib.gemm_epi_plan.restype = i32
+    lib.gemm_epi_plan_set_ld.argtypes = [vp, i64, i64, i64]
+    lib.gemm_epi_plan_set_ld.restype = i32
     lib.gemm_epi_run.argtypes = [vp, vp, vp, vp, vp, vp]
     lib.gemm_epi_run.restype = i32
     lib.gemm_epi_workspace_size.argtypes = [vp]
@@ -125,6 +127,10 @@ def gemm_epi_plan_status(M, N, K, in_dtype, out_dtype, layout_a, layout_b, epilo
     if st == OK:
         lib.gemm_epi_destroy(h)
     return st
+
+
+def gemm_epi_plan_set_ld(plan, lda=0, ldb=0, ldc=0) -> int:
+    return load_library().gemm_epi_plan_set_ld(plan, int(lda), int(ldb), int(ldc))
 
 
 def gemm_epi_run(plan, A_ptr, B_ptr, bias_ptr, C_ptr, stream) -> int:
@@ -217,11 +223,23 @@ class Plan:
     CUDA stream (or the given one) and returns without synchronising."""
 
     def __init__(self, M, N, K, in_dtype, out_dtype, layout_a="row", layout_b="row", epilogue="none",
-                 kernel: str = "auto", config: int = -1):
+                 kernel: str = "auto", config: int = -1, lda: int = 0, ldb: int = 0, ldc: int = 0):
         self.M, self.N, self.K = int(M), int(N), int(K)
         self.in_dtype, self.out_dtype = in_dtype, out_dtype
         self.layout_a, self.layout_b, self.epilogue = layout_a, layout_b, epilogue
         self.handle = gemm_epi_plan(M, N, K, in_dtype, out_dtype, layout_a, layout_b, epilogue)
+        # stored extents (elements) of A, B and C: (rows - 1) * ld + row length
+        a_rows, a_cols = (self.M, self.K) if layout_a == "row" else (self.K, self.M)
+        b_rows, b_cols = (self.K, self.N) if layout_b == "row" else (self.N, self.K)
+        self.lda, self.ldb, self.ldc = int(lda) or a_cols, int(ldb) or b_cols, int(ldc) or self.N
+        self._extent = {"A": (a_rows - 1) * self.lda + a_cols, "B": (b_rows - 1) * self.ldb + b_cols,
+                        "C": (self.M - 1) * self.ldc + self.N}
+        if lda or ldb or ldc:
+            st = gemm_epi_plan_set_ld(self.handle, lda, ldb, ldc)
+            if st != OK:
+                gemm_epi_destroy(self.handle)
+                self.handle = None
+                raise GemmEpiError("gemm_epi_plan_set_ld", st)
         if kernel != "auto":
             st = gemm_epi_plan_select(self.handle, kernel, config)
             if st != OK:
@@ -237,7 +255,7 @@ class Plan:
             raise ValueError(f"{name}: expected a contiguous CUDA tensor")
         if _dtype_name(t) != dtype:
             raise ValueError(f"{name}: dtype {t.dtype} does not match {dtype}")
-        if t.numel() != numel:
+        if t.numel() < numel or (name not in ("A", "B", "C", "residual") and t.numel() != numel):
             raise ValueError(f"{name}: {t.numel()} elements, expected {numel}")
         return t.data_ptr()
 
@@ -256,14 +274,14 @@ class Plan:
         scale of an fp8 output)."""
         import torch
 
-        a = self._check(A, "A", self.in_dtype, self.M * self.K)
-        b = self._check(B, "B", self.in_dtype, self.K * self.N)
+        a = self._check(A, "A", self.in_dtype, self._extent["A"])
+        b = self._check(B, "B", self.in_dtype, self._extent["B"])
         bi = self._check(bias, "bias", self.in_dtype, self.N)
-        c = self._check(C, "C", self.out_dtype, self.M * self.N)
+        c = self._check(C, "C", self.out_dtype, self._extent["C"])
         s = (stream or torch.cuda.current_stream()).cuda_stream
         if scale is not None or residual is not None or out_scale is not None:
             sc = self._check(scale, "scale", "f32", self.N)
-            r = self._check(residual, "residual", self.out_dtype, self.M * self.N)
+            r = self._check(residual, "residual", self.out_dtype, self._extent["C"])
             q = self._check(out_scale, "out_scale", "f32", 1)
             ws, nbytes = None, 0
             if workspace is not None:
@@ -293,10 +311,10 @@ class Plan:
         winner's mean microseconds per launch; synchronises the stream."""
         import torch
 
-        a = self._check(A, "A", self.in_dtype, self.M * self.K)
-        b = self._check(B, "B", self.in_dtype, self.K * self.N)
+        a = self._check(A, "A", self.in_dtype, self._extent["A"])
+        b = self._check(B, "B", self.in_dtype, self._extent["B"])
         bi = self._check(bias, "bias", self.in_dtype, self.N)
-        c = self._check(C, "C", self.out_dtype, self.M * self.N)
+        c = self._check(C, "C", self.out_dtype, self._extent["C"])
         s = (stream or torch.cuda.current_stream()).cuda_stream
         st, us = gemm_epi_tune(self.handle, a, b, bi, c, iters, s, TUNE_COLD if cold else 0)
         if st != OK:

@@ -49,6 +49,7 @@ struct LaunchArgs {
   const void* bias;
   void* C;
   int M, N, K;
+  int lda, ldb, ldc;  // leading dimensions (elements between rows of the stored layout)
   int epi;     // gemm_epi_epilogue
   int la, lb;  // gemm_epi_layout of A and B
   hipStream_t stream;

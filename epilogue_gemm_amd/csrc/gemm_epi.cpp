@@ -29,11 +29,12 @@ bool tile_supports(int cfg, const Problem& p) {
   // M and N need not be tile multiples (the last tile row or column is
   // shifted back to end at M or N), but must hold one tile; rows of every
   // operand and of C must stay 16-byte aligned (N % 8, N % 16 for 1-byte
-  // E4M3 output; M % 8 when A is column-major), and K must be whole k-steps.
+  // E4M3 output; M % 8 when A is column-major; leading dimensions likewise),
+  // and K must be whole k-steps.
   const TileConfig& c = kTile[cfg];
   const int n_align = p.out_dt == GEMM_EPI_FP8_E4M3 ? 16 : 8;
   return p.M >= c.bm && p.N >= c.bn && p.N % n_align == 0 && (p.la == GEMM_EPI_ROW_MAJOR || p.M % 8 == 0) &&
-         p.K % 64 == 0 && p.K >= 128;
+         p.K % 64 == 0 && p.K >= 128 && p.lda % 8 == 0 && p.ldb % 8 == 0 && p.ldc % n_align == 0;
 }
 
 int tile_choose(const Problem& p) {
@@ -173,7 +174,8 @@ gemm_epi_status launch(gemm_epi_plan_t plan, const void* A, const void* B, const
     // no residual for a quantised output; and it must not overlap C (edge
     // tiles write some outputs twice)
     if (plan->p.out_dt == GEMM_EPI_FP8_E4M3) return GEMM_EPI_ERR_INVALID_ARG;
-    const uintptr_t bytes = (uintptr_t)(plan->p.M * plan->p.N) * (plan->p.out_dt == GEMM_EPI_F32 ? 4u : 2u);
+    const uintptr_t bytes =
+        (uintptr_t)((plan->p.M - 1) * plan->p.ldc + plan->p.N) * (plan->p.out_dt == GEMM_EPI_F32 ? 4u : 2u);
     const uintptr_t r0 = (uintptr_t)residual, c0 = (uintptr_t)C;
     if (r0 < c0 + bytes && c0 < r0 + bytes) return GEMM_EPI_ERR_INVALID_ARG;
   }
@@ -185,6 +187,9 @@ gemm_epi_status launch(gemm_epi_plan_t plan, const void* A, const void* B, const
   a.M = (int)plan->p.M;
   a.N = (int)plan->p.N;
   a.K = (int)plan->p.K;
+  a.lda = (int)plan->p.lda;
+  a.ldb = (int)plan->p.ldb;
+  a.ldc = (int)plan->p.ldc;
   a.epi = plan->p.epi;
   a.la = plan->p.la;
   a.lb = plan->p.lb;
@@ -224,7 +229,17 @@ gemm_epi_status gemm_epi_plan(gemm_epi_plan_t* out, int64_t M, int64_t N, int64_
     return GEMM_EPI_ERR_UNSUPPORTED;
   gemm_epi_plan_s* pl = new (std::nothrow) gemm_epi_plan_s();
   if (!pl) return GEMM_EPI_ERR_NO_MEMORY;
-  pl->p = ge::Problem{M, N, K, (int)in_dtype, (int)out_dtype, (int)layout_a, (int)layout_b, (int)epilogue};
+  pl->p = ge::Problem{M,
+                      N,
+                      K,
+                      (int)in_dtype,
+                      (int)out_dtype,
+                      (int)layout_a,
+                      (int)layout_b,
+                      (int)epilogue,
+                      layout_a == GEMM_EPI_ROW_MAJOR ? K : M,
+                      layout_b == GEMM_EPI_ROW_MAJOR ? N : K,
+                      N};
   pl->generic = ge::generic_launcher(pl->p);
   if (!pl->generic || !resolve(pl, GEMM_EPI_KERNEL_AUTO, -1)) {
     delete pl;
@@ -295,6 +310,9 @@ gemm_epi_status gemm_epi_tune(gemm_epi_plan_t plan, const void* A, const void* B
     a.M = (int)trial.p.M;
     a.N = (int)trial.p.N;
     a.K = (int)trial.p.K;
+    a.lda = (int)trial.p.lda;
+    a.ldb = (int)trial.p.ldb;
+    a.ldc = (int)trial.p.ldc;
     a.epi = trial.p.epi;
     a.la = trial.p.la;
     a.lb = trial.p.lb;
@@ -340,6 +358,29 @@ gemm_epi_status gemm_epi_tune(gemm_epi_plan_t plan, const void* A, const void* B
   resolve(plan, cands[best].kernel, cands[best].config);
   ge::tuning_record(plan->p, cands[best].kernel, cands[best].config, us);
   if (best_us) *best_us = us;
+  return GEMM_EPI_OK;
+}
+
+gemm_epi_status gemm_epi_plan_set_ld(gemm_epi_plan_t plan, int64_t lda, int64_t ldb, int64_t ldc) {
+  if (!plan) return GEMM_EPI_ERR_INVALID_ARG;
+  const ge::Problem& p = plan->p;
+  // extent of a stored row (the contiguous one) and the number of rows
+  const int64_t a_cols = p.la == GEMM_EPI_ROW_MAJOR ? p.K : p.M, a_rows = p.la == GEMM_EPI_ROW_MAJOR ? p.M : p.K;
+  const int64_t b_cols = p.lb == GEMM_EPI_ROW_MAJOR ? p.N : p.K, b_rows = p.lb == GEMM_EPI_ROW_MAJOR ? p.K : p.N;
+  if (lda == 0) lda = a_cols;
+  if (ldb == 0) ldb = b_cols;
+  if (ldc == 0) ldc = p.N;
+  if (lda < a_cols || ldb < b_cols || ldc < p.N) return GEMM_EPI_ERR_INVALID_ARG;
+  const int64_t lim = (int64_t)1 << 31;
+  if (lda >= lim || ldb >= lim || ldc >= lim || (a_rows - 1) * lda + a_cols >= lim ||
+      (b_rows - 1) * ldb + b_cols >= lim || (p.M - 1) * ldc + p.N >= lim)
+    return GEMM_EPI_ERR_UNSUPPORTED;
+  gemm_epi_plan_s trial = *plan;
+  trial.p.lda = lda;
+  trial.p.ldb = ldb;
+  trial.p.ldc = ldc;
+  if (!resolve(&trial, GEMM_EPI_KERNEL_AUTO, -1)) return GEMM_EPI_ERR_UNSUPPORTED;
+  *plan = trial;
   return GEMM_EPI_OK;
 }
 

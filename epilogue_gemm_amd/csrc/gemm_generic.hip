@@ -17,6 +17,7 @@ template <typename TIn, typename TOut, int EPI>
 __global__ __launch_bounds__(256) void gemm_generic_kernel(const TIn* __restrict__ A, const TIn* __restrict__ B,
                                                            const TIn* __restrict__ bias, TOut* __restrict__ C,
                                                            int64_t M, int64_t N, int64_t K, int la, int lb,
+                                                           int64_t lda, int64_t ldb, int64_t ldc,
                                                            const float* __restrict__ scale,
                                                            const TOut* __restrict__ res,
                                                            const float* __restrict__ out_scale) {
@@ -25,18 +26,18 @@ __global__ __launch_bounds__(256) void gemm_generic_kernel(const TIn* __restrict
   const int64_t i_step = (int64_t)gridDim.y * kGenThreadsY;
   for (int64_t i = (int64_t)blockIdx.y * kGenThreadsY + threadIdx.x / kGenThreadsX; i < M; i += i_step) {
     // element strides of a(i, k) and b(k, j) along k
-    const TIn* pa = la == GEMM_EPI_ROW_MAJOR ? A + i * K : A + i;
-    const int64_t sa = la == GEMM_EPI_ROW_MAJOR ? 1 : M;
-    const TIn* pb = lb == GEMM_EPI_ROW_MAJOR ? B + j : B + j * K;
-    const int64_t sb = lb == GEMM_EPI_ROW_MAJOR ? N : 1;
+    const TIn* pa = la == GEMM_EPI_ROW_MAJOR ? A + i * lda : A + i;
+    const int64_t sa = la == GEMM_EPI_ROW_MAJOR ? 1 : lda;
+    const TIn* pb = lb == GEMM_EPI_ROW_MAJOR ? B + j : B + j * ldb;
+    const int64_t sb = lb == GEMM_EPI_ROW_MAJOR ? ldb : 1;
     float acc = 0.0f;
     for (int64_t k = 0; k < K; ++k) acc = __builtin_fmaf(to_f32(pa[k * sa]), to_f32(pb[k * sb]), acc);
     float b = 0.0f;
     if constexpr (epi_has_bias<EPI>()) b = to_f32(bias[j]);
     const float s = scale ? scale[j] : 1.0f;
-    const float r = res ? out_to_f32(res[i * N + j]) : 0.0f;
+    const float r = res ? out_to_f32(res[i * ldc + j]) : 0.0f;
     const float os = out_scale ? *out_scale : 1.0f;
-    C[i * N + j] = from_f32<TOut>(epilogue_ex<EPI>(acc, b, scale != nullptr, s, res != nullptr, r, out_scale != nullptr, os));
+    C[i * ldc + j] = from_f32<TOut>(epilogue_ex<EPI>(acc, b, scale != nullptr, s, res != nullptr, r, out_scale != nullptr, os));
   }
 }
 
@@ -47,7 +48,8 @@ hipError_t launch_generic(const LaunchArgs& a) {
   if (gy > 65535) gy = 65535;
   hipLaunchKernelGGL((gemm_generic_kernel<TIn, TOut, EPI>), dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, a.stream,
                      (const TIn*)a.A, (const TIn*)a.B, (const TIn*)a.bias, (TOut*)a.C, (int64_t)a.M, (int64_t)a.N,
-                     (int64_t)a.K, a.la, a.lb, a.scale, (const TOut*)a.residual, a.out_scale);
+                     (int64_t)a.K, a.la, a.lb, (int64_t)a.lda, (int64_t)a.ldb, (int64_t)a.ldc, a.scale,
+                     (const TOut*)a.residual, a.out_scale);
   return hipGetLastError();
 }
 

@@ -93,7 +93,8 @@ __device__ __forceinline__ void arrive() {
 template <typename TIn, typename TOut, int NW, int P, int KC, int EPI>
 __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const TIn* __restrict__ A, const TIn* __restrict__ B,
                                                               const TIn* __restrict__ bias, TOut* __restrict__ C,
-                                                              int M, int N, int K, float* __restrict__ part,
+                                                              int M, int N, int K, int lda, int ldb, int ldc,
+                                                              float* __restrict__ part,
                                                               unsigned* __restrict__ arrivals,
                                                               const float* __restrict__ scale,
                                                               const TOut* __restrict__ res,
@@ -136,8 +137,8 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const TIn* __restr
   // byte 1024 t + 16 L, i.e. row r = (1024 t + 16 L) / RB at chunk
   // position p; chunk g of row r is stored at position g ^ (r % 16), so the
   // lane fetches global chunk p ^ (r % 16) of its row segment.
-  const uint32_t row_bytes = (uint32_t)K * 2u;
-  const __amdgpu_buffer_rsrc_t rb = make_rsrc(B + (int64_t)n0 * K, 32u * row_bytes);
+  const uint32_t row_bytes = (uint32_t)ldb * 2u, a_row_bytes = (uint32_t)lda * 2u;
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(B + (int64_t)n0 * ldb, 32u * row_bytes);
   // A's chunk uses the same mapping, but with the whole row offset in the
   // per-lane part: the buffer's range check covers only that part, and it
   // is what turns rows past M into zeros.
@@ -150,13 +151,13 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const TIn* __restr
     const int r0 = (1024 * t) / RB;  // first row of the instruction (wave-uniform)
     vb[d] = (uint32_t)(r - r0) * row_bytes + (uint32_t)((p ^ (r & 15)) << 4);
     sb[d] = (uint32_t)r0 * row_bytes;
-    vas[d] = (uint32_t)r * row_bytes + (uint32_t)((p ^ (r & 15)) << 4);
+    vas[d] = (uint32_t)r * a_row_bytes + (uint32_t)((p ^ (r & 15)) << 4);
   }
 
   // A: rows past M read as zero (outside the buffer resource).  Wave w's
   // k-values of a chunk are [16 MF w, 16 MF (w + 1)).
   const int r = lane & 31, h = lane >> 5;
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(A, (uint32_t)M * row_bytes);
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(A, (uint32_t)M * a_row_bytes);
 
   // B fragment of MFMA q: row r, global chunk g = 2 (w MF + q) + h.
   int rd[MF];
@@ -289,7 +290,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const TIn* __restr
     const int n = n0 + 4 * oq;
     f32x4 sc = f32x4{1.0f, 1.0f, 1.0f, 1.0f}, r = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     if (scale) sc = *(const f32x4*)(scale + n);
-    if (res) r = load4<TOut>(res + (int64_t)om * N + n);
+    if (res) r = load4<TOut>(res + (int64_t)om * ldc + n);
     const float os = out_scale ? *out_scale : 1.0f;
     float v[4];
 #pragma unroll
@@ -299,7 +300,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const TIn* __restr
         b = to_f32(__builtin_bit_cast(TIn, (uint16_t)((e & 1) ? (bias_q[e >> 1] >> 16) : (bias_q[e >> 1] & 0xffffu))));
       v[e] = epilogue_ex<EPI>(z[e], b, scale != nullptr, sc[e], res != nullptr, r[e], out_scale != nullptr, os);
     }
-    store4<TOut>(C + (int64_t)om * N + n, v[0], v[1], v[2], v[3]);
+    store4<TOut>(C + (int64_t)om * ldc + n, v[0], v[1], v[2], v[3]);
   };
   if (part != nullptr) {
     // Split K: store this workgroup's fp32 partial block (row-major 32 x 32
@@ -365,7 +366,8 @@ hipError_t launch_skinny(const LaunchArgs& a) {
   unsigned* arrivals = a.split > 1 ? (unsigned*)((char*)a.workspace + (size_t)nblocks * a.split * 4096) : nullptr;
   hipLaunchKernelGGL((gemm_skinny_kernel<TIn, TOut, NW, P, KC, EPI>), dim3(nblocks, a.split > 1 ? a.split : 1),
                      dim3(NW * 64), 0, a.stream, (const TIn*)a.A, (const TIn*)a.B, (const TIn*)a.bias, (TOut*)a.C,
-                     a.M, a.N, a.K, part, arrivals, a.scale, (const TOut*)a.residual, a.out_scale);
+                     a.M, a.N, a.K, a.lda, a.ldb, a.ldc, part, arrivals, a.scale, (const TOut*)a.residual,
+                     a.out_scale);
   return hipGetLastError();
 }
 
@@ -416,11 +418,13 @@ const SkinnyConfig& skinny_config(int cfg) { return kSkinny[cfg]; }
 
 bool skinny_supports(int cfg, const Problem& p) {
   if (cfg < 0 || cfg >= skinny_num_configs()) return false;
-  // K in whole chunks, at least one turn of the ring; 32 rows of B and all
-  // of A must be addressable by one buffer resource
+  // K in whole chunks, at least one turn of the ring; rows 16-byte aligned
+  // (leading dimensions multiples of 8); 32 rows of B and all of A must be
+  // addressable by one buffer resource
   const SkinnyConfig& c = kSkinny[cfg];
   return p.M >= 1 && p.M <= 32 && p.la == GEMM_EPI_ROW_MAJOR && p.lb == GEMM_EPI_COL_MAJOR && p.N >= 32 && p.N % 8 == 0 &&
-         p.K % c.kc == 0 && p.K / c.kc >= c.stages && 32 * p.K * 2 < ((int64_t)1 << 32);
+         p.K % c.kc == 0 && p.K / c.kc >= c.stages && p.lda % 8 == 0 && p.ldb % 8 == 0 && p.ldc % 8 == 0 &&
+         32 * p.ldb * 2 < ((int64_t)1 << 32) && p.M * p.lda * 2 < ((int64_t)1 << 32);
 }
 
 int skinny_split(int cfg, const Problem& p) {

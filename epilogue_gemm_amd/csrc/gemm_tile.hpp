@@ -191,7 +191,7 @@ __device__ __forceinline__ void raster(int bid, int tiles_m, int tiles_n, int pa
 // processed one after another so that few values are live at a time.
 template <int WM, int WN, typename TIn, typename TOut, int EPI, bool EXTRAS>
 __device__ __forceinline__ void write_tile(const f32x16 (&acc)[WM / 32][WN / 32], const TIn* __restrict__ bias,
-                                          TOut* __restrict__ C, int N, int m_w, int n_w, int lane, char* stage,
+                                          TOut* __restrict__ C, int ldc, int m_w, int n_w, int lane, char* stage,
                                           const float* __restrict__ scale, const TOut* __restrict__ res,
                                           const float* __restrict__ out_scale) {
   constexpr int TM = WM / 32, TN = WN / 32;
@@ -224,7 +224,7 @@ __device__ __forceinline__ void write_tile(const f32x16 (&acc)[WM / 32][WN / 32]
         f32x4 sc = f32x4{1.0f, 1.0f, 1.0f, 1.0f}, r = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
         if constexpr (EXTRAS) {
           if (scale) sc = *(const f32x4*)(scale + col);
-          if (res) r = load4<TOut>(res + (int64_t)(m_w + i * 32 + m_l) * N + col);
+          if (res) r = load4<TOut>(res + (int64_t)(m_w + i * 32 + m_l) * ldc + col);
         }
         float v[4];
 #pragma unroll
@@ -259,7 +259,7 @@ __device__ __forceinline__ void write_tile(const f32x16 (&acc)[WM / 32][WN / 32]
     for (int t = 0; t < 32 / RPI; ++t) {
       const int r = t * RPI + lane / CPR, c = lane % CPR;
       const u32x4 d = *(const u32x4*)(stage + r * (WN * OSZ) + ((c ^ (r & SWM)) << 4));
-      *(u32x4*)((char*)(C + (int64_t)(m_w + i * 32 + r) * N + n_w) + c * 16) = d;
+      *(u32x4*)((char*)(C + (int64_t)(m_w + i * 32 + r) * ldc + n_w) + c * 16) = d;
     }
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -285,7 +285,8 @@ template <int BM, int BN, int NW, typename TIn, typename TOut, bool A_KMAJ, bool
 __global__ __launch_bounds__(NW * 64) void gemm_tile_kernel(const TIn* __restrict__ A, const TIn* __restrict__ B,
                                                              const TIn* __restrict__ bias, TOut* __restrict__ C,
                                                              int M, int N, int K, int tiles_m, int tiles_n,
-                                                             int panel, const float* __restrict__ scale,
+                                                             int panel, int lda, int ldb, int ldc,
+                                                             const float* __restrict__ scale,
                                                              const TOut* __restrict__ res,
                                                              const float* __restrict__ out_scale) {
   // NW waves in a 2 x (NW / 2) grid, each owning a WM x WN sub-tile
@@ -321,10 +322,10 @@ __global__ __launch_bounds__(NW * 64) void gemm_tile_kernel(const TIn* __restric
 
   // Operand movers: direct (k-contiguous) or register-staged (transposed).
   // The unused kind of each operand is never called.
-  DirectLoader<BM, NW> da(A, m0, M, K, tid, wave);
-  DirectLoader<BN, NW> db(B, n0, N, K, tid, wave);
-  RegLoader<BM, NT> ra(A, m0, K, M, tid);
-  RegLoader<BN, NT> rb(B, n0, K, N, tid);
+  DirectLoader<BM, NW> da(A, m0, M, lda, tid, wave);
+  DirectLoader<BN, NW> db(B, n0, N, ldb, tid, wave);
+  RegLoader<BM, NT> ra(A, m0, K, lda, tid);
+  RegLoader<BN, NT> rb(B, n0, K, ldb, tid);
 
   // Per-lane LDS read offsets.  Fragment i of a wave's operand covers rows
   // w0 + 32 i + (lane % 32), logical chunk 2 kk + lane / 32 for k-substep kk;
@@ -480,10 +481,10 @@ __global__ __launch_bounds__(NW * 64) void gemm_tile_kernel(const TIn* __restric
   // (the optional column scale, residual and output scale get their own
   // copy of the epilogue, so that the plain one carries no tests for them)
   if (scale != nullptr || res != nullptr || out_scale != nullptr)
-    write_tile<WM, WN, TIn, TOut, EPI, true>(acc, bias, C, N, m0 + wm * WM, n0 + wn * WN, lane, stage_w, scale, res,
+    write_tile<WM, WN, TIn, TOut, EPI, true>(acc, bias, C, ldc, m0 + wm * WM, n0 + wn * WN, lane, stage_w, scale, res,
                                              out_scale);
   else
-    write_tile<WM, WN, TIn, TOut, EPI, false>(acc, bias, C, N, m0 + wm * WM, n0 + wn * WN, lane, stage_w, nullptr,
+    write_tile<WM, WN, TIn, TOut, EPI, false>(acc, bias, C, ldc, m0 + wm * WM, n0 + wn * WN, lane, stage_w, nullptr,
                                               nullptr, nullptr);
 }
 
@@ -494,7 +495,8 @@ hipError_t launch(const LaunchArgs& a) {
   const int panel = tiles_m < 4 ? tiles_m : 4;
   hipLaunchKernelGGL((gemm_tile_kernel<BM, BN, NW, TIn, TOut, A_KMAJ, B_KMAJ, EPI>), dim3(tiles_m * tiles_n),
                      dim3(NW * 64), 0, a.stream, (const TIn*)a.A, (const TIn*)a.B, (const TIn*)a.bias, (TOut*)a.C,
-                     a.M, a.N, a.K, tiles_m, tiles_n, panel, a.scale, (const TOut*)a.residual, a.out_scale);
+                     a.M, a.N, a.K, tiles_m, tiles_n, panel, a.lda, a.ldb, a.ldc, a.scale, (const TOut*)a.residual,
+                     a.out_scale);
   return hipGetLastError();
 }
 

@@ -12,6 +12,7 @@ using LaunchFn = hipError_t (*)(const LaunchArgs&);
 struct Problem {
   int64_t M, N, K;
   int in_dt, out_dt, la, lb, epi;
+  int64_t lda, ldb, ldc;  // leading dimensions of A, B, C (packed: the contiguous extent)
 };
 
 // ---- generic: any shape, layout and alignment -----------------------------

@@ -99,7 +99,8 @@ typedef struct gemm_epi_plan_s* gemm_epi_plan_t;
 /* gemm_epi_plan -- validate a problem and choose its kernel.
  *
  * A is M x K in layout_a, B is K x N in layout_b, C is M x N row-major,
- * all packed (leading dimension = the contiguous extent).
+ * all packed (leading dimension = the contiguous extent) unless
+ * gemm_epi_plan_set_ld gives other leading dimensions.
  * in_dtype in {F16, BF16}; out_dtype in {in_dtype, F32, FP8_E4M3}.
  * Host only: no device allocation, no launch, no HIP call; allocates the
  * small host plan object only.  *out is written only on GEMM_EPI_OK.
@@ -111,6 +112,22 @@ typedef struct gemm_epi_plan_s* gemm_epi_plan_t;
 gemm_epi_status gemm_epi_plan(gemm_epi_plan_t* out, int64_t M, int64_t N, int64_t K, gemm_epi_dtype in_dtype,
                               gemm_epi_dtype out_dtype, gemm_epi_layout layout_a, gemm_epi_layout layout_b,
                               gemm_epi_epilogue epilogue);
+
+/* gemm_epi_plan_set_ld -- leading dimensions of the stored operands, for
+ * products on sub-matrices of larger arrays.
+ *
+ * lda: elements between consecutive rows of A as stored (row-major: rows
+ * of M x K, so >= K; column-major: columns, >= M); ldb likewise for B
+ * (row-major >= N, column-major >= K); ldc between rows of C (>= N), which
+ * a residual (gemm_epi_run_ex) shares.  0 keeps the packed value.  The
+ * kernel is chosen again: the fast kernels need every leading dimension a
+ * multiple of 8 elements (ldc of 16 for FP8_E4M3 output in the tile
+ * kernels), else the generic kernel runs.  Padding between rows is never
+ * read or written.  Host only.
+ * Errors: INVALID_ARG (NULL plan, a leading dimension below its minimum),
+ * UNSUPPORTED (an operand then spans 2^31 elements or more); the plan is
+ * unchanged on error. */
+gemm_epi_status gemm_epi_plan_set_ld(gemm_epi_plan_t plan, int64_t lda, int64_t ldb, int64_t ldc);
 
 /* gemm_epi_run -- enqueue C = act(A.B [+ bias]) on `stream` and return
  * without synchronising.
@@ -161,8 +178,8 @@ gemm_epi_status gemm_epi_run_ws(gemm_epi_plan_t plan, const void* A, const void*
  * computed in fp32 and rounded once.
  *   col_scale  N fp32 values (a per-output-column factor such as a weight
  *              dequantisation scale), or NULL for 1.
- *   residual   M x N row-major elements of the output format, or NULL for
- *              0.  It must not overlap C: where M or N is not a multiple of
+ *   residual   M x N row-major elements of the output format (with C's
+ *              leading dimension), or NULL for 0.  It must not overlap C: where M or N is not a multiple of
  *              a tile, neighbouring workgroups compute some outputs twice,
  *              and an in-place residual would then be added twice.  Not
  *              allowed with FP8_E4M3 output.

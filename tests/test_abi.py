@@ -313,3 +313,41 @@ def test_tune_rejects_invalid_arguments_without_touching_the_device(lib):
     finally:
         gb.gemm_epi_destroy(h)
     assert gb.gemm_epi_tuning_size() == 0
+
+
+def test_plan_set_ld_validates_and_reselects(lib):
+    h = gb.gemm_epi_plan(512, 512, 256, "bf16", "bf16", "row", "col", "none")
+    try:
+        kern0 = gb.gemm_epi_plan_describe(h)
+        assert gb.gemm_epi_plan_set_ld(None, 0, 0, 0) == 1
+        assert gb.gemm_epi_plan_set_ld(h, 255, 0, 0) == 1  # A row-major: lda >= K
+        assert gb.gemm_epi_plan_set_ld(h, 0, 255, 0) == 1  # B column-major: ldb >= K
+        assert gb.gemm_epi_plan_set_ld(h, 0, 0, 511) == 1  # ldc >= N
+        assert gb.gemm_epi_plan_describe(h) == kern0  # unchanged on error
+        assert gb.gemm_epi_plan_set_ld(h, 264, 320, 520) == 0
+        assert gb.gemm_epi_plan_describe(h)[0] == "tile"
+        assert gb.gemm_epi_plan_set_ld(h, 260, 0, 0) == 0  # rows no longer 16-byte aligned
+        assert gb.gemm_epi_plan_describe(h)[0] == "generic"
+        assert gb.gemm_epi_plan_set_ld(h, 0, 0, 0) == 0  # packed again
+        assert gb.gemm_epi_plan_describe(h) == kern0
+        assert gb.gemm_epi_plan_set_ld(h, 1 << 31, 0, 0) == 2
+        assert gb.gemm_epi_plan_set_ld(h, 1 << 24, 0, 0) == 2  # 511 rows of 2^24: past 2^31 elements
+    finally:
+        gb.gemm_epi_destroy(h)
+    h = gb.gemm_epi_plan(32, 1024, 4096, "bf16", "bf16", "row", "col", "bias")
+    try:
+        assert gb.gemm_epi_plan_describe(h)[0] == "skinny"
+        assert gb.gemm_epi_plan_set_ld(h, 4096 + 64, 4096 + 8, 2048) == 0
+        assert gb.gemm_epi_plan_describe(h)[0] == "skinny"
+        assert gb.gemm_epi_plan_set_ld(h, 0, 4100, 0) == 0
+        assert gb.gemm_epi_plan_describe(h)[0] == "generic"
+    finally:
+        gb.gemm_epi_destroy(h)
+    # column-major A: lda >= M
+    h = gb.gemm_epi_plan(256, 256, 128, "f16", "f16", "col", "row", "none")
+    try:
+        assert gb.gemm_epi_plan_set_ld(h, 255, 0, 0) == 1
+        assert gb.gemm_epi_plan_set_ld(h, 264, 264, 0) == 0
+        assert gb.gemm_epi_plan_describe(h)[0] == "tile"
+    finally:
+        gb.gemm_epi_destroy(h)
