@@ -30,11 +30,12 @@ bool tile_supports(int cfg, const Problem& p) {
   // shifted back to end at M or N), but must hold one tile; rows of every
   // operand and of C must stay 16-byte aligned (N % 8, N % 16 for 1-byte
   // E4M3 output; M % 8 when A is column-major; leading dimensions likewise),
-  // and K must be whole k-steps.
+  // and K a multiple of 8 (16-byte chunks) spanning at least two k-steps of
+  // 64 (a partial one first, when K % 64 != 0).
   const TileConfig& c = kTile[cfg];
   const int n_align = p.out_dt == GEMM_EPI_FP8_E4M3 ? 16 : 8;
   return p.M >= c.bm && p.N >= c.bn && p.N % n_align == 0 && (p.la == GEMM_EPI_ROW_MAJOR || p.M % 8 == 0) &&
-         p.K % 64 == 0 && p.K >= 128 && p.lda % 8 == 0 && p.ldb % 8 == 0 && p.ldc % n_align == 0;
+         p.K % 8 == 0 && p.K > 64 && p.lda % 8 == 0 && p.ldb % 8 == 0 && p.ldc % n_align == 0;
 }
 
 int tile_choose(const Problem& p) {

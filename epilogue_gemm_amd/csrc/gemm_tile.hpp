@@ -75,7 +75,11 @@ __device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t voff,
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
 // k-contiguous operand, global -> LDS directly.  Row r of the tile is
-// X[(r0 + r) * ld + k].  Instruction i of wave w (of NW) fills tile rows
+// X[(r0 + r) * ld + k].  When K is not a multiple of the 64-deep k-step,
+// the k axis is shifted by kpad = 64 - K % 64 so that the partial step is
+// the first one: k-step t covers k in [64 t - kpad, 64 t - kpad + 64), and
+// the chunks of step 0 with k < 0 are loaded as zeros (issue_first).
+// Instruction i of wave w (of NW) fills tile rows
 // (NW i + w) * 8 .. +7; lane L writes LDS bytes 16 L .. 16 L + 15 of that
 // KiB, i.e. row (NW i + w) * 8 + L / 8 at chunk position L % 8, so it loads
 // logical chunk (L % 8) ^ swz(row).  swz depends on the row only through
@@ -91,9 +95,10 @@ struct DirectLoader {
   uint32_t rows64;  // bytes of 64 rows
   int wave;
 
-  __device__ __forceinline__ DirectLoader(const void* X, int r0, int rows_total, int ld, int tid, int wave_) {
-    const char* base = (const char*)X + (int64_t)r0 * ld * 2;
-    rsrc = make_rsrc(base, (uint32_t)((int64_t)(rows_total - r0) * ld * 2));
+  __device__ __forceinline__ DirectLoader(const void* X, int r0, int rows_total, int ld, int kpad, int tid,
+                                          int wave_) {
+    const char* base = (const char*)X + (int64_t)r0 * ld * 2 - (int64_t)kpad * 2;
+    rsrc = make_rsrc(base, (uint32_t)((int64_t)(rows_total - r0) * ld * 2 + (int64_t)kpad * 2));
     wave = wave_;
     const int lane = tid & 63;
     const int rl = lane >> 3, pc = lane & 7;
@@ -109,12 +114,25 @@ struct DirectLoader {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr)(dst + (NW * i + wave) * 1024), 16, voff[i % NV],
                                              (i / NV) * rows64 + kt * kRowBytes, 0, 0);
   }
+  // Instruction i of k-step 0 when the axis is shifted by kpad (a multiple
+  // of 8): a lane whose logical chunk lies at k < 0 takes a per-lane offset
+  // past the end of the buffer, which the buffer's range check turns into
+  // zeros without a memory access.  (Rows of instruction i are rows of
+  // instruction i % NV plus a multiple of 64, so they share the swizzle.)
+  __device__ __forceinline__ void issue_first(char* dst, int i, int lane, int kpad) const {
+    const int row = (NW * (i % NV) + wave) * 8 + (lane >> 3);
+    const int chunk = (lane & 7) ^ swz(row);
+    const uint32_t v = chunk * 8 < kpad ? 0xFFFFFFF0u : voff[i % NV];
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr)(dst + (NW * i + wave) * 1024), 16, v,
+                                             (i / NV) * rows64, 0, 0);
+  }
 };
 
 // M/N-contiguous operand through registers: row r of the tile (an M or N
 // index) at k is X[k * ld + r0 + r].  Each thread loads KB k-rows of 8
 // consecutive M/N values and writes, for each of the 8, its KB k-values
-// contiguously.
+// contiguously.  The k axis is shifted by kpad as for DirectLoader; rows of
+// step 0 with k < 0 load as zeros (load_first).
 template <int R, int NT>
 struct RegLoader {
   static constexpr int KB = R * 8 / NT;  // k values per thread: 8, 4 or 2
@@ -127,17 +145,23 @@ struct RegLoader {
   int ng, kg;
   u32x4 r[KB];
 
-  __device__ __forceinline__ RegLoader(const void* X, int r0, int k_total, int ld, int tid) {
+  __device__ __forceinline__ RegLoader(const void* X, int r0, int k_total, int ld, int kpad, int tid) {
     ng = tid % NG;
     kg = tid / NG;
     kstep = (uint32_t)(ld * 2);
-    const char* base = (const char*)X + (int64_t)r0 * 2;
-    rsrc = make_rsrc(base, (uint32_t)((int64_t)k_total * ld * 2 - (int64_t)r0 * 2));
+    const char* base = (const char*)X + (int64_t)r0 * 2 - (int64_t)kpad * ld * 2;
+    rsrc = make_rsrc(base, (uint32_t)((int64_t)(k_total + kpad) * ld * 2 - (int64_t)r0 * 2));
     voff = (uint32_t)(kg * KB * ld * 2 + ng * 16);
   }
   __device__ __forceinline__ void load(int kt) {
 #pragma unroll
     for (int i = 0; i < KB; ++i) r[i] = load16(rsrc, voff, (uint32_t)(kt * kBK + i) * kstep);
+  }
+  // k-step 0 with the axis shifted by kpad: rows at k < 0 read as zeros
+  // (per-lane offset past the end of the buffer: no memory access)
+  __device__ __forceinline__ void load_first(int kpad) {
+#pragma unroll
+    for (int i = 0; i < KB; ++i) r[i] = load16(rsrc, kg * KB + i < kpad ? 0xFFFFFFF0u : voff, (uint32_t)i * kstep);
   }
   // 16-bit element j (0..7) of a 128-bit register
   static __device__ __forceinline__ uint32_t half_of(const u32x4& v, int j) {
@@ -319,13 +343,16 @@ __global__ __launch_bounds__(NW * 64) void gemm_tile_kernel(const TIn* __restric
   // identical values) part of its neighbour, and no access leaves A, B,
   // bias or C.
   const int m0 = min(tm * BM, M - BM), n0 = min(tn * BN, N - BN);
+  // K need only be a multiple of 8: the first k-step is then partial, its
+  // first kpad k-values zeros (see DirectLoader)
+  const int kpad = (-K) & (kBK - 1);
 
   // Operand movers: direct (k-contiguous) or register-staged (transposed).
   // The unused kind of each operand is never called.
-  DirectLoader<BM, NW> da(A, m0, M, lda, tid, wave);
-  DirectLoader<BN, NW> db(B, n0, N, ldb, tid, wave);
-  RegLoader<BM, NT> ra(A, m0, K, lda, tid);
-  RegLoader<BN, NT> rb(B, n0, K, ldb, tid);
+  DirectLoader<BM, NW> da(A, m0, M, lda, kpad, tid, wave);
+  DirectLoader<BN, NW> db(B, n0, N, ldb, kpad, tid, wave);
+  RegLoader<BM, NT> ra(A, m0, K, lda, kpad, tid);
+  RegLoader<BN, NT> rb(B, n0, K, ldb, kpad, tid);
 
   // Per-lane LDS read offsets.  Fragment i of a wave's operand covers rows
   // w0 + 32 i + (lane % 32), logical chunk 2 kk + lane / 32 for k-substep kk;
@@ -425,22 +452,28 @@ __global__ __launch_bounds__(NW * 64) void gemm_tile_kernel(const TIn* __restric
   // Tile t lives in stage (t + KT) % 2, so that the last two tiles are
   // always in stages 0 and 1 and the k loop ends with two peeled k-steps
   // and no other branches (one straight path keeps the accumulators in
-  // place).  KT >= 2 (checked on the host).
-  const int KT = K / kBK;
+  // place).  KT >= 2, i.e. K > 64 (checked on the host).
+  const int KT = (K + kpad) / kBK;
   auto prologue = [&](const Stage& s_first, const Stage& s_second) __attribute__((always_inline)) {
+    if (kpad == 0) {
 #pragma unroll
-    for (int d = 0; d < NDL; ++d) {
-      if (d < NDA) da.issue(s_first.a, 0, d);
-      else db.issue(s_first.b, 0, d - NDA);
+      for (int d = 0; d < NDL; ++d) {
+        if (d < NDA) da.issue(s_first.a, 0, d);
+        else db.issue(s_first.b, 0, d - NDA);
+      }
+      if constexpr (!A_KMAJ) ra.load(0);
+      if constexpr (!B_KMAJ) rb.load(0);
+    } else {
+#pragma unroll
+      for (int d = 0; d < NDL; ++d) {
+        if (d < NDA) da.issue_first(s_first.a, d, lane, kpad);
+        else db.issue_first(s_first.b, d - NDA, lane, kpad);
+      }
+      if constexpr (!A_KMAJ) ra.load_first(kpad);
+      if constexpr (!B_KMAJ) rb.load_first(kpad);
     }
-    if constexpr (!A_KMAJ) {
-      ra.load(0);
-      ra.store(s_first.a);
-    }
-    if constexpr (!B_KMAJ) {
-      rb.load(0);
-      rb.store(s_first.b);
-    }
+    if constexpr (!A_KMAJ) ra.store(s_first.a);
+    if constexpr (!B_KMAJ) rb.store(s_first.b);
 #pragma unroll
     for (int d = 0; d < NDL; ++d) {
       if (d < NDA) da.issue(s_second.a, 1, d);

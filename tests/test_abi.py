@@ -146,7 +146,11 @@ def test_fp8_output_needs_16_columns_in_tile_kernels(lib):
     (1001, 1000, 1024, "col", "col", "generic", "generic"),  # column-major A needs M % 8
     (1000, 1004, 1024, "row", "col", "generic", "generic"),  # N % 8
     (37, 53, 29, "row", "row", "generic", "generic"),
-    (256, 256, 100, "col", "row", "generic", "generic"),  # K not a multiple of 64
+    (256, 256, 100, "col", "row", "generic", "generic"),  # K not a multiple of 8
+    (1024, 1024, 1000, "row", "col", "tile", "tile_64x64x64"),  # K % 64 = 40: a partial first k-step
+    (4096, 4096, 4040, "row", "col", "tile", "tile_256x256x64_8w"),
+    (256, 256, 72, "col", "row", "tile", "tile_64x64x64"),
+    (256, 256, 64, "row", "row", "generic", "generic"),  # one k-step: the tile pipeline needs two
 ])
 def test_auto_selection(lib, M, N, K, la, lb, want_kernel, want_name):
     h = gb.gemm_epi_plan(M, N, K, "bf16", "bf16", la, lb, "none")

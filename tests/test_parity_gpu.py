@@ -107,6 +107,27 @@ def test_tile_edge_integer_bitexact(config, la, lb, in_dt, out_dt):
         assert name.startswith("tile_")
 
 
+# K a multiple of 8 but not of 64: the first k-step is partial, its leading
+# 64 - K % 64 k-values loaded as zeros
+@pytest.mark.parametrize("config", [0, 1, 2, 3])
+@pytest.mark.parametrize("la,lb", [("row", "col"), ("row", "row"), ("col", "col"), ("col", "row")])
+def test_tile_ktail_integer_bitexact(config, la, lb):
+    M, N = {0: (264, 520), 1: (256, 136), 2: (72, 200), 3: (304, 264)}[config]
+    for K in (72, 104, 1000):
+        for in_dt, out_dt, epi in (("bf16", "bf16", "bias_relu"), ("f16", "f32", "none")):
+            bits = inputs.integer_inputs(M, N, K, in_dt, la, lb, epi.startswith("bias"), seed=K + config)
+            name = check_case(bits, M, N, K, in_dt, out_dt, la, lb, epi, "tile", config, True)
+            assert name.startswith("tile_")
+
+
+@pytest.mark.parametrize("kpad", [8, 16, 24, 32, 40, 48, 56])
+def test_tile_ktail_every_padding(kpad):
+    M, N, K = 128, 128, 128 - kpad
+    for la, lb in (("row", "col"), ("col", "row")):
+        bits = inputs.integer_inputs(M, N, K, "bf16", la, lb, True, seed=kpad)
+        check_case(bits, M, N, K, "bf16", "bf16", la, lb, "bias", "tile", 2, True)
+
+
 @pytest.mark.parametrize("M", [1, 32])
 @pytest.mark.parametrize("N", [40, 1000])
 def test_skinny_edge_integer_bitexact(M, N):
@@ -203,6 +224,9 @@ def test_generic_integer_bitexact(M, N, K, la, lb):
     ("tile", 3, 512, 1024, 704, "row", "col"),
     ("tile", 3, 768, 512, 384, "row", "row"),
     ("tile", 3, 1000, 1000, 1024, "row", "col"),
+    ("tile", 3, 1000, 1000, 1000, "row", "col"),
+    ("tile", 0, 512, 768, 584, "row", "row"),
+    ("tile", 1, 384, 256, 968, "col", "col"),
     ("tile", 2, 1000, 1000, 1024, "col", "row"),
     ("tile", 1, 384, 256, 1024, "row", "row"),
     ("tile", 2, 320, 192, 448, "col", "col"),
