@@ -14,7 +14,7 @@ launched on.  The CPU oracle is timed on a bounded sample of the main
 workload as a reported baseline (rank 0, N = 1 only).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only main|skinny]
-                       [--no-cpu-baseline]
+                       [--no-cpu-baseline] [--no-variants] [--calib-copy]
 """
 from __future__ import annotations
 
@@ -143,6 +143,41 @@ def _cpu_baseline(w, bits):
     }
 
 
+def _run_variants(w, sets, args, variants, binding, inputs, parity, torch):
+    """The further epilogues on the main shape and operands (reported beside
+    the headline, not in it): bias+SiLU; bias+GELU with a column scale and a
+    residual (one residual per operand set, none overlapping C); bias+GELU to
+    FP8 E4M3 with an output scale."""
+    ex = inputs.extras_inputs(w.M, w.N, w.out_dtype, seed=w.seed)
+    scale = torch.from_numpy(ex["scale"]).cuda()
+    res0 = parity.to_device_out(ex["residual"], w.out_dtype)
+    extras = [(scale, res0 if i == 0 else res0.clone()) for i in range(len(sets))]
+    vsteps = min(args.steps, 50)
+    warm = max(args.warmup // 2, 5)
+    for epi, with_extras in (("bias_silu", False), ("bias_gelu", True)):
+        p = binding.Plan(w.M, w.N, w.K, w.in_dtype, w.out_dtype, w.layout_a, w.layout_b, epi)
+        vms = _time_launches(p, sets, vsteps, warm, torch, extras if with_extras else None)
+        variants.append({"epilogue": epi, "out_dtype": w.out_dtype, "col_scale": with_extras,
+                         "residual": with_extras, "out_scale": False, "kernel": p.name,
+                         "ms_per_step": round(vms, 4), "TFLOP/s": round(w.flops / (vms * 1e-3) / 1e12, 1),
+                         "steps": vsteps})
+        p.close()
+    del extras, res0
+    sets8 = [(A, B, bias, parity.empty_out(w.M * w.N, "fp8")) for A, B, bias, _ in sets]
+    q = torch.tensor([ex["out_scale"]], dtype=torch.float32, device="cuda")
+    p = binding.Plan(w.M, w.N, w.K, w.in_dtype, "fp8", w.layout_a, w.layout_b, "bias_gelu")
+
+    class _WithOutScale:  # runs the plan with the output scale
+        def run(self, A, B, bias, C, stream):
+            p.run(A, B, bias, C, stream, out_scale=q)
+
+    vms = _time_launches(_WithOutScale(), sets8, vsteps, warm, torch)
+    variants.append({"epilogue": "bias_gelu", "out_dtype": "fp8", "col_scale": False, "residual": False,
+                     "out_scale": True, "kernel": p.name, "ms_per_step": round(vms, 4),
+                     "TFLOP/s": round(w.flops / (vms * 1e-3) / 1e12, 1), "steps": vsteps})
+    p.close()
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -150,6 +185,8 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--only", choices=["main", "skinny", "both"], default="both")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the further-epilogue variants (so that a profile sees the headline kernel only)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="after timing, run a plain 1 GiB device copy (elementwise kernel) three times, so that "
                          "HBM byte counters can be scaled against a kernel of known traffic")
@@ -179,44 +216,17 @@ def main(argv=None):
         tflops = w.flops / (ms * 1e-3) / 1e12
         out["main"] = dict(w=w, bits=bits, ms=ms, value=tflops, kernel=plan.name)
         plan.close()
-        # the further epilogues on the same shape and operands (reported, not
-        # the headline): bias+SiLU, and bias+GELU with a column scale and a
-        # residual (one residual per operand set, none overlapping C)
+        # the further epilogues on the same shape and operands (_run_variants)
         variants = []
-        ex = inputs.extras_inputs(w.M, w.N, w.out_dtype, seed=w.seed)
-        scale = torch.from_numpy(ex["scale"]).cuda()
-        res0 = parity.to_device_out(ex["residual"], w.out_dtype)
-        extras = [(scale, res0 if i == 0 else res0.clone()) for i in range(len(sets))]
-        vsteps = min(args.steps, 50)
-        for epi, with_extras in (("bias_silu", False), ("bias_gelu", True)):
-            p = binding.Plan(w.M, w.N, w.K, w.in_dtype, w.out_dtype, w.layout_a, w.layout_b, epi)
-            vms = _time_launches(p, sets, vsteps, max(args.warmup // 2, 5), torch, extras if with_extras else None)
-            variants.append({"epilogue": epi, "out_dtype": w.out_dtype, "col_scale": with_extras,
-                             "residual": with_extras, "out_scale": False, "kernel": p.name,
-                             "ms_per_step": round(vms, 4), "TFLOP/s": round(w.flops / (vms * 1e-3) / 1e12, 1),
-                             "steps": vsteps})
-            p.close()
-        # quantised output: bias+GELU, then the output scale and FP8 E4M3
-        del extras, res0
-        sets8 = [(A, B, bias, parity.empty_out(w.M * w.N, "fp8")) for A, B, bias, _ in sets]
-        q = torch.tensor([ex["out_scale"]], dtype=torch.float32, device="cuda")
-        p = binding.Plan(w.M, w.N, w.K, w.in_dtype, "fp8", w.layout_a, w.layout_b, "bias_gelu")
-        stream = torch.cuda.current_stream()
-
-        class _Q:  # runs the plan with the output scale
-            name = p.name
-
-            def run(self, A, B, bias, C, s):
-                p.run(A, B, bias, C, s, out_scale=q)
-        vms = _time_launches(_Q(), sets8, vsteps, max(args.warmup // 2, 5), torch)
-        variants.append({"epilogue": "bias_gelu", "out_dtype": "fp8", "col_scale": False, "residual": False,
-                         "out_scale": True, "kernel": p.name, "ms_per_step": round(vms, 4),
-                         "TFLOP/s": round(w.flops / (vms * 1e-3) / 1e12, 1), "steps": vsteps})
-        p.close()
-        del sets8, stream
-        out["main"]["variants"] = variants
-        del sets
-        torch.cuda.empty_cache()
+        if args.no_variants:
+            del sets
+            torch.cuda.empty_cache()
+            out["main"]["variants"] = variants
+        else:
+            _run_variants(w, sets, args, variants, binding, inputs, parity, torch)
+            out["main"]["variants"] = variants
+            del sets
+            torch.cuda.empty_cache()
     if args.only in ("skinny", "both"):
         w = inputs.WORKLOADS[SKINNY]
         # 5 sets x 128 MiB of B: more than the 256 MB last-level cache
