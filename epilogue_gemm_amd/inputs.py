@@ -172,3 +172,52 @@ def extras_inputs(M: int, N: int, out_dtype: str, seed: int, integer: bool = Fal
     else:
         rbits = to_bits(resid.to(_TORCH_DT[out_dtype])).reshape(-1)
     return {"scale": scale.numpy().astype(np.float32), "residual": rbits, "out_scale": out_scale}
+
+
+# ---------------------------------------------------------------------------
+# attention forward (the second workload)
+# ---------------------------------------------------------------------------
+
+@dataclasses.dataclass(frozen=True)
+class AttentionWorkload:
+    """Scaled dot-product attention, Q, K, V, O laid out [B, S, H, D]."""
+    name: str
+    B: int
+    S: int
+    H: int
+    D: int
+    dtype: str  # "f16" | "bf16"
+    causal: bool
+    seed: int
+
+    @property
+    def flops(self) -> float:
+        # two products of 2 S^2 D per (batch, head); half of them when causal
+        return 4.0 * self.B * self.H * self.S * self.S * self.D * (0.5 if self.causal else 1.0)
+
+    def compulsory_bytes(self) -> int:
+        return 4 * self.B * self.S * self.H * self.D * 2
+
+
+# The ainew.jp page's section-6 example: B, H, S, D = 4, 8, 1024, 64, fp16,
+# full and causal.
+ATTENTION_WORKLOADS = {
+    w.name: w
+    for w in [
+        AttentionWorkload("attn_fwd_f16_b4_s1024_h8_d64_full", 4, 1024, 8, 64, "f16", False, 5),
+        AttentionWorkload("attn_fwd_f16_b4_s1024_h8_d64_causal", 4, 1024, 8, 64, "f16", True, 6),
+    ]
+}
+
+
+def attention_inputs(B: int, S: int, H: int, D: int, dtype: str, seed: int):
+    """dict(Q=..., K=..., V=...) of uint16 bit arrays laid out [B, S, H, D]:
+    torch.randn in fp32 in the order Q, K, V from one seeded generator,
+    rounded to `dtype` (the page draws q, k, v with torch.randn)."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    dt = _TORCH_DT[dtype]
+    out = {}
+    for name in ("Q", "K", "V"):
+        out[name] = to_bits(torch.randn(B, S, H, D, generator=g, dtype=torch.float32).to(dt)).reshape(-1)
+    return out

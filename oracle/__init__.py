@@ -1,4 +1,5 @@
-"""CPU oracle for C = act(s * A.B [+ bias]) [+ r] -- TEST INFRASTRUCTURE ONLY.
+"""CPU oracle for C = act(s * A.B [+ bias]) [+ r] and for scaled dot-product
+attention -- TEST INFRASTRUCTURE ONLY.
 
 Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
 import this package.  The GPU library and its Python binding never import,
@@ -7,6 +8,7 @@ it computes and the passages it follows.
 """
 from .oracle import (  # noqa: F401
     FORMATS,
+    attention,
     LAYOUTS,
     EPILOGUES,
     build,

@@ -350,6 +350,105 @@ int oracle_gemm_epi_points(int64_t M, int64_t N, int64_t K, int in_fmt, int out_
                                    cols, y_out, bits_out, nthreads);
 }
 
+/* ------------------------------------------------------------------------
+ * Attention forward (the second workload):
+ *
+ *   S[i][j] = (1 / sqrt(D)) * sum_d Q[i][d] K[j][d]
+ *   P[i][j] = exp(S[i][j] - max_j' S[i][j']) / sum_j' exp(S[i][j'] - max_j' S[i][j'])
+ *   O[i][d] = sum_j P[i][j] V[j][d]
+ *
+ * for every batch b and head h, with j (and j') running over all keys, or
+ * over j <= i when causal; O rounded once (RNE) to the input format.
+ * Scaled dot-product attention as the csdn tutorial defines it (ch.13
+ * "FlashAttention", sec. 13.1), the layout [batch, seq, heads, dim] and the
+ * causal rule (key j visible to query i when j <= i) of the ainew.jp page's
+ * section 6 example.  The blocked, online form of the softmax (sec. 13.7) is
+ * the GPU's business; this is the definition, in fp64.
+ * ------------------------------------------------------------------------ */
+
+/* One query row: y[d] for d < D (fp64), keys j < nk. */
+static void attn_row(const double* tab, const uint16_t* Q, const uint16_t* K, const uint16_t* V, int64_t S,
+                     int64_t H, int64_t D, int64_t b, int64_t h, int64_t i, int causal, double* s, double* y) {
+  const int64_t nk = causal ? i + 1 : S;
+  const double scale = 1.0 / sqrt((double)D);
+  const uint16_t* q = Q + ((b * S + i) * H + h) * D;
+  double mx = -INFINITY;
+  for (int64_t j = 0; j < nk; ++j) {
+    const uint16_t* k = K + ((b * S + j) * H + h) * D;
+    double acc = 0.0;
+    for (int64_t d = 0; d < D; ++d) acc += tab[q[d]] * tab[k[d]];
+    s[j] = acc * scale;
+    if (s[j] > mx) mx = s[j];
+  }
+  double sum = 0.0;
+  for (int64_t j = 0; j < nk; ++j) {
+    s[j] = exp(s[j] - mx);
+    sum += s[j];
+  }
+  for (int64_t d = 0; d < D; ++d) y[d] = 0.0;
+  for (int64_t j = 0; j < nk; ++j) {
+    const uint16_t* v = V + ((b * S + j) * H + h) * D;
+    const double p = s[j] / sum;
+    for (int64_t d = 0; d < D; ++d) y[d] += p * tab[v[d]];
+  }
+}
+
+/* Rows (b[r], i[r], h[r]) for r < count, or every row when count < 0 (then
+ * the outputs are laid out [B, S, H, D] like O).  y_out (fp64) and o_out
+ * (bit patterns of fmt) may each be NULL.  Returns 0, -1 (bad arguments)
+ * or -2 (no memory). */
+int oracle_attention(int64_t B, int64_t S, int64_t H, int64_t D, int fmt, int causal, const void* Q,
+                     const void* K, const void* V, int64_t count, const int64_t* rb, const int64_t* ri,
+                     const int64_t* rh, double* y_out, void* o_out, int nthreads) {
+  if (B <= 0 || S <= 0 || H <= 0 || D <= 0 || (fmt != ORC_F16 && fmt != ORC_BF16) || !Q || !K || !V) return -1;
+  if (count >= 0 && count > 0 && (!rb || !ri || !rh)) return -1;
+  const int64_t rows = count < 0 ? B * S * H : count;
+  for (int64_t r = 0; count >= 0 && r < count; ++r)
+    if (rb[r] < 0 || rb[r] >= B || ri[r] < 0 || ri[r] >= S || rh[r] < 0 || rh[r] >= H) return -1;
+  double* tab = make_table(fmt);
+  if (!tab) return -2;
+  int fail = 0;
+#ifdef _OPENMP
+  if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel num_threads(nthreads)
+#endif
+  {
+    double* s = (double*)malloc((size_t)S * sizeof(double));
+    double* y = (double*)malloc((size_t)D * sizeof(double));
+    if (!s || !y) {
+#ifdef _OPENMP
+#pragma omp atomic write
+#endif
+      fail = 1;
+    } else {
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 4)
+#endif
+      for (int64_t r = 0; r < rows; ++r) {
+        int64_t b, i, h;
+        if (count < 0) {
+          b = r / (S * H);
+          i = (r / H) % S;
+          h = r % H;
+        } else {
+          b = rb[r];
+          i = ri[r];
+          h = rh[r];
+        }
+        attn_row(tab, (const uint16_t*)Q, (const uint16_t*)K, (const uint16_t*)V, S, H, D, b, h, i, causal, s, y);
+        for (int64_t d = 0; d < D; ++d) {
+          if (y_out) y_out[r * D + d] = y[d];
+          if (o_out) ((uint16_t*)o_out)[r * D + d] = (uint16_t)oracle_encode(fmt, y[d]);
+        }
+      }
+    }
+    free(s);
+    free(y);
+  }
+  free(tab);
+  return fail ? -2 : 0;
+}
+
 /* Threads an OpenMP region of this library uses by default. */
 int oracle_max_threads(void) {
 #ifdef _OPENMP

@@ -64,6 +64,8 @@ def _load():
     lib.oracle_gemm_epi_points_ex.argtypes = [i64, i64, i64, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp,
                                               i64, vp, vp, vp, vp, i32]
     lib.oracle_gemm_epi_points_ex.restype = i32
+    lib.oracle_attention.argtypes = [i64, i64, i64, i64, i32, i32, vp, vp, vp, i64, vp, vp, vp, vp, vp, i32]
+    lib.oracle_attention.restype = i32
     lib.oracle_max_threads.argtypes = []
     lib.oracle_max_threads.restype = i32
     _lib = lib
@@ -187,3 +189,28 @@ def gemm_epi_points(A, B, bias, M, N, K, in_dtype, out_dtype, layout_a, layout_b
     if rc != 0:
         raise ValueError(f"oracle_gemm_epi_points rejected its arguments (rc={rc})")
     return y, bits
+
+
+def attention(Q, K, V, B, S, H, D, dtype, causal, rows=None, want_y=True, want_o=True, nthreads=0):
+    """Scaled dot-product attention, fp64.  Q, K, V: uint16 bit patterns laid
+    out [B, S, H, D].  rows: None for every query row (outputs [B, S, H, D]),
+    or a tuple of index arrays (b, i, h) (outputs [len, D]).  Returns (y, o):
+    fp64 values and their RNE bit patterns in `dtype`."""
+    Q, K, V = _bits16(Q, "Q"), _bits16(K, "K"), _bits16(V, "V")
+    n = B * S * H * D
+    if Q.size != n or K.size != n or V.size != n:
+        raise ValueError("Q, K, V must each hold B*S*H*D elements")
+    if rows is None:
+        count, rb, ri, rh, shape = -1, None, None, None, (B, S, H, D)
+    else:
+        rb, ri, rh = (np.ascontiguousarray(x, np.int64) for x in rows)
+        if not (rb.shape == ri.shape == rh.shape):
+            raise ValueError("row index arrays differ in length")
+        count, shape = rb.size, (rb.size, D)
+    y = np.empty(shape, np.float64) if want_y else None
+    o = np.empty(shape, np.uint16) if want_o else None
+    rc = _load().oracle_attention(B, S, H, D, FORMATS[dtype], int(bool(causal)), _ptr(Q), _ptr(K), _ptr(V), count,
+                                  _ptr(rb), _ptr(ri), _ptr(rh), _ptr(y), _ptr(o), int(nthreads))
+    if rc != 0:
+        raise ValueError(f"oracle_attention rejected its arguments (rc={rc})")
+    return y, o
