@@ -6,7 +6,10 @@ One step = one launch of the library on one batch of synthetic input:
     M = N = K = 8192, A row-major, B column-major (value = TFLOP/s, 2MNK
     per step);
   * "skinny": C = A.B + bias, bf16, M = 32, N = K = 8192, B column-major
-    (GB/s of compulsory A + B + bias + C bytes per step).
+    (GB/s of compulsory A + B + bias + C bytes per step);
+  * "epilogue_variants" (the further epilogues on the main shape) and
+    "attention" (attention forward, B, H, S, D = 4, 8, 1024, 64, fp16, full
+    and causal): reported beside the headline.
 Inputs are resident in HBM before timing starts; operand sets are rotated
 across launches so that the 256 MB last-level cache cannot serve B from a
 previous launch.  Timing uses HIP events on the stream the kernels are
@@ -178,12 +181,40 @@ def _run_variants(w, sets, args, variants, binding, inputs, parity, torch):
     p.close()
 
 
+def _bench_attention(steps, warmup, torch, binding, inputs, parity):
+    """The attention forward workloads (B, H, S, D = 4, 8, 1024, 64, fp16, full
+    and causal): TFLOP/s of 4 B H S^2 D (half when causal) per launch."""
+    recs = []
+    for w in inputs.ATTENTION_WORKLOADS.values():
+        d = inputs.attention_inputs(w.B, w.S, w.H, w.D, w.dtype, w.seed)
+        q, k, v = (parity.to_device(d[n], w.dtype).view(w.B, w.S, w.H, w.D) for n in ("Q", "K", "V"))
+        o = torch.empty_like(q)
+        stream = torch.cuda.current_stream()
+        for _ in range(warmup):
+            binding.attention_fwd(q, k, v, o, causal=w.causal, stream=stream)
+        torch.cuda.synchronize()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        for _ in range(steps):
+            binding.attention_fwd(q, k, v, o, causal=w.causal, stream=stream)
+        end.record(stream)
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(end) / steps
+        tf = w.flops / (ms * 1e-3) / 1e12
+        recs.append({"workload": w.name, "B": w.B, "S": w.S, "H": w.H, "D": w.D, "causal": w.causal,
+                     "ms_per_step": round(ms, 5), "TFLOP/s": round(tf, 1), "steps": steps,
+                     "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_BF16_TFLOPS,
+                                  "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None}})
+        del q, k, v, o
+    return recs
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--only", choices=["main", "skinny", "both"], default="both")
+    ap.add_argument("--only", choices=["main", "skinny", "both", "attention"], default="both")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the further-epilogue variants (so that a profile sees the headline kernel only)")
@@ -240,6 +271,10 @@ def main(argv=None):
         del sets
         torch.cuda.empty_cache()
 
+    attention = None
+    if args.only in ("both", "attention") and not args.no_variants:
+        attention = _bench_attention(max(args.steps, 50), max(args.warmup, 10), torch, binding, inputs, parity)
+
     if args.calib_copy:
         src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
         dst = torch.empty_like(src)
@@ -294,6 +329,11 @@ def main(argv=None):
         else:
             rec = {**sk, "n_gpus": 1, "warmup": args.warmup, "higher_is_better": True, "scaling": "weak",
                    "vs_baseline": None, "dtype": "bf16", "data": "synthetic"}
+    if attention is not None:
+        if rec:
+            rec["attention"] = attention
+        else:
+            rec = {"metric": "attention forward TFLOP/s", "attention": attention, "n_gpus": 1}
     if "main" in out and not args.no_cpu_baseline:
         rec["cpu_baseline"] = _cpu_baseline(out["main"]["w"], out["main"]["bits"])
     print(json.dumps(rec), flush=True)

@@ -79,6 +79,8 @@ def load_library(path: str = LIB_PATH):
     lib.gemm_epi_tuning_clear.restype = None
     lib.gemm_epi_tuning_size.argtypes = []
     lib.gemm_epi_tuning_size.restype = i32
+    lib.gemm_epi_attention_fwd.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i32, i32, vp]
+    lib.gemm_epi_attention_fwd.restype = i32
     lib.gemm_epi_destroy.argtypes = [vp]
     lib.gemm_epi_destroy.restype = i32
     lib.gemm_epi_status_string.argtypes = [i32]
@@ -178,6 +180,30 @@ def gemm_epi_tuning_clear() -> None:
 
 def gemm_epi_tuning_size() -> int:
     return int(load_library().gemm_epi_tuning_size())
+
+
+def gemm_epi_attention_fwd(Q_ptr, K_ptr, V_ptr, O_ptr, B, S, H, D, dtype, causal, stream) -> int:
+    return load_library().gemm_epi_attention_fwd(Q_ptr, K_ptr, V_ptr, O_ptr, int(B), int(S), int(H), int(D),
+                                                 DTYPES[dtype], int(bool(causal)), stream)
+
+
+def attention_fwd(q, k, v, o, causal=False, stream=None):
+    """Scaled dot-product attention on torch CUDA tensors [B, S, H, D]
+    (contiguous, fp16 or bf16): fills `o`; enqueued on torch's current
+    stream (or `stream`), not synchronised."""
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+        if not t.is_cuda or not t.is_contiguous() or t.dim() != 4:
+            raise ValueError(f"{name}: expected a contiguous 4-d CUDA tensor [B, S, H, D]")
+        if t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError(f"{name}: shape/dtype differ from q")
+    B, S, H, D = q.shape
+    s = (stream or torch.cuda.current_stream()).cuda_stream
+    st = gemm_epi_attention_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), B, S, H, D,
+                                _dtype_name(q), causal, s)
+    if st != OK:
+        raise GemmEpiError("gemm_epi_attention_fwd", st)
 
 
 def gemm_epi_destroy(plan) -> int:

@@ -1,0 +1,273 @@
+// attention.hip -- scaled dot-product attention forward, O = softmax(Q K^T /
+// sqrt(D)) V per batch and head, Q/K/V/O laid out [B, S, H, D], fp16 or bf16,
+// full or causal (key j visible to query i when j <= i).
+//
+// The blocked form with an online softmax: each workgroup owns 128 queries
+// of one (batch, head) and streams the keys and values in blocks of 64
+// through LDS, keeping per query the running maximum m, the running sum l
+// and the unnormalised output o, rescaled by exp(m_old - m_new) whenever
+// the maximum grows, and divides by l at the end (csdn "从零开始学习
+// TileLang", ch.13 "FlashAttention", sec. 13.6-13.8; ainew.jp "TileLang で
+// GPU カーネル設計を解説", section 6).  Scores are scaled by log2(e) / sqrt(D)
+// so that exp is the hardware exp2 (sec. 9.6 of the same tutorial).
+//
+// gfx950 layout.  Each wave owns 32 queries and every product is a
+// v_mfma_f32_32x32x16 chain arranged so that no data crosses lanes except
+// one max exchange per key block:
+//   * S^T = K Q^T: first operand K (key rows from LDS), second Q (registers);
+//     lane (i, h) = (lane % 32, lane / 32) receives, for query i, the scores
+//     of 16 of every 32 keys.  Key rows are fed to the MFMA in the order
+//     kappa(r) (bits 2 and 3 of r swapped) so that lane h holds keys
+//     16 t + 8 h + 0..7 of each 32-key group in accumulator order 8 t + u;
+//   * those 8 fp32 probabilities, rounded to the input format, are exactly
+//     the lane's second operand of O^T = V^T P^T for 16 keys: P never leaves
+//     the registers;
+//   * O^T accumulates with V^T (from LDS) as first operand, so lane (i, h)
+//     holds 32 of query i's 64 outputs: the rescale by exp(m_old - m_new) is
+//     per lane, and the two halves of a query exchange their partial sums l
+//     once at the end.
+// K goes to LDS by direct buffer loads (rows of 128 bytes, 16-byte chunks
+// XOR-swizzled by row); V is transposed on the way (each thread loads two
+// key rows of 8 values and writes 8 d-rows of two keys), so that both MFMA
+// operand reads are 16-byte LDS reads free of bank conflicts.  Two LDS
+// stages: block kb + 1 is loaded while block kb is multiplied.
+#include "gemm_tile.hpp"
+
+namespace ge {
+namespace attn {
+
+using tile::lds_ptr;
+using tile::load16;
+using tile::make_rsrc;
+using tile::swz;
+
+constexpr int kD = 64;        // head dimension
+constexpr int kBM = 128;      // queries per workgroup (4 waves x 32)
+constexpr int kBN = 64;       // keys per block
+constexpr int kRow = kD * 2;  // bytes of one LDS row (64 16-bit values)
+constexpr int kStage = kBN * kRow;
+
+// 16-bit element j (0..7) of a 128-bit register
+__device__ __forceinline__ uint32_t half_of(const u32x4& v, int j) {
+  const uint32_t w = v[j >> 1];
+  return (j & 1) ? (w >> 16) : (w & 0xffffu);
+}
+
+template <typename T>
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  return (uint32_t)bits16(from_f32<T>(a)) | ((uint32_t)bits16(from_f32<T>(b)) << 16);
+}
+
+template <typename T, bool CAUSAL>
+__global__ __launch_bounds__(256) void attn_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K,
+                                                       const T* __restrict__ V, T* __restrict__ O, int S, int H,
+                                                       float scale_log2) {
+  __shared__ __attribute__((aligned(1024))) char sK0[kStage];
+  __shared__ __attribute__((aligned(1024))) char sK1[kStage];
+  __shared__ __attribute__((aligned(1024))) char sV0[kStage];
+  __shared__ __attribute__((aligned(1024))) char sV1[kStage];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int il = lane & 31, h = lane >> 5;
+  const int q0 = blockIdx.x * kBM, hd = blockIdx.y, b = blockIdx.z;
+  const int64_t rs = (int64_t)H * kD;  // elements between consecutive sequence positions
+  const int64_t base = ((int64_t)b * S * H + hd) * kD;
+  const int qi = q0 + wave * 32 + il;  // this lane's query
+
+  // Q fragments of this lane's query: d = 16 kk + 8 h .. + 7
+  u32x4 qf[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) qf[kk] = *(const u32x4*)(Q + base + qi * rs + 16 * kk + 8 * h);
+  // pass them through an empty asm here, so that the wait for these loads
+  // is placed before the key loop and not, conservatively, inside it (where
+  // it would also wait for the next block's loads)
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) asm volatile("" : "+v"(qf[kk]));
+
+  // K: direct loads, 8 wave instructions of 1 KiB per block (2 per wave);
+  // instruction t fills rows 8 t .. 8 t + 7, lane L row 8 t + L / 8 at chunk
+  // position L % 8, which holds logical chunk (L % 8) ^ swz(row)
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + base, (uint32_t)(((int64_t)(S - 1) * rs + kD) * 2));
+  uint32_t kvoff[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int row = 8 * (2 * wave + u) + (lane >> 3);
+    kvoff[u] = (uint32_t)(row * rs * 2 + (((lane & 7) ^ swz(row)) << 4));
+  }
+  auto load_k = [&](char* st, int kb) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr)(st + (2 * wave + u) * 1024), 16, kvoff[u],
+                                               (uint32_t)((int64_t)kb * kBN * rs * 2), 0, 0);
+  };
+
+  // V: thread (ng, kg) loads keys 2 kg, 2 kg + 1, d = 8 ng .. + 7 and writes
+  // V^T rows d at keys 2 kg, 2 kg + 1
+  const int ng = tid & 7, kg = tid >> 3;
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + base, (uint32_t)(((int64_t)(S - 1) * rs + kD) * 2));
+  const uint32_t vvoff = (uint32_t)((2 * kg) * rs * 2 + ng * 16);
+  u32x4 vr[2];
+  auto load_v = [&](int kb) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) vr[u] = load16(rv, vvoff, (uint32_t)(((int64_t)kb * kBN + u) * rs * 2));
+  };
+  auto store_v = [&](char* st) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int d = 8 * ng + j;
+      *(uint32_t*)(st + d * kRow + (((kg >> 2) ^ swz(d)) << 4) + 4 * (kg & 3)) =
+          half_of(vr[0], j) | (half_of(vr[1], j) << 16);
+    }
+  };
+
+  // MFMA operand read offsets.  S^T: lane (r, h) reads key row kappa(r) of
+  // group g, chunk 2 kk + h.  O^T: lane (r, h) reads V^T row 32 dt + r,
+  // chunk 4 g + 2 t + h.
+  const int kr = (il & 0x13) | ((il & 4) << 1) | ((il & 8) >> 1);  // kappa: swap bits 2 and 3
+  auto k_off = [&](int g, int kk) __attribute__((always_inline)) {
+    const int row = 32 * g + kr;
+    return row * kRow + (((2 * kk + h) ^ swz(row)) << 4);
+  };
+  auto v_off = [&](int dt, int g, int t) __attribute__((always_inline)) {
+    const int row = 32 * dt + il;
+    return row * kRow + (((4 * g + 2 * t + h) ^ swz(row)) << 4);
+  };
+
+  f32x16 acc_o[2] = {f32x16{}, f32x16{}};
+  float m_run = -__builtin_inff();  // running maximum of the raw scores
+  float l_run = 0.0f;               // this half's running sum of exp
+
+  const int nblk = CAUSAL ? (q0 + kBM) / kBN : S / kBN;
+
+  auto block = [&](int kb, const char* sk, const char* sv) __attribute__((always_inline)) {
+    // S^T for the two 32-key groups
+    f32x16 s[2];
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      s[g] = f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) s[g] = mfma32<T>(*(const u32x4*)(sk + k_off(g, kk)), qf[kk], s[g]);
+    }
+    // causal: keys after the query count as -inf
+    if constexpr (CAUSAL) {
+      if (kb * kBN + kBN - 1 > q0 + wave * 32) {
+#pragma unroll
+        for (int g = 0; g < 2; ++g)
+#pragma unroll
+          for (int x = 0; x < 16; ++x) {
+            const int q = x >> 2, e = x & 3;
+            const int key = kb * kBN + 32 * g + 16 * (q >> 1) + 8 * h + 4 * (q & 1) + e;
+            if (key > qi) s[g][x] = -__builtin_inff();
+          }
+      }
+    }
+    // block maximum over the query's 64 scores (32 here, 32 in lane ^ 32)
+    float mx = s[0][0];
+#pragma unroll
+    for (int x = 1; x < 16; ++x) mx = fmaxf(mx, s[0][x]);
+#pragma unroll
+    for (int x = 0; x < 16; ++x) mx = fmaxf(mx, s[1][x]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * scale_log2);
+    const float moff = m_new * scale_log2;
+    m_run = m_new;
+    float psum = 0.0f;
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int x = 0; x < 16; ++x) {
+        s[g][x] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[g][x], scale_log2, -moff));
+        psum += s[g][x];
+      }
+    l_run = l_run * alpha + psum;
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt) acc_o[dt] *= alpha;
+    // O^T += V^T P^T, 16 keys at a time
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        u32x4 p;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) p[w] = pack2<T>(s[g][8 * t + 2 * w], s[g][8 * t + 2 * w + 1]);
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt) acc_o[dt] = mfma32<T>(*(const u32x4*)(sv + v_off(dt, g, t)), p, acc_o[dt]);
+      }
+  };
+
+  auto barrier = [&]() __attribute__((always_inline)) {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0);  // vmcnt(0) expcnt(0) lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+
+  // block kb lives in stage kb % 2
+  load_k(sK0, 0);
+  load_v(0);
+  store_v(sV0);
+  barrier();
+  auto step = [&](int kb, const char* sk, const char* sv, char* nk, char* nv) __attribute__((always_inline)) {
+    const bool more = kb + 1 < nblk;
+    if (more) {
+      load_k(nk, kb + 1);
+      load_v(kb + 1);
+    }
+    block(kb, sk, sv);
+    if (more) store_v(nv);
+    barrier();
+  };
+  for (int kb = 0; kb < nblk; kb += 2) {
+    step(kb, sK0, sV0, sK1, sV1);
+    if (kb + 1 < nblk) step(kb + 1, sK1, sV1, sK0, sV0);
+  }
+
+  // O = o / l, both halves' sums combined; lane (i, h) writes d = 32 dt +
+  // 8 q + 4 h .. + 3 of its query
+  const float inv = 1.0f / (l_run + __shfl_xor(l_run, 32));
+  T* orow = O + base + qi * rs;
+#pragma unroll
+  for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      u32x2 w;
+      w.x = pack2<T>(acc_o[dt][4 * q] * inv, acc_o[dt][4 * q + 1] * inv);
+      w.y = pack2<T>(acc_o[dt][4 * q + 2] * inv, acc_o[dt][4 * q + 3] * inv);
+      *(u32x2*)(orow + 32 * dt + 8 * q + 4 * h) = w;
+    }
+}
+
+template <typename T, bool CAUSAL>
+hipError_t launch(const void* Q, const void* K, const void* V, void* O, int B, int S, int H, hipStream_t stream) {
+  const float scale_log2 = (float)(1.4426950408889634 / 8.0);  // log2(e) / sqrt(64)
+  hipLaunchKernelGGL((attn_fwd_kernel<T, CAUSAL>), dim3(S / kBM, H, B), dim3(256), 0, stream, (const T*)Q,
+                     (const T*)K, (const T*)V, (T*)O, S, H, scale_log2);
+  return hipGetLastError();
+}
+
+}  // namespace attn
+}  // namespace ge
+
+extern "C" gemm_epi_status gemm_epi_attention_fwd(const void* Q, const void* K, const void* V, void* O, int64_t B,
+                                                   int64_t S, int64_t H, int64_t D, gemm_epi_dtype dtype, int causal,
+                                                   void* stream) {
+  if (!Q || !K || !V || !O || B <= 0 || S <= 0 || H <= 0 || D <= 0) return GEMM_EPI_ERR_INVALID_ARG;
+  if (dtype != GEMM_EPI_F16 && dtype != GEMM_EPI_BF16) return GEMM_EPI_ERR_INVALID_ARG;
+  const int64_t n = B * S * H * D;
+  if (D != ge::attn::kD || S % ge::attn::kBM != 0 || n >= ((int64_t)1 << 31) || S / ge::attn::kBM > 65535 ||
+      H > 65535 || B > 65535)
+    return GEMM_EPI_ERR_UNSUPPORTED;
+  for (const void* p : {Q, K, V, (const void*)O})
+    if (((uintptr_t)p & 15u) != 0) return GEMM_EPI_ERR_UNSUPPORTED;
+  const hipStream_t s = (hipStream_t)stream;
+  hipError_t e;
+  if (dtype == GEMM_EPI_F16)
+    e = causal ? ge::attn::launch<ge::f16, true>(Q, K, V, O, (int)B, (int)S, (int)H, s)
+               : ge::attn::launch<ge::f16, false>(Q, K, V, O, (int)B, (int)S, (int)H, s);
+  else
+    e = causal ? ge::attn::launch<ge::bf16, true>(Q, K, V, O, (int)B, (int)S, (int)H, s)
+               : ge::attn::launch<ge::bf16, false>(Q, K, V, O, (int)B, (int)S, (int)H, s);
+  return e == hipSuccess ? GEMM_EPI_OK : GEMM_EPI_ERR_HIP;
+}

@@ -251,6 +251,26 @@ void gemm_epi_tuning_clear(void);
 /* Number of entries in the tuning table. */
 int gemm_epi_tuning_size(void);
 
+/* gemm_epi_attention_fwd -- enqueue scaled dot-product attention forward,
+ *
+ *     O[b, i, h, :] = sum_j softmax_j(Q[b, i, h, :] . K[b, j, h, :] / sqrt(D)) V[b, j, h, :]
+ *
+ * on `stream` and return without synchronising.  Q, K, V, O are device
+ * arrays laid out [B, S, H, D] (D contiguous) in the input format `dtype`
+ * (F16 or BF16), caller-owned; O must not overlap the others.  causal != 0
+ * lets query i see keys j <= i only.  fp32 scores and accumulation, an
+ * online softmax over blocks of 64 keys, probabilities rounded to `dtype`
+ * for the second product, O rounded once.  (Scaled dot-product attention
+ * and its blocked form with an online softmax: csdn "从零开始学习 TileLang",
+ * ch.13 "FlashAttention", sec. 13.1, 13.6-13.8; layout, causal rule and the
+ * B, H, S, D = 4, 8, 1024, 64 example: ainew.jp "TileLang で GPU カーネル設計を
+ * 解説", section 6.)
+ * Errors: INVALID_ARG (a NULL pointer, B/S/H/D <= 0, dtype not F16/BF16),
+ * UNSUPPORTED (D != 64, S not a multiple of 128, B*S*H*D >= 2^31, a pointer
+ * not 16-byte aligned), HIP (the launch failed). */
+gemm_epi_status gemm_epi_attention_fwd(const void* Q, const void* K, const void* V, void* O, int64_t B, int64_t S,
+                                       int64_t H, int64_t D, gemm_epi_dtype dtype, int causal, void* stream);
+
 /* gemm_epi_destroy -- free the host plan object.  NULL is a no-op (OK).
  * No device synchronisation: runs already enqueued are unaffected. */
 gemm_epi_status gemm_epi_destroy(gemm_epi_plan_t plan);

@@ -355,3 +355,14 @@ def test_plan_set_ld_validates_and_reselects(lib):
         assert gb.gemm_epi_plan_describe(h)[0] == "tile"
     finally:
         gb.gemm_epi_destroy(h)
+
+
+def test_attention_validates_without_touching_the_device(lib):
+    p = 0x10000
+    assert gb.gemm_epi_attention_fwd(None, p, p, p, 1, 128, 1, 64, "f16", 0, None) == 1
+    assert gb.gemm_epi_attention_fwd(p, p, p, p, 0, 128, 1, 64, "f16", 0, None) == 1
+    assert gb.gemm_epi_attention_fwd(p, p, p, p, 1, 128, 1, 64, "fp8", 0, None) == 1
+    assert gb.gemm_epi_attention_fwd(p, p, p, p, 1, 128, 1, 128, "bf16", 1, None) == 2  # D = 128
+    assert gb.gemm_epi_attention_fwd(p, p, p, p, 1, 192, 1, 64, "bf16", 1, None) == 2  # S % 128
+    assert gb.gemm_epi_attention_fwd(p + 8, p, p, p, 1, 128, 1, 64, "bf16", 1, None) == 2  # alignment
+    assert gb.gemm_epi_attention_fwd(p, p, p, p, 1 << 12, 1 << 12, 1 << 4, 64, "bf16", 0, None) == 2  # 2^34 elements

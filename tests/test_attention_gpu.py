@@ -1,0 +1,106 @@
+"""Parity of the attention forward kernel (gemm_epi_attention_fwd, through
+the C ABI) with the fp64 oracle, on seeded N(0, 1) inputs laid out
+[B, S, H, D]: small shapes in full, the B, H, S, D = 4, 8, 1024, 64
+workloads on sampled query rows, and closed-form cases."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from epilogue_gemm_amd import binding as gb
+from epilogue_gemm_amd import inputs
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+# Tolerance (after output rounding; see tests/parity.py for the tie rule):
+# the kernel rounds the probabilities to the input format before the second
+# product (relative error <= 2^-11 for fp16, 2^-8 for bf16 per weight), so
+# the bar is the format's: rel-Fro 2e-3 / max-abs 2e-2 for fp16 and
+# 1e-2 / 3e-2 for bf16.
+TOL = {"f16": (2e-3, 2e-2), "bf16": (1e-2, 3e-2)}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    gb.load_library()
+
+
+def run_gpu(d, B, S, H, D, dtype, causal):
+    q, k, v = (parity.to_device(d[n], dtype).view(B, S, H, D) for n in ("Q", "K", "V"))
+    o = torch.full_like(q, float("nan"))
+    gb.attention_fwd(q, k, v, o, causal=causal)
+    torch.cuda.synchronize()
+    return parity.out_bits(o).reshape(B, S, H, D)
+
+
+def check(got, y, o, dtype, what):
+    rel, ab = TOL[dtype]
+    r = parity.compare(got.reshape(-1), o.reshape(-1), y.reshape(-1), dtype, rel_tol=rel, abs_tol=ab)
+    assert r["ok"], f"{what}: {r}"
+    return r
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("B,S,H", [(1, 128, 1), (2, 384, 3), (1, 640, 2)])
+def test_attention_small_full_parity(dtype, causal, B, S, H):
+    D = 64
+    d = inputs.attention_inputs(B, S, H, D, dtype, seed=S + H)
+    got = run_gpu(d, B, S, H, D, dtype, causal)
+    y, o = oracle.attention(d["Q"], d["K"], d["V"], B, S, H, D, dtype, causal)
+    r = check(got, y, o, dtype, f"B{B} S{S} H{H} {dtype} causal={causal}")
+    print(f"attention {dtype} causal={causal} B{B} S{S} H{H}: rel_fro={r['rel_fro']:.2e} max_abs={r['max_abs']:.2e}")
+
+
+@pytest.mark.parametrize("name", list(inputs.ATTENTION_WORKLOADS))
+def test_attention_workload_sampled_rows(name):
+    w = inputs.ATTENTION_WORKLOADS[name]
+    d = inputs.attention_inputs(w.B, w.S, w.H, w.D, w.dtype, w.seed)
+    got = run_gpu(d, w.B, w.S, w.H, w.D, w.dtype, w.causal)
+    rng = np.random.default_rng(w.seed)
+    n = 1024
+    rb, ri, rh = rng.integers(0, w.B, n), rng.integers(0, w.S, n), rng.integers(0, w.H, n)
+    # plus every query of one (batch, head), first and last rows included
+    rb = np.concatenate([rb, np.full(w.S, w.B - 1)])
+    ri = np.concatenate([ri, np.arange(w.S)])
+    rh = np.concatenate([rh, np.full(w.S, w.H // 2)])
+    y, o = oracle.attention(d["Q"], d["K"], d["V"], w.B, w.S, w.H, w.D, w.dtype, w.causal, rows=(rb, ri, rh))
+    r = check(got[rb, ri, rh], y, o, w.dtype, name)
+    print(f"{name}: rel_fro={r['rel_fro']:.2e} max_abs={r['max_abs']:.2e} on {rb.size} rows")
+
+
+def test_attention_closed_forms():
+    B, S, H, D, dtype = 1, 256, 2, 64, "f16"
+    d = inputs.attention_inputs(B, S, H, D, dtype, seed=1)
+    # every value row the same vector: O is that vector (exactly, up to the
+    # sum of the rounded weights)
+    row = np.linspace(-2.0, 2.0, D)
+    vconst = oracle.encode_array(dtype, np.broadcast_to(row, (B, S, H, D)).reshape(-1)).astype(np.uint16)
+    for causal in (False, True):
+        got = run_gpu({**d, "V": vconst}, B, S, H, D, dtype, causal)
+        y, o = oracle.attention(d["Q"], d["K"], vconst, B, S, H, D, dtype, causal)
+        check(got, y, o, dtype, f"constant V causal={causal}")
+    # causal query 0 sees key 0 only: O[0] = V[0] bit for bit
+    got = run_gpu(d, B, S, H, D, dtype, True)
+    assert np.array_equal(got[:, 0], d["V"].reshape(B, S, H, D)[:, 0])
+    # Q = 0: uniform weights (the mean of the visible values)
+    zq = np.zeros_like(d["Q"])
+    for causal in (False, True):
+        got = run_gpu({**d, "Q": zq}, B, S, H, D, dtype, causal)
+        y, o = oracle.attention(zq, d["K"], d["V"], B, S, H, D, dtype, causal)
+        check(got, y, o, dtype, f"Q = 0 causal={causal}")
+
+
+def test_attention_rejects_unsupported():
+    B, S, H = 1, 128, 1
+    t = torch.zeros(B * S * H * 64 + 8, dtype=torch.float16, device="cuda")
+    p = t.data_ptr()
+    st = torch.cuda.current_stream().cuda_stream
+    assert gb.gemm_epi_attention_fwd(p, p, p, p, B, S, H, 32, "f16", 0, st) == 2  # D != 64
+    assert gb.gemm_epi_attention_fwd(p, p, p, p, B, 100, H, 64, "f16", 0, st) == 2  # S % 128
+    assert gb.gemm_epi_attention_fwd(p + 2, p, p, p, B, S, H, 64, "f16", 0, st) == 2  # unaligned
+    assert gb.gemm_epi_attention_fwd(None, p, p, p, B, S, H, 64, "f16", 0, st) == 1
+    assert gb.gemm_epi_attention_fwd(p, p, p, p, B, S, H, 64, "f32", 0, st) == 1
