@@ -11,7 +11,8 @@
 // GPU カーネル設計を解説", section 6).  Scores are scaled by log2(e) / sqrt(D)
 // so that exp is the hardware exp2 (sec. 9.6 of the same tutorial).
 //
-// gfx950 layout.  Each wave owns 32 queries and every product is a
+// gfx950 layout.  Each wave owns 32 queries (and every other key block:
+// two waves per query group, see the kernel) and every product is a
 // v_mfma_f32_32x32x16 chain arranged so that no data crosses lanes except
 // one max exchange per key block:
 //   * S^T = K Q^T: first operand K (key rows from LDS), second Q (registers);
@@ -59,21 +60,28 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
 }
 
 template <typename T, bool CAUSAL>
-__global__ __launch_bounds__(256) void attn_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K,
+__global__ __launch_bounds__(512) void attn_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                                                        const T* __restrict__ V, T* __restrict__ O, int S, int H,
                                                        float scale_log2) {
-  __shared__ __attribute__((aligned(1024))) char sK0[kStage];
-  __shared__ __attribute__((aligned(1024))) char sK1[kStage];
-  __shared__ __attribute__((aligned(1024))) char sV0[kStage];
-  __shared__ __attribute__((aligned(1024))) char sV1[kStage];
+  // Two buffers of K and of V^T, each holding one block per key parity.
+  __shared__ __attribute__((aligned(1024))) char sK0[2 * kStage];
+  __shared__ __attribute__((aligned(1024))) char sK1[2 * kStage];
+  __shared__ __attribute__((aligned(1024))) char sV0[2 * kStage];
+  __shared__ __attribute__((aligned(1024))) char sV1[2 * kStage];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // 8 waves: query group qg (32 queries) x key parity kp.  The two waves of
+  // a query group take alternate key blocks -- two waves per SIMD, so one
+  // can multiply while the other computes its softmax -- and merge their
+  // partial results at the end.
+  const int qg = wave & 3, kp = wave >> 2;
+  const int pt = tid & 255;  // thread index within the parity's four waves
   const int il = lane & 31, h = lane >> 5;
   const int q0 = blockIdx.x * kBM, hd = blockIdx.y, b = blockIdx.z;
   const int64_t rs = (int64_t)H * kD;  // elements between consecutive sequence positions
   const int64_t base = ((int64_t)b * S * H + hd) * kD;
-  const int qi = q0 + wave * 32 + il;  // this lane's query
+  const int qi = q0 + qg * 32 + il;  // this lane's query
 
   // Q fragments of this lane's query: d = 16 kk + 8 h .. + 7
   u32x4 qf[4];
@@ -85,26 +93,27 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const T* __restrict__ Q, 
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) asm volatile("" : "+v"(qf[kk]));
 
-  // K: direct loads, 8 wave instructions of 1 KiB per block (2 per wave);
-  // instruction t fills rows 8 t .. 8 t + 7, lane L row 8 t + L / 8 at chunk
-  // position L % 8, which holds logical chunk (L % 8) ^ swz(row)
+  // K: direct loads, 8 wave instructions of 1 KiB per block, 2 per wave of
+  // the parity; instruction t fills rows 8 t .. 8 t + 7, lane L row
+  // 8 t + L / 8 at chunk position L % 8, which holds logical chunk
+  // (L % 8) ^ swz(row)
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + base, (uint32_t)(((int64_t)(S - 1) * rs + kD) * 2));
   uint32_t kvoff[2];
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    const int row = 8 * (2 * wave + u) + (lane >> 3);
+    const int row = 8 * (2 * qg + u) + (lane >> 3);
     kvoff[u] = (uint32_t)(row * rs * 2 + (((lane & 7) ^ swz(row)) << 4));
   }
   auto load_k = [&](char* st, int kb) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < 2; ++u)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr)(st + (2 * wave + u) * 1024), 16, kvoff[u],
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr)(st + (2 * qg + u) * 1024), 16, kvoff[u],
                                                (uint32_t)((int64_t)kb * kBN * rs * 2), 0, 0);
   };
 
-  // V: thread (ng, kg) loads keys 2 kg, 2 kg + 1, d = 8 ng .. + 7 and writes
-  // V^T rows d at keys 2 kg, 2 kg + 1
-  const int ng = tid & 7, kg = tid >> 3;
+  // V: thread (ng, kg) of the parity loads keys 2 kg, 2 kg + 1, d = 8 ng .. + 7
+  // and writes V^T rows d at keys 2 kg, 2 kg + 1
+  const int ng = pt & 7, kg = pt >> 3;
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + base, (uint32_t)(((int64_t)(S - 1) * rs + kD) * 2));
   const uint32_t vvoff = (uint32_t)((2 * kg) * rs * 2 + ng * 16);
   u32x4 vr[2];
@@ -138,7 +147,7 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const T* __restrict__ Q, 
   float m_run = -__builtin_inff();  // running maximum of the raw scores
   float l_run = 0.0f;               // this half's running sum of exp
 
-  const int nblk = CAUSAL ? (q0 + kBM) / kBN : S / kBN;
+  const int nblk = CAUSAL ? (q0 + kBM) / kBN : S / kBN;  // >= 2: each parity has a block
 
   auto block = [&](int kb, const char* sk, const char* sv) __attribute__((always_inline)) {
     // S^T for the two 32-key groups
@@ -151,7 +160,7 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const T* __restrict__ Q, 
     }
     // causal: keys after the query count as -inf
     if constexpr (CAUSAL) {
-      if (kb * kBN + kBN - 1 > q0 + wave * 32) {
+      if (kb * kBN + kBN - 1 > q0 + qg * 32) {
 #pragma unroll
         for (int g = 0; g < 2; ++g)
 #pragma unroll
@@ -170,8 +179,12 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const T* __restrict__ Q, 
     for (int x = 0; x < 16; ++x) mx = fmaxf(mx, s[1][x]);
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float m_new = fmaxf(m_run, mx);
-    const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * scale_log2);
-    const float moff = m_new * scale_log2;
+    // (a causal query group can meet only masked keys in its parity's first
+    // blocks: m stays -inf, and the reference point 0 keeps exp2 away from
+    // inf - inf)
+    const float m_ref = m_new == -__builtin_inff() ? 0.0f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f((m_run - m_ref) * scale_log2);
+    const float moff = m_ref * scale_log2;
     m_run = m_new;
     float psum = 0.0f;
 #pragma unroll
@@ -182,8 +195,11 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const T* __restrict__ Q, 
         psum += s[g][x];
       }
     l_run = l_run * alpha + psum;
+    // the rescale only when some lane's maximum grew (alpha < 1)
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
 #pragma unroll
-    for (int dt = 0; dt < 2; ++dt) acc_o[dt] *= alpha;
+      for (int dt = 0; dt < 2; ++dt) acc_o[dt] *= alpha;
+    }
     // O^T += V^T P^T, 16 keys at a time
 #pragma unroll
     for (int g = 0; g < 2; ++g)
@@ -204,45 +220,77 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const T* __restrict__ Q, 
     asm volatile("" ::: "memory");
   };
 
-  // block kb lives in stage kb % 2
-  load_k(sK0, 0);
-  load_v(0);
-  store_v(sV0);
+  // Iteration it: parity kp multiplies block 2 it + kp from buffer it % 2
+  // while it loads block 2 it + 2 + kp into the other buffer.
+  const int poff = kp * kStage;
+  load_k(sK0 + poff, kp);
+  load_v(kp);
+  store_v(sV0 + poff);
   barrier();
-  auto step = [&](int kb, const char* sk, const char* sv, char* nk, char* nv) __attribute__((always_inline)) {
-    const bool more = kb + 1 < nblk;
+  const int niter = (nblk + 1) / 2;
+  auto step = [&](int it, const char* ck, const char* cv, char* nk, char* nv) __attribute__((always_inline)) {
+    const int kb = 2 * it + kp, nkb = kb + 2;
+    const bool more = nkb < nblk;
     if (more) {
-      load_k(nk, kb + 1);
-      load_v(kb + 1);
+      load_k(nk + poff, nkb);
+      load_v(nkb);
     }
-    block(kb, sk, sv);
-    if (more) store_v(nv);
+    if (kb < nblk) block(kb, ck + poff, cv + poff);
+    if (more) store_v(nv + poff);
     barrier();
   };
-  for (int kb = 0; kb < nblk; kb += 2) {
-    step(kb, sK0, sV0, sK1, sV1);
-    if (kb + 1 < nblk) step(kb + 1, sK1, sV1, sK0, sV0);
+  for (int it = 0; it < niter; it += 2) {
+    step(it, sK0, sV0, sK1, sV1);
+    if (it + 1 < niter) step(it + 1, sK1, sV1, sK0, sV0);
   }
 
+  // Merge the two parities of each query group: parity 1 leaves (m, l, o)
+  // in LDS (the stages are free after the last barrier), parity 0 combines
+  // o = a0 o0 + a1 o1 and l = a0 l0 + a1 l1 with a = exp(m_p - max m).
+  float* xo0 = (float*)sV0 + qg * 16 * 64;  // o of d-tile 0: [qg][x][lane]
+  float* xo1 = (float*)sV1 + qg * 16 * 64;  // o of d-tile 1
+  float* xm = (float*)sK0 + qg * 2 * 64;    // m, l: [qg][2][lane]
+  if (kp == 1) {
+#pragma unroll
+    for (int x = 0; x < 16; ++x) {
+      xo0[x * 64 + lane] = acc_o[0][x];
+      xo1[x * 64 + lane] = acc_o[1][x];
+    }
+    xm[lane] = m_run;
+    xm[64 + lane] = l_run;
+  }
+  barrier();
+  if (kp == 1) return;
+  const float m1 = xm[lane], l1 = xm[64 + lane];
+  const float m = fmaxf(m_run, m1);
+  const float a0 = __builtin_amdgcn_exp2f((m_run - m) * scale_log2);
+  const float a1 = __builtin_amdgcn_exp2f((m1 - m) * scale_log2);
+  const float lh = a0 * l_run + a1 * l1;
   // O = o / l, both halves' sums combined; lane (i, h) writes d = 32 dt +
   // 8 q + 4 h .. + 3 of its query
-  const float inv = 1.0f / (l_run + __shfl_xor(l_run, 32));
+  const float inv = 1.0f / (lh + __shfl_xor(lh, 32));
+  const float c0 = a0 * inv, c1 = a1 * inv;
   T* orow = O + base + qi * rs;
 #pragma unroll
-  for (int dt = 0; dt < 2; ++dt)
+  for (int dt = 0; dt < 2; ++dt) {
+    const float* xo = dt == 0 ? xo0 : xo1;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = acc_o[dt][4 * q + e] * c0 + xo[(4 * q + e) * 64 + lane] * c1;
       u32x2 w;
-      w.x = pack2<T>(acc_o[dt][4 * q] * inv, acc_o[dt][4 * q + 1] * inv);
-      w.y = pack2<T>(acc_o[dt][4 * q + 2] * inv, acc_o[dt][4 * q + 3] * inv);
+      w.x = pack2<T>(v[0], v[1]);
+      w.y = pack2<T>(v[2], v[3]);
       *(u32x2*)(orow + 32 * dt + 8 * q + 4 * h) = w;
     }
+  }
 }
 
 template <typename T, bool CAUSAL>
 hipError_t launch(const void* Q, const void* K, const void* V, void* O, int B, int S, int H, hipStream_t stream) {
   const float scale_log2 = (float)(1.4426950408889634 / 8.0);  // log2(e) / sqrt(64)
-  hipLaunchKernelGGL((attn_fwd_kernel<T, CAUSAL>), dim3(S / kBM, H, B), dim3(256), 0, stream, (const T*)Q,
+  hipLaunchKernelGGL((attn_fwd_kernel<T, CAUSAL>), dim3(S / kBM, H, B), dim3(512), 0, stream, (const T*)Q,
                      (const T*)K, (const T*)V, (T*)O, S, H, scale_log2);
   return hipGetLastError();
 }
