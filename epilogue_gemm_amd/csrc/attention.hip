@@ -54,9 +54,22 @@ __device__ __forceinline__ uint32_t half_of(const u32x4& v, int j) {
   return (j & 1) ? (w >> 16) : (w & 0xffffu);
 }
 
+// a, b rounded to nearest even in T and packed (one v_cvt_pk_{f16,bf16}_f32)
 template <typename T>
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
-  return (uint32_t)bits16(from_f32<T>(a)) | ((uint32_t)bits16(from_f32<T>(b)) << 16);
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  typedef T t2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2){a, b}, t2));
+}
+
+// The value of x in lane l ^ 32.  v_permlane32_swap exchanges the upper
+// half of its first operand with the lower half of its second; with x in
+// both, the second result holds the partner's value in lanes 0..31 and the
+// first in lanes 32..63.
+__device__ __forceinline__ float partner32(float x, int upper) {
+  const uint32_t a = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(a, a, false, false);
+  return __builtin_bit_cast(float, upper ? r[0] : r[1]);
 }
 
 template <typename T, bool CAUSAL>
@@ -177,7 +190,7 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(const T* __restrict__ Q, 
     for (int x = 1; x < 16; ++x) mx = fmaxf(mx, s[0][x]);
 #pragma unroll
     for (int x = 0; x < 16; ++x) mx = fmaxf(mx, s[1][x]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = fmaxf(mx, partner32(mx, h));
     const float m_new = fmaxf(m_run, mx);
     // (a causal query group can meet only masked keys in its parity's first
     // blocks: m stays -inf, and the reference point 0 keeps exp2 away from
@@ -268,7 +281,7 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(const T* __restrict__ Q, 
   const float lh = a0 * l_run + a1 * l1;
   // O = o / l, both halves' sums combined; lane (i, h) writes d = 32 dt +
   // 8 q + 4 h .. + 3 of its query
-  const float inv = 1.0f / (lh + __shfl_xor(lh, 32));
+  const float inv = 1.0f / (lh + partner32(lh, h));
   const float c0 = a0 * inv, c1 = a1 * inv;
   T* orow = O + base + qi * rs;
 #pragma unroll
