@@ -55,6 +55,19 @@ __device__ __forceinline__ uint32_t half_of(const u32x4& v, int j) {
 }
 
 // a, b rounded to nearest even in T and packed (one v_cvt_pk_{f16,bf16}_f32)
+// a.x + a.y + acc for two packed 16-bit values (v_dot2c_f32_{f16,bf16} with
+// (1, 1)): the row sum of the rounded probabilities the MFMA multiplies
+template <typename T>
+__device__ __forceinline__ float add_pair(uint32_t a, float acc) {
+  if constexpr (__is_same(T, f16)) {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, a), (h2){(_Float16)1.0f, (_Float16)1.0f}, acc, false);
+  } else {
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2, a), __builtin_bit_cast(b2, 0x3f803f80u), acc, false);
+  }
+}
+
 template <typename T>
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
   typedef float f2 __attribute__((ext_vector_type(2)));
@@ -191,36 +204,37 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(const T* __restrict__ Q, 
 #pragma unroll
     for (int x = 0; x < 16; ++x) mx = fmaxf(mx, s[1][x]);
     mx = fmaxf(mx, partner32(mx, h));
-    const float m_new = fmaxf(m_run, mx);
-    // (a causal query group can meet only masked keys in its parity's first
-    // blocks: m stays -inf, and the reference point 0 keeps exp2 away from
-    // inf - inf)
-    const float m_ref = m_new == -__builtin_inff() ? 0.0f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f((m_run - m_ref) * scale_log2);
-    const float moff = m_ref * scale_log2;
-    m_run = m_new;
-    float psum = 0.0f;
-#pragma unroll
-    for (int g = 0; g < 2; ++g)
-#pragma unroll
-      for (int x = 0; x < 16; ++x) {
-        s[g][x] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[g][x], scale_log2, -moff));
-        psum += s[g][x];
-      }
-    l_run = l_run * alpha + psum;
-    // the rescale only when some lane's maximum grew (alpha < 1)
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+    // The reference point m_run moves only when a score exceeds it by more
+    // than 2^8 in probability (any lane of the wave): the probabilities
+    // then stay below 256, well inside the 16-bit formats, and the rescale
+    // of o and l (and its vector work) is skipped for most blocks.
+    if (__builtin_amdgcn_ballot_w64((mx - m_run) * scale_log2 > 8.0f)) {
+      const float m_new = fmaxf(m_run, mx);
+      // (a causal query group can meet only masked keys in its parity's
+      // first blocks: a lane whose m is still -inf keeps it, with alpha 1
+      // and o = l = 0, when another lane moves)
+      const float alpha = m_new == -__builtin_inff() ? 1.0f : __builtin_amdgcn_exp2f((m_run - m_new) * scale_log2);
+      m_run = m_new;
+      l_run *= alpha;
 #pragma unroll
       for (int dt = 0; dt < 2; ++dt) acc_o[dt] *= alpha;
     }
-    // O^T += V^T P^T, 16 keys at a time
+    const float moff = m_run == -__builtin_inff() ? 0.0f : m_run * scale_log2;
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int x = 0; x < 16; ++x) s[g][x] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[g][x], scale_log2, -moff));
+    // O^T += V^T P^T, 16 keys at a time; l += the rounded P's row sums
 #pragma unroll
     for (int g = 0; g < 2; ++g)
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         u32x4 p;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) p[w] = pack2<T>(s[g][8 * t + 2 * w], s[g][8 * t + 2 * w + 1]);
+        for (int w = 0; w < 4; ++w) {
+          p[w] = pack2<T>(s[g][8 * t + 2 * w], s[g][8 * t + 2 * w + 1]);
+          l_run = add_pair<T>(p[w], l_run);
+        }
 #pragma unroll
         for (int dt = 0; dt < 2; ++dt) acc_o[dt] = mfma32<T>(*(const u32x4*)(sv + v_off(dt, g, t)), p, acc_o[dt]);
       }
