@@ -15,10 +15,11 @@ namespace ge {
 // more; smaller ones give small problems enough workgroups for 256 CUs;
 // 8 waves put two on each SIMD so one can multiply while the other waits.
 static const TileConfig kTile[] = {
-    {256, 256, 4, "tile_256x256x64"},
-    {128, 128, 4, "tile_128x128x64"},
-    {64, 64, 4, "tile_64x64x64"},
-    {256, 256, 8, "tile_256x256x64_8w"},
+    {256, 256, 4, "tile_256x256x64", 32},
+    {128, 128, 4, "tile_128x128x64", 32},
+    {64, 64, 4, "tile_64x64x64", 32},
+    {256, 256, 8, "tile_256x256x64_8w", 32},
+    {256, 256, 4, "tile_256x256x64_m16", 16},
 };
 
 int tile_num_configs() { return (int)(sizeof(kTile) / sizeof(kTile[0])); }
@@ -32,8 +33,11 @@ bool tile_supports(int cfg, const Problem& p) {
   // E4M3 output; M % 8 when A is column-major; leading dimensions likewise),
   // and K a multiple of 8 (16-byte chunks) spanning at least two k-steps of
   // 64 (a partial one first, when K % 64 != 0).
+  // The 16x16x32 configuration takes k-contiguous operands only (A
+  // row-major, B column-major).
   const TileConfig& c = kTile[cfg];
   const int n_align = p.out_dt == GEMM_EPI_FP8_E4M3 ? 16 : 8;
+  if (c.mfma == 16 && (p.la != GEMM_EPI_ROW_MAJOR || p.lb != GEMM_EPI_COL_MAJOR)) return false;
   return p.M >= c.bm && p.N >= c.bn && p.N % n_align == 0 && (p.la == GEMM_EPI_ROW_MAJOR || p.M % 8 == 0) &&
          p.K % 8 == 0 && p.K > 64 && p.lda % 8 == 0 && p.ldb % 8 == 0 && p.ldc % n_align == 0;
 }
@@ -41,9 +45,10 @@ bool tile_supports(int cfg, const Problem& p) {
 int tile_choose(const Problem& p) {
   // Largest tile that still gives at least one workgroup per CU; else the
   // smallest tile that fits (most parallelism).  With both operands
-  // k-contiguous the 256 x 256 tile runs with 8 waves (measured about 1 %
-  // faster at 8192^3); a register-staged operand keeps 4 (8 waves measured
-  // 12 % slower at 4096^3 with B row-major).
+  // k-contiguous the 256 x 256 tile runs on 16x16x32 MFMAs with 4 waves
+  // (8192^3 bf16: 759 us against 829 us for 8 waves on 32x32x16); a
+  // register-staged operand keeps the 4-wave 32x32x16 kernel (8 waves
+  // measured 12 % slower at 4096^3 with B row-major).
   const bool direct = p.la == GEMM_EPI_ROW_MAJOR && p.lb == GEMM_EPI_COL_MAJOR;
   int fallback = -1;
   for (int c = 0; c < 3; ++c) {
@@ -55,7 +60,7 @@ int tile_choose(const Problem& p) {
     }
     fallback = c;
   }
-  return fallback == 0 && direct ? 3 : fallback;
+  return fallback == 0 && direct ? 4 : fallback;
 }
 
 LaunchFn tile_launcher(int cfg, const Problem& p) {

@@ -1,0 +1,324 @@
+// gemm_tile16.hpp -- the 256x256 tile kernel of gemm_tile.hpp built on
+// v_mfma_f32_16x16x32_{f16,bf16} with four waves, for k-contiguous operands
+// (A row-major, B column-major).
+//
+// Why 16x16x32.  A 32x32x16 MFMA reads and rewrites 16 fp32 accumulators per
+// lane for 32 768 FLOP; a 16x16x32 one reads and rewrites 4 for 16 384 FLOP,
+// so per FLOP it moves half the accumulator bytes through the register file
+// (the operands cost the same per FLOP).  The large squares run at the
+// chip's power limit, where the clock follows the energy spent per FLOP.
+// With four waves (one per SIMD, 128x128 each) the fragments of both
+// operands are double-buffered in the 256 architectural registers next to
+// the 256 accumulator registers, and each LDS byte read feeds 128 MACs.
+//
+// The LDS layout, the direct global->LDS copies (with the K-tail shift), the
+// swizzle, the raster and the two-stage pipeline are those of gemm_tile.hpp;
+// a 64-deep k-step is two substeps of k = 32:
+//   substep 0   multiply k 0..31 of tile kt, read k 32..63 of it;
+//   barrier     after this wave's copies of tile kt + 1 have landed: every
+//               wave is done reading tile kt's stage, tile kt + 1 is whole;
+//   substep 1   multiply k 32..63, read k 0..31 of tile kt + 1, and copy
+//               tile kt + 2 into the stage tile kt leaves, one copy every
+//               four MFMAs.
+// Fragment f (A or B) of substep kk: rows w0 + 16 f + lane % 16, logical
+// 16-byte chunk 4 kk + lane / 16; 16 consecutive rows at one chunk fall on
+// 16 distinct bank groups under the swizzle.  With B's fragment as the first
+// operand the 16x16 result arrives transposed: lane l holds
+// C[m = l % 16][n = 4 (l / 16) + e], e = 0..3 -- four consecutive columns of
+// one row.  (Tile-level fusion of load -> GEMM -> epilogue -> store:
+// TileFusion "基础GEMM示例"; epilogue on the accumulator fragment: csdn
+// "从零开始学习 TileLang" ch.10 sec. 10.8; pipelining and rasterisation:
+// atlascloud.ai "Writing high-performance kernels in TileLang", section
+// "Écrivons un GEMM".)
+#pragma once
+
+#include "gemm_tile.hpp"
+
+namespace ge {
+namespace tile16 {
+
+using tile::DirectLoader;
+using tile::kBK;
+using tile::kRowBytes;
+
+template <typename TIn>
+__device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
+  if constexpr (__is_same(TIn, f16))
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
+                                                   0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                    0, 0, 0);
+}
+
+// Epilogue of one wave's WM x WN sub-tile from 16x16 blocks, as
+// tile::write_tile: bias, optional column scale, activation, optional
+// residual and output scale on the accumulators, conversion, then each
+// 16-row band through a private LDS staging area (16-byte chunks swizzled by
+// row) and out with 16-byte stores along rows.
+template <int WM, int WN, typename TIn, typename TOut, int EPI, bool EXTRAS>
+__device__ __forceinline__ void write_tile16(const f32x4 (&acc)[WM / 16][WN / 16], const TIn* __restrict__ bias,
+                                            TOut* __restrict__ C, int ldc, int m_w, int n_w, int lane, char* stage,
+                                            const float* __restrict__ scale, const TOut* __restrict__ res,
+                                            const float* __restrict__ out_scale) {
+  constexpr int TM = WM / 16, TN = WN / 16;
+  constexpr int OSZ = (int)sizeof(TOut);
+  constexpr int CPR = WN * OSZ / 16;              // 16-byte chunks per staged row
+  constexpr int SWM = (CPR < 16 ? CPR : 16) - 1;  // swizzle mask
+  constexpr int RPI = 64 / CPR;                   // rows per store instruction
+  const int m_l = lane & 15, g = lane >> 4;
+  const bool has_os = EXTRAS && out_scale != nullptr;
+  const float os = has_os ? *out_scale : 1.0f;
+
+  // bias of this lane's four columns in each 16-column block
+  u32x2 bq[TN];
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    if constexpr (epi_has_bias<EPI>()) bq[j] = *(const u32x2*)(bias + n_w + j * 16 + 4 * g);
+    else bq[j] = u32x2{0u, 0u};
+  }
+
+  static_for<TM>([&](auto i_c) __attribute__((always_inline)) {
+    constexpr int i = decltype(i_c)::value;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int col = n_w + j * 16 + 4 * g;
+      f32x4 sc = f32x4{1.0f, 1.0f, 1.0f, 1.0f}, r = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      if constexpr (EXTRAS) {
+        if (scale) sc = *(const f32x4*)(scale + col);
+        if (res) r = load4<TOut>(res + (int64_t)(m_w + i * 16 + m_l) * ldc + col);
+      }
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float b = 0.0f;
+        if constexpr (epi_has_bias<EPI>()) {
+          const uint32_t w = bq[j][e >> 1];
+          b = to_f32(__builtin_bit_cast(TIn, (uint16_t)((e & 1) ? (w >> 16) : (w & 0xffffu))));
+        }
+        v[e] = epilogue_ex<EPI>(acc[i][j][e], b, EXTRAS && scale != nullptr, sc[e], EXTRAS && res != nullptr, r[e],
+                                has_os, os);
+      }
+      // columns j*16 + 4g .. +3 of row m_l
+      if constexpr (OSZ == 1) {
+        *(uint32_t*)(stage + m_l * WN + ((j ^ (m_l & SWM)) << 4) + 4 * g) = pack4_e4m3(v[0], v[1], v[2], v[3]);
+      } else if constexpr (OSZ == 4) {
+        const int c = 4 * j + g;
+        *(f32x4*)(stage + m_l * (WN * 4) + ((c ^ (m_l & SWM)) << 4)) = f32x4{v[0], v[1], v[2], v[3]};
+      } else {
+        const int c = 2 * j + (g >> 1);
+        u32x2 w;
+        w.x = (uint32_t)bits16(from_f32<TOut>(v[0])) | ((uint32_t)bits16(from_f32<TOut>(v[1])) << 16);
+        w.y = (uint32_t)bits16(from_f32<TOut>(v[2])) | ((uint32_t)bits16(from_f32<TOut>(v[3])) << 16);
+        *(u32x2*)(stage + m_l * (WN * 2) + ((c ^ (m_l & SWM)) << 4) + 8 * (g & 1)) = w;
+      }
+    }
+    // read back along rows: lane -> (row r, chunk c), store 16 bytes
+#pragma unroll
+    for (int t = 0; t < 16 / RPI; ++t) {
+      const int r = t * RPI + lane / CPR, c = lane % CPR;
+      const u32x4 d = *(const u32x4*)(stage + r * (WN * OSZ) + ((c ^ (r & SWM)) << 4));
+      *(u32x4*)((char*)(C + (int64_t)(m_w + i * 16 + r) * ldc + n_w) + c * 16) = d;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  });
+}
+
+template <typename TIn, typename TOut, int EPI>
+__global__ __launch_bounds__(256) void gemm_tile16_kernel(const TIn* __restrict__ A, const TIn* __restrict__ B,
+                                                          const TIn* __restrict__ bias, TOut* __restrict__ C, int M,
+                                                          int N, int K, int tiles_m, int tiles_n, int panel, int lda,
+                                                          int ldb, int ldc, const float* __restrict__ scale,
+                                                          const TOut* __restrict__ res,
+                                                          const float* __restrict__ out_scale) {
+  constexpr int NW = 4, BM = 256, BN = 256;
+  constexpr int WM = BM / 2, WN = BN / 2;
+  constexpr int TM = WM / 16, TN = WN / 16;
+  constexpr int A_BYTES = BM * kRowBytes, B_BYTES = BN * kRowBytes;
+  __shared__ __attribute__((aligned(1024))) char sA0[A_BYTES];
+  __shared__ __attribute__((aligned(1024))) char sA1[A_BYTES];
+  __shared__ __attribute__((aligned(1024))) char sB0[B_BYTES];
+  __shared__ __attribute__((aligned(1024))) char sB1[B_BYTES];
+  struct Stage {
+    char* a;
+    char* b;
+  };
+  const Stage stage0{sA0, sB0}, stage1{sA1, sB1};
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / 2, wn = wave % 2;
+
+  int tm, tn;
+  tile::raster(blockIdx.x, tiles_m, tiles_n, panel, tm, tn);
+  // the last tile row or column is shifted back to end at M or N (it
+  // rewrites part of its neighbour with identical values)
+  const int m0 = min(tm * BM, M - BM), n0 = min(tn * BN, N - BN);
+  const int kpad = (-K) & (kBK - 1);
+
+  const DirectLoader<BM, NW> da(A, m0, M, lda, kpad, tid, wave);
+  const DirectLoader<BN, NW> db(B, n0, N, ldb, kpad, tid, wave);
+
+  // Swizzle of fragment rows w0 + 16 f + lane % 16 (w0 a multiple of 64):
+  // (lane & 7) ^ ((lane >> 3) & 1) ^ (2 f & 7), so the chunk position of
+  // substep kk is base ^ (4 kk) ^ 2 (f & 3) with base from the lane alone:
+  // eight per-lane offsets per operand (row and position) cover every
+  // fragment, the rest (16 f rows, the stage) is an immediate.
+  const int g_l = (lane & 7) ^ ((lane >> 3) & 1);
+  const int base = (lane >> 4) ^ g_l;
+  const int a_row = (wm * WM + (lane & 15)) * kRowBytes;
+  const int b_row = (wn * WN + (lane & 15)) * kRowBytes;
+  int aoff[2][4], boff[2][4];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      aoff[kk][p] = a_row + ((base ^ (4 * kk) ^ (2 * p)) << 4);
+      boff[kk][p] = b_row + ((base ^ (4 * kk) ^ (2 * p)) << 4);
+    }
+
+  f32x4 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  // fragments of one substep, double buffered
+  u32x4 fa[2][TM], fb[2][TN];
+  // read f of a substep: B's fragments first (the first row of MFMAs needs
+  // all of them), then A's in the order the rows use them
+  auto read_frag = [&](const Stage& st, int kk, int f, u32x4 (&xa)[TM], u32x4 (&xb)[TN]) __attribute__((always_inline)) {
+    if (f < TN) xb[f] = *(const u32x4*)(st.b + boff[kk][f & 3] + f * 16 * kRowBytes);
+    else xa[f - TN] = *(const u32x4*)(st.a + aoff[kk][(f - TN) & 3] + (f - TN) * 16 * kRowBytes);
+  };
+
+  constexpr int NMF = TM * TN;  // 64 MFMAs per substep
+  constexpr int NDR = TM + TN;  // 16 fragment reads per substep
+  constexpr int NDA = DirectLoader<BM, NW>::NI;
+  constexpr int NDL = NDA + DirectLoader<BN, NW>::NI;  // 16 copies per k-step
+
+  // One substep: NMF slots of one MFMA and its share of the memory work,
+  // expanded at compile time (a rolled loop would index the accumulators
+  // dynamically); nothing moves across a slot boundary.
+  //   fragment read f of the next substep: slot f * NMF / NDR;
+  //   copies of tile kt + 2 (substep 1 only): spread over the slots.
+  auto substep = [&](auto sub_c, const u32x4 (&xa)[TM], const u32x4 (&xb)[TN], const Stage& rd, int rd_kk,
+                     bool do_read, u32x4 (&na)[TM], u32x4 (&nb)[TN], const Stage& dl_dst, bool do_direct, int kt)
+                     __attribute__((always_inline)) {
+    constexpr int sub = decltype(sub_c)::value;
+    static_for<NMF>([&](auto slot_c) __attribute__((always_inline)) {
+      constexpr int slot = decltype(slot_c)::value;
+      constexpr int i = slot / TN, j = slot % TN;
+      acc[i][j] = mfma16<TIn>(xb[j], xa[i], acc[i][j]);
+      if constexpr (slot % (NMF / NDR) == 0)
+        if (do_read) read_frag(rd, rd_kk, slot / (NMF / NDR), na, nb);
+      if constexpr (sub == 1) {
+        if (do_direct) {
+          static_for<NDL>([&](auto d_c) __attribute__((always_inline)) {
+            constexpr int d = decltype(d_c)::value;
+            if constexpr (d * NMF / NDL == slot) {
+              if constexpr (d < NDA) da.issue(dl_dst.a, kt + 2, d);
+              else db.issue(dl_dst.b, kt + 2, d - NDA);
+            }
+          });
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+
+  // k-step kt with tile kt in `cur` and `nxt` receiving kt + 1
+  auto kstep = [&](const Stage& cur, const Stage& nxt, int kt, bool more1, bool more2) __attribute__((always_inline)) {
+    substep(std::integral_constant<int, 0>{}, fa[0], fb[0], cur, 1, true, fa[1], fb[1], cur, false, kt);
+    // this wave's copies of tile kt + 1 are its only outstanding ones
+    tile::kloop_barrier<0>();
+    __builtin_amdgcn_sched_barrier(0);
+    substep(std::integral_constant<int, 1>{}, fa[1], fb[1], nxt, 0, more1, fa[0], fb[0], cur, more2, kt);
+  };
+
+  // Tile t lives in stage (t + KT) % 2, so that the last two tiles are
+  // always in stages 0 and 1 and the k loop ends with two peeled k-steps.
+  // KT >= 2, i.e. K > 64 (checked on the host).
+  const int KT = (K + kpad) / kBK;
+  auto prologue = [&](const Stage& s_first, const Stage& s_second) __attribute__((always_inline)) {
+    if (kpad == 0) {
+#pragma unroll
+      for (int d = 0; d < NDL; ++d) {
+        if (d < NDA) da.issue(s_first.a, 0, d);
+        else db.issue(s_first.b, 0, d - NDA);
+      }
+    } else {
+#pragma unroll
+      for (int d = 0; d < NDL; ++d) {
+        if (d < NDA) da.issue_first(s_first.a, d, lane, kpad);
+        else db.issue_first(s_first.b, d - NDA, lane, kpad);
+      }
+    }
+#pragma unroll
+    for (int d = 0; d < NDL; ++d) {
+      if (d < NDA) da.issue(s_second.a, 1, d);
+      else db.issue(s_second.b, 1, d - NDA);
+    }
+    // tile 0 complete; tile 1's copies may stay in flight
+    tile::kloop_barrier<NDL>();
+#pragma unroll
+    for (int f = 0; f < NDR; ++f) read_frag(s_first, 0, f, fa[0], fb[0]);
+  };
+
+  int kt = 0;
+  if (KT & 1) {
+    prologue(stage1, stage0);
+    kstep(stage1, stage0, 0, true, true);
+    kt = 1;
+  } else {
+    prologue(stage0, stage1);
+  }
+  for (; kt + 4 <= KT; kt += 2) {
+    kstep(stage0, stage1, kt, true, true);
+    kstep(stage1, stage0, kt + 1, true, true);
+  }
+  kstep(stage0, stage1, kt, true, false);
+  kstep(stage1, stage0, kt + 1, false, false);
+
+  // Every wave is done with the operand stages: reuse them as the staging
+  // areas of the epilogue, one array per wave.
+  __syncthreads();
+  static_assert(16 * WN * sizeof(TOut) <= (size_t)A_BYTES, "staging area");
+  char* const stage_w = wave == 0 ? sA0 : wave == 1 ? sA1 : wave == 2 ? sB0 : sB1;
+  if (scale != nullptr || res != nullptr || out_scale != nullptr)
+    write_tile16<WM, WN, TIn, TOut, EPI, true>(acc, bias, C, ldc, m0 + wm * WM, n0 + wn * WN, lane, stage_w, scale,
+                                               res, out_scale);
+  else
+    write_tile16<WM, WN, TIn, TOut, EPI, false>(acc, bias, C, ldc, m0 + wm * WM, n0 + wn * WN, lane, stage_w,
+                                                nullptr, nullptr, nullptr);
+}
+
+template <typename TIn, typename TOut, int EPI>
+hipError_t launch(const LaunchArgs& a) {
+  const int tiles_m = (a.M + 255) / 256, tiles_n = (a.N + 255) / 256;
+  const int panel = tiles_m < 4 ? tiles_m : 4;
+  hipLaunchKernelGGL((gemm_tile16_kernel<TIn, TOut, EPI>), dim3(tiles_m * tiles_n), dim3(256), 0, a.stream,
+                     (const TIn*)a.A, (const TIn*)a.B, (const TIn*)a.bias, (TOut*)a.C, a.M, a.N, a.K, tiles_m,
+                     tiles_n, panel, a.lda, a.ldb, a.ldc, a.scale, (const TOut*)a.residual, a.out_scale);
+  return hipGetLastError();
+}
+
+// Only A row-major with B column-major (both k-contiguous) is served.
+template <typename TIn, typename TOut>
+LaunchFn pick(int la, int lb, int epi) {
+  if (la != GEMM_EPI_ROW_MAJOR || lb != GEMM_EPI_COL_MAJOR) return nullptr;
+  switch (epi) {
+    case GEMM_EPI_NONE: return &launch<TIn, TOut, GEMM_EPI_NONE>;
+    case GEMM_EPI_RELU: return &launch<TIn, TOut, GEMM_EPI_RELU>;
+    case GEMM_EPI_BIAS_RELU: return &launch<TIn, TOut, GEMM_EPI_BIAS_RELU>;
+    case GEMM_EPI_BIAS_GELU: return &launch<TIn, TOut, GEMM_EPI_BIAS_GELU>;
+    case GEMM_EPI_BIAS: return &launch<TIn, TOut, GEMM_EPI_BIAS>;
+    case GEMM_EPI_SILU: return &launch<TIn, TOut, GEMM_EPI_SILU>;
+    case GEMM_EPI_BIAS_SILU: return &launch<TIn, TOut, GEMM_EPI_BIAS_SILU>;
+    default: return nullptr;
+  }
+}
+
+}  // namespace tile16
+}  // namespace ge

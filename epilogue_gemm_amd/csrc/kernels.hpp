@@ -24,6 +24,7 @@ struct TileConfig {
   int bm, bn;  // workgroup tile
   int waves;   // waves per workgroup
   const char* name;
+  int mfma;    // MFMA block: 32 (32x32x16, any layout) or 16 (16x16x32, k-contiguous operands only)
 };
 int tile_num_configs();
 const TileConfig& tile_config(int cfg);

@@ -3,6 +3,7 @@
 #pragma once
 
 #include "gemm_tile.hpp"
+#include "gemm_tile16.hpp"
 
 namespace ge {
 namespace tile {
@@ -14,6 +15,7 @@ LaunchFn pick_config(int cfg, int la, int lb, int epi) {
     case 1: return pick_layout<128, 128, 4, TIn, TOut>(la, lb, epi);
     case 2: return pick_layout<64, 64, 4, TIn, TOut>(la, lb, epi);
     case 3: return pick_layout<256, 256, 8, TIn, TOut>(la, lb, epi);
+    case 4: return tile16::pick<TIn, TOut>(la, lb, epi);
     default: return nullptr;
   }
 }

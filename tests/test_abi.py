@@ -129,9 +129,9 @@ def test_fp8_output_needs_16_columns_in_tile_kernels(lib):
 
 
 @pytest.mark.parametrize("M,N,K,la,lb,want_kernel,want_name", [
-    (8192, 8192, 8192, "row", "col", "tile", "tile_256x256x64_8w"),
+    (8192, 8192, 8192, "row", "col", "tile", "tile_256x256x64_m16"),
     (4096, 4096, 4096, "row", "row", "tile", "tile_256x256x64"),
-    (4096, 4096, 4096, "row", "col", "tile", "tile_256x256x64_8w"),
+    (4096, 4096, 4096, "row", "col", "tile", "tile_256x256x64_m16"),
     (1024, 1024, 1024, "row", "row", "tile", "tile_64x64x64"),
     (128, 64, 256, "row", "col", "tile", "tile_64x64x64"),
     (32, 8192, 8192, "row", "col", "skinny", "skinny_32n_8w_5x256k"),
@@ -139,7 +139,7 @@ def test_fp8_output_needs_16_columns_in_tile_kernels(lib):
     (32, 4096, 768, "row", "col", "skinny", "skinny_32n_4w_2x256k"),  # three chunks of 256
     (32, 4096, 192, "row", "col", "generic", "generic"),  # K too short for a skinny ring, M for a tile
     (32, 8192, 8192, "row", "row", "generic", "generic"),  # small M, N-contiguous B: no fast path yet
-    (2000, 8200, 4096, "row", "col", "tile", "tile_256x256x64_8w"),  # last tile row and column shifted back
+    (2000, 8200, 4096, "row", "col", "tile", "tile_256x256x64_m16"),  # last tile row and column shifted back
     (1000, 1000, 1024, "row", "col", "tile", "tile_64x64x64"),  # 16 x 16 edge-tiled 64 x 64 tiles
     (3000, 2000, 4096, "row", "row", "tile", "tile_128x128x64"),  # 24 x 16 tiles of 128
     (1000, 1000, 1024, "col", "col", "tile", "tile_64x64x64"),
@@ -148,7 +148,7 @@ def test_fp8_output_needs_16_columns_in_tile_kernels(lib):
     (37, 53, 29, "row", "row", "generic", "generic"),
     (256, 256, 100, "col", "row", "generic", "generic"),  # K not a multiple of 8
     (1024, 1024, 1000, "row", "col", "tile", "tile_64x64x64"),  # K % 64 = 40: a partial first k-step
-    (4096, 4096, 4040, "row", "col", "tile", "tile_256x256x64_8w"),
+    (4096, 4096, 4040, "row", "col", "tile", "tile_256x256x64_m16"),
     (256, 256, 72, "col", "row", "tile", "tile_64x64x64"),
     (256, 256, 64, "row", "row", "generic", "generic"),  # one k-step: the tile pipeline needs two
 ])
@@ -164,18 +164,19 @@ def test_auto_selection(lib, M, N, K, la, lb, want_kernel, want_name):
 def test_select_forces_and_validates(lib):
     h = gb.gemm_epi_plan(512, 512, 256, "f16", "f32", "row", "col", "none")
     try:
-        assert gb.gemm_epi_num_configs("tile") == 4
+        assert gb.gemm_epi_num_configs("tile") == 5
         assert gb.gemm_epi_num_configs("skinny") == 6
         assert gb.gemm_epi_num_configs("generic") == 1
         assert gb.gemm_epi_num_configs("auto") == 0
         for cfg in range(4):
             assert gb.gemm_epi_plan_select(h, "tile", cfg) == 0
             assert gb.gemm_epi_plan_describe(h)[:2] == ("tile", cfg)
+        assert gb.gemm_epi_plan_select(h, "tile", 4) == 0  # 16x16x32, k-contiguous operands
         assert gb.gemm_epi_plan_select(h, "generic", 0) == 0
         assert gb.gemm_epi_plan_describe(h)[0] == "generic"
         assert gb.gemm_epi_plan_select(h, "skinny", -1) == 2  # M = 512 > 32: unsupported, plan unchanged
         assert gb.gemm_epi_plan_describe(h)[0] == "generic"
-        assert gb.gemm_epi_plan_select(h, "tile", 4) == 1  # no such config
+        assert gb.gemm_epi_plan_select(h, "tile", 5) == 1  # no such config
         assert lib.gemm_epi_plan_select(ctypes.c_void_p(h), 9, 0) == 1  # bad enum
         assert gb.gemm_epi_plan_select(h, "auto", -1) == 0
         assert gb.gemm_epi_plan_describe(h) == ("tile", 2, "tile_64x64x64")  # 64 workgroups beats 16
@@ -187,6 +188,11 @@ def test_select_forces_and_validates(lib):
         assert gb.gemm_epi_plan_select(h, "skinny", 0) == 2  # four chunks of 256 do not fill five slots
         assert gb.gemm_epi_plan_select(h, "skinny", 3) == 0
         assert gb.gemm_epi_plan_select(h, "tile", -1) == 2  # M = 32 holds no 64 x 64 tile
+    finally:
+        gb.gemm_epi_destroy(h)
+    h = gb.gemm_epi_plan(512, 512, 320, "bf16", "bf16", "row", "row", "bias")
+    try:
+        assert gb.gemm_epi_plan_select(h, "tile", 4) != 0  # k-contiguous operands only
     finally:
         gb.gemm_epi_destroy(h)
 

@@ -1,0 +1,83 @@
+"""Parity of the 16x16x32-MFMA tile configuration (four waves, 256 x 256
+tiles; A row-major and B column-major only) with the oracle: bit-exact on
+integer operands for every epilogue that is exact, K tails of every
+padding, shifted edge tiles, leading dimensions, the optional scale,
+residual and FP8 output; within the tolerance on random operands."""
+import numpy as np
+import pytest
+import torch
+
+from epilogue_gemm_amd import binding as gb
+from epilogue_gemm_amd import inputs
+from tests.test_parity_gpu import BITWISE_EPIS, EPIS, check_case
+from tests.test_parity_epilogues_gpu import EXTRA_CASES, check_ex
+from tests.test_strides_gpu import run_strided
+
+pytestmark = pytest.mark.gpu
+
+CFG = 4
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    gb.load_library()
+    torch.cuda.init()
+
+
+@pytest.mark.parametrize("in_dt,out_dt", [("f16", "f16"), ("bf16", "bf16"), ("f16", "f32"), ("bf16", "f32")])
+def test_tile16_integer_bitexact(in_dt, out_dt):
+    M, N, K = 512, 768, 640
+    for epi in EPIS:
+        bits = inputs.integer_inputs(M, N, K, in_dt, "row", "col", epi.startswith("bias"), seed=len(epi))
+        name = check_case(bits, M, N, K, in_dt, out_dt, "row", "col", epi, "tile", CFG, epi in BITWISE_EPIS)
+        assert name == "tile_256x256x64_m16"
+
+
+# K % 64 != 0 shifts the k axis (the first k-step partial, its leading
+# k-values zeros); odd and even k-step counts start in either stage; M and N
+# that are not multiples of 256 shift the last tile row and column back.
+@pytest.mark.parametrize("K", [72, 104, 136, 168, 200, 232, 248, 128, 192, 1000, 4104])
+def test_tile16_ktails_and_edges_bitexact(K):
+    M, N = 264, 520
+    for in_dt, out_dt, epi in (("bf16", "bf16", "bias_relu"), ("f16", "f32", "none")):
+        bits = inputs.integer_inputs(M, N, K, in_dt, "row", "col", epi.startswith("bias"), seed=K)
+        name = check_case(bits, M, N, K, in_dt, out_dt, "row", "col", epi, "tile", CFG, True)
+        assert name == "tile_256x256x64_m16"
+
+
+@pytest.mark.parametrize("M,N,K", [(1024, 1024, 1024), (768, 512, 2056)])
+def test_tile16_random_bias_gelu(M, N, K):
+    for in_dt in ("bf16", "f16"):
+        bits = inputs.make_inputs(M, N, K, in_dt, "row", "col", True, float(np.sqrt(K)), 0.1, seed=M + K)
+        check_case(bits, M, N, K, in_dt, in_dt, "row", "col", "bias_gelu", "tile", CFG, False)
+
+
+@pytest.mark.parametrize("edge", [False, True])
+def test_tile16_extras_integer_bitexact(edge):
+    M, N, K = (264, 520, 328) if edge else (512, 512, 320)
+    for in_dt, out_dt in (("bf16", "bf16"), ("f16", "f32")):
+        for epi, use_s, use_r in EXTRA_CASES:
+            name = check_ex(M, N, K, in_dt, out_dt, "row", "col", epi, "tile", CFG, use_s, use_r, True,
+                            seed=13 + len(epi))
+            assert name == "tile_256x256x64_m16"
+
+
+def test_tile16_silu_and_fp8_output():
+    M, N, K = 512, 528, 352
+    for integer in (True, False):
+        name = check_ex(M, N, K, "bf16", "fp8", "row", "col", "bias_gelu" if not integer else "bias", "tile", CFG,
+                        False, False, integer, seed=40 + integer, use_oscale=True)
+        assert name == "tile_256x256x64_m16"
+    for epi in ("silu", "bias_silu"):
+        check_ex(M, N, K, "bf16", "bf16", "row", "col", epi, "tile", CFG, True, True, False, seed=len(epi))
+
+
+def test_tile16_strided_integer_bitexact():
+    M, N, K = 520, 272, 328
+    for in_dt, out_dt, epi, pads, extras in (("bf16", "bf16", "bias_relu", (8, 16, 24), False),
+                                             ("f16", "f32", "relu", (64, 8, 8), True),
+                                             ("bf16", "fp8", "bias", (16, 8, 16), False)):
+        name = run_strided(M, N, K, in_dt, out_dt, "row", "col", epi, pads, "tile", CFG, extras)
+        assert name == "tile_256x256x64_m16"
