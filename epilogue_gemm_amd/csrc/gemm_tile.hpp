@@ -61,6 +61,14 @@ constexpr int kRowBytes = kBK * 2;  // one LDS row: 64 16-bit elements
 // (t = 0..7) and get positions c ^ j ^ t, again distinct.
 __device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
 
+// The swizzle of the 16x16x32 kernel (gemm_tile16.hpp).  Its fragment reads
+// take chunks c and c ^ 2 of the same 8 rows in one LDS pass (lanes i and
+// i + 32 together), where the 32x32x16 reads take c and c ^ 1; moving row
+// bits 1 and 2 to position bits 0 and 2 puts the even rows of 8 (and the odd
+// ones) in distinct {0, 2}-cosets, so both chunks of all 8 rows land on
+// distinct bank groups.
+__device__ __forceinline__ int swz16(int row) { return ((row >> 1) & 1) | (row & 4); }
+
 // Buffer resource over [base, base + bytes): 128-bit raw buffer loads then
 // take one per-lane 32-bit offset plus one wave-uniform offset, so the loop
 // carries no 64-bit addresses.  Offsets at or past `bytes` read as zero.
@@ -85,8 +93,9 @@ typedef __attribute__((address_space(3))) void* lds_ptr;
 // logical chunk (L % 8) ^ swz(row).  swz depends on the row only through
 // L / 8 and (NW i + w) % 8, which takes NV = 8 / NW values as i varies, so NV
 // per-lane offsets cover every instruction; the rest is wave-uniform.
-template <int R, int NW>
+template <int R, int NW, bool M16 = false>
 struct DirectLoader {
+  __device__ static __forceinline__ int sw(int row) { return M16 ? swz16(row) : swz(row); }
   static constexpr int NI = R / (8 * NW);  // wave instructions per wave per k-step
   static constexpr int NV = 8 / NW;
   static_assert(NV >= 1 && NV <= 2, "4 or 8 waves");
@@ -105,7 +114,7 @@ struct DirectLoader {
 #pragma unroll
     for (int p = 0; p < NV; ++p) {
       const int row = (NW * p + wave) * 8 + rl;
-      voff[p] = (uint32_t)(row * ld * 2 + ((pc ^ swz(row)) << 4));
+      voff[p] = (uint32_t)(row * ld * 2 + ((pc ^ sw(row)) << 4));
     }
     rows64 = (uint32_t)(64 * ld * 2);
   }
@@ -121,7 +130,7 @@ struct DirectLoader {
   // instruction i % NV plus a multiple of 64, so they share the swizzle.)
   __device__ __forceinline__ void issue_first(char* dst, int i, int lane, int kpad) const {
     const int row = (NW * (i % NV) + wave) * 8 + (lane >> 3);
-    const int chunk = (lane & 7) ^ swz(row);
+    const int chunk = (lane & 7) ^ sw(row);
     const uint32_t v = chunk * 8 < kpad ? 0xFFFFFFF0u : voff[i % NV];
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr)(dst + (NW * i + wave) * 1024), 16, v,
                                              (i / NV) * rows64, 0, 0);

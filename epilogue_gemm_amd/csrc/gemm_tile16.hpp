@@ -11,8 +11,9 @@
 // operands are double-buffered in the 256 architectural registers next to
 // the 256 accumulator registers, and each LDS byte read feeds 128 MACs.
 //
-// The LDS layout, the direct global->LDS copies (with the K-tail shift), the
-// swizzle, the raster and the two-stage pipeline are those of gemm_tile.hpp;
+// The LDS layout (but for the swizzle), the direct global->LDS copies (with
+// the K-tail shift), the raster and the two-stage pipeline are those of
+// gemm_tile.hpp;
 // a 64-deep k-step is two substeps of k = 32:
 //   substep 0   multiply k 0..31 of tile kt, read k 32..63 of it;
 //   barrier     after this wave's copies of tile kt + 1 have landed: every
@@ -21,8 +22,8 @@
 //               tile kt + 2 into the stage tile kt leaves, one copy every
 //               four MFMAs.
 // Fragment f (A or B) of substep kk: rows w0 + 16 f + lane % 16, logical
-// 16-byte chunk 4 kk + lane / 16; 16 consecutive rows at one chunk fall on
-// 16 distinct bank groups under the swizzle.  With B's fragment as the first
+// 16-byte chunk 4 kk + lane / 16, under the swizzle swz16 (gemm_tile.hpp)
+// that keeps these reads free of bank conflicts.  With B's fragment as the first
 // operand the 16x16 result arrives transposed: lane l holds
 // C[m = l % 16][n = 4 (l / 16) + e], e = 0..3 -- four consecutive columns of
 // one row.  (Tile-level fusion of load -> GEMM -> epilogue -> store:
@@ -157,26 +158,21 @@ __global__ __launch_bounds__(256) void gemm_tile16_kernel(const TIn* __restrict_
   const int m0 = min(tm * BM, M - BM), n0 = min(tn * BN, N - BN);
   const int kpad = (-K) & (kBK - 1);
 
-  const DirectLoader<BM, NW> da(A, m0, M, lda, kpad, tid, wave);
-  const DirectLoader<BN, NW> db(B, n0, N, ldb, kpad, tid, wave);
+  const DirectLoader<BM, NW, true> da(A, m0, M, lda, kpad, tid, wave);
+  const DirectLoader<BN, NW, true> db(B, n0, N, ldb, kpad, tid, wave);
 
-  // Swizzle of fragment rows w0 + 16 f + lane % 16 (w0 a multiple of 64):
-  // (lane & 7) ^ ((lane >> 3) & 1) ^ (2 f & 7), so the chunk position of
-  // substep kk is base ^ (4 kk) ^ 2 (f & 3) with base from the lane alone:
-  // eight per-lane offsets per operand (row and position) cover every
-  // fragment, the rest (16 f rows, the stage) is an immediate.
-  const int g_l = (lane & 7) ^ ((lane >> 3) & 1);
-  const int base = (lane >> 4) ^ g_l;
+  // Fragment rows w0 + 16 f + lane % 16 (w0 a multiple of 64) have the
+  // swizzle swz16(lane % 16), so one per-lane offset per operand and substep
+  // covers every fragment; the rest (16 f rows, the stage) is an immediate.
+  const int sl = tile::swz16(lane & 15);
   const int a_row = (wm * WM + (lane & 15)) * kRowBytes;
   const int b_row = (wn * WN + (lane & 15)) * kRowBytes;
-  int aoff[2][4], boff[2][4];
+  int aoff[2], boff[2];
 #pragma unroll
-  for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      aoff[kk][p] = a_row + ((base ^ (4 * kk) ^ (2 * p)) << 4);
-      boff[kk][p] = b_row + ((base ^ (4 * kk) ^ (2 * p)) << 4);
-    }
+  for (int kk = 0; kk < 2; ++kk) {
+    aoff[kk] = a_row + (((4 * kk + (lane >> 4)) ^ sl) << 4);
+    boff[kk] = b_row + (((4 * kk + (lane >> 4)) ^ sl) << 4);
+  }
 
   f32x4 acc[TM][TN];
 #pragma unroll
@@ -189,14 +185,14 @@ __global__ __launch_bounds__(256) void gemm_tile16_kernel(const TIn* __restrict_
   // read f of a substep: B's fragments first (the first row of MFMAs needs
   // all of them), then A's in the order the rows use them
   auto read_frag = [&](const Stage& st, int kk, int f, u32x4 (&xa)[TM], u32x4 (&xb)[TN]) __attribute__((always_inline)) {
-    if (f < TN) xb[f] = *(const u32x4*)(st.b + boff[kk][f & 3] + f * 16 * kRowBytes);
-    else xa[f - TN] = *(const u32x4*)(st.a + aoff[kk][(f - TN) & 3] + (f - TN) * 16 * kRowBytes);
+    if (f < TN) xb[f] = *(const u32x4*)(st.b + boff[kk] + f * 16 * kRowBytes);
+    else xa[f - TN] = *(const u32x4*)(st.a + aoff[kk] + (f - TN) * 16 * kRowBytes);
   };
 
   constexpr int NMF = TM * TN;  // 64 MFMAs per substep
   constexpr int NDR = TM + TN;  // 16 fragment reads per substep
-  constexpr int NDA = DirectLoader<BM, NW>::NI;
-  constexpr int NDL = NDA + DirectLoader<BN, NW>::NI;  // 16 copies per k-step
+  constexpr int NDA = DirectLoader<BM, NW, true>::NI;
+  constexpr int NDL = NDA + DirectLoader<BN, NW, true>::NI;  // 16 copies per k-step
 
   // One substep: NMF slots of one MFMA and its share of the memory work,
   // expanded at compile time (a rolled loop would index the accumulators

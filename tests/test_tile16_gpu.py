@@ -15,7 +15,8 @@ from tests.test_strides_gpu import run_strided
 
 pytestmark = pytest.mark.gpu
 
-CFG = 4
+NAMES = {4: "tile_256x256x64_m16"}
+CFGS = list(NAMES)
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -26,58 +27,65 @@ def _gpu():
     torch.cuda.init()
 
 
+@pytest.mark.parametrize("config", CFGS)
 @pytest.mark.parametrize("in_dt,out_dt", [("f16", "f16"), ("bf16", "bf16"), ("f16", "f32"), ("bf16", "f32")])
-def test_tile16_integer_bitexact(in_dt, out_dt):
+def test_tile16_integer_bitexact(config, in_dt, out_dt):
     M, N, K = 512, 768, 640
     for epi in EPIS:
         bits = inputs.integer_inputs(M, N, K, in_dt, "row", "col", epi.startswith("bias"), seed=len(epi))
-        name = check_case(bits, M, N, K, in_dt, out_dt, "row", "col", epi, "tile", CFG, epi in BITWISE_EPIS)
-        assert name == "tile_256x256x64_m16"
+        name = check_case(bits, M, N, K, in_dt, out_dt, "row", "col", epi, "tile", config, epi in BITWISE_EPIS)
+        assert name == NAMES[config]
 
 
 # K % 64 != 0 shifts the k axis (the first k-step partial, its leading
 # k-values zeros); odd and even k-step counts start in either stage; M and N
 # that are not multiples of 256 shift the last tile row and column back.
-@pytest.mark.parametrize("K", [72, 104, 136, 168, 200, 232, 248, 128, 192, 1000, 4104])
-def test_tile16_ktails_and_edges_bitexact(K):
+@pytest.mark.parametrize("config", CFGS)
+@pytest.mark.parametrize("K", [72, 104, 136, 168, 200, 232, 248, 128, 192, 256, 264, 296, 328, 360, 376,
+                               384, 1000, 4104])
+def test_tile16_ktails_and_edges_bitexact(config, K):
     M, N = 264, 520
     for in_dt, out_dt, epi in (("bf16", "bf16", "bias_relu"), ("f16", "f32", "none")):
         bits = inputs.integer_inputs(M, N, K, in_dt, "row", "col", epi.startswith("bias"), seed=K)
-        name = check_case(bits, M, N, K, in_dt, out_dt, "row", "col", epi, "tile", CFG, True)
-        assert name == "tile_256x256x64_m16"
+        name = check_case(bits, M, N, K, in_dt, out_dt, "row", "col", epi, "tile", config, True)
+        assert name == NAMES[config]
 
 
+@pytest.mark.parametrize("config", CFGS)
 @pytest.mark.parametrize("M,N,K", [(1024, 1024, 1024), (768, 512, 2056)])
-def test_tile16_random_bias_gelu(M, N, K):
+def test_tile16_random_bias_gelu(config, M, N, K):
     for in_dt in ("bf16", "f16"):
         bits = inputs.make_inputs(M, N, K, in_dt, "row", "col", True, float(np.sqrt(K)), 0.1, seed=M + K)
-        check_case(bits, M, N, K, in_dt, in_dt, "row", "col", "bias_gelu", "tile", CFG, False)
+        check_case(bits, M, N, K, in_dt, in_dt, "row", "col", "bias_gelu", "tile", config, False)
 
 
+@pytest.mark.parametrize("config", CFGS)
 @pytest.mark.parametrize("edge", [False, True])
-def test_tile16_extras_integer_bitexact(edge):
+def test_tile16_extras_integer_bitexact(config, edge):
     M, N, K = (264, 520, 328) if edge else (512, 512, 320)
     for in_dt, out_dt in (("bf16", "bf16"), ("f16", "f32")):
         for epi, use_s, use_r in EXTRA_CASES:
-            name = check_ex(M, N, K, in_dt, out_dt, "row", "col", epi, "tile", CFG, use_s, use_r, True,
+            name = check_ex(M, N, K, in_dt, out_dt, "row", "col", epi, "tile", config, use_s, use_r, True,
                             seed=13 + len(epi))
-            assert name == "tile_256x256x64_m16"
+            assert name == NAMES[config]
 
 
-def test_tile16_silu_and_fp8_output():
+@pytest.mark.parametrize("config", CFGS)
+def test_tile16_silu_and_fp8_output(config):
     M, N, K = 512, 528, 352
     for integer in (True, False):
-        name = check_ex(M, N, K, "bf16", "fp8", "row", "col", "bias_gelu" if not integer else "bias", "tile", CFG,
-                        False, False, integer, seed=40 + integer, use_oscale=True)
-        assert name == "tile_256x256x64_m16"
+        name = check_ex(M, N, K, "bf16", "fp8", "row", "col", "bias_gelu" if not integer else "bias", "tile",
+                        config, False, False, integer, seed=40 + integer, use_oscale=True)
+        assert name == NAMES[config]
     for epi in ("silu", "bias_silu"):
-        check_ex(M, N, K, "bf16", "bf16", "row", "col", epi, "tile", CFG, True, True, False, seed=len(epi))
+        check_ex(M, N, K, "bf16", "bf16", "row", "col", epi, "tile", config, True, True, False, seed=len(epi))
 
 
-def test_tile16_strided_integer_bitexact():
+@pytest.mark.parametrize("config", CFGS)
+def test_tile16_strided_integer_bitexact(config):
     M, N, K = 520, 272, 328
     for in_dt, out_dt, epi, pads, extras in (("bf16", "bf16", "bias_relu", (8, 16, 24), False),
                                              ("f16", "f32", "relu", (64, 8, 8), True),
                                              ("bf16", "fp8", "bias", (16, 8, 16), False)):
-        name = run_strided(M, N, K, in_dt, out_dt, "row", "col", epi, pads, "tile", CFG, extras)
-        assert name == "tile_256x256x64_m16"
+        name = run_strided(M, N, K, in_dt, out_dt, "row", "col", epi, pads, "tile", config, extras)
+        assert name == NAMES[config]
