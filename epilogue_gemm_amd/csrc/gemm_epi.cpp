@@ -10,10 +10,12 @@
 
 namespace ge {
 
-// Tile configurations: workgroup tile BM x BN (k-step 64) and its waves,
-// each owning (BM/2) x (BN/(waves/2)).  Larger tiles reuse each loaded byte
-// more; smaller ones give small problems enough workgroups for 256 CUs;
-// 8 waves put two on each SIMD so one can multiply while the other waits.
+// Tile configurations: workgroup tile BM x BN (k-step 64), its waves, each
+// owning (BM/2) x (BN/(waves/2)), and the MFMA block.  Larger tiles reuse
+// each loaded byte more; smaller ones give small problems enough workgroups
+// for 256 CUs; 8 waves put two on each SIMD so one can multiply while the
+// other waits; 16x16x32 blocks move half the accumulator bytes per FLOP
+// (k-contiguous operands only).
 static const TileConfig kTile[] = {
     {256, 256, 4, "tile_256x256x64", 32},
     {128, 128, 4, "tile_128x128x64", 32},

@@ -1,11 +1,13 @@
 // gemm_tile.hpp -- the LDS-pipelined MFMA tile kernel for gfx950.
 //
-// One workgroup (256 threads = 4 waves of 64) computes a BM x BN tile of C,
-// looping over k in steps of 64.  Both operands are staged in LDS in one
-// layout: rows along M (for A) or N (for B), 64 k values per row, k
-// contiguous, the 16-byte chunks of each row XOR-swizzled.  Each wave owns
-// a (BM/2) x (BN/2) sub-tile made of 32x32 blocks and feeds
-// v_mfma_f32_32x32x16_{f16,bf16} from LDS, accumulating in fp32.
+// One workgroup (4 or 8 waves of 64) computes a BM x BN tile of C, looping
+// over k in steps of 64.  Both operands are staged in LDS in one layout:
+// rows along M (for A) or N (for B), 64 k values per row, k contiguous, the
+// 16-byte chunks of each row XOR-swizzled.  The waves form a 2 x (NW / 2)
+// grid, each owning a (BM / 2) x (2 BN / NW) sub-tile made of 32x32 blocks,
+// and feed v_mfma_f32_32x32x16_{f16,bf16} from LDS, accumulating in fp32.
+// (gemm_tile16.hpp builds the 256 x 256, four-wave tile for k-contiguous
+// operands on 16x16x32 MFMAs from the same loaders, raster and pipeline.)
 //
 // Getting a k-step into LDS:
 //   * an operand whose k index is contiguous in memory (A row-major, B
