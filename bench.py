@@ -48,15 +48,25 @@ _FAMILY_SOURCES = {
 }
 
 
+def _code_only(text: str) -> str:
+    """C++ source with comments removed and whitespace collapsed."""
+    import re
+
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_sha(family: str) -> str:
-    """sha256 over the sources of one kernel family (detects a kernel changed
-    since its HBM counters were taken)."""
+    """sha256 over the code (comments and layout aside) of one kernel
+    family's sources: detects a kernel changed since its HBM counters were
+    taken."""
     import hashlib
 
     h = hashlib.sha256()
     for f in _FAMILY_SOURCES[family]:
-        with open(os.path.join(CSRC, f), "rb") as fh:
-            h.update(f.encode() + b"\0" + fh.read())
+        with open(os.path.join(CSRC, f), encoding="utf-8") as fh:
+            h.update(f.encode() + b"\0" + _code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 
