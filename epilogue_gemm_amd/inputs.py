@@ -143,6 +143,22 @@ def integer_inputs(M: int, N: int, K: int, in_dtype: str, layout_a: str, layout_
     }
 
 
+def integer_bits(rows: int, cols: int, in_dtype: str, seed: int, lo: int = -2, hi: int = 2,
+                 chunk_rows: int = 4096):
+    """rows x cols uint16 bit patterns of integers drawn uniformly from
+    [lo, hi] (numpy PCG64 seeded with `seed`), generated chunk by chunk so
+    that operands of 2^31 elements need no wider temporary than a chunk.
+    The integers are exact in fp16 and bf16."""
+    vals = np.arange(lo, hi + 1, dtype=np.float32)
+    table = to_bits(torch.from_numpy(vals).to(_TORCH_DT[in_dtype])).astype(np.uint16)
+    rng = np.random.default_rng(int(seed))
+    out = np.empty((rows, cols), np.uint16)
+    for r0 in range(0, rows, chunk_rows):
+        r1 = min(rows, r0 + chunk_rows)
+        out[r0:r1] = table[rng.integers(0, hi - lo + 1, size=(r1 - r0, cols), dtype=np.int8)]
+    return out
+
+
 def extras_inputs(M: int, N: int, out_dtype: str, seed: int, integer: bool = False):
     """Optional epilogue operands: dict(scale=float32 array of N, residual=bit
     patterns of an M x N row-major array in the output format (uint16 for
