@@ -1,8 +1,9 @@
-"""The largest problem the boundary accepts: A of 262143 x 8192 = 2^31 - 8192
-elements (4 GiB in bf16), whose buffer extent and offsets sit just inside
-the kernels' 32-bit range.  Integer operands make the comparison with the
-oracle bit-exact on whole sampled rows: the first, a middle one, and the
-last 257 (the last tile row is shifted back to end at M)."""
+"""The largest operands the boundary accepts (fewer than 2^31 elements, 4 GiB
+in bf16), whose buffer extents and offsets sit just inside the kernels'
+32-bit range: A of 262143 x 8192 for the tile kernel, and a weight of
+8192 x 261888 for the skinny kernel.  Integer operands make the comparison
+with the oracle bit-exact on whole sampled rows or columns (for the tile
+kernel the last 257 rows, where the last tile row is shifted back)."""
 import sys
 
 import numpy as np
@@ -58,3 +59,33 @@ def test_largest_accepted_a_operand(epi):
     assert name.startswith("tile_")
     assert mism == 0, f"{name}: {mism} of {got.size} sampled outputs differ"
     assert bool(torch.isfinite(C.float()).all())
+
+
+def test_largest_accepted_weight_skinny():
+    # the decode shape with a weight of 8192 x 261888 = 2^31 - 2^21 elements
+    # (K whole 256-deep chunks), its buffer extent within 2 MiB of 4 GiB
+    M, N, K = 32, 8192, 261888
+    assert K * N < 2**31 and K % 256 == 0
+    _say("[limits] generating the skinny operands")
+    A = inputs.integer_bits(M, K, "bf16", seed=41)
+    B = inputs.integer_bits(N, K, "bf16", seed=42)  # column-major B: N x K
+    bias = inputs.integer_bits(1, N, "bf16", seed=43).reshape(-1)
+    dA, dB, dbias = parity.to_device(A, "bf16"), parity.to_device(B, "bf16"), parity.to_device(bias, "bf16")
+    C = parity.empty_out(M * N, "bf16")
+    C.fill_(float("nan"))
+    plan = gb.Plan(M, N, K, "bf16", "bf16", "row", "col", "bias")
+    _say(f"[limits] running {plan.name}")
+    plan.run(dA, dB, dbias, C)
+    torch.cuda.synchronize()
+    name = plan.name
+    plan.close()
+    got = parity.out_bits(C).reshape(-1)
+    # every row at the first, a middle and the last 40 columns
+    cols = np.concatenate([[0, N // 2 + 3], np.arange(N - 40, N)])
+    rr = np.repeat(np.arange(M), cols.size)
+    cc = np.tile(cols, M)
+    _say(f"[limits] oracle on {rr.size} outputs")
+    _, bits = oracle.gemm_epi_points(A, B, bias, M, N, K, "bf16", "bf16", "row", "col", "bias", rr, cc)
+    mism = np.count_nonzero(got.reshape(M, N)[rr, cc] != bits.astype(np.uint16))
+    assert name.startswith("skinny_")
+    assert mism == 0, f"{name}: {mism} of {rr.size} sampled outputs differ"
