@@ -144,7 +144,8 @@ def _cpu_baseline(w, bits):
         return time.perf_counter() - t0
 
     t1 = run_rows(1)
-    rows = int(max(1, min(w.M, round(12.0 / max(t1, 1e-3)))))
+    # a one-row run overstates the per-row time (fixed costs), so aim high
+    rows = int(max(1, min(w.M, round(18.0 / max(t1, 1e-3)))))
     t = run_rows(rows)
     flops = 2.0 * rows * w.N * w.K
     return {
