@@ -116,7 +116,11 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const TIn* __restr
   // Split K (part != NULL): workgroup (b, s) of the gridDim.y splits takes
   // chunks [s n, (s + 1) n) of column block b, n = K / KC / splits.
   const int nsplit = (int)gridDim.y, split = (int)blockIdx.y;
-  const int nchunks = K / KC / nsplit;  // at least P (checked on the host)
+  // K not a multiple of KC: the k axis is shifted by kpad = KC - K % KC so
+  // that the partial chunk is chunk 0, which covers k in [-kpad, KC - kpad);
+  // its positions k < 0 are loaded as zeros (issue).
+  const int kpad = (-K) & (KC - 1);
+  const int nchunks = (K + kpad) / KC / nsplit;  // at least P (checked on the host)
   const int cbase = split * nchunks;
 
   // Workgroup b walks the chunks starting at chunk b (mod the count): at
@@ -142,16 +146,18 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const TIn* __restr
   // A's chunk uses the same mapping, but with the whole row offset in the
   // per-lane part: the buffer's range check covers only that part, and it
   // is what turns rows past M into zeros.
-  uint32_t vb[ND], sb[ND], vas[ND];
+  // kz: byte offset of the lane's 16-byte chunk within its row segment.
+  uint32_t vb[ND], sb[ND], vas[ND], kz[ND];
 #pragma unroll
   for (int d = 0; d < ND; ++d) {
     const int t = wave * ND + d;
     const int r = (1024 * t + 16 * lane) / RB;
     const int p = ((1024 * t + 16 * lane) % RB) / 16;
     const int r0 = (1024 * t) / RB;  // first row of the instruction (wave-uniform)
-    vb[d] = (uint32_t)(r - r0) * row_bytes + (uint32_t)((p ^ (r & 15)) << 4);
+    kz[d] = (uint32_t)((p ^ (r & 15)) << 4);
+    vb[d] = (uint32_t)(r - r0) * row_bytes + kz[d];
     sb[d] = (uint32_t)r0 * row_bytes;
-    vas[d] = (uint32_t)r * a_row_bytes + (uint32_t)((p ^ (r & 15)) << 4);
+    vas[d] = (uint32_t)r * a_row_bytes + kz[d];
   }
 
   // A: rows past M read as zero (outside the buffer resource).  Wave w's
@@ -166,13 +172,33 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const TIn* __restr
 
   f32x16 acc = f32x16{};
 
+  // The shift is kept out of the buffer resources (whose ranges end at the
+  // last row's end and, for A, make rows past M read as zero): chunk gc >= 1
+  // starts 2 kpad bytes before gc RB in the wave-uniform offset (RB > 2 kpad);
+  // in chunk 0 a lane whose 16 bytes lie at k < 0 takes a per-lane offset
+  // past the end of the buffer, which the range check turns into zeros
+  // without a memory access (kpad is a multiple of 8, so no lane straddles
+  // k = 0), and the others move back by 2 kpad in their own offset.  Both
+  // operands are masked, so that no value from before a row's start enters
+  // a product.
   auto issue = [&](int j, int c) __attribute__((always_inline)) {
-    const uint32_t kb = (uint32_t)((c + rot) % nchunks + cbase) * RB;
+    const int gc = (c + rot) % nchunks + cbase;
+    const uint32_t pad2 = 2u * (uint32_t)kpad;
+    if (gc == 0 && kpad != 0) {
 #pragma unroll
-    for (int d = 0; d < ND; ++d)
-      load_lds16(rb, slot[j] + (wave * ND + d) * 1024, vb[d], sb[d] + kb);
+      for (int d = 0; d < ND; ++d)
+        load_lds16(rb, slot[j] + (wave * ND + d) * 1024, kz[d] < pad2 ? 0xFFFFFFF0u : vb[d] - pad2, sb[d]);
 #pragma unroll
-    for (int d = 0; d < ND; ++d) load_lds16(ra, slot_a[j] + (wave * ND + d) * 1024, vas[d], kb);
+      for (int d = 0; d < ND; ++d)
+        load_lds16(ra, slot_a[j] + (wave * ND + d) * 1024, kz[d] < pad2 ? 0xFFFFFFF0u : vas[d] - pad2, 0u);
+    } else {
+      const uint32_t kb = (uint32_t)gc * RB - pad2;
+#pragma unroll
+      for (int d = 0; d < ND; ++d)
+        load_lds16(rb, slot[j] + (wave * ND + d) * 1024, vb[d], sb[d] + kb);
+#pragma unroll
+      for (int d = 0; d < ND; ++d) load_lds16(ra, slot_a[j] + (wave * ND + d) * 1024, vas[d], kb);
+    }
   };
   auto compute = [&](int j) __attribute__((always_inline)) {
     u32x4 b[MF];
@@ -310,6 +336,11 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const TIn* __restr
     // last), applies the epilogue, writes C and re-arms the counter for
     // the next run.
     //
+    // The summing workgroup also clears the partials it read (the rows
+    // below M, the only ones written), so that every completed run leaves
+    // the whole workspace zero-filled, as it found it: a workspace may be
+    // shared by plans whose partial and counter areas overlap.
+    //
     // Visibility across XCDs without whole-cache maintenance (a release
     // fence would write back, and an acquire fence invalidate, the XCD's
     // entire L2 -- which also evicts A, shared by every workgroup): the
@@ -336,7 +367,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const TIn* __restr
                  (unsigned)(nsplit - 1);
     __syncthreads();
     if (!*is_last) return;
-    const float* blk = part + (size_t)blockIdx.x * nsplit * 1024;
+    float* blk = part + (size_t)blockIdx.x * nsplit * 1024;
     for (int t = tid; t < 256; t += NW * 64) {
       const int om = t >> 3;
       if (om >= M) break;
@@ -345,6 +376,10 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const TIn* __restr
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           z[e] += __hip_atomic_load(blk + s * 1024 + om * 32 + 4 * oq + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int s = 0; s < nsplit; ++s)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          __hip_atomic_store(blk + s * 1024 + om * 32 + 4 * oq + e, 0.0f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       finish(om, z);
     }
     if (tid == 0) __hip_atomic_store(arrivals + blockIdx.x, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -400,7 +435,7 @@ LaunchFn pick_types(const Problem& p) {
 }
 
 // In order of preference; the plan takes the first one whose chunk divides
-// K into at least P chunks.  LDS: B and A rings, each P x 32 rows x 2 KC
+// K into at least P chunks, else the first one that fits with K padded.  LDS: B and A rings, each P x 32 rows x 2 KC
 // bytes.
 const SkinnyConfig kSkinny[] = {
     {8, 5, 256, "skinny_32n_8w_5x256k"},  // 80 + 80 KiB: four chunks of 512-byte row segments in flight
@@ -418,24 +453,30 @@ const SkinnyConfig& skinny_config(int cfg) { return kSkinny[cfg]; }
 
 bool skinny_supports(int cfg, const Problem& p) {
   if (cfg < 0 || cfg >= skinny_num_configs()) return false;
-  // K in whole chunks, at least one turn of the ring; rows 16-byte aligned
-  // (leading dimensions multiples of 8); 32 rows of B and all of A must be
-  // addressable by one buffer resource
+  // K a multiple of 8 (a partial chunk is padded to KC with zeros) and at
+  // least one chunk per ring slot; rows 16-byte aligned (leading dimensions
+  // multiples of 8); 32 rows of B and all of A must be addressable by one
+  // buffer resource
   const SkinnyConfig& c = kSkinny[cfg];
   return p.M >= 1 && p.M <= 32 && p.la == GEMM_EPI_ROW_MAJOR && p.lb == GEMM_EPI_COL_MAJOR && p.N >= 32 && p.N % 8 == 0 &&
-         p.K % c.kc == 0 && p.K / c.kc >= c.stages && p.lda % 8 == 0 && p.ldb % 8 == 0 && p.ldc % 8 == 0 &&
+         p.K % 8 == 0 && (p.K + c.kc - 1) / c.kc >= c.stages && p.lda % 8 == 0 && p.ldb % 8 == 0 && p.ldc % 8 == 0 &&
          32 * p.ldb * 2 < ((int64_t)1 << 32) && p.M * p.lda * 2 < ((int64_t)1 << 32);
 }
 
 int skinny_split(int cfg, const Problem& p) {
   const SkinnyConfig& c = kSkinny[cfg];
-  const int64_t nblocks = (p.N + 31) / 32, chunks = p.K / c.kc;
+  const int64_t nblocks = (p.N + 31) / 32, chunks = (p.K + c.kc - 1) / c.kc;
   int s = 1;
   while (nblocks * s < 256 && chunks % (2 * s) == 0 && chunks / (2 * s) >= c.stages && s < 16) s *= 2;
   return s;
 }
 
+// The first configuration whose chunk divides K; else the first one that
+// pads the last partial chunk (fewest wasted bytes of B come second to the
+// configuration order).
 int skinny_choose(const Problem& p) {
+  for (int c = 0; c < skinny_num_configs(); ++c)
+    if (p.K % kSkinny[c].kc == 0 && skinny_supports(c, p)) return c;
   for (int c = 0; c < skinny_num_configs(); ++c)
     if (skinny_supports(c, p)) return c;
   return -1;

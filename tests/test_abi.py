@@ -137,7 +137,11 @@ def test_fp8_output_needs_16_columns_in_tile_kernels(lib):
     (32, 8192, 8192, "row", "col", "skinny", "skinny_32n_8w_5x256k"),
     (1, 4096, 4096, "row", "col", "skinny", "skinny_32n_8w_5x256k"),
     (32, 4096, 768, "row", "col", "skinny", "skinny_32n_4w_2x256k"),  # three chunks of 256
-    (32, 4096, 192, "row", "col", "generic", "generic"),  # K too short for a skinny ring, M for a tile
+    (32, 4096, 192, "row", "col", "skinny", "skinny_32n_2w_2x128k"),  # two chunks of 128, the first padded
+    (32, 4096, 128, "row", "col", "generic", "generic"),  # K too short for a skinny ring, M for a tile
+    (32, 8192, 8200, "row", "col", "skinny", "skinny_32n_8w_5x256k"),  # 33 chunks of 256, the first padded
+    (32, 8192, 8320, "row", "col", "skinny", "skinny_32n_4w_8x128k"),  # whole chunks of 128 come first
+    (32, 8192, 8196, "row", "col", "generic", "generic"),  # K not a multiple of 8
     (32, 8192, 8192, "row", "row", "generic", "generic"),  # small M, N-contiguous B: no fast path yet
     (2000, 8200, 4096, "row", "col", "tile", "tile_256x256x64_m16"),  # last tile row and column shifted back
     (1000, 1000, 1024, "row", "col", "tile", "tile_64x64x64"),  # 16 x 16 edge-tiled 64 x 64 tiles
@@ -198,7 +202,8 @@ def test_select_forces_and_validates(lib):
 
 
 # (k per chunk, ring slots) of each skinny configuration, in order: K must
-# be whole chunks, at least one per slot
+# be a multiple of 8 that makes at least one chunk per slot, the first chunk
+# padded with zeros when K is not a whole number of chunks
 SKINNY_CHUNKS = [(256, 5), (256, 4), (256, 4), (128, 8), (256, 2), (128, 2)]
 
 
@@ -206,7 +211,7 @@ def test_skinny_k_granularity(lib):
     assert gb.gemm_epi_num_configs("skinny") == len(SKINNY_CHUNKS)
     for cfg, (kc, slots) in enumerate(SKINNY_CHUNKS):
         for K, ok in ((kc * slots, True), (kc * (slots + 1), True), (kc * (slots - 1), False),
-                      (kc * slots + 64, False)):
+                      (kc * slots + 64, True), (kc * (slots - 1) + 8, True), (kc * slots + 4, False)):
             h = gb.gemm_epi_plan(32, 64, K, "bf16", "bf16", "row", "col", "none")
             try:
                 assert (gb.gemm_epi_plan_select(h, "skinny", cfg) == 0) == ok, (cfg, K)

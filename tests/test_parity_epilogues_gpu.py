@@ -119,7 +119,7 @@ def test_skinny_split_extras_integer_bitexact(M, N, K):
     for rep in range(2):  # the split path leaves its counters at zero for the next run
         check_ex(M, N, K, "bf16", "bf16", "row", "col", "bias_relu", "auto", -1, True, True, True, seed=N + rep,
                  workspace=ws)
-    assert not ws[-256:].cpu().numpy().any()
+    assert not ws.cpu().numpy().any()  # the whole workspace is left zero-filled
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 1, 1), (37, 53, 29), (65, 130, 200)])
@@ -222,7 +222,7 @@ def test_skinny_split_fp8_integer_bitexact():
     for rep in range(2):
         check_ex(M, N, K, "bf16", "fp8", "row", "col", "bias", "auto", -1, True, False, True, seed=rep,
                  workspace=ws, use_oscale=True)
-    assert not ws[-256:].cpu().numpy().any()
+    assert not ws.cpu().numpy().any()  # the whole workspace is left zero-filled
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 1, 1), (37, 53, 29), (65, 130, 200)])

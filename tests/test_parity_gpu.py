@@ -160,8 +160,38 @@ def test_skinny_split_integer_bitexact(M, N, K):
             got = parity.out_bits(C)
             mism = np.count_nonzero(got.reshape(-1) != c.reshape(-1).astype(got.dtype))
             assert mism == 0, (rep, epi, mism)
-        counters = ws[-256:].cpu().numpy()
-        assert not counters.any()
+        # every completed run leaves the whole workspace zero-filled
+        # (partials cleared by the summing workgroup, counters re-armed)
+        assert not ws.cpu().numpy().any()
+        plan.close()
+
+
+def test_skinny_split_shared_workspace():
+    # two split plans on one workspace: the narrower plan's counters lie
+    # inside the wider plan's partial area, so each run must leave the
+    # whole workspace zero-filled for the other's next run
+    M, K = 32, 8192
+    plans, data = [], []
+    for N in (2048, 1024):
+        bits = inputs.integer_inputs(M, N, K, "bf16", "row", "col", True, seed=N)
+        plan = gb.Plan(M, N, K, "bf16", "bf16", "row", "col", "bias_relu")
+        assert plan.kernel == "skinny" and plan.workspace_size > 0
+        A, B = parity.to_device(bits["A"], "bf16"), parity.to_device(bits["B"], "bf16")
+        bias = parity.to_device(bits["bias"], "bf16")
+        c = oracle_full(bits, M, N, K, "bf16", "bf16", "row", "col", "bias_relu")[1]
+        plans.append(plan)
+        data.append((A, B, bias, c, N))
+    assert plans[0].workspace_size > plans[1].workspace_size
+    ws = torch.zeros(plans[0].workspace_size, dtype=torch.uint8, device="cuda")
+    for rep in range(3):
+        for plan, (A, B, bias, c, N) in zip(plans, data):
+            C = parity.empty_out(M * N, "bf16")
+            plan.run(A, B, bias, C, workspace=ws)
+            torch.cuda.synchronize()
+            mism = np.count_nonzero(parity.out_bits(C).reshape(-1) != c.reshape(-1).astype(np.uint16))
+            assert mism == 0, (rep, N, mism)
+    assert not ws.cpu().numpy().any()
+    for plan in plans:
         plan.close()
 
 
@@ -203,6 +233,56 @@ def test_skinny_integer_bitexact(config, M, in_dt, out_dt):
         bits = inputs.integer_inputs(M, N, K, in_dt, "row", "col", epi.startswith("bias"), seed=M + config)
         name = check_case(bits, M, N, K, in_dt, out_dt, "row", "col", epi, "skinny", config, epi in BITWISE_EPIS)
         assert name.startswith("skinny_")
+
+
+@pytest.mark.parametrize("config", range(len(SKINNY_CHUNKS)))
+@pytest.mark.parametrize("M", [1, 32])
+def test_skinny_k_tail_integer_bitexact(config, M):
+    # K not a whole number of chunks: the axis is shifted so that the first
+    # chunk is the partial one, its positions before k = 0 loaded as zeros;
+    # the largest pad (K % kc = 8), a middle one and the smallest (kc - 8),
+    # with chunk counts that leave different heads before the ring turns
+    N = 96
+    kc, slots = SKINNY_CHUNKS[config]
+    for K, epi in ((kc * (slots - 1) + 8, "bias_relu"), (kc * slots + kc // 2 + 8, "bias"),
+                   (kc * 2 * slots - 8, "none")):
+        for in_dt, out_dt in (("bf16", "bf16"), ("f16", "f32")):
+            bits = inputs.integer_inputs(M, N, K, in_dt, "row", "col", epi.startswith("bias"), seed=K + M)
+            name = check_case(bits, M, N, K, in_dt, out_dt, "row", "col", epi, "skinny", config, True)
+            assert name.startswith("skinny_")
+
+
+def test_skinny_k_tail_split_and_auto():
+    # the automatic plan for a padded K is the skinny kernel; with a
+    # workspace it splits K (the padded chunk belongs to split 0)
+    for M, N, K in ((32, 1024, 7944), (5, 200, 3336)):  # 32 chunks in 4 splits, 14 in 2
+        bits = inputs.integer_inputs(M, N, K, "bf16", "row", "col", True, seed=K)
+        plan = gb.Plan(M, N, K, "bf16", "bf16", "row", "col", "bias_relu")
+        assert plan.kernel == "skinny" and plan.workspace_size > 0, plan.name
+        A, B = parity.to_device(bits["A"], "bf16"), parity.to_device(bits["B"], "bf16")
+        bias = parity.to_device(bits["bias"], "bf16")
+        y, c = oracle_full(bits, M, N, K, "bf16", "bf16", "row", "col", "bias_relu")
+        ws = torch.zeros(plan.workspace_size, dtype=torch.uint8, device="cuda")
+        for w in (ws, ws, None):
+            C = parity.empty_out(M * N, "bf16")
+            C.fill_(float("nan"))
+            plan.run(A, B, bias, C, workspace=w)
+            torch.cuda.synchronize()
+            mism = np.count_nonzero(parity.out_bits(C).reshape(-1) != c.reshape(-1).astype(np.uint16))
+            assert mism == 0, (M, N, K, w is None, mism)
+        assert not ws.cpu().numpy().any()
+        plan.close()
+
+
+def test_skinny_k_tail_random_decode_shape():
+    # 32 x 8192 x 8200, random operands, automatic plan
+    M, N, K = 32, 8192, 8200
+    bits = inputs.make_inputs(M, N, K, "bf16", "row", "col", True, float(np.sqrt(K)), 0.1, seed=21)
+    got, name = run_gpu(bits, M, N, K, "bf16", "bf16", "row", "col", "bias_gelu")
+    assert name == "skinny_32n_8w_5x256k"
+    y, c = oracle_full(bits, M, N, K, "bf16", "bf16", "row", "col", "bias_gelu")
+    r = parity.compare(got, c, y, "bf16")
+    assert r["ok"], r
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 1, 1), (2, 8, 4), (37, 53, 29), (65, 130, 200), (3, 700, 5)])
