@@ -44,6 +44,17 @@
 //
 // Within each 16-k MFMA step lane half h takes k = 8h .. 8h + 7 of both
 // operands, so every product pairs matching k.
+//
+// B row-major (K x N, n contiguous; BROW): a chunk of B is KC k-rows of the
+// workgroup's 32 columns (64 contiguous bytes per row), stored in the slot
+// row after row by the same direct loads (16 k-rows per wave instruction).
+// The MFMA still wants eight consecutive k of one column n per lane; gfx950's
+// transposing LDS read ds_read_b64_tr_b16 delivers them: within each group
+// of 16 lanes, lane s = 4 i + a supplies the address of 4 consecutive values
+// of a row and lane j = 4 a + b receives value b of the rows supplied by
+// lanes a, 4 + a, 8 + a, 12 + a.  With lane s pointing at k-row kb + i,
+// columns nb + 4 a .. + 3, lane j gets column nb + j at k-rows kb .. kb + 3;
+// a second read at kb + 4 completes the eight.
 #include "kernels.hpp"
 
 namespace ge {
@@ -90,7 +101,7 @@ __device__ __forceinline__ void arrive() {
   asm volatile("" ::: "memory");
 }
 
-template <typename TIn, typename TOut, int NW, int P, int KC, int EPI>
+template <typename TIn, typename TOut, int NW, int P, int KC, int EPI, bool BROW>
 __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const TIn* __restrict__ A, const TIn* __restrict__ B,
                                                               const TIn* __restrict__ bias, TOut* __restrict__ C,
                                                               int M, int N, int K, int lda, int ldb, int ldc,
@@ -142,7 +153,13 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const TIn* __restr
   // position p; chunk g of row r is stored at position g ^ (r % 16), so the
   // lane fetches global chunk p ^ (r % 16) of its row segment.
   const uint32_t row_bytes = (uint32_t)ldb * 2u, a_row_bytes = (uint32_t)lda * 2u;
-  const __amdgpu_buffer_rsrc_t rb = make_rsrc(B + (int64_t)n0 * ldb, 32u * row_bytes);
+  // (row-major B: the workgroup's 32 columns of all K rows; K ldb 2 < 2^32
+  // is checked on the host)
+  const __amdgpu_buffer_rsrc_t rb =
+      BROW ? make_rsrc(B + n0, (uint32_t)((int64_t)(K - 1) * ldb * 2 + 64)) : make_rsrc(B + (int64_t)n0 * ldb, 32u * row_bytes);
+  // Row-major B: instruction t of a chunk fills k-rows 16 t .. 16 t + 15;
+  // lane L takes k-row 16 t + L / 4, bytes 16 (L % 4) .. + 15 of its 64.
+  const uint32_t vbr = (uint32_t)(lane >> 2) * row_bytes + (uint32_t)((lane & 3) << 4);
   // A's chunk uses the same mapping, but with the whole row offset in the
   // per-lane part: the buffer's range check covers only that part, and it
   // is what turns rows past M into zeros.
@@ -181,29 +198,69 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const TIn* __restr
   // k = 0), and the others move back by 2 kpad in their own offset.  Both
   // operands are masked, so that no value from before a row's start enters
   // a product.
+  // Row-major B shifts whole k-rows: chunk gc >= 1 starts kpad rows early
+  // in the wave-uniform offset; in chunk 0 rows below kpad load as zeros
+  // and the others move back by kpad rows in their own offset.
+  auto issue_brow = [&](int j, int gc) __attribute__((always_inline)) {
+#pragma unroll
+    for (int d = 0; d < ND; ++d) {
+      const int t = wave * ND + d;
+      if (gc == 0 && kpad != 0) {
+        const int row = 16 * t + (lane >> 2);
+        const uint32_t v =
+            row < kpad ? 0xFFFFFFF0u : (uint32_t)(row - kpad) * row_bytes + (uint32_t)((lane & 3) << 4);
+        load_lds16(rb, slot[j] + t * 1024, v, 0u);
+      } else {
+        load_lds16(rb, slot[j] + t * 1024, vbr, (uint32_t)(16 * t + gc * KC - kpad) * row_bytes);
+      }
+    }
+  };
   auto issue = [&](int j, int c) __attribute__((always_inline)) {
     const int gc = (c + rot) % nchunks + cbase;
     const uint32_t pad2 = 2u * (uint32_t)kpad;
+    if constexpr (BROW) issue_brow(j, gc);
     if (gc == 0 && kpad != 0) {
+      if constexpr (!BROW) {
 #pragma unroll
-      for (int d = 0; d < ND; ++d)
-        load_lds16(rb, slot[j] + (wave * ND + d) * 1024, kz[d] < pad2 ? 0xFFFFFFF0u : vb[d] - pad2, sb[d]);
+        for (int d = 0; d < ND; ++d)
+          load_lds16(rb, slot[j] + (wave * ND + d) * 1024, kz[d] < pad2 ? 0xFFFFFFF0u : vb[d] - pad2, sb[d]);
+      }
 #pragma unroll
       for (int d = 0; d < ND; ++d)
         load_lds16(ra, slot_a[j] + (wave * ND + d) * 1024, kz[d] < pad2 ? 0xFFFFFFF0u : vas[d] - pad2, 0u);
     } else {
       const uint32_t kb = (uint32_t)gc * RB - pad2;
+      if constexpr (!BROW) {
 #pragma unroll
-      for (int d = 0; d < ND; ++d)
-        load_lds16(rb, slot[j] + (wave * ND + d) * 1024, vb[d], sb[d] + kb);
+        for (int d = 0; d < ND; ++d)
+          load_lds16(rb, slot[j] + (wave * ND + d) * 1024, vb[d], sb[d] + kb);
+      }
 #pragma unroll
       for (int d = 0; d < ND; ++d) load_lds16(ra, slot_a[j] + (wave * ND + d) * 1024, vas[d], kb);
     }
   };
+  // Row-major B, MFMA q: lane (r, h) needs column r at k-rows
+  // 16 (w MF + q) + 8 h .. + 7; lane s = l % 16 of its 16-lane group
+  // addresses k-row 8 h + s / 4 (+ 4 for the second read), columns
+  // 16 ((l / 16) % 2) + 4 (s % 4) .. + 3.
+  const int rtr = (8 * h + ((lane & 15) >> 2)) * 64 + 32 * ((lane >> 4) & 1) + 8 * (lane & 3);
   auto compute = [&](int j) __attribute__((always_inline)) {
     u32x4 b[MF];
+    if constexpr (BROW) {
+      typedef short s4v __attribute__((vector_size(8)));
+      typedef __attribute__((address_space(3))) s4v lds_s4v;
 #pragma unroll
-    for (int q = 0; q < MF; ++q) b[q] = *(const u32x4*)(slot[j] + rd[q]);
+      for (int q = 0; q < MF; ++q) {
+        char* p0 = slot[j] + 1024 * (wave * MF + q) + rtr;
+        const s4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4v*)(lds_ptr)p0);
+        const s4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4v*)(lds_ptr)(p0 + 256));
+        const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+        b[q] = u32x4{l2.x, l2.y, h2.x, h2.y};
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < MF; ++q) b[q] = *(const u32x4*)(slot[j] + rd[q]);
+    }
     // A's slot has B's layout: lane (m, h) reads row m at B's positions
     u32x4 x[MF];
 #pragma unroll
@@ -392,44 +449,44 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const TIn* __restr
   }
 }
 
-template <typename TIn, typename TOut, int NW, int P, int KC, int EPI>
+template <typename TIn, typename TOut, int NW, int P, int KC, int EPI, bool BROW>
 hipError_t launch_skinny(const LaunchArgs& a) {
   // split K when the caller gave a workspace: partial blocks, then one
   // arrival counter per column block
   const int nblocks = (a.N + 31) / 32;
   float* part = a.split > 1 ? (float*)a.workspace : nullptr;
   unsigned* arrivals = a.split > 1 ? (unsigned*)((char*)a.workspace + (size_t)nblocks * a.split * 4096) : nullptr;
-  hipLaunchKernelGGL((gemm_skinny_kernel<TIn, TOut, NW, P, KC, EPI>), dim3(nblocks, a.split > 1 ? a.split : 1),
+  hipLaunchKernelGGL((gemm_skinny_kernel<TIn, TOut, NW, P, KC, EPI, BROW>), dim3(nblocks, a.split > 1 ? a.split : 1),
                      dim3(NW * 64), 0, a.stream, (const TIn*)a.A, (const TIn*)a.B, (const TIn*)a.bias, (TOut*)a.C,
                      a.M, a.N, a.K, a.lda, a.ldb, a.ldc, part, arrivals, a.scale, (const TOut*)a.residual,
                      a.out_scale);
   return hipGetLastError();
 }
 
-template <typename TIn, typename TOut, int NW, int P, int KC>
+template <typename TIn, typename TOut, int NW, int P, int KC, bool BROW>
 LaunchFn pick_epi(int epi) {
   switch (epi) {
-    case GEMM_EPI_NONE: return &launch_skinny<TIn, TOut, NW, P, KC, GEMM_EPI_NONE>;
-    case GEMM_EPI_RELU: return &launch_skinny<TIn, TOut, NW, P, KC, GEMM_EPI_RELU>;
-    case GEMM_EPI_BIAS_RELU: return &launch_skinny<TIn, TOut, NW, P, KC, GEMM_EPI_BIAS_RELU>;
-    case GEMM_EPI_BIAS_GELU: return &launch_skinny<TIn, TOut, NW, P, KC, GEMM_EPI_BIAS_GELU>;
-    case GEMM_EPI_BIAS: return &launch_skinny<TIn, TOut, NW, P, KC, GEMM_EPI_BIAS>;
-    case GEMM_EPI_SILU: return &launch_skinny<TIn, TOut, NW, P, KC, GEMM_EPI_SILU>;
-    case GEMM_EPI_BIAS_SILU: return &launch_skinny<TIn, TOut, NW, P, KC, GEMM_EPI_BIAS_SILU>;
+    case GEMM_EPI_NONE: return &launch_skinny<TIn, TOut, NW, P, KC, GEMM_EPI_NONE, BROW>;
+    case GEMM_EPI_RELU: return &launch_skinny<TIn, TOut, NW, P, KC, GEMM_EPI_RELU, BROW>;
+    case GEMM_EPI_BIAS_RELU: return &launch_skinny<TIn, TOut, NW, P, KC, GEMM_EPI_BIAS_RELU, BROW>;
+    case GEMM_EPI_BIAS_GELU: return &launch_skinny<TIn, TOut, NW, P, KC, GEMM_EPI_BIAS_GELU, BROW>;
+    case GEMM_EPI_BIAS: return &launch_skinny<TIn, TOut, NW, P, KC, GEMM_EPI_BIAS, BROW>;
+    case GEMM_EPI_SILU: return &launch_skinny<TIn, TOut, NW, P, KC, GEMM_EPI_SILU, BROW>;
+    case GEMM_EPI_BIAS_SILU: return &launch_skinny<TIn, TOut, NW, P, KC, GEMM_EPI_BIAS_SILU, BROW>;
     default: return nullptr;
   }
 }
 
-template <int NW, int P, int KC>
+template <int NW, int P, int KC, bool BROW = false>
 LaunchFn pick_types(const Problem& p) {
   if (p.in_dt == GEMM_EPI_F16) {
-    if (p.out_dt == GEMM_EPI_F16) return pick_epi<f16, f16, NW, P, KC>(p.epi);
-    if (p.out_dt == GEMM_EPI_F32) return pick_epi<f16, float, NW, P, KC>(p.epi);
-    if (p.out_dt == GEMM_EPI_FP8_E4M3) return pick_epi<f16, fp8e4m3, NW, P, KC>(p.epi);
+    if (p.out_dt == GEMM_EPI_F16) return pick_epi<f16, f16, NW, P, KC, BROW>(p.epi);
+    if (p.out_dt == GEMM_EPI_F32) return pick_epi<f16, float, NW, P, KC, BROW>(p.epi);
+    if (p.out_dt == GEMM_EPI_FP8_E4M3) return pick_epi<f16, fp8e4m3, NW, P, KC, BROW>(p.epi);
   } else if (p.in_dt == GEMM_EPI_BF16) {
-    if (p.out_dt == GEMM_EPI_BF16) return pick_epi<bf16, bf16, NW, P, KC>(p.epi);
-    if (p.out_dt == GEMM_EPI_F32) return pick_epi<bf16, float, NW, P, KC>(p.epi);
-    if (p.out_dt == GEMM_EPI_FP8_E4M3) return pick_epi<bf16, fp8e4m3, NW, P, KC>(p.epi);
+    if (p.out_dt == GEMM_EPI_BF16) return pick_epi<bf16, bf16, NW, P, KC, BROW>(p.epi);
+    if (p.out_dt == GEMM_EPI_F32) return pick_epi<bf16, float, NW, P, KC, BROW>(p.epi);
+    if (p.out_dt == GEMM_EPI_FP8_E4M3) return pick_epi<bf16, fp8e4m3, NW, P, KC, BROW>(p.epi);
   }
   return nullptr;
 }
@@ -438,12 +495,16 @@ LaunchFn pick_types(const Problem& p) {
 // K into at least P chunks, else the first one that fits with K padded.  LDS: B and A rings, each P x 32 rows x 2 KC
 // bytes.
 const SkinnyConfig kSkinny[] = {
-    {8, 5, 256, "skinny_32n_8w_5x256k"},  // 80 + 80 KiB: four chunks of 512-byte row segments in flight
-    {8, 4, 256, "skinny_32n_8w_4x256k"},  // 64 + 64 KiB
-    {4, 4, 256, "skinny_32n_4w_4x256k"},  // 64 + 64 KiB, fewer waves
-    {4, 8, 128, "skinny_32n_4w_8x128k"},  // 64 + 64 KiB, 256-byte row segments, seven chunks in flight
-    {4, 2, 256, "skinny_32n_4w_2x256k"},  // 32 + 32 KiB: K down to 512
-    {2, 2, 128, "skinny_32n_2w_2x128k"},  // 16 + 16 KiB: K down to 256
+    {8, 5, 256, "skinny_32n_8w_5x256k", false},  // 80 + 80 KiB: four chunks of 512-byte row segments in flight
+    {8, 4, 256, "skinny_32n_8w_4x256k", false},  // 64 + 64 KiB
+    {4, 4, 256, "skinny_32n_4w_4x256k", false},  // 64 + 64 KiB, fewer waves
+    {4, 8, 128, "skinny_32n_4w_8x128k", false},  // 64 + 64 KiB, 256-byte row segments, seven chunks in flight
+    {4, 2, 256, "skinny_32n_4w_2x256k", false},  // 32 + 32 KiB: K down to 512
+    {2, 2, 128, "skinny_32n_2w_2x128k", false},  // 16 + 16 KiB: K down to 256
+    // B row-major: 64-byte row pieces of 32 columns, transposing LDS reads
+    {8, 5, 256, "skinny_rowb_32n_8w_5x256k", true},
+    {4, 8, 128, "skinny_rowb_32n_4w_8x128k", true},
+    {2, 2, 128, "skinny_rowb_32n_2w_2x128k", true},
 };
 
 }  // namespace
@@ -457,10 +518,13 @@ bool skinny_supports(int cfg, const Problem& p) {
   // least one chunk per ring slot; rows 16-byte aligned (leading dimensions
   // multiples of 8); 32 rows of B and all of A must be addressable by one
   // buffer resource
+  // (row-major B: the workgroup's buffer spans all K rows, K ldb 2 < 2^32)
   const SkinnyConfig& c = kSkinny[cfg];
-  return p.M >= 1 && p.M <= 32 && p.la == GEMM_EPI_ROW_MAJOR && p.lb == GEMM_EPI_COL_MAJOR && p.N >= 32 && p.N % 8 == 0 &&
-         p.K % 8 == 0 && (p.K + c.kc - 1) / c.kc >= c.stages && p.lda % 8 == 0 && p.ldb % 8 == 0 && p.ldc % 8 == 0 &&
-         32 * p.ldb * 2 < ((int64_t)1 << 32) && p.M * p.lda * 2 < ((int64_t)1 << 32);
+  const bool b_ok = c.brow ? p.lb == GEMM_EPI_ROW_MAJOR && p.K * p.ldb * 2 < ((int64_t)1 << 32)
+                           : p.lb == GEMM_EPI_COL_MAJOR && 32 * p.ldb * 2 < ((int64_t)1 << 32);
+  return p.M >= 1 && p.M <= 32 && p.la == GEMM_EPI_ROW_MAJOR && b_ok && p.N >= 32 && p.N % 8 == 0 && p.K % 8 == 0 &&
+         (p.K + c.kc - 1) / c.kc >= c.stages && p.lda % 8 == 0 && p.ldb % 8 == 0 && p.ldc % 8 == 0 &&
+         p.M * p.lda * 2 < ((int64_t)1 << 32);
 }
 
 int skinny_split(int cfg, const Problem& p) {
@@ -490,6 +554,9 @@ LaunchFn skinny_launcher(int cfg, const Problem& p) {
     case 3: return pick_types<4, 8, 128>(p);
     case 4: return pick_types<4, 2, 256>(p);
     case 5: return pick_types<2, 2, 128>(p);
+    case 6: return pick_types<8, 5, 256, true>(p);
+    case 7: return pick_types<4, 8, 128, true>(p);
+    case 8: return pick_types<2, 2, 128, true>(p);
     default: return nullptr;
   }
 }

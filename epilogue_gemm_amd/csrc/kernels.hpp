@@ -45,6 +45,7 @@ struct SkinnyConfig {
   int stages;  // LDS ring slots: chunks in flight + the one being multiplied
   int kc;      // k-values per chunk
   const char* name;
+  bool brow;   // B row-major (K x N, n contiguous) instead of column-major
 };
 int skinny_num_configs();
 const SkinnyConfig& skinny_config(int cfg);

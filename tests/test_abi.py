@@ -142,7 +142,10 @@ def test_fp8_output_needs_16_columns_in_tile_kernels(lib):
     (32, 8192, 8200, "row", "col", "skinny", "skinny_32n_8w_5x256k"),  # 33 chunks of 256, the first padded
     (32, 8192, 8320, "row", "col", "skinny", "skinny_32n_4w_8x128k"),  # whole chunks of 128 come first
     (32, 8192, 8196, "row", "col", "generic", "generic"),  # K not a multiple of 8
-    (32, 8192, 8192, "row", "row", "generic", "generic"),  # small M, N-contiguous B: no fast path yet
+    (32, 8192, 8192, "row", "row", "skinny", "skinny_rowb_32n_8w_5x256k"),  # N-contiguous B: transposing LDS reads
+    (32, 4096, 1152, "row", "row", "skinny", "skinny_rowb_32n_4w_8x128k"),  # nine chunks of 128
+    (32, 4096, 200, "row", "row", "skinny", "skinny_rowb_32n_2w_2x128k"),  # two chunks of 128, the first padded
+    (32, 8192, 8192, "col", "row", "generic", "generic"),  # column-major A: no decode-shape kernel
     (2000, 8200, 4096, "row", "col", "tile", "tile_256x256x64_m16"),  # last tile row and column shifted back
     (1000, 1000, 1024, "row", "col", "tile", "tile_64x64x64"),  # 16 x 16 edge-tiled 64 x 64 tiles
     (3000, 2000, 4096, "row", "row", "tile", "tile_128x128x64"),  # 24 x 16 tiles of 128
@@ -169,7 +172,7 @@ def test_select_forces_and_validates(lib):
     h = gb.gemm_epi_plan(512, 512, 256, "f16", "f32", "row", "col", "none")
     try:
         assert gb.gemm_epi_num_configs("tile") == 5
-        assert gb.gemm_epi_num_configs("skinny") == 6
+        assert gb.gemm_epi_num_configs("skinny") == 9
         assert gb.gemm_epi_num_configs("generic") == 1
         assert gb.gemm_epi_num_configs("auto") == 0
         for cfg in range(4):
@@ -204,19 +207,22 @@ def test_select_forces_and_validates(lib):
 # (k per chunk, ring slots) of each skinny configuration, in order: K must
 # be a multiple of 8 that makes at least one chunk per slot, the first chunk
 # padded with zeros when K is not a whole number of chunks
-SKINNY_CHUNKS = [(256, 5), (256, 4), (256, 4), (128, 8), (256, 2), (128, 2)]
+# (configurations 0-5 take a column-major B, 6-8 a row-major one)
+SKINNY_CHUNKS = [(256, 5), (256, 4), (256, 4), (128, 8), (256, 2), (128, 2), (256, 5), (128, 8), (128, 2)]
 
 
 def test_skinny_k_granularity(lib):
     assert gb.gemm_epi_num_configs("skinny") == len(SKINNY_CHUNKS)
     for cfg, (kc, slots) in enumerate(SKINNY_CHUNKS):
+        lb, other = ("col", "row") if cfg < 6 else ("row", "col")
         for K, ok in ((kc * slots, True), (kc * (slots + 1), True), (kc * (slots - 1), False),
                       (kc * slots + 64, True), (kc * (slots - 1) + 8, True), (kc * slots + 4, False)):
-            h = gb.gemm_epi_plan(32, 64, K, "bf16", "bf16", "row", "col", "none")
-            try:
-                assert (gb.gemm_epi_plan_select(h, "skinny", cfg) == 0) == ok, (cfg, K)
-            finally:
-                gb.gemm_epi_destroy(h)
+            for layout, want in ((lb, ok), (other, False)):
+                h = gb.gemm_epi_plan(32, 64, K, "bf16", "bf16", "row", layout, "none")
+                try:
+                    assert (gb.gemm_epi_plan_select(h, "skinny", cfg) == 0) == want, (cfg, K, layout)
+                finally:
+                    gb.gemm_epi_destroy(h)
 
 
 def test_workspace_size(lib):

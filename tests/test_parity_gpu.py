@@ -285,6 +285,57 @@ def test_skinny_k_tail_random_decode_shape():
     assert r["ok"], r
 
 
+# row-major B (K x N, n contiguous): configurations 6-8, whose B fragments
+# come from transposing LDS reads
+SKINNY_ROWB = {6: (256, 5), 7: (128, 8), 8: (128, 2)}
+
+
+@pytest.mark.parametrize("config", sorted(SKINNY_ROWB))
+@pytest.mark.parametrize("M", [1, 7, 32])
+@pytest.mark.parametrize("in_dt,out_dt", [("bf16", "bf16"), ("f16", "f32")])
+def test_skinny_rowb_integer_bitexact(config, M, in_dt, out_dt):
+    # one ring turn, heads of one and of P - 1 chunks before the whole turns,
+    # K tails (the largest and a middle pad); N = 1000 shifts the last
+    # column block back to end at N
+    kc, slots = SKINNY_ROWB[config]
+    cases = [(kc * slots, "bias_relu", 96), (kc * (2 * slots + 1), "bias", 1000), (kc * (2 * slots - 1), "none", 96),
+             (kc * (slots - 1) + 8, "relu", 40), (kc * slots + kc // 2 + 8, "bias", 96)]
+    for K, epi, N in cases:
+        bits = inputs.integer_inputs(M, N, K, in_dt, "row", "row", epi.startswith("bias"), seed=M + K)
+        name = check_case(bits, M, N, K, in_dt, out_dt, "row", "row", epi, "skinny", config, True)
+        assert name.startswith("skinny_rowb_"), name
+
+
+def test_skinny_rowb_split_and_random():
+    # split K with a workspace (bit-exact on two runs, workspace left
+    # zero-filled), then the 32 x 8192 x 8192 decode shape with random
+    # operands through the automatic plan
+    M, N, K = 32, 1024, 7944
+    bits = inputs.integer_inputs(M, N, K, "bf16", "row", "row", True, seed=5)
+    plan = gb.Plan(M, N, K, "bf16", "bf16", "row", "row", "bias_relu")
+    assert plan.name == "skinny_rowb_32n_8w_5x256k" and plan.workspace_size > 0
+    A, B = parity.to_device(bits["A"], "bf16"), parity.to_device(bits["B"], "bf16")
+    bias = parity.to_device(bits["bias"], "bf16")
+    c = oracle_full(bits, M, N, K, "bf16", "bf16", "row", "row", "bias_relu")[1]
+    ws = torch.zeros(plan.workspace_size, dtype=torch.uint8, device="cuda")
+    for w in (ws, ws, None):
+        C = parity.empty_out(M * N, "bf16")
+        C.fill_(float("nan"))
+        plan.run(A, B, bias, C, workspace=w)
+        torch.cuda.synchronize()
+        mism = np.count_nonzero(parity.out_bits(C).reshape(-1) != c.reshape(-1).astype(np.uint16))
+        assert mism == 0, (w is None, mism)
+    assert not ws.cpu().numpy().any()
+    plan.close()
+    M, N, K = 32, 8192, 8192
+    bits = inputs.make_inputs(M, N, K, "bf16", "row", "row", True, float(np.sqrt(K)), 0.1, seed=22)
+    got, name = run_gpu(bits, M, N, K, "bf16", "bf16", "row", "row", "bias_gelu")
+    assert name == "skinny_rowb_32n_8w_5x256k"
+    y, c = oracle_full(bits, M, N, K, "bf16", "bf16", "row", "row", "bias_gelu")
+    r = parity.compare(got, c, y, "bf16")
+    assert r["ok"], r
+
+
 @pytest.mark.parametrize("M,N,K", [(1, 1, 1), (2, 8, 4), (37, 53, 29), (65, 130, 200), (3, 700, 5)])
 @pytest.mark.parametrize("la,lb", [("row", "col"), ("row", "row"), ("col", "col"), ("col", "row")])
 def test_generic_integer_bitexact(M, N, K, la, lb):
