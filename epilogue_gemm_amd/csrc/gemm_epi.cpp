@@ -162,12 +162,13 @@ bool resolve(gemm_epi_plan_s* pl, int kernel, int config) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-// Workspace of a split-K skinny run: one fp32 32 x 32 partial block per
+// Workspace of a split-K skinny run: one fp32 32 x cols partial block per
 // (column block, split), then one arrival counter per column block.
 size_t workspace_bytes(const gemm_epi_plan_s* pl) {
   if (pl->kernel != GEMM_EPI_KERNEL_SKINNY || pl->split <= 1) return 0;
-  const size_t nblocks = (size_t)((pl->p.N + 31) / 32);
-  return nblocks * (size_t)pl->split * 4096 + ((nblocks * 4 + 255) & ~(size_t)255);
+  const int cols = ge::skinny_config(pl->config).cols;
+  const size_t nblocks = (size_t)((pl->p.N + cols - 1) / cols);
+  return nblocks * (size_t)pl->split * (128 * (size_t)cols) + ((nblocks * 4 + 255) & ~(size_t)255);
 }
 
 gemm_epi_status launch(gemm_epi_plan_t plan, const void* A, const void* B, const void* bias,

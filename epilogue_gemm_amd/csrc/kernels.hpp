@@ -46,6 +46,7 @@ struct SkinnyConfig {
   int kc;      // k-values per chunk
   const char* name;
   bool brow;   // B row-major (K x N, n contiguous) instead of column-major
+  int cols;    // output columns per workgroup (32, or 64 with a row-major B)
 };
 int skinny_num_configs();
 const SkinnyConfig& skinny_config(int cfg);

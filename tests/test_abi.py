@@ -142,8 +142,9 @@ def test_fp8_output_needs_16_columns_in_tile_kernels(lib):
     (32, 8192, 8200, "row", "col", "skinny", "skinny_32n_8w_5x256k"),  # 33 chunks of 256, the first padded
     (32, 8192, 8320, "row", "col", "skinny", "skinny_32n_4w_8x128k"),  # whole chunks of 128 come first
     (32, 8192, 8196, "row", "col", "generic", "generic"),  # K not a multiple of 8
-    (32, 8192, 8192, "row", "row", "skinny", "skinny_rowb_32n_8w_5x256k"),  # N-contiguous B: transposing LDS reads
-    (32, 4096, 1152, "row", "row", "skinny", "skinny_rowb_32n_4w_8x128k"),  # nine chunks of 128
+    (32, 8192, 8192, "row", "row", "skinny", "skinny_rowb_64n_8w_6x128k"),  # N-contiguous B: transposing LDS reads
+    (32, 4096, 1152, "row", "row", "skinny", "skinny_rowb_64n_8w_6x128k"),  # nine chunks of 128
+    (32, 40, 1152, "row", "row", "skinny", "skinny_rowb_32n_4w_8x128k"),  # N < 64: 32-column workgroups
     (32, 4096, 200, "row", "row", "skinny", "skinny_rowb_32n_2w_2x128k"),  # two chunks of 128, the first padded
     (32, 8192, 8192, "col", "row", "generic", "generic"),  # column-major A: no decode-shape kernel
     (2000, 8200, 4096, "row", "col", "tile", "tile_256x256x64_m16"),  # last tile row and column shifted back
@@ -172,7 +173,7 @@ def test_select_forces_and_validates(lib):
     h = gb.gemm_epi_plan(512, 512, 256, "f16", "f32", "row", "col", "none")
     try:
         assert gb.gemm_epi_num_configs("tile") == 5
-        assert gb.gemm_epi_num_configs("skinny") == 9
+        assert gb.gemm_epi_num_configs("skinny") == 10
         assert gb.gemm_epi_num_configs("generic") == 1
         assert gb.gemm_epi_num_configs("auto") == 0
         for cfg in range(4):
@@ -207,8 +208,8 @@ def test_select_forces_and_validates(lib):
 # (k per chunk, ring slots) of each skinny configuration, in order: K must
 # be a multiple of 8 that makes at least one chunk per slot, the first chunk
 # padded with zeros when K is not a whole number of chunks
-# (configurations 0-5 take a column-major B, 6-8 a row-major one)
-SKINNY_CHUNKS = [(256, 5), (256, 4), (256, 4), (128, 8), (256, 2), (128, 2), (256, 5), (128, 8), (128, 2)]
+# (configurations 0-5 take a column-major B, 6-9 a row-major one)
+SKINNY_CHUNKS = [(256, 5), (256, 4), (256, 4), (128, 8), (256, 2), (128, 2), (256, 5), (128, 8), (128, 2), (128, 6)]
 
 
 def test_skinny_k_granularity(lib):

@@ -97,12 +97,12 @@ def test_skinny_strided_k_tail_integer_bitexact(config):
         assert name.startswith("skinny_")
 
 
-@pytest.mark.parametrize("config", [6, 7, 8])
+@pytest.mark.parametrize("config", [6, 7, 8, 9])
 def test_skinny_rowb_strided_integer_bitexact(config):
     # row-major B with padded rows (and K tails): the NaN padding past
     # column N, and the rows before k = 0 of the shifted first chunk, must
     # never reach a product
-    K = {6: 1288, 7: 1160, 8: 264}[config]
+    K = {6: 1288, 7: 1160, 8: 264, 9: 1160}[config]
     for M, N, in_dt, out_dt, epi, pads in ((32, 96, "bf16", "bf16", "bias", (8, 24, 8)),
                                            (5, 200, "f16", "f32", "none", (64, 8, 0))):
         name = run_strided(M, N, K, in_dt, out_dt, "row", "row", epi, pads, "skinny", config)
