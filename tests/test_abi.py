@@ -384,3 +384,21 @@ def test_attention_validates_without_touching_the_device(lib):
     assert gb.gemm_epi_attention_fwd(p, p, p, p, 1, 192, 1, 64, "bf16", 1, None) == 2  # S % 128
     assert gb.gemm_epi_attention_fwd(p + 8, p, p, p, 1, 128, 1, 64, "bf16", 1, None) == 2  # alignment
     assert gb.gemm_epi_attention_fwd(p, p, p, p, 1 << 12, 1 << 12, 1 << 4, 64, "bf16", 0, None) == 2  # 2^34 elements
+
+
+def test_skinny_rowb_64_columns(lib):
+    # configuration 9 gives a workgroup 64 columns of a row-major B: it needs
+    # N >= 64, and its split-K partial blocks are 32 x 64 fp32 (8 KiB)
+    for N, ok in ((40, False), (64, True), (72, True)):
+        h = gb.gemm_epi_plan(32, N, 1152, "bf16", "bf16", "row", "row", "none")
+        try:
+            assert (gb.gemm_epi_plan_select(h, "skinny", 9) == 0) == ok, N
+        finally:
+            gb.gemm_epi_destroy(h)
+    h = gb.gemm_epi_plan(32, 1024, 7928, "bf16", "bf16", "row", "row", "bias")
+    try:
+        assert gb.gemm_epi_plan_describe(h)[:3] == ("skinny", 9, "skinny_rowb_64n_8w_6x128k")
+        # 16 column blocks x 2 splits of 31 chunks of 128, then 16 counters (256 bytes)
+        assert gb.gemm_epi_workspace_size(h) == 16 * 2 * 8192 + 256
+    finally:
+        gb.gemm_epi_destroy(h)
