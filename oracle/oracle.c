@@ -19,11 +19,9 @@
  *   list of its closing chapter).  E4M3 follows the OCP 8-bit floating
  *   point definition: 1 sign, 4 exponent (bias 7), 3 fraction bits, no
  *   infinities, S.1111.111 the only NaN, largest finite 448.  Encoding to
- *   E4M3 saturates: |q y| >= 448 gives +-448.  Its rounding decision is
- *   taken from q y rounded to fp32 first (round to nearest even), then
- *   rounded to nearest even in E4M3 -- the precision in which a GPU kernel
- *   that works in fp32 decides the code; a residual is not defined for
- *   FP8 output.
+ *   E4M3 is, like every other output format, one round-to-nearest-even
+ *   step straight from the fp64 value q y, saturating: |q y| >= 448 gives
+ *   +-448.  A residual is not defined for FP8 output.
  *
  *   s[j] (an optional fp32 per-column scale, 1 when absent) and r[i][j] (an
  *   optional M x N row-major residual in the output format, 0 when absent)
@@ -183,12 +181,9 @@ uint32_t oracle_encode(int fmt, double x) {
   return encode_bits(x, fmt_mant(fmt), fmt_expb(fmt));
 }
 
-/* Output code of y: one RNE to a 16- or 32-bit format; for E4M3, RNE to
- * fp32 first, then RNE (saturating) to E4M3. */
-static uint32_t encode_out(int fmt, double y) {
-  if (fmt == ORC_FP8) return encode_e4m3(oracle_decode(ORC_F32, oracle_encode(ORC_F32, y)));
-  return oracle_encode(fmt, y);
-}
+/* Output code of y: one RNE step from fp64 to the output format
+ * (saturating for E4M3). */
+static uint32_t encode_out(int fmt, double y) { return oracle_encode(fmt, y); }
 
 /* Element-wise forms of the two conversions above, for n values. */
 void oracle_decode_n(int fmt, const uint32_t* bits, double* out, int64_t n) {

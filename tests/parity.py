@@ -3,10 +3,14 @@
 Tolerance (stated for this path): relative Frobenius error <= 1e-3 and
 max elementwise error <= 2e-2, both measured between the GPU output and the
 oracle's output rounded to the same format.  An element whose error exceeds
-2e-2 is still accepted when the GPU value is one of the two output-format
-neighbours that bracket the oracle's exact fp64 value: near a rounding tie,
-fp32 accumulation noise may legitimately pick either neighbour, and in bf16
-one ulp is 0.03125 for |y| in [4, 8).
+2e-2 is still accepted when the GPU value is the other of the two
+output-format neighbours that bracket the oracle's exact fp64 value: near a
+rounding tie, fp32 accumulation noise may legitimately pick either
+neighbour, and in bf16 one ulp is 0.03125 for |y| in [4, 8).  Such accepted
+flips are counted, and at most max(1, 1e-3 n) of n outputs may take one: a
+systematic one-ulp bias (truncation, say) flips a large share of them.  The
+same rule holds for every output format; the relative error is always taken
+over the outputs as the GPU wrote them.
 """
 from __future__ import annotations
 
@@ -17,9 +21,8 @@ REL_FRO_TOL = 1e-3
 MAX_ABS_TOL = 2e-2
 
 _TORCH_DT = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32, "fp8": torch.float8_e4m3fn}
-# largest fraction of outputs allowed to take the other rounding at a near-tie
-# (a quantised fp8 code); a systematic one-ulp bias (truncation, say) flips
-# about half of them
+# largest fraction of outputs (at least one) allowed to take the other
+# rounding at a near-tie with an error above the max-abs bound
 MAX_TIE_FLIP_FRACTION = 1e-3
 
 
@@ -104,16 +107,9 @@ def compare(gpu_bits, oracle_bits, oracle_y, dtype: str, rel_tol=REL_FRO_TOL, ab
         if y[idx] == o[idx] or gpu_bits[idx] != other[0]:
             rejected.append(int(idx))
     max_abs = float(err.max()) if err.size else 0.0
-    ok = finite and rel <= rel_tol and not rejected
-    if dtype == "fp8":
-        # one fp8 ulp is 1/16 to 1/8 relative: an accepted near-tie flip is
-        # not an error, so rel is taken with those elements at the oracle's
-        # code, and the share of flips is bounded instead
-        accepted = np.setdiff1d(over, np.array(rejected, dtype=over.dtype))
-        g2 = g.copy()
-        g2[accepted] = o[accepted]
-        rel = float(np.linalg.norm(g2 - o) / max(float(np.linalg.norm(o)), 1e-12))
-        ok = finite and rel <= rel_tol and not rejected and accepted.size <= MAX_TIE_FLIP_FRACTION * g.size
+    n_accepted = int(over.size) - len(rejected)
+    max_flips = max(1, int(MAX_TIE_FLIP_FRACTION * g.size))
+    ok = finite and rel <= rel_tol and not rejected and n_accepted <= max_flips
     return {
         "ok": ok,
         "rel_fro": rel,
@@ -121,6 +117,7 @@ def compare(gpu_bits, oracle_bits, oracle_y, dtype: str, rel_tol=REL_FRO_TOL, ab
         "n": int(g.size),
         "n_over_abs_tol": int(over.size),
         "n_rejected": len(rejected),
+        "n_accepted": n_accepted,
         "n_mismatch_bits": int(np.count_nonzero(gpu_bits != oracle_bits)),
         "finite": finite,
     }

@@ -587,26 +587,83 @@ def test_fp8_output_all_ones_and_out_scale(fmt):
     assert np.array_equal(y, np.broadcast_to(-2.0 * np.maximum(8.0 + _values(bias, fmt), 0.0), (M, N)))
 
 
-def test_fp8_rounding_decided_from_fp32():
-    # a value just above an E4M3 tie in fp64 that rounds onto the tie in fp32
-    # is decided from the fp32 value: ties to even
+def _e4m3_brute_force(x):
+    """Nearest E4M3 code of each fp64 value by exhaustive search over the
+    finite codes (decoded by torch), ties to the code with an even last
+    fraction bit, saturating at +-448 -- no frexp/ldexp arithmetic, so it
+    shares nothing with the oracle's encoder."""
+    codes = np.arange(256, dtype=np.uint8)
+    vals = _torch_e4m3_values(codes)
+    fin = ~np.isnan(vals)
+    codes, vals = codes[fin], vals[fin]
+    out = np.empty(len(x), np.uint8)
+    for i, v in enumerate(x):
+        if np.isnan(v):
+            out[i] = 0x7F
+            continue
+        c = min(max(v, -448.0), 448.0)
+        d = np.abs(vals - c)
+        best = np.nonzero(d == d.min())[0]
+        if len(best) > 1:  # a tie (or +-0): the even code, positive zero's sign from v
+            even = [b for b in best if codes[b] & 1 == 0]
+            best = [b for b in even if (codes[b] >> 7) == (1 if np.signbit(v) else 0)] or even
+        out[i] = codes[best[0]]
+    return out
+
+
+def test_encode_fp8_single_rounding_from_fp64_brute_force():
+    # values that are not fp32-representable (so a rounding through fp32 would
+    # show), against an exhaustive nearest-code search
+    rng = np.random.default_rng(23)
+    x = np.concatenate([rng.standard_normal(4000) * 40, rng.standard_normal(1000) * 0.02,
+                        np.ldexp(rng.random(2000) + 1.0, rng.integers(-11, 9, 2000)),
+                        [500.0, -1e9, 0.0, -0.0, np.nan]])
+    # push a quarter of them onto near-ties: a midpoint between two codes plus
+    # or minus a few fp64 ulps (below fp32 resolution)
+    codes = np.arange(0, 0x7E, dtype=np.uint8)
+    v = _torch_e4m3_values(codes)
+    mids = (v[:-1] + v[1:]) / 2
+    pick = mids[rng.integers(0, len(mids), 3000)]
+    off = rng.choice([-1.0, 1.0], 3000) * np.ldexp(1.0, rng.integers(-45, -30, 3000)) * np.maximum(pick, 2.0**-9)
+    sgn = rng.choice([-1.0, 1.0], 3000)
+    x = np.concatenate([x, sgn * (pick + off), sgn * pick])
+    got = oracle.encode_array("fp8", x.astype(np.float64)).astype(np.uint8)
+    assert np.array_equal(got, _e4m3_brute_force(x))
+
+
+def test_fp8_output_rounded_once_from_fp64():
+    # A value just above (or below) an E4M3 tie by less than half an fp32 ulp
+    # goes to the nearer code: the output is rounded once, from the fp64
+    # value, like every other output format.
     fmt, M, N, K = "f16", 1, 1, 2
     a = _bits_of([1.0, 1.0], fmt)
-    # 1 + 1/16 + 2^-20 (an fp16 subnormal addend): exact in fp32, above the tie
+    # 1 + 1/16 lies halfway between the codes 1 (0x38) and 1.125 (0x39)
     b = _bits_of([1.0 + 1 / 16, 2.0**-20], fmt)
     y, c = oracle.gemm_epi(a, b, None, M, N, K, fmt, "fp8", "row", "row", "none")
-    assert y[0, 0] == 1.0 + 1 / 16 + 2.0**-20
-    assert c[0, 0] == 0x39
-    # 1 + 1/16 + 2^-24 is half an fp32 ulp above the tie: fp32 rounds it to
-    # the tie (even), and the tie goes to even in E4M3
+    assert y[0, 0] == 1.0 + 1 / 16 + 2.0**-20 and c[0, 0] == 0x39
+    # 1 + 1/16 + 2^-24 (the smallest fp16 subnormal as the second product):
+    # fp32 would round this onto the tie, which goes to even (0x38); one
+    # rounding from fp64 gives the upper neighbour
     b = _bits_of([1.0 + 1 / 16, 2.0**-24], fmt)
     y, c = oracle.gemm_epi(a, b, None, M, N, K, fmt, "fp8", "row", "row", "none")
-    assert y[0, 0] == 1.0 + 1 / 16 + 2.0**-24
-    assert c[0, 0] == 0x38
-    bf = _bits_of([1.0 + 1 / 16, 2.0**-30], "bf16")
-    y, c = oracle.gemm_epi(_bits_of([1.0, 1.0], "bf16"), bf, None, M, N, K, "bf16", "fp8", "row", "row", "none")
-    assert y[0, 0] == 1.0 + 1 / 16 + 2.0**-30
-    assert c[0, 0] == 0x38  # fp32 rounds 1 + 1/16 + 2^-30 onto the tie, which goes to even
+    assert y[0, 0] == 1.0 + 1 / 16 + 2.0**-24 and c[0, 0] == 0x39
+    # and just below the tie, by the same amount: the lower neighbour
+    b = _bits_of([1.0 + 1 / 16, -(2.0**-24)], fmt)
+    y, c = oracle.gemm_epi(a, b, None, M, N, K, fmt, "fp8", "row", "row", "none")
+    assert y[0, 0] == 1.0 + 1 / 16 - 2.0**-24 and c[0, 0] == 0x38
+    # bf16: 2^-30 above the tie between 1.125 and 1.25 (1 + 3/16, which goes
+    # to the even 1.25 = 0x3A when exact) is still the upper code; 2^-30
+    # below is the lower one
+    abf = _bits_of([1.0, 1.0], "bf16")
+    for extra, want in ((2.0**-30, 0x3A), (-(2.0**-30), 0x39), (0.0, 0x3A)):
+        bf = _bits_of([1.0 + 3 / 16, extra], "bf16")
+        y, c = oracle.gemm_epi(abf, bf, None, M, N, K, "bf16", "fp8", "row", "row", "none")
+        assert y[0, 0] == 1.0 + 3 / 16 + extra and c[0, 0] == want, (extra, hex(c[0, 0]))
+    # the exact tie 1 + 1/16 goes to even (0x38), as torch's fp32 -> e4m3fn does
+    ref = torch.tensor([1.0 + 1 / 16], dtype=torch.float32).to(torch.float8_e4m3fn).view(torch.uint8).item()
+    b = _bits_of([1.0 + 1 / 16, 0.0], fmt)
+    y, c = oracle.gemm_epi(a, b, None, M, N, K, fmt, "fp8", "row", "row", "none")
+    assert c[0, 0] == ref == 0x38
 
 
 def test_fp8_rejects_residual():
