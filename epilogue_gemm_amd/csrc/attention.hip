@@ -22,7 +22,8 @@
 //     16 t + 8 h + 0..7 of each 32-key group in accumulator order 8 t + u;
 //   * those 8 fp32 probabilities, rounded to the input format, are exactly
 //     the lane's second operand of O^T = V^T P^T for 16 keys: P never leaves
-//     the registers;
+//     the registers (bf16 adds a second operand, the rounded remainder, so
+//     that the weights keep about 16 bits);
 //   * O^T accumulates with V^T (from LDS) as first operand, so lane (i, h)
 //     holds 32 of query i's 64 outputs: the rescale by exp(m_old - m_new) is
 //     per lane, and the two halves of a query exchange their partial sums l
@@ -67,6 +68,11 @@ __device__ __forceinline__ float add_pair(uint32_t a, float acc) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2, a), __builtin_bit_cast(b2, 0x3f803f80u), acc, false);
   }
 }
+
+// bf16 probabilities are split into a rounded part and its rounded
+// remainder (see the kernel); fp16 ones are rounded once
+template <typename T>
+constexpr bool kSplitP = __is_same(T, bf16);
 
 template <typename T>
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
@@ -224,19 +230,34 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(const T* __restrict__ Q, 
     for (int g = 0; g < 2; ++g)
 #pragma unroll
       for (int x = 0; x < 16; ++x) s[g][x] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[g][x], scale_log2, -moff));
-    // O^T += V^T P^T, 16 keys at a time; l += the rounded P's row sums
+    // O^T += V^T P^T, 16 keys at a time; l += the rounded P's row sums.
+    // bf16 keeps 8 significant bits, so its P is carried as two bf16 parts:
+    // p_hi = bf16(p) and p_lo = bf16(p - p_hi) (the difference is exact in
+    // fp32), multiplied by two MFMAs into the same accumulator.  The
+    // weights then hold about 16 bits, like fp16's single part holds 11.
 #pragma unroll
     for (int g = 0; g < 2; ++g)
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        u32x4 p;
+        u32x4 p, plo;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-          p[w] = pack2<T>(s[g][8 * t + 2 * w], s[g][8 * t + 2 * w + 1]);
+          const float a = s[g][8 * t + 2 * w], b = s[g][8 * t + 2 * w + 1];
+          p[w] = pack2<T>(a, b);
           l_run = add_pair<T>(p[w], l_run);
+          if constexpr (kSplitP<T>) {
+            const float ah = __builtin_bit_cast(float, p[w] << 16);
+            const float bh = __builtin_bit_cast(float, p[w] & 0xffff0000u);
+            plo[w] = pack2<T>(a - ah, b - bh);
+            l_run = add_pair<T>(plo[w], l_run);
+          }
         }
 #pragma unroll
-        for (int dt = 0; dt < 2; ++dt) acc_o[dt] = mfma32<T>(*(const u32x4*)(sv + v_off(dt, g, t)), p, acc_o[dt]);
+        for (int dt = 0; dt < 2; ++dt) {
+          const u32x4 vf = *(const u32x4*)(sv + v_off(dt, g, t));
+          acc_o[dt] = mfma32<T>(vf, p, acc_o[dt]);
+          if constexpr (kSplitP<T>) acc_o[dt] = mfma32<T>(vf, plo, acc_o[dt]);
+        }
       }
   };
 
