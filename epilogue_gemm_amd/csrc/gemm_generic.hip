@@ -10,8 +10,13 @@
 namespace ge {
 namespace {
 
-constexpr int kGenThreadsX = 64;  // along N: a wave reads/writes consecutive columns
-constexpr int kGenThreadsY = 4;   // along M
+// Workgroups of 64 x 4 threads: x along N (a wave reads and writes
+// consecutive columns), y along M.  The grid's x extent in work-items is
+// then N rounded up to 64 (below 2^31 + 64, inside the 2^32 - 1 a grid
+// dimension allows, for every N a plan accepts); rows beyond what the y
+// extent covers are looped over.
+constexpr int kGenThreadsX = 64;
+constexpr int kGenThreadsY = 4;
 
 template <typename TIn, typename TOut, int EPI>
 __global__ __launch_bounds__(256) void gemm_generic_kernel(const TIn* __restrict__ A, const TIn* __restrict__ B,
@@ -21,10 +26,10 @@ __global__ __launch_bounds__(256) void gemm_generic_kernel(const TIn* __restrict
                                                            const float* __restrict__ scale,
                                                            const TOut* __restrict__ res,
                                                            const float* __restrict__ out_scale) {
-  const int64_t j = (int64_t)blockIdx.x * kGenThreadsX + (threadIdx.x % kGenThreadsX);
+  const int64_t j = (int64_t)blockIdx.x * kGenThreadsX + threadIdx.x;
   if (j >= N) return;
   const int64_t i_step = (int64_t)gridDim.y * kGenThreadsY;
-  for (int64_t i = (int64_t)blockIdx.y * kGenThreadsY + threadIdx.x / kGenThreadsX; i < M; i += i_step) {
+  for (int64_t i = (int64_t)blockIdx.y * kGenThreadsY + threadIdx.y; i < M; i += i_step) {
     // element strides of a(i, k) and b(k, j) along k
     const TIn* pa = la == GEMM_EPI_ROW_MAJOR ? A + i * lda : A + i;
     const int64_t sa = la == GEMM_EPI_ROW_MAJOR ? 1 : lda;
@@ -46,7 +51,7 @@ hipError_t launch_generic(const LaunchArgs& a) {
   const int64_t gx = ((int64_t)a.N + kGenThreadsX - 1) / kGenThreadsX;
   int64_t gy = ((int64_t)a.M + kGenThreadsY - 1) / kGenThreadsY;
   if (gy > 65535) gy = 65535;
-  hipLaunchKernelGGL((gemm_generic_kernel<TIn, TOut, EPI>), dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, a.stream,
+  hipLaunchKernelGGL((gemm_generic_kernel<TIn, TOut, EPI>), dim3((unsigned)gx, (unsigned)gy), dim3(kGenThreadsX, kGenThreadsY), 0, a.stream,
                      (const TIn*)a.A, (const TIn*)a.B, (const TIn*)a.bias, (TOut*)a.C, (int64_t)a.M, (int64_t)a.N,
                      (int64_t)a.K, a.la, a.lb, (int64_t)a.lda, (int64_t)a.ldb, (int64_t)a.ldc, a.scale,
                      (const TOut*)a.residual, a.out_scale);

@@ -9,8 +9,9 @@
 //
 //   - a workgroup owns 32 consecutive output columns n and all of K, so
 //     there is no reduction across workgroups and bias and activation are
-//     applied exactly once (when N % 32 != 0 the last workgroup's columns
-//     overlap its neighbour's, which it rewrites with identical values);
+//     applied exactly once (when N % 32 != 0 the last workgroup is shifted
+//     back to end at N: it also computes some of its neighbour's columns,
+//     in another k order, and stores only the columns it owns);
 //   - K is walked in chunks of KC values.  A chunk of B is 32 rows x KC
 //     k-values, and every row segment of it (2 KC bytes) is contiguous in
 //     memory: the NW waves copy it into one LDS ring slot with 128-bit
@@ -130,9 +131,14 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const TIn* __restr
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   // When N % 32 != 0 the last workgroup's columns are shifted back to end
-  // at N: it recomputes (and rewrites, with identical values) some of its
-  // neighbour's columns, and no access leaves B, bias or C.
+  // at N, so that no access leaves B, bias or C.  It computes some of its
+  // neighbour's columns too, but in another k order (its walk starts at
+  // another chunk), so its fp32 sums of them may differ in the last bit:
+  // it stores only the columns from n_own on, which no other workgroup
+  // writes.  (n0 is a multiple of 8, n_own of 32, so an output quad lies
+  // wholly on one side.)
   const int n0 = min((int)blockIdx.x * CW, N - CW);
+  const int n_own = (int)blockIdx.x * CW;
   const int hc = wave / NWH, wi = wave % NWH;  // column half, wave within it
   // Split K (part != NULL): workgroup (b, s) of the gridDim.y splits takes
   // chunks [s n, (s + 1) n) of column block b, n = K / KC / splits.
@@ -382,9 +388,11 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const TIn* __restr
     return z;
   };
   // Column scale, bias, activation, residual, output scale, conversion and
-  // one vector store of outputs (om, n0 + 4 oq .. + 3).
+  // one vector store of outputs (om, n0 + 4 oq .. + 3), if this workgroup
+  // owns them.
   auto finish = [&](int om, f32x4 z) __attribute__((always_inline)) {
     const int n = n0 + 4 * oq;
+    if (n < n_own) return;
     f32x4 sc = f32x4{1.0f, 1.0f, 1.0f, 1.0f}, r = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     if (scale) sc = *(const f32x4*)(scale + n);
     if (res) r = load4<TOut>(res + (int64_t)om * ldc + n);
@@ -412,14 +420,18 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const TIn* __restr
     // the whole workspace zero-filled, as it found it: a workspace may be
     // shared by plans whose partial and counter areas overlap.
     //
-    // Visibility across XCDs without whole-cache maintenance (a release
-    // fence would write back, and an acquire fence invalidate, the XCD's
-    // entire L2 -- which also evicts A, shared by every workgroup): the
-    // partials, the counter and the partial reads are agent-scope atomic
-    // accesses, which go to the device-coherent level; every thread waits
-    // for its partial stores to complete before the workgroup barrier that
-    // precedes the count, and the reads are issued only after the count
-    // has returned.
+    // Visibility across XCDs.  The partials, the counter and the partial
+    // reads are agent-scope atomic accesses, which go to the device-coherent
+    // level.  The writing side has no release fence (one would write back
+    // the XCD's whole L2 in every workgroup -- measured 1.7-4x slower, as
+    // every workgroup then also lost A from L2): each thread waits for its
+    // partial stores to be acknowledged (s_waitcnt vmcnt(0)) before the
+    // workgroup barrier that precedes the relaxed count.  That the stores
+    // are then visible device-wide before the count is a property of
+    // gfx950's memory system (acknowledged agent-scope stores have reached
+    // the coherent level), not a guarantee of the HIP memory model.  The
+    // finishing workgroup does take an agent-scope acquire fence after the
+    // count, so its partial reads are ordered after it.
     float* mine = part + (size_t)(blockIdx.x * nsplit + split) * (32 * CW);
     for (int t = tid; t < NG; t += NW * 64) {
       const int om = t / (CW / 4);
@@ -438,6 +450,10 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const TIn* __restr
                  (unsigned)(nsplit - 1);
     __syncthreads();
     if (!*is_last) return;
+    // Acquire at agent scope, so that the partial reads below are ordered
+    // after the count that saw every other split arrive (only the finishing
+    // workgroup pays for the cache maintenance this implies).
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     float* blk = part + (size_t)blockIdx.x * nsplit * (32 * CW);
     for (int t = tid; t < NG; t += NW * 64) {
       const int om = t / (CW / 4);

@@ -59,10 +59,10 @@ int skinny_split(int cfg, const Problem& p);
 LaunchFn skinny_launcher(int cfg, const Problem& p);
 
 // ---- cache eviction for cold-cache timing (flush.hip) ------------------------
-// Bytes of the scratch buffer flush_caches writes: twice the 256 MB
+// Bytes of the scratch buffer flush_caches reads: twice the 256 MB
 // last-level cache.
 constexpr size_t kFlushBytes = (size_t)512 << 20;
-// Enqueue a kernel on `stream` that writes all kFlushBytes of `scratch`.
+// Enqueue a kernel on `stream` that reads all kFlushBytes of `scratch`.
 hipError_t flush_caches(void* scratch, hipStream_t stream);
 
 // ---- tuning table (tuning.cpp) ---------------------------------------------

@@ -4,7 +4,7 @@ the tuning table (gemm_epi_tune, gemm_epi_tuning_save).
     python -m epilogue_gemm_amd.tune [--out FILE] [--iters N] [--warm] [--shape M,N,K,in,out,la,lb,epi ...]
 
 Without --shape it tunes the five reference workloads.  Launches are timed
-with cold caches (a 512 MiB write before each) unless --warm is given.  Each problem runs on
+with cold caches (a 512 MiB read before each) unless --warm is given.  Each problem runs on
 seeded synthetic operands (epilogue_gemm_amd.inputs); the table file can then
 be loaded by any process with gemm_epi_tuning_load before planning.
 """

@@ -98,6 +98,13 @@ typedef struct gemm_epi_plan_s* gemm_epi_plan_t;
 
 /* gemm_epi_plan -- validate a problem and choose its kernel.
  *
+ * The per-shape build step: the pages build a kernel for fixed M, N, K and
+ * block sizes once and get back a callable (atlascloud.ai "Writing
+ * high-performance kernels in TileLang", section "Écrivons un GEMM", the
+ * matmul(M, N, K, ...) call; csdn "从零开始学习 TileLang", ch.10 sec. 10.5,
+ * the compile step before the call).  Here nothing is compiled at run time:
+ * the plan picks one of the prebuilt kernels and its launch shape.
+ *
  * A is M x K in layout_a, B is K x N in layout_b, C is M x N row-major,
  * all packed (leading dimension = the contiguous extent) unless
  * gemm_epi_plan_set_ld gives other leading dimensions.
@@ -132,6 +139,10 @@ gemm_epi_status gemm_epi_plan_set_ld(gemm_epi_plan_t plan, int64_t lda, int64_t 
 /* gemm_epi_run -- enqueue C = act(A.B [+ bias]) on `stream` and return
  * without synchronising.
  *
+ * The call of the built kernel on caller-allocated tensors, output
+ * included (atlascloud.ai "Écrivons un GEMM", kernel(a, b, c) with c made
+ * by the caller; csdn ch.10 sec. 10.5).
+ *
  * A, B, bias, C are device pointers owned by the caller, who keeps them
  * alive until the stream has passed the kernel.  bias must be non-NULL
  * exactly when the epilogue uses it.  C must not overlap A, B or bias.
@@ -148,8 +159,12 @@ gemm_epi_status gemm_epi_run(gemm_epi_plan_t plan, const void* A, const void* B,
  * gemm_epi_run_ws split K across workgroups (0: this plan never splits).
  *
  * Only skinny plans (M <= 32) whose N gives fewer than 256 column blocks
- * of 32 split: a decode-like product with a narrow weight, e.g. one GPU's
- * column shard of a larger one, would otherwise leave most CUs idle.
+ * split: a decode-like product with a narrow weight, e.g. one GPU's column
+ * shard of a larger one, would otherwise leave most CUs idle.  A column
+ * block is 32 columns (64 for the 64-column row-major-weight configuration,
+ * skinny_rowb_64n_8w_6x128k); the workspace holds one fp32 32 x width
+ * partial block (4 or 8 KiB) per column block and split, then one 32-bit
+ * arrival counter per column block, rounded up to 256 bytes.
  * (Split-K as the remedy when one block's share of the work is too large:
  * csdn "从零开始学习 TileLang", ch.17 "常见性能问题", sec. 17.1.)
  * Host only.  0 for a NULL plan. */
@@ -214,7 +229,7 @@ gemm_epi_status gemm_epi_run_ex(gemm_epi_plan_t plan, const void* A, const void*
  * then `iters` times, and the mean time per launch decides.  Without
  * flags the timed launches run back to back between two events, so
  * operands that fit in the 256 MB last-level cache stay there; with
- * GEMM_EPI_TUNE_COLD every timed launch follows a kernel that writes a
+ * GEMM_EPI_TUNE_COLD every timed launch follows a kernel that reads a
  * 512 MiB scratch buffer (allocated and freed by this call) and is timed
  * by its own pair of events -- the condition of a weight streamed once per
  * step, which decides among HBM-bound configurations.  Candidates are the tile and skinny configurations the problem
@@ -259,8 +274,9 @@ int gemm_epi_tuning_size(void);
  * arrays laid out [B, S, H, D] (D contiguous) in the input format `dtype`
  * (F16 or BF16), caller-owned; O must not overlap the others.  causal != 0
  * lets query i see keys j <= i only.  fp32 scores and accumulation, an
- * online softmax over blocks of 64 keys, probabilities rounded to `dtype`
- * for the second product, O rounded once.  (Scaled dot-product attention
+ * online softmax over blocks of 64 keys, probabilities carried into the
+ * second product as one fp16 value (F16) or as a bf16 value plus its bf16
+ * remainder (BF16), O rounded once.  (Scaled dot-product attention
  * and its blocked form with an online softmax: csdn "从零开始学习 TileLang",
  * ch.13 "FlashAttention", sec. 13.1, 13.6-13.8; layout, causal rule and the
  * B, H, S, D = 4, 8, 1024, 64 example: ainew.jp "TileLang で GPU カーネル設計を
