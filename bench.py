@@ -1,22 +1,34 @@
 """Benchmark: GEMM+epilogue TFLOP/s (% of dense MFMA peak) and skinny-M GB/s
 (% of HBM peak) on one MI355X.
 
-One step = one launch of the library on one batch of synthetic input:
-  * main line: C = GELU_tanh(A.B + bias), bf16 in/out, fp32 accumulate,
-    M = N = K = 8192, A row-major, B column-major (value = TFLOP/s, 2MNK
-    per step);
-  * "skinny": C = A.B + bias, bf16, M = 32, N = K = 8192, B column-major
-    (GB/s of compulsory A + B + bias + C bytes per step);
-  * "epilogue_variants" (the further epilogues on the main shape) and
-    "attention" (attention forward, B, H, S, D = 4, 8, 1024, 64, fp16, full
-    and causal): reported beside the headline.
-Inputs are resident in HBM before timing starts; operand sets are rotated
-across launches so that the 256 MB last-level cache cannot serve B from a
-previous launch.  Timing uses HIP events on the stream the kernels are
-launched on.  The CPU oracle is timed on a bounded sample of the main
-workload as a reported baseline (rank 0, N = 1 only).
+One step = one launch of the library on one batch of synthetic input.  The
+headline (`value`) is C = GELU_tanh(A.B + bias), bf16 in/out, fp32
+accumulate, M = N = K = 8192, A row-major, B column-major, in TFLOP/s of
+2MNK per step.  Beside it, under "workloads", every workload the library is
+measured on, each through the automatic plan with its own roofline:
+  * 128 x 64 x 256 fp16 -> fp32, A row-major, B column-major (one tile);
+  * 1024^3 and 4096^3 fp16 ReLU, A and B row-major;
+  * 8192^3 bf16 bias+GELU (the headline);
+  * the decode shape C = A.B + bias, bf16, M = 32, N = K = 8192, B
+    column-major (GB/s of compulsory A + B + bias + C bytes per step; also
+    under "skinny").
+"probes" holds the on-box ceilings (a streaming HBM read and back-to-back
+bf16 MFMAs) that each roofline also reports a fraction of;
+"epilogue_variants" the further epilogues on the headline shape and
+"attention" the attention forward (B, H, S, D = 4, 8, 1024, 64, fp16, full
+and causal).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only main|skinny]
+Inputs are resident in HBM before timing starts; operand sets are rotated
+across launches so that their total exceeds the 256 MB last-level cache
+(3 sets for 8192^3, 5 for the decode shape, enough for 512 MiB for the
+others).  Timing uses HIP events on the stream the library launches on: the
+mean over one timed region of `steps` launches (`ms_per_step`, `value`), and
+a second pass with an event pair around each launch for the median and
+p10/p90 (`per_launch`).  The CPU oracle is timed on a bounded sample of the
+main workload as a reported baseline (N = 1 only).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+                       [--only all|main|skinny|workloads|attention|probes]
                        [--no-cpu-baseline] [--no-variants] [--calib-copy]
 """
 from __future__ import annotations
@@ -103,30 +115,121 @@ def _device_sets(w, n_sets, torch, parity, inputs):
     return bits, sets
 
 
-def _time_launches(plan, sets, steps, warmup, torch, extras=None):
-    """ms per launch over `steps` launches rotating through `sets`; `extras`
-    (optional) is a list, per set, of (column scale, residual) tensors."""
+def _n_sets(w, floor, cap=64):
+    """Operand sets to rotate so that their total exceeds 2 x the 256 MB
+    last-level cache (at least `floor`, at most `cap`)."""
+    per_set = w.compulsory_bytes()
+    return int(max(floor, min(cap, -(-(512 << 20) // per_set))))
+
+
+def _percentiles(xs):
+    import numpy as np
+
+    a = np.asarray(xs, np.float64)
+    return {"median_ms": round(float(np.median(a)), 6), "p10_ms": round(float(np.percentile(a, 10)), 6),
+            "p90_ms": round(float(np.percentile(a, 90)), 6), "n": int(a.size)}
+
+
+def _time(launch, n_sets, steps, warmup, torch):
+    """Times `launch(i)` (i rotating over n_sets operand sets) on torch's
+    current stream, where the library enqueues.  Returns (mean ms per launch
+    over one timed region of `steps` launches, per-launch statistics of a
+    second pass timing each launch with its own event pair)."""
     stream = torch.cuda.current_stream()
-
-    def launch(i):
-        A, B, bias, C = sets[i % len(sets)]
-        if extras is None:
-            plan.run(A, B, bias, C, stream)
-        else:
-            sc, res = extras[i % len(sets)]
-            plan.run(A, B, bias, C, stream, scale=sc, residual=res)
-
     for i in range(warmup):
-        launch(i)
+        launch(i % n_sets)
     torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     start.record(stream)
     for i in range(steps):
-        launch(i)
+        launch(i % n_sets)
     end.record(stream)
     torch.cuda.synchronize()
-    return start.elapsed_time(end) / steps  # ms per launch
+    mean_ms = start.elapsed_time(end) / steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i, (a, b) in enumerate(ev):
+        a.record(stream)
+        launch(i % n_sets)
+        b.record(stream)
+    torch.cuda.synchronize()
+    return mean_ms, _percentiles([a.elapsed_time(b) for a, b in ev])
+
+
+def _plan_launcher(plan, sets, extras=None):
+    def launch(i):
+        A, B, bias, C = sets[i]
+        if extras is None:
+            plan.run(A, B, bias, C)
+        else:
+            sc, res = extras[i]
+            plan.run(A, B, bias, C, scale=sc, residual=res)
+    return launch
+
+
+def _roofline(bound, achieved, peak, unit, traffic, probe_peak=None):
+    r = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+         "frac": round(achieved / peak, 4), "traffic": traffic}
+    if probe_peak:
+        r["probe_peak"] = round(probe_peak, 1)
+        r["frac_of_probe"] = round(achieved / probe_peak, 4)
+    return r
+
+
+def _bench_workload(w, steps, warmup, n_sets, torch, binding, inputs, parity, family):
+    """One workload through the automatic plan: mean and per-launch times, the
+    roofline of its kernel (TFLOP/s of 2MNK, or GB/s of compulsory bytes for
+    the HBM-bound decode shape)."""
+    bits, sets = _device_sets(w, n_sets, torch, parity, inputs)
+    plan = binding.Plan(w.M, w.N, w.K, w.in_dtype, w.out_dtype, w.layout_a, w.layout_b, w.epilogue)
+    mean_ms, per = _time(_plan_launcher(plan, sets), n_sets, steps, warmup, torch)
+    rec = {"workload": w.name, "kernel": plan.name, "ms_per_step": round(mean_ms, 6), "per_launch": per,
+           "steps": steps, "operand_sets_rotated": n_sets,
+           "TFLOP/s": round(w.flops / (mean_ms * 1e-3) / 1e12, 2),
+           "GB/s": round(w.compulsory_bytes() / (mean_ms * 1e-3) / 1e9, 1),
+           "compulsory_bytes": w.compulsory_bytes(), "flops": w.flops}
+    plan.close()
+    del sets
+    torch.cuda.empty_cache()
+    return rec, bits
+
+
+def _probes(torch, binding):
+    """On-box ceilings: streaming read of 5 rotated 128 MiB buffers (640 MiB,
+    past the 256 MB last-level cache) and back-to-back bf16 MFMAs."""
+    out = {}
+    stream = torch.cuda.current_stream().cuda_stream
+    nb = 128 << 20
+    bufs = [torch.full((nb // 4,), i + 1, dtype=torch.int32, device="cuda") for i in range(5)]
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    def read(i):
+        st = binding.gemm_epi_probe_hbm_read(bufs[i].data_ptr(), nb, sink.data_ptr(), stream)
+        if st != 0:
+            raise RuntimeError(f"gemm_epi_probe_hbm_read: status {st}")
+
+    mean_ms, per = _time(read, len(bufs), 200, 20, torch)
+    best = nb / (per["p10_ms"] * 1e-3) / 1e9
+    out["hbm_read"] = {"GB/s": round(nb / (mean_ms * 1e-3) / 1e9, 1), "GB/s_p10_launch": round(best, 1),
+                       "bytes_per_launch": nb, "buffers_rotated": len(bufs), "ms_per_launch": round(mean_ms, 6),
+                       "per_launch": per}
+    del bufs
+    wg, iters = 1024, 8000
+    res = torch.empty(wg * 256, dtype=torch.float32, device="cuda")
+
+    def mfma(_):
+        st = binding.gemm_epi_probe_mfma(iters, wg, res.data_ptr(), stream)
+        if st != 0:
+            raise RuntimeError(f"gemm_epi_probe_mfma: status {st}")
+
+    mean_ms, per = _time(mfma, 1, 20, 5, torch)
+    flops = binding.gemm_epi_probe_mfma_flops(iters, wg)
+    out["mfma_bf16"] = {"TFLOP/s": round(flops / (mean_ms * 1e-3) / 1e12, 1), "flops_per_launch": flops,
+                        "instruction": "v_mfma_f32_16x16x32_bf16", "ms_per_launch": round(mean_ms, 6),
+                        "per_launch": per}
+    del res
+    torch.cuda.empty_cache()
+    return out
 
 
 def _cpu_baseline(w, bits):
@@ -158,39 +261,42 @@ def _cpu_baseline(w, bits):
     }
 
 
-def _run_variants(w, sets, args, variants, binding, inputs, parity, torch):
+def _run_variants(w, sets, args, binding, inputs, parity, torch):
     """The further epilogues on the main shape and operands (reported beside
     the headline, not in it): bias+SiLU; bias+GELU with a column scale and a
     residual (one residual per operand set, none overlapping C); bias+GELU to
     FP8 E4M3 with an output scale."""
+    variants = []
     ex = inputs.extras_inputs(w.M, w.N, w.out_dtype, seed=w.seed)
     scale = torch.from_numpy(ex["scale"]).cuda()
     res0 = parity.to_device_out(ex["residual"], w.out_dtype)
     extras = [(scale, res0 if i == 0 else res0.clone()) for i in range(len(sets))]
     vsteps = min(args.steps, 50)
     warm = max(args.warmup // 2, 5)
+
+    def rec(epi, out_dtype, with_extras, out_scale, kernel, ms, per):
+        return {"epilogue": epi, "out_dtype": out_dtype, "col_scale": with_extras, "residual": with_extras,
+                "out_scale": out_scale, "kernel": kernel, "ms_per_step": round(ms, 4), "per_launch": per,
+                "TFLOP/s": round(w.flops / (ms * 1e-3) / 1e12, 1), "steps": vsteps}
+
     for epi, with_extras in (("bias_silu", False), ("bias_gelu", True)):
         p = binding.Plan(w.M, w.N, w.K, w.in_dtype, w.out_dtype, w.layout_a, w.layout_b, epi)
-        vms = _time_launches(p, sets, vsteps, warm, torch, extras if with_extras else None)
-        variants.append({"epilogue": epi, "out_dtype": w.out_dtype, "col_scale": with_extras,
-                         "residual": with_extras, "out_scale": False, "kernel": p.name,
-                         "ms_per_step": round(vms, 4), "TFLOP/s": round(w.flops / (vms * 1e-3) / 1e12, 1),
-                         "steps": vsteps})
+        ms, per = _time(_plan_launcher(p, sets, extras if with_extras else None), len(sets), vsteps, warm, torch)
+        variants.append(rec(epi, w.out_dtype, with_extras, False, p.name, ms, per))
         p.close()
     del extras, res0
     sets8 = [(A, B, bias, parity.empty_out(w.M * w.N, "fp8")) for A, B, bias, _ in sets]
     q = torch.tensor([ex["out_scale"]], dtype=torch.float32, device="cuda")
     p = binding.Plan(w.M, w.N, w.K, w.in_dtype, "fp8", w.layout_a, w.layout_b, "bias_gelu")
 
-    class _WithOutScale:  # runs the plan with the output scale
-        def run(self, A, B, bias, C, stream):
-            p.run(A, B, bias, C, stream, out_scale=q)
+    def launch8(i):
+        A, B, bias, C = sets8[i]
+        p.run(A, B, bias, C, out_scale=q)
 
-    vms = _time_launches(_WithOutScale(), sets8, vsteps, warm, torch)
-    variants.append({"epilogue": "bias_gelu", "out_dtype": "fp8", "col_scale": False, "residual": False,
-                     "out_scale": True, "kernel": p.name, "ms_per_step": round(vms, 4),
-                     "TFLOP/s": round(w.flops / (vms * 1e-3) / 1e12, 1), "steps": vsteps})
+    ms, per = _time(launch8, len(sets8), vsteps, warm, torch)
+    variants.append(rec("bias_gelu", "fp8", False, True, p.name, ms, per))
     p.close()
+    return variants
 
 
 def _bench_attention(steps, warmup, torch, binding, inputs, parity):
@@ -201,22 +307,15 @@ def _bench_attention(steps, warmup, torch, binding, inputs, parity):
         d = inputs.attention_inputs(w.B, w.S, w.H, w.D, w.dtype, w.seed)
         q, k, v = (parity.to_device(d[n], w.dtype).view(w.B, w.S, w.H, w.D) for n in ("Q", "K", "V"))
         o = torch.empty_like(q)
-        stream = torch.cuda.current_stream()
-        for _ in range(warmup):
-            binding.attention_fwd(q, k, v, o, causal=w.causal, stream=stream)
-        torch.cuda.synchronize()
-        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        start.record(stream)
-        for _ in range(steps):
-            binding.attention_fwd(q, k, v, o, causal=w.causal, stream=stream)
-        end.record(stream)
-        torch.cuda.synchronize()
-        ms = start.elapsed_time(end) / steps
+
+        def launch(_):
+            binding.attention_fwd(q, k, v, o, causal=w.causal)
+
+        ms, per = _time(launch, 1, steps, warmup, torch)
         tf = w.flops / (ms * 1e-3) / 1e12
         recs.append({"workload": w.name, "B": w.B, "S": w.S, "H": w.H, "D": w.D, "causal": w.causal,
-                     "ms_per_step": round(ms, 5), "TFLOP/s": round(tf, 1), "steps": steps,
-                     "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_BF16_TFLOPS,
-                                  "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None}})
+                     "ms_per_step": round(ms, 5), "per_launch": per, "TFLOP/s": round(tf, 1), "steps": steps,
+                     "roofline": _roofline("mfma", tf, PEAK_BF16_TFLOPS, "TFLOP/s", None)})
         del q, k, v, o
     return recs
 
@@ -226,10 +325,13 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--only", choices=["main", "skinny", "both", "attention"], default="both")
+    ap.add_argument("--only", choices=["all", "main", "skinny", "workloads", "attention", "probes"], default="all",
+                    help="main: the 8192^3 headline only; skinny: the decode shape only; workloads: the three "
+                         "other GEMM workloads; attention; probes: the on-box ceilings")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true",
-                    help="skip the further-epilogue variants (so that a profile sees the headline kernel only)")
+                    help="skip the further-epilogue variants and attention (so that a profile of --only main "
+                         "sees the headline kernel only)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="after timing, run a plain 1 GiB device copy (elementwise kernel) three times, so that "
                          "HBM byte counters can be scaled against a kernel of known traffic")
@@ -249,42 +351,51 @@ def main(argv=None):
         return 2
     binding.load_library()
     torch.cuda.set_device(0)
+    sel = args.only
 
-    out = {}
-    if args.only in ("main", "both"):
+    def say(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    probes = None
+    if sel in ("all", "probes"):
+        say("probes")
+        probes = _probes(torch, binding)
+    hbm_probe = probes["hbm_read"]["GB/s"] if probes else None
+    mfma_probe = probes["mfma_bf16"]["TFLOP/s"] if probes else None
+
+    workloads = {}
+    main_bits, variants, attention = None, None, None
+    if sel in ("all", "main"):
         w = inputs.WORKLOADS[MAIN]
-        bits, sets = _device_sets(w, 3, torch, parity, inputs)
-        plan = binding.Plan(w.M, w.N, w.K, w.in_dtype, w.out_dtype, w.layout_a, w.layout_b, w.epilogue)
-        ms = _time_launches(plan, sets, args.steps, args.warmup, torch)
-        tflops = w.flops / (ms * 1e-3) / 1e12
-        out["main"] = dict(w=w, bits=bits, ms=ms, value=tflops, kernel=plan.name)
-        plan.close()
-        # the further epilogues on the same shape and operands (_run_variants)
-        variants = []
-        if args.no_variants:
+        say(w.name)
+        rec, main_bits = _bench_workload(w, args.steps, args.warmup, 3, torch, binding, inputs, parity, "tile")
+        workloads[w.name] = rec
+        if sel == "all" and not args.no_variants:
+            say("epilogue variants")
+            _, sets = _device_sets(w, 3, torch, parity, inputs)
+            variants = _run_variants(w, sets, args, binding, inputs, parity, torch)
             del sets
             torch.cuda.empty_cache()
-            out["main"]["variants"] = variants
-        else:
-            _run_variants(w, sets, args, variants, binding, inputs, parity, torch)
-            out["main"]["variants"] = variants
-            del sets
-            torch.cuda.empty_cache()
-    if args.only in ("skinny", "both"):
+    if sel in ("all", "skinny"):
         w = inputs.WORKLOADS[SKINNY]
+        say(w.name)
         # 5 sets x 128 MiB of B: more than the 256 MB last-level cache
-        bits_s, sets = _device_sets(w, 5, torch, parity, inputs)
-        plan = binding.Plan(w.M, w.N, w.K, w.in_dtype, w.out_dtype, w.layout_a, w.layout_b, w.epilogue)
-        steps = max(args.steps, 200)
-        ms = _time_launches(plan, sets, steps, max(args.warmup, 20), torch)
-        gbs = w.compulsory_bytes() / (ms * 1e-3) / 1e9
-        out["skinny"] = dict(w=w, ms=ms, value=gbs, kernel=plan.name, steps=steps)
-        plan.close()
-        del sets
-        torch.cuda.empty_cache()
-
-    attention = None
-    if args.only in ("both", "attention") and not args.no_variants:
+        rec, _ = _bench_workload(w, max(args.steps, 200), max(args.warmup, 20), 5, torch, binding, inputs, parity,
+                                 "skinny")
+        workloads[w.name] = rec
+    if sel in ("all", "workloads"):
+        for name in inputs.WORKLOADS:
+            if name in (MAIN, SKINNY):
+                continue
+            w = inputs.WORKLOADS[name]
+            say(w.name)
+            # operand sets past twice the last-level cache (the 128 x 64 x 256
+            # case: 64 sets, still cache-resident; one tile, launch-bound)
+            rec, _ = _bench_workload(w, max(args.steps, 100), max(args.warmup, 20), _n_sets(w, 3), torch, binding,
+                                     inputs, parity, "tile")
+            workloads[w.name] = rec
+    if sel in ("all", "attention") and not args.no_variants:
+        say("attention")
         attention = _bench_attention(max(args.steps, 50), max(args.warmup, 10), torch, binding, inputs, parity)
 
     if args.calib_copy:
@@ -295,18 +406,30 @@ def main(argv=None):
         torch.cuda.synchronize()
         del src, dst
 
+    # roofline of each workload's kernel
+    for name, r in workloads.items():
+        w = inputs.WORKLOADS[name]
+        fam = "skinny" if name == SKINNY else "tile"
+        traffic = measured_traffic(fam, r["kernel"], name)
+        if name == SKINNY:
+            r["roofline"] = _roofline("hbm", r["GB/s"], PEAK_HBM_GBS, "GB/s", traffic, hbm_probe)
+        else:
+            r["roofline"] = _roofline("mfma", r["TFLOP/s"], PEAK_BF16_TFLOPS, "TFLOP/s", traffic, mfma_probe)
+        if name == "gemm_f16_f32out_128x64x256_rm_cm":
+            r["limited_by"] = "launch latency: one 128 x 64 output block, 4.2 MFLOP"
+
     rec = {}
-    if "main" in out:
-        m = out["main"]
-        w = m["w"]
+    if MAIN in workloads:
+        m = workloads[MAIN]
+        w = inputs.WORKLOADS[MAIN]
         rec = {
             "metric": "GEMM+epilogue TFLOP/s (% MFMA peak); skinny-M GB/s (% HBM peak), 1 GPU",
-            "value": round(m["value"], 2),
+            "value": m["TFLOP/s"],
             "unit": "TFLOP/s",
             "n_gpus": 1,
             "steps": args.steps,
             "warmup": args.warmup,
-            "ms_per_step": round(m["ms"], 4),
+            "ms_per_step": round(m["ms_per_step"], 5),
             "higher_is_better": True,
             "scaling": "weak",
             "vs_baseline": None,
@@ -314,40 +437,31 @@ def main(argv=None):
             "data": "synthetic",
             "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "epilogue": w.epilogue,
                        "layout_a": w.layout_a, "layout_b": w.layout_b, "kernel": m["kernel"],
-                       "operand_sets_rotated": 3},
-            "roofline": {"bound": "mfma", "achieved": round(m["value"], 2), "peak": PEAK_BF16_TFLOPS,
-                         "unit": "TFLOP/s", "frac": round(m["value"] / PEAK_BF16_TFLOPS, 4),
-                         "traffic": measured_traffic("tile", m["kernel"], w.name)},
-            "epilogue_variants": m.get("variants", []),
+                       "operand_sets_rotated": m["operand_sets_rotated"]},
+            "roofline": m["roofline"],
+            "per_launch": m["per_launch"],
         }
-    if "skinny" in out:
-        s = out["skinny"]
-        w = s["w"]
-        sk = {
-            "metric": "skinny-M GB/s (% HBM peak)",
-            "value": round(s["value"], 1),
-            "unit": "GB/s",
-            "ms_per_step": round(s["ms"], 5),
-            "steps": s["steps"],
-            "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "epilogue": w.epilogue,
-                       "kernel": s["kernel"], "operand_sets_rotated": 5,
-                       "compulsory_bytes": w.compulsory_bytes()},
-            "roofline": {"bound": "hbm", "achieved": round(s["value"], 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": round(s["value"] / PEAK_HBM_GBS, 4),
-                         "traffic": measured_traffic("skinny", s["kernel"], w.name)},
-        }
-        if rec:
-            rec["skinny"] = sk
-        else:
-            rec = {**sk, "n_gpus": 1, "warmup": args.warmup, "higher_is_better": True, "scaling": "weak",
-                   "vs_baseline": None, "dtype": "bf16", "data": "synthetic"}
+    elif workloads:
+        first = next(iter(workloads.values()))
+        rec = {"metric": "GEMM+epilogue TFLOP/s (% MFMA peak); skinny-M GB/s (% HBM peak), 1 GPU",
+               "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
+               "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+               "config": {"workload": first["workload"]}}
+    else:
+        rec = {"metric": "on-box probes" if probes else "attention forward TFLOP/s", "n_gpus": 1}
+    if workloads:
+        rec["workloads"] = workloads
+    if SKINNY in workloads:
+        rec["skinny"] = workloads[SKINNY]
+    if variants is not None:
+        rec["epilogue_variants"] = variants
     if attention is not None:
-        if rec:
-            rec["attention"] = attention
-        else:
-            rec = {"metric": "attention forward TFLOP/s", "attention": attention, "n_gpus": 1}
-    if "main" in out and not args.no_cpu_baseline:
-        rec["cpu_baseline"] = _cpu_baseline(out["main"]["w"], out["main"]["bits"])
+        rec["attention"] = attention
+    if probes is not None:
+        rec["probes"] = probes
+    if main_bits is not None and not args.no_cpu_baseline:
+        say("cpu baseline (oracle)")
+        rec["cpu_baseline"] = _cpu_baseline(inputs.WORKLOADS[MAIN], main_bits)
     print(json.dumps(rec), flush=True)
     return 0
 

@@ -93,15 +93,32 @@ def load_library(path: str = LIB_PATH):
     lib.gemm_epi_num_configs.restype = i32
     lib.gemm_epi_plan_describe.argtypes = [vp, ctypes.POINTER(i32), ctypes.POINTER(i32)]
     lib.gemm_epi_plan_describe.restype = cp
+    # measurement helpers (include/gemm_epi_probes.h)
+    lib.gemm_epi_probe_hbm_read.argtypes = [vp, ctypes.c_size_t, vp, vp]
+    lib.gemm_epi_probe_hbm_read.restype = i32
+    lib.gemm_epi_probe_mfma.argtypes = [i32, i32, vp, vp]
+    lib.gemm_epi_probe_mfma.restype = i32
+    lib.gemm_epi_probe_mfma_flops.argtypes = [i32, i32]
+    lib.gemm_epi_probe_mfma_flops.restype = ctypes.c_double
     _lib = lib
     return lib
 
 
-def header_functions(header: str = HEADER):
-    """Names of the functions include/gemm_epi.h declares."""
-    text = open(header).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(gemm_epi_\w+)\s*\(", text)))
+def headers():
+    """Every header of the C ABI (include/*.h)."""
+    d = os.path.dirname(HEADER)
+    return sorted(os.path.join(d, f) for f in os.listdir(d) if f.endswith(".h"))
+
+
+def header_functions(header: str | None = None):
+    """Names of the functions the C ABI headers declare (all of include/*.h,
+    or the one given)."""
+    names = set()
+    for h in [header] if header else headers():
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names.update(re.findall(r"\b(gemm_epi_\w+)\s*\(", text))
+    return sorted(names)
 
 
 # ---- the C entry points, same names ----------------------------------------
@@ -204,6 +221,20 @@ def attention_fwd(q, k, v, o, causal=False, stream=None):
                                 _dtype_name(q), causal, s)
     if st != OK:
         raise GemmEpiError("gemm_epi_attention_fwd", st)
+
+
+# ---- measurement helpers (include/gemm_epi_probes.h) -------------------------
+
+def gemm_epi_probe_hbm_read(buf_ptr, nbytes, sink_ptr, stream) -> int:
+    return load_library().gemm_epi_probe_hbm_read(buf_ptr, int(nbytes), sink_ptr, stream)
+
+
+def gemm_epi_probe_mfma(iters, workgroups, out_ptr, stream) -> int:
+    return load_library().gemm_epi_probe_mfma(int(iters), int(workgroups), out_ptr, stream)
+
+
+def gemm_epi_probe_mfma_flops(iters, workgroups) -> float:
+    return float(load_library().gemm_epi_probe_mfma_flops(int(iters), int(workgroups)))
 
 
 def gemm_epi_destroy(plan) -> int:

@@ -32,11 +32,20 @@ def test_exports_every_declared_function(lib):
 
 
 def test_header_is_plain_c():
-    # the header must compile as C with no HIP or C++ headers
-    src = os.path.join(ROOT, "include", "gemm_epi.h")
-    r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-fsyntax-only", "-x", "c", src], capture_output=True,
-                       text=True)
-    assert r.returncode == 0, r.stderr
+    # every header must compile as C with no HIP or C++ headers
+    srcs = gb.headers()
+    assert os.path.join(ROOT, "include", "gemm_epi.h") in srcs and len(srcs) >= 2
+    for src in srcs:
+        r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-fsyntax-only", "-x", "c", src],
+                           capture_output=True, text=True)
+        assert r.returncode == 0, (src, r.stderr)
+
+
+def test_probe_argument_checks(lib):
+    # argument validation happens before any HIP call
+    assert gb.gemm_epi_probe_hbm_read(None, 1024, None, None) == 1
+    assert gb.gemm_epi_probe_mfma(0, 1, None, None) == 1
+    assert gb.gemm_epi_probe_mfma_flops(10, 4) == 4 * 4 * 10 * 8 * 16 * 16 * 32 * 2
 
 
 def test_status_strings(lib):
