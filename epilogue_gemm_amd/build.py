@@ -1,8 +1,11 @@
 """Build the HIP library libgemm_epi.so for gfx950, in-tree.
 
 Every .hip/.cpp file under csrc/ is compiled by hipcc for gfx950 only, in
-parallel, then linked into epilogue_gemm_amd/libgemm_epi.so.  The build
-always recompiles (it is the "does it build" check).
+parallel, then linked into epilogue_gemm_amd/libgemm_epi.so.  build()
+recompiles everything by default (it is the "does it build" check);
+build(incremental=True) (``python -m epilogue_gemm_amd.build --incremental``)
+recompiles only the sources whose object is older than the source or any
+header it includes (from the compiler's dependency files).
 """
 from __future__ import annotations
 
@@ -30,21 +33,45 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
 
 
+def _obj(src: str) -> str:
+    return os.path.join(BUILD, os.path.basename(src) + ".o")
+
+
+def _up_to_date(src: str) -> bool:
+    """The object exists and is newer than the source and every file its
+    dependency file lists."""
+    obj, dep = _obj(src), _obj(src) + ".d"
+    if not (os.path.exists(obj) and os.path.exists(dep)):
+        return False
+    t = os.path.getmtime(obj)
+    with open(dep) as fh:
+        text = fh.read().replace("\\\n", " ")
+    files = text.split(":", 1)[1].split() if ":" in text else []
+    for f in [src, *files]:
+        if not os.path.exists(f) or os.path.getmtime(f) > t:
+            return False
+    return True
+
+
 def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, "-x", "hip", *FLAGS, "-c", src, "-o", obj]
+    obj = _obj(src)
+    cmd = [HIPCC, "-x", "hip", *FLAGS, "-MMD", "-MF", obj + ".d", "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")
     return obj
 
 
-def build(jobs: int | None = None, verbose: bool = False) -> str:
+def build(jobs: int | None = None, verbose: bool = False, incremental: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     srcs = sources()
-    jobs = jobs or min(len(srcs), max(1, min(8, os.cpu_count() or 1)))
+    todo = [s for s in srcs if not (incremental and _up_to_date(s))]
+    jobs = jobs or min(max(len(todo), 1), max(1, min(8, os.cpu_count() or 1)))
     with cf.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(_compile, srcs))
+        list(ex.map(_compile, todo))
+    if verbose and incremental:
+        print(f"compiled {len(todo)} of {len(srcs)} sources: {[os.path.basename(s) for s in todo]}")
+    objs = [_obj(s) for s in srcs]
     tmp = LIB + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -57,5 +84,5 @@ def build(jobs: int | None = None, verbose: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    build(verbose=True, incremental="--incremental" in sys.argv[1:])
     sys.exit(0)
