@@ -67,6 +67,8 @@ def load_library(path: str = LIB_PATH):
     lib.gemm_epi_workspace_size.restype = ctypes.c_size_t
     lib.gemm_epi_run_ws.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.gemm_epi_run_ws.restype = i32
+    lib.gemm_epi_run_noalloc.argtypes = [vp, vp, vp, vp, vp, vp]
+    lib.gemm_epi_run_noalloc.restype = i32
     lib.gemm_epi_run_ex.argtypes = [vp, vp, vp, vp, ctypes.POINTER(Extras), vp, vp, ctypes.c_size_t, vp]
     lib.gemm_epi_run_ex.restype = i32
     lib.gemm_epi_tune.argtypes = [vp, vp, vp, vp, vp, i32, i32, vp, ctypes.POINTER(ctypes.c_float)]
@@ -154,6 +156,10 @@ def gemm_epi_plan_set_ld(plan, lda=0, ldb=0, ldc=0) -> int:
 
 def gemm_epi_run(plan, A_ptr, B_ptr, bias_ptr, C_ptr, stream) -> int:
     return load_library().gemm_epi_run(plan, A_ptr, B_ptr, bias_ptr, C_ptr, stream)
+
+
+def gemm_epi_run_noalloc(plan, A_ptr, B_ptr, bias_ptr, C_ptr, stream) -> int:
+    return load_library().gemm_epi_run_noalloc(plan, A_ptr, B_ptr, bias_ptr, C_ptr, stream)
 
 
 def gemm_epi_workspace_size(plan) -> int:

@@ -91,6 +91,21 @@ namespace {
 
 thread_local int g_last_hip_error = 0;
 
+}  // namespace
+
+void ge::set_last_hip_error(int code) { g_last_hip_error = code; }
+
+gemm_epi_status ge::check_run_args(gemm_epi_plan_t plan, const void* A, const void* B, const void* bias,
+                                   const void* C) {
+  if (!plan || !A || !B || !C) return GEMM_EPI_ERR_INVALID_ARG;
+  const bool need_bias = plan->p.epi == GEMM_EPI_BIAS_RELU || plan->p.epi == GEMM_EPI_BIAS_GELU ||
+                         plan->p.epi == GEMM_EPI_BIAS || plan->p.epi == GEMM_EPI_BIAS_SILU;
+  if (need_bias != (bias != nullptr)) return GEMM_EPI_ERR_INVALID_ARG;
+  return GEMM_EPI_OK;
+}
+
+namespace {
+
 bool valid_enum_args(gemm_epi_dtype in, gemm_epi_dtype out, gemm_epi_layout la, gemm_epi_layout lb,
                      gemm_epi_epilogue epi) {
   if (in != GEMM_EPI_F16 && in != GEMM_EPI_BF16) return false;
@@ -173,9 +188,8 @@ size_t workspace_bytes(const gemm_epi_plan_s* pl) {
 
 gemm_epi_status launch(gemm_epi_plan_t plan, const void* A, const void* B, const void* bias,
                        const gemm_epi_extras* extras, void* C, void* workspace, size_t ws_bytes, void* stream) {
-  if (!plan || !A || !B || !C) return GEMM_EPI_ERR_INVALID_ARG;
-  const bool need_bias = uses_bias(plan->p.epi);
-  if (need_bias != (bias != nullptr)) return GEMM_EPI_ERR_INVALID_ARG;
+  const gemm_epi_status chk = ge::check_run_args(plan, A, B, bias, C);
+  if (chk != GEMM_EPI_OK) return chk;
   const float* scale = extras ? extras->col_scale : nullptr;
   const void* residual = extras ? extras->residual : nullptr;
   const float* out_scale = extras ? extras->out_scale : nullptr;

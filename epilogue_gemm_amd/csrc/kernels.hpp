@@ -65,6 +65,12 @@ constexpr size_t kFlushBytes = (size_t)512 << 20;
 // Enqueue a kernel on `stream` that reads all kFlushBytes of `scratch`.
 hipError_t flush_caches(void* scratch, hipStream_t stream);
 
+// ---- diagnostics (gemm_epi.cpp) ----------------------------------------------
+// Record a failed HIP call's code for gemm_epi_last_hip_error (per thread).
+void set_last_hip_error(int code);
+// The argument checks of gemm_epi_run (GEMM_EPI_OK when a run may proceed).
+gemm_epi_status check_run_args(gemm_epi_plan_t plan, const void* A, const void* B, const void* bias, const void* C);
+
 // ---- tuning table (tuning.cpp) ---------------------------------------------
 // The measured choice for this exact problem, if one was recorded.
 bool tuning_lookup(const Problem& p, int* kernel, int* config);

@@ -186,6 +186,31 @@ size_t gemm_epi_workspace_size(gemm_epi_plan_t plan);
 gemm_epi_status gemm_epi_run_ws(gemm_epi_plan_t plan, const void* A, const void* B, const void* bias, void* C,
                                 void* workspace, size_t workspace_bytes, void* stream);
 
+/* Size of the static device array gemm_epi_run_noalloc uses on each GPU:
+ * 4 MiB of split-K partial blocks plus room for the arrival counters.
+ * (The largest workspace any plan asks for is under 4 MiB + 1 KiB.) */
+#define GEMM_EPI_NOALLOC_SCRATCH_BYTES (4194304 + 4096)
+
+/* gemm_epi_run_noalloc -- gemm_epi_run_ws for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  It allocates nothing (no
+ * hipMalloc, hipFree or allocating library call).
+ *
+ * A plan that splits K (gemm_epi_workspace_size > 0) uses, as its
+ * workspace, a file-scope device array of GEMM_EPI_NOALLOC_SCRATCH_BYTES
+ * that the library holds on each GPU it runs on until the process ends
+ * (the current device's copy; the stream must belong to that device).
+ * Before the split kernel, a small fill kernel on `stream` clears the part
+ * of the array the run uses.  Every call on a GPU shares that GPU's array,
+ * so calls that overlap in time on one GPU race: order them on one stream
+ * or with events.  A plan with no split is exactly gemm_epi_run.
+ * Same results as gemm_epi_run_ws with a workspace of the plan's size.
+ * Errors: those of gemm_epi_run; UNSUPPORTED if the plan's workspace
+ * exceeds GEMM_EPI_NOALLOC_SCRATCH_BYTES; HIP (the symbol lookup, the fill
+ * or the launch failed). */
+gemm_epi_status gemm_epi_run_noalloc(gemm_epi_plan_t plan, const void* A, const void* B, const void* bias, void* C,
+                                     void* stream);
+
 /* Optional epilogue operands of gemm_epi_run_ex.  With them the output is
  *
  *     C[m][n] = out_scale * (act(col_scale[n] * (A.B)[m][n] + bias[n]) + residual[m][n])
