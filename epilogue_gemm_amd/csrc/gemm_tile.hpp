@@ -63,13 +63,15 @@ constexpr int kRowBytes = kBK * 2;  // one LDS row: 64 16-bit elements
 // (t = 0..7) and get positions c ^ j ^ t, again distinct.
 __device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
 
-// The swizzle of the 16x16x32 kernel (gemm_tile16.hpp).  Its fragment reads
-// take chunks c and c ^ 2 of the same 8 rows in one LDS pass (lanes i and
-// i + 32 together), where the 32x32x16 reads take c and c ^ 1; moving row
-// bits 1 and 2 to position bits 0 and 2 puts the even rows of 8 (and the odd
-// ones) in distinct {0, 2}-cosets, so both chunks of all 8 rows land on
-// distinct bank groups.
-__device__ __forceinline__ int swz16(int row) { return ((row >> 1) & 1) | (row & 4); }
+// The swizzle of the 16x16x32 kernel (gemm_tile16.hpp), chosen by
+// measurement: its fragment reads (16 consecutive rows per quarter-wave, the
+// four quarters at chunks c .. c + 3) were timed on the chip in a
+// ds_read_b128 probe, counting SQ_LDS_BANK_CONFLICT and SQ_LDS_IDX_ACTIVE
+// per instruction: c ^ (row & 7) takes 4 LDS cycles per read with no
+// conflict cycles, while c ^ swz(row), and c ^ (bits 1 and 2 of the row
+// moved to bits 0 and 2), take 8 (a 2-way conflict) and the unswizzled
+// layout 16.  (The 32x32x16 reads under swz() measured conflict-free too.)
+__device__ __forceinline__ int swz16(int row) { return row & 7; }
 
 // Buffer resource over [base, base + bytes): 128-bit raw buffer loads then
 // take one per-lane 32-bit offset plus one wave-uniform offset, so the loop

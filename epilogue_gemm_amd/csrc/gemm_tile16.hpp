@@ -22,8 +22,8 @@
 //               tile kt + 2 into the stage tile kt leaves, one copy every
 //               four MFMAs.
 // Fragment f (A or B) of substep kk: rows w0 + 16 f + lane % 16, logical
-// 16-byte chunk 4 kk + lane / 16, under the swizzle swz16 (gemm_tile.hpp)
-// that keeps these reads free of bank conflicts.  With B's fragment as the first
+// 16-byte chunk 4 kk + lane / 16, at chunk position (4 kk + lane / 16) ^
+// (row & 7) (swz16 in gemm_tile.hpp: measured free of bank conflicts).  With B's fragment as the first
 // operand the 16x16 result arrives transposed: lane l holds
 // C[m = l % 16][n = 4 (l / 16) + e], e = 0..3 -- four consecutive columns of
 // one row.  (Tile-level fusion of load -> GEMM -> epilogue -> store:
