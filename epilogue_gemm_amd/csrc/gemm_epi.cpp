@@ -16,12 +16,18 @@ namespace ge {
 // for 256 CUs; 8 waves put two on each SIMD so one can multiply while the
 // other waits; 16x16x32 blocks move half the accumulator bytes per FLOP
 // (k-contiguous operands only).
+// The ring configurations (64 x 64 tiles, K in 64-deep chunks through 8, 4
+// or 2 LDS slots) serve problems whose tiles must be small to fill the CUs,
+// where the two-stage pipeline waits on load latency at every k-step.
 static const TileConfig kTile[] = {
-    {256, 256, 4, "tile_256x256x64", 32},
-    {128, 128, 4, "tile_128x128x64", 32},
-    {64, 64, 4, "tile_64x64x64", 32},
-    {256, 256, 8, "tile_256x256x64_8w", 32},
-    {256, 256, 4, "tile_256x256x64_m16", 16},
+    {256, 256, 4, "tile_256x256x64", 32, 0},
+    {128, 128, 4, "tile_128x128x64", 32, 0},
+    {64, 64, 4, "tile_64x64x64", 32, 0},
+    {256, 256, 8, "tile_256x256x64_8w", 32, 0},
+    {256, 256, 4, "tile_256x256x64_m16", 16, 0},
+    {64, 64, 4, "tile_64x64_ring8", 32, 8},
+    {64, 64, 4, "tile_64x64_ring4", 32, 4},
+    {64, 64, 4, "tile_64x64_ring2", 32, 2},
 };
 
 int tile_num_configs() { return (int)(sizeof(kTile) / sizeof(kTile[0])); }
@@ -37,9 +43,16 @@ bool tile_supports(int cfg, const Problem& p) {
   // 64 (a partial one first, when K % 64 != 0).
   // The 16x16x32 configuration takes k-contiguous operands only (A
   // row-major, B column-major).
+  // The ring configurations take A row-major (either B) and a number of
+  // 64-deep chunks of K that is a multiple of the slot count; a row-major
+  // B's buffer range (K + 64 rows of ldb elements) must fit 32-bit byte
+  // offsets.
   const TileConfig& c = kTile[cfg];
   const int n_align = p.out_dt == GEMM_EPI_FP8_E4M3 ? 16 : 8;
   if (c.mfma == 16 && (p.la != GEMM_EPI_ROW_MAJOR || p.lb != GEMM_EPI_COL_MAJOR)) return false;
+  if (c.ring > 0 && (p.la != GEMM_EPI_ROW_MAJOR || ((p.K + 63) / 64) % c.ring != 0 ||
+                     (p.lb == GEMM_EPI_ROW_MAJOR && (p.K + 64) * p.ldb * 2 >= ((int64_t)1 << 32))))
+    return false;
   return p.M >= c.bm && p.N >= c.bn && p.N % n_align == 0 && (p.la == GEMM_EPI_ROW_MAJOR || p.M % 8 == 0) &&
          p.K % 8 == 0 && p.K > 64 && p.lda % 8 == 0 && p.ldb % 8 == 0 && p.ldc % n_align == 0;
 }
@@ -62,7 +75,12 @@ int tile_choose(const Problem& p) {
     }
     fallback = c;
   }
-  return fallback == 0 && direct ? 4 : fallback;
+  if (fallback == 0 && direct) return 4;
+  // 64 x 64 tiles: the deepest ring whose slot count divides the chunk count
+  if (fallback == 2)
+    for (int c = 5; c < 8; ++c)
+      if (tile_supports(c, p)) return c;
+  return fallback;
 }
 
 LaunchFn tile_launcher(int cfg, const Problem& p) {

@@ -25,6 +25,7 @@ struct TileConfig {
   int waves;   // waves per workgroup
   const char* name;
   int mfma;    // MFMA block: 32 (32x32x16, any layout) or 16 (16x16x32, k-contiguous operands only)
+  int ring;    // 0: two LDS stages; P > 0: the deep ring of P slots (gemm_ring.hpp, A row-major only)
 };
 int tile_num_configs();
 const TileConfig& tile_config(int cfg);

@@ -2,6 +2,7 @@
 // output format, in the order of the host-side table (gemm_epi.cpp).
 #pragma once
 
+#include "gemm_ring.hpp"
 #include "gemm_tile.hpp"
 #include "gemm_tile16.hpp"
 
@@ -16,6 +17,9 @@ LaunchFn pick_config(int cfg, int la, int lb, int epi) {
     case 2: return pick_layout<64, 64, 4, TIn, TOut>(la, lb, epi);
     case 3: return pick_layout<256, 256, 8, TIn, TOut>(la, lb, epi);
     case 4: return tile16::pick<TIn, TOut>(la, lb, epi);
+    case 5: return ring::pick<TIn, TOut, 8>(la, lb, epi);
+    case 6: return ring::pick<TIn, TOut, 4>(la, lb, epi);
+    case 7: return ring::pick<TIn, TOut, 2>(la, lb, epi);
     default: return nullptr;
   }
 }

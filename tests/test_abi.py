@@ -141,8 +141,8 @@ def test_fp8_output_needs_16_columns_in_tile_kernels(lib):
     (8192, 8192, 8192, "row", "col", "tile", "tile_256x256x64_m16"),
     (4096, 4096, 4096, "row", "row", "tile", "tile_256x256x64"),
     (4096, 4096, 4096, "row", "col", "tile", "tile_256x256x64_m16"),
-    (1024, 1024, 1024, "row", "row", "tile", "tile_64x64x64"),
-    (128, 64, 256, "row", "col", "tile", "tile_64x64x64"),
+    (1024, 1024, 1024, "row", "row", "tile", "tile_64x64_ring8"),  # 16 chunks of 64 through 8 slots
+    (128, 64, 256, "row", "col", "tile", "tile_64x64_ring4"),  # 4 chunks of 64
     (32, 8192, 8192, "row", "col", "skinny", "skinny_32n_8w_5x256k"),
     (1, 4096, 4096, "row", "col", "skinny", "skinny_32n_8w_5x256k"),
     (32, 4096, 768, "row", "col", "skinny", "skinny_32n_4w_2x256k"),  # three chunks of 256
@@ -157,14 +157,16 @@ def test_fp8_output_needs_16_columns_in_tile_kernels(lib):
     (32, 4096, 200, "row", "row", "skinny", "skinny_rowb_32n_2w_2x128k"),  # two chunks of 128, the first padded
     (32, 8192, 8192, "col", "row", "generic", "generic"),  # column-major A: no decode-shape kernel
     (2000, 8200, 4096, "row", "col", "tile", "tile_256x256x64_m16"),  # last tile row and column shifted back
-    (1000, 1000, 1024, "row", "col", "tile", "tile_64x64x64"),  # 16 x 16 edge-tiled 64 x 64 tiles
+    (1000, 1000, 1024, "row", "col", "tile", "tile_64x64_ring8"),  # 16 x 16 edge-tiled 64 x 64 tiles
     (3000, 2000, 4096, "row", "row", "tile", "tile_128x128x64"),  # 24 x 16 tiles of 128
     (1000, 1000, 1024, "col", "col", "tile", "tile_64x64x64"),
     (1001, 1000, 1024, "col", "col", "generic", "generic"),  # column-major A needs M % 8
     (1000, 1004, 1024, "row", "col", "generic", "generic"),  # N % 8
     (37, 53, 29, "row", "row", "generic", "generic"),
     (256, 256, 100, "col", "row", "generic", "generic"),  # K not a multiple of 8
-    (1024, 1024, 1000, "row", "col", "tile", "tile_64x64x64"),  # K % 64 = 40: a partial first k-step
+    (1024, 1024, 1000, "row", "col", "tile", "tile_64x64_ring8"),  # K % 64 = 40: a partial first chunk
+    (1024, 1024, 320, "row", "row", "tile", "tile_64x64x64"),  # 5 chunks: no ring size divides it
+    (1024, 1024, 384, "row", "col", "tile", "tile_64x64_ring2"),  # 6 chunks
     (4096, 4096, 4040, "row", "col", "tile", "tile_256x256x64_m16"),
     (256, 256, 72, "col", "row", "tile", "tile_64x64x64"),
     (256, 256, 64, "row", "row", "generic", "generic"),  # one k-step: the tile pipeline needs two
@@ -181,7 +183,7 @@ def test_auto_selection(lib, M, N, K, la, lb, want_kernel, want_name):
 def test_select_forces_and_validates(lib):
     h = gb.gemm_epi_plan(512, 512, 256, "f16", "f32", "row", "col", "none")
     try:
-        assert gb.gemm_epi_num_configs("tile") == 5
+        assert gb.gemm_epi_num_configs("tile") == 8
         assert gb.gemm_epi_num_configs("skinny") == 10
         assert gb.gemm_epi_num_configs("generic") == 1
         assert gb.gemm_epi_num_configs("auto") == 0
@@ -193,10 +195,12 @@ def test_select_forces_and_validates(lib):
         assert gb.gemm_epi_plan_describe(h)[0] == "generic"
         assert gb.gemm_epi_plan_select(h, "skinny", -1) == 2  # M = 512 > 32: unsupported, plan unchanged
         assert gb.gemm_epi_plan_describe(h)[0] == "generic"
-        assert gb.gemm_epi_plan_select(h, "tile", 5) == 1  # no such config
+        assert gb.gemm_epi_plan_select(h, "tile", 8) == 1  # no such config
+        assert gb.gemm_epi_plan_select(h, "tile", 5) == 2  # ring of 8: 4 chunks are too few
+        assert gb.gemm_epi_plan_select(h, "tile", 6) == 0  # ring of 4
         assert lib.gemm_epi_plan_select(ctypes.c_void_p(h), 9, 0) == 1  # bad enum
         assert gb.gemm_epi_plan_select(h, "auto", -1) == 0
-        assert gb.gemm_epi_plan_describe(h) == ("tile", 2, "tile_64x64x64")  # 64 workgroups beats 16
+        assert gb.gemm_epi_plan_describe(h) == ("tile", 6, "tile_64x64_ring4")  # 64 workgroups beats 16
     finally:
         gb.gemm_epi_destroy(h)
     h = gb.gemm_epi_plan(32, 128, 1024, "bf16", "bf16", "row", "col", "bias")
@@ -272,12 +276,12 @@ def _describe(*args):
 def test_tuning_table_drives_the_plan(lib, tmp_path):
     gb.gemm_epi_tuning_clear()
     args = (1024, 1024, 1024, "f16", "f16", "row", "row", "relu")
-    assert _describe(*args)[:2] == ("tile", 2)  # static rule: 64 x 64 fills the CUs
+    assert _describe(*args)[:2] == ("tile", 5)  # static rule: 64 x 64 fills the CUs, 16 chunks ring through 8 slots
     f = tmp_path / "t.txt"
     f.write_text("# a comment\n\n1024 1024 1024 0 0 0 0 1 2 1 12.5  # tile config 1\n")
     assert gb.gemm_epi_tuning_load(f) == 0 and gb.gemm_epi_tuning_size() == 1
     assert _describe(*args)[:2] == ("tile", 1)
-    assert _describe(1024, 1024, 1024, "f16", "f16", "row", "row", "none")[:2] == ("tile", 2)  # other epilogue
+    assert _describe(1024, 1024, 1024, "f16", "f16", "row", "row", "none")[:2] == ("tile", 5)  # other epilogue
     # plan_select(AUTO) restores the tuned choice
     h = gb.gemm_epi_plan(*args)
     try:
@@ -290,7 +294,7 @@ def test_tuning_table_drives_the_plan(lib, tmp_path):
     g = tmp_path / "saved.txt"
     assert gb.gemm_epi_tuning_save(g) == 0
     gb.gemm_epi_tuning_clear()
-    assert gb.gemm_epi_tuning_size() == 0 and _describe(*args)[:2] == ("tile", 2)
+    assert gb.gemm_epi_tuning_size() == 0 and _describe(*args)[:2] == ("tile", 5)
     assert gb.gemm_epi_tuning_load(g) == 0 and _describe(*args)[:2] == ("tile", 1)
     lines = [l for l in g.read_text().splitlines() if l and not l.startswith("#")]
     assert lines == ["1024 1024 1024 0 0 0 0 1 2 1 12.500"]
@@ -304,7 +308,7 @@ def test_tuning_entry_that_cannot_run_is_ignored(lib, tmp_path):
     f.write_text("1024 1024 1024 0 0 0 1 0 3 0 1.0\n64 64 256 1 1 0 1 0 2 0 1.0\n")
     assert gb.gemm_epi_tuning_load(f) == 0 and gb.gemm_epi_tuning_size() == 2
     assert _describe(1024, 1024, 1024, "f16", "f16", "row", "col", "none")[0] == "tile"
-    assert _describe(64, 64, 256, "bf16", "bf16", "row", "col", "none")[:2] == ("tile", 2)
+    assert _describe(64, 64, 256, "bf16", "bf16", "row", "col", "none")[:2] == ("tile", 6)  # the static rule: ring of 4
     gb.gemm_epi_tuning_clear()
 
 

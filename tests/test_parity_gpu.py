@@ -408,11 +408,22 @@ def test_all_tile_configs_agree_on_integers():
     for cfg in range(4):
         got, _ = run_gpu(bits, M, N, K, "f16", "f16", "row", "row", "bias_relu", "tile", cfg)
         assert np.array_equal(got, ref), cfg
-    bits = inputs.integer_inputs(M, N, K, "bf16", "row", "col", True, seed=9)
-    ref, _ = run_gpu(bits, M, N, K, "bf16", "bf16", "row", "col", "bias_relu", "generic", 0)
-    for cfg in range(gb.gemm_epi_num_configs("tile")):
-        got, _ = run_gpu(bits, M, N, K, "bf16", "bf16", "row", "col", "bias_relu", "tile", cfg)
-        assert np.array_equal(got, ref), cfg
+    # K = 384 (6 chunks of 64) also suits the rings of 2 slots; K = 512 those
+    # of 4 and 8
+    for K in (384, 512):
+        bits = inputs.integer_inputs(M, N, K, "bf16", "row", "col", True, seed=9)
+        ref, _ = run_gpu(bits, M, N, K, "bf16", "bf16", "row", "col", "bias_relu", "generic", 0)
+        ran = 0
+        for cfg in range(gb.gemm_epi_num_configs("tile")):
+            h = gb.gemm_epi_plan(M, N, K, "bf16", "bf16", "row", "col", "bias_relu")
+            ok = gb.gemm_epi_plan_select(h, "tile", cfg) == 0
+            gb.gemm_epi_destroy(h)
+            if not ok:
+                continue
+            got, _ = run_gpu(bits, M, N, K, "bf16", "bf16", "row", "col", "bias_relu", "tile", cfg)
+            assert np.array_equal(got, ref), (K, cfg)
+            ran += 1
+        assert ran >= 6, K
 
 
 # ---------------------------------------------------------------------------

@@ -1,0 +1,90 @@
+"""Parity of the deep-ring 64 x 64 tile configurations (8, 4 or 2 LDS slots;
+A row-major, B row-major through transposing LDS reads or column-major) with
+the oracle: bit-exact on integer operands for every exact epilogue, every
+K padding (the first chunk partial), chunk counts of one to several ring
+turns, shifted edge tiles, leading dimensions, the optional scale, residual
+and FP8 output; within the tolerance on random operands and on the two
+workloads the ring serves (1024^3 row-major ReLU and 128 x 64 x 256)."""
+import numpy as np
+import pytest
+import torch
+
+from epilogue_gemm_amd import binding as gb
+from epilogue_gemm_amd import inputs
+from tests.test_parity_epilogues_gpu import EXTRA_CASES, check_ex
+from tests.test_parity_gpu import BITWISE_EPIS, EPIS, check_case
+from tests.test_strides_gpu import run_strided
+
+pytestmark = pytest.mark.gpu
+
+RINGS = {5: ("tile_64x64_ring8", 8), 6: ("tile_64x64_ring4", 4), 7: ("tile_64x64_ring2", 2)}
+LBS = ["row", "col"]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    gb.load_library()
+    torch.cuda.init()
+
+
+def _k(P, turns, kpad=0):
+    """K of `turns` ring turns of P 64-deep chunks, the first chunk short by kpad."""
+    return 64 * P * turns - kpad
+
+
+@pytest.mark.parametrize("config", list(RINGS))
+@pytest.mark.parametrize("lb", LBS)
+@pytest.mark.parametrize("in_dt,out_dt", [("f16", "f16"), ("bf16", "bf16"), ("f16", "f32")])
+def test_ring_integer_bitexact(config, lb, in_dt, out_dt):
+    name, P = RINGS[config]
+    M, N, K = 192, 256, _k(P, 2)
+    for epi in EPIS:
+        bits = inputs.integer_inputs(M, N, K, in_dt, "row", lb, epi.startswith("bias"), seed=len(epi) + config)
+        got = check_case(bits, M, N, K, in_dt, out_dt, "row", lb, epi, "tile", config, epi in BITWISE_EPIS)
+        assert got == name
+
+
+# every K padding (a multiple of 8 below 64) and one to three ring turns;
+# M and N not multiples of 64 shift the last tile row and column back
+@pytest.mark.parametrize("config", list(RINGS))
+@pytest.mark.parametrize("lb", LBS)
+@pytest.mark.parametrize("kpad,turns", [(0, 1), (8, 1), (16, 2), (24, 1), (32, 3), (40, 2), (48, 1), (56, 2)])
+def test_ring_ktails_and_edges_bitexact(config, lb, kpad, turns):
+    name, P = RINGS[config]
+    M, N, K = 200, 136, _k(P, turns, kpad)
+    for in_dt, out_dt, epi in (("bf16", "bf16", "bias_relu"), ("f16", "f32", "none")):
+        bits = inputs.integer_inputs(M, N, K, in_dt, "row", lb, epi.startswith("bias"), seed=K + kpad)
+        got = check_case(bits, M, N, K, in_dt, out_dt, "row", lb, epi, "tile", config, True)
+        assert got == name
+
+
+@pytest.mark.parametrize("config", list(RINGS))
+@pytest.mark.parametrize("lb", LBS)
+def test_ring_random_tolerance(config, lb):
+    name, P = RINGS[config]
+    M, N, K = 320, 384, _k(P, 2, 16)
+    for in_dt in ("bf16", "f16"):
+        for epi in ("bias_gelu", "relu"):
+            bits = inputs.make_inputs(M, N, K, in_dt, "row", lb, epi.startswith("bias"), float(np.sqrt(K)), 0.1,
+                                      seed=M + K)
+            assert check_case(bits, M, N, K, in_dt, in_dt, "row", lb, epi, "tile", config, False) == name
+
+
+@pytest.mark.parametrize("config", list(RINGS))
+@pytest.mark.parametrize("lb", LBS)
+def test_ring_extras_fp8_and_strides(config, lb):
+    name, P = RINGS[config]
+    M, N, K = 136, 200, _k(P, 1, 24)
+    for in_dt, out_dt in (("bf16", "bf16"), ("f16", "f32")):
+        for epi, use_s, use_r in EXTRA_CASES:
+            assert check_ex(M, N, K, in_dt, out_dt, "row", lb, epi, "tile", config, use_s, use_r, True,
+                            seed=13 + len(epi)) == name
+    # FP8 output (N a multiple of 16), with the output scale
+    assert check_ex(M, 208, K, "bf16", "fp8", "row", lb, "bias_relu", "tile", config, True, False, True, seed=5,
+                    use_oscale=True) == name
+    # leading dimensions with NaN padding in A and B, a sentinel in C's
+    for in_dt, out_dt, epi, pads, extras in (("bf16", "bf16", "bias_relu", (8, 16, 24), False),
+                                             ("f16", "f32", "relu", (64, 8, 8), True)):
+        assert run_strided(M, N, K, in_dt, out_dt, "row", lb, epi, pads, "tile", config, extras) == name
