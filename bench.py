@@ -18,7 +18,10 @@ bf16 MFMAs) that each roofline also reports a fraction of;
 "attention" the attention forward (B, H, S, D = 4, 8, 1024, 64, fp16, full
 and causal).
 
-Inputs are resident in HBM before timing starts; operand sets are rotated
+Warm-up: the W warm-up launches, then untimed launches until 150 ms have run
+on the GPU, so that the clock has settled under the power limit (it dips for
+some tens of milliseconds after a burst starts).  The timed region is
+exactly K launches.  Inputs are resident in HBM before timing starts; operand sets are rotated
 across launches so that their total exceeds the 256 MB last-level cache
 (3 sets for 8192^3, 5 for the decode shape, enough for 512 MiB for the
 others).  Timing uses HIP events on the stream the library launches on: the
@@ -29,7 +32,7 @@ main workload as a reported baseline (N = 1 only).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
                        [--only all|main|skinny|workloads|attention|probes]
-                       [--no-cpu-baseline] [--no-variants] [--calib-copy]
+                       [--no-cpu-baseline] [--no-variants] [--no-graph] [--calib-copy]
 """
 from __future__ import annotations
 
@@ -130,6 +133,31 @@ def _percentiles(xs):
             "p90_ms": round(float(np.percentile(a, 90)), 6), "n": int(a.size)}
 
 
+# Untimed launches continue after the W warm-up steps until at least this
+# long has run on the GPU: under the power limit the clock dips after the
+# first launches of a burst and takes some tens of milliseconds to settle
+# (8192^3: 787, then 990 us at the fourth launch, back near 775 us after
+# about 40), so a short warm-up would time the transient.
+SETTLE_MS = 150.0
+
+
+def _settle(launch, n_sets, start_index, torch):
+    """Untimed launches until SETTLE_MS have elapsed on the GPU (in batches
+    of 8, timed with events); returns the milliseconds spent."""
+    stream = torch.cuda.current_stream()
+    spent, i = 0.0, start_index
+    while spent < SETTLE_MS:
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(8):
+            launch(i % n_sets)
+            i += 1
+        b.record(stream)
+        torch.cuda.synchronize()
+        spent += a.elapsed_time(b)
+    return spent
+
+
 def _time(launch, n_sets, steps, warmup, torch):
     """Times `launch(i)` (i rotating over n_sets operand sets) on torch's
     current stream, where the library enqueues.  Returns (mean ms per launch
@@ -138,7 +166,7 @@ def _time(launch, n_sets, steps, warmup, torch):
     stream = torch.cuda.current_stream()
     for i in range(warmup):
         launch(i % n_sets)
-    torch.cuda.synchronize()
+    _settle(launch, n_sets, warmup, torch)
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     start.record(stream)
@@ -154,6 +182,37 @@ def _time(launch, n_sets, steps, warmup, torch):
         b.record(stream)
     torch.cuda.synchronize()
     return mean_ms, _percentiles([a.elapsed_time(b) for a, b in ev])
+
+
+def _time_graph(launch, n_sets, per_graph, replays, torch):
+    """Per-launch time of `launch` with the host out of the way: `per_graph`
+    launches (rotating over the operand sets) captured in one HIP graph and
+    replayed `replays` times, each replay timed by an event pair on the
+    replay stream.  Returns (mean ms per launch over all replays, statistics
+    over replays of the mean ms per launch within a replay)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(max(n_sets, 3)):  # warm-up outside the capture
+            launch(i % n_sets)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(per_graph):
+            launch(i % n_sets)
+    stream = torch.cuda.current_stream()
+    g.replay()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(replays)]
+    for a, b in ev:
+        a.record(stream)
+        g.replay()
+        b.record(stream)
+    torch.cuda.synchronize()
+    per = [a.elapsed_time(b) / per_graph for a, b in ev]
+    del g
+    return sum(per) / len(per), _percentiles(per)
 
 
 def _plan_launcher(plan, sets, extras=None):
@@ -176,18 +235,30 @@ def _roofline(bound, achieved, peak, unit, traffic, probe_peak=None):
     return r
 
 
-def _bench_workload(w, steps, warmup, n_sets, torch, binding, inputs, parity, family):
+def _bench_workload(w, steps, warmup, n_sets, torch, binding, inputs, parity, family, graph=True):
     """One workload through the automatic plan: mean and per-launch times, the
     roofline of its kernel (TFLOP/s of 2MNK, or GB/s of compulsory bytes for
     the HBM-bound decode shape)."""
     bits, sets = _device_sets(w, n_sets, torch, parity, inputs)
     plan = binding.Plan(w.M, w.N, w.K, w.in_dtype, w.out_dtype, w.layout_a, w.layout_b, w.epilogue)
-    mean_ms, per = _time(_plan_launcher(plan, sets), n_sets, steps, warmup, torch)
+    launch = _plan_launcher(plan, sets)
+    mean_ms, per = _time(launch, n_sets, steps, warmup, torch)
     rec = {"workload": w.name, "kernel": plan.name, "ms_per_step": round(mean_ms, 6), "per_launch": per,
            "steps": steps, "operand_sets_rotated": n_sets,
            "TFLOP/s": round(w.flops / (mean_ms * 1e-3) / 1e12, 2),
            "GB/s": round(w.compulsory_bytes() / (mean_ms * 1e-3) / 1e9, 1),
            "compulsory_bytes": w.compulsory_bytes(), "flops": w.flops}
+    if graph and mean_ms < 0.05:
+        # launches this short are paced by the host's launch rate when
+        # enqueued one by one from Python: time them replayed from a graph
+        # as well, and check that a replay writes what an eager run writes
+        ref = sets[0][3].clone()
+        gmean, gper = _time_graph(launch, n_sets, max(n_sets, 100), 20, torch)
+        same = bool(torch.equal(sets[0][3].view(torch.uint8), ref.view(torch.uint8)))
+        rec["graph"] = {"ms_per_launch": round(gmean, 6), "per_replay": gper,
+                        "TFLOP/s": round(w.flops / (gmean * 1e-3) / 1e12, 2),
+                        "GB/s": round(w.compulsory_bytes() / (gmean * 1e-3) / 1e9, 1),
+                        "launches_per_graph": max(n_sets, 100), "replay_equals_eager": same}
     plan.close()
     del sets
     torch.cuda.empty_cache()
@@ -332,6 +403,8 @@ def main(argv=None):
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the further-epilogue variants and attention (so that a profile of --only main "
                          "sees the headline kernel only)")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time short workloads eagerly only (no graph replays; for counter collection)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="after timing, run a plain 1 GiB device copy (elementwise kernel) three times, so that "
                          "HBM byte counters can be scaled against a kernel of known traffic")
@@ -368,7 +441,8 @@ def main(argv=None):
     if sel in ("all", "main"):
         w = inputs.WORKLOADS[MAIN]
         say(w.name)
-        rec, main_bits = _bench_workload(w, args.steps, args.warmup, 3, torch, binding, inputs, parity, "tile")
+        rec, main_bits = _bench_workload(w, args.steps, args.warmup, 3, torch, binding, inputs, parity, "tile",
+                                         not args.no_graph)
         workloads[w.name] = rec
         if sel == "all" and not args.no_variants:
             say("epilogue variants")
@@ -381,7 +455,7 @@ def main(argv=None):
         say(w.name)
         # 5 sets x 128 MiB of B: more than the 256 MB last-level cache
         rec, _ = _bench_workload(w, max(args.steps, 200), max(args.warmup, 20), 5, torch, binding, inputs, parity,
-                                 "skinny")
+                                 "skinny", not args.no_graph)
         workloads[w.name] = rec
     if sel in ("all", "workloads"):
         for name in inputs.WORKLOADS:
@@ -392,7 +466,7 @@ def main(argv=None):
             # operand sets past twice the last-level cache (the 128 x 64 x 256
             # case: 64 sets, still cache-resident; one tile, launch-bound)
             rec, _ = _bench_workload(w, max(args.steps, 100), max(args.warmup, 20), _n_sets(w, 3), torch, binding,
-                                     inputs, parity, "tile")
+                                     inputs, parity, "tile", not args.no_graph)
             workloads[w.name] = rec
     if sel in ("all", "attention") and not args.no_variants:
         say("attention")
@@ -429,6 +503,7 @@ def main(argv=None):
             "n_gpus": 1,
             "steps": args.steps,
             "warmup": args.warmup,
+            "warmup_settle_ms": SETTLE_MS,
             "ms_per_step": round(m["ms_per_step"], 5),
             "higher_is_better": True,
             "scaling": "weak",
