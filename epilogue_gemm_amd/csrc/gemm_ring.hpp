@@ -29,16 +29,19 @@
 // of a read touch 8 distinct 16-byte bank groups, each as two 8-byte halves.
 //
 // Synchronisation is the ring's: chunk c sits in slot c % P (the chunk
-// count is a multiple of P, so every slot index is a compile-time constant;
+// count is a multiple of P, or odd with P = 2, where the one chunk past the
+// last whole turn has a code path of its own; so every slot index is a
+// compile-time constant;
 // one __shared__ object per slot, so the compiler can tell a read of one
 // slot from a copy in flight into another); one barrier per chunk, after each
 // wave's s_waitcnt on its own copies of that chunk, makes the slot complete
 // and proves every wave is past the previous chunk, whose slot then receives
 // chunk c + P - 1.  K not a multiple of 64: the k axis is shifted by
 // kpad = 64 - K % 64 so that chunk 0 is the partial one and its positions
-// k < 0 load as zeros.  The last tile row and column are shifted back to end
-// at M and N (they recompute part of a neighbour with the same k order, so
-// with identical values).  (Pipelined tile copies and block rasterisation:
+// k < 0 load as zeros.  The last tile row and column
+// are shifted back to end at M and N (they recompute part of a neighbour
+// with the same k order, so with identical values); a problem with fewer
+// than 64 rows or columns takes one tile there, masked past the end.  (Pipelined tile copies and block rasterisation:
 // atlascloud.ai "Writing high-performance kernels in TileLang", section
 // "Écrivons un GEMM"; epilogue on the accumulator fragment: csdn
 // "从零开始学习 TileLang" ch.10 sec. 10.8; small problems that leave the
@@ -101,14 +104,19 @@ struct RowBLoader {
   uint32_t row_bytes;  // ldb * 2
   int wave, lane;
 
-  __device__ __forceinline__ RowBLoader(const void* B, int n0, int K, int ldb, int kpad, int lane_, int wave_) {
+  __device__ __forceinline__ RowBLoader(const void* B, int n0, int N, int K, int ldb, int kpad, int lane_,
+                                        int wave_) {
     // base at k = -kpad, column n0; the range ends with the last k-row
     const char* base = (const char*)B + (int64_t)n0 * 2 - (int64_t)kpad * ldb * 2;
     rsrc = tile::make_rsrc(base, (uint32_t)((int64_t)(K + kpad) * ldb * 2 - (int64_t)n0 * 2));
     row_bytes = (uint32_t)ldb * 2u;
     lane = lane_;
     wave = wave_;
-    voff = (uint32_t)(lane >> 3) * row_bytes + (uint32_t)(((lane & 7) ^ (2 * ((lane >> 3) & 3))) << 4);
+    const int chunk = (lane & 7) ^ (2 * ((lane >> 3) & 3));
+    voff = (uint32_t)(lane >> 3) * row_bytes + (uint32_t)(chunk << 4);
+    // fewer than 64 columns (N < 64): columns past N load nothing (N is a
+    // multiple of 8, so a 16-byte chunk lies wholly on one side)
+    if (n0 + 8 * chunk >= N) voff = 0xFFFFFFF0u;
   }
   // instruction i (0, 1) of chunk kt
   __device__ __forceinline__ void issue(char* dst, int kt, int i) const {
@@ -142,9 +150,12 @@ __global__ __launch_bounds__(kNW * 64) void gemm_ring_kernel(const TIn* __restri
 
   int tm, tn;
   tile::raster(blockIdx.x, tiles_m, tiles_n, panel, tm, tn);
-  const int m0 = min(tm * kTile, M - kTile), n0 = min(tn * kTile, N - kTile);
+  // A problem smaller than the tile (M or N below 64) is covered by one
+  // tile row or column at 0, its rows or columns past the end loading
+  // nothing and storing nothing (MASK below).
+  const int m0 = max(0, min(tm * kTile, M - kTile)), n0 = max(0, min(tn * kTile, N - kTile));
   const int kpad = (-K) & (kBK - 1);
-  const int nchunks = (K + kpad) / kBK;  // a multiple of P (checked on the host)
+  const int nchunks = (K + kpad) / kBK;
 
   char* sa[P];
   char* sb[P];
@@ -153,7 +164,7 @@ __global__ __launch_bounds__(kNW * 64) void gemm_ring_kernel(const TIn* __restri
   const DirectLoader<kTile, kNW> da(A, m0, M, lda, kpad, tid, wave);
   // (only one of the two B movers is used)
   const DirectLoader<kTile, kNW> db(B, n0, N, ldb, kpad, tid, wave);
-  const RowBLoader rb(B, n0, K, ldb, kpad, lane, wave);
+  const RowBLoader rb(B, n0, N, K, ldb, kpad, lane, wave);
 
   auto issue = [&](int j, int c) __attribute__((always_inline)) {
     if (c == 0 && kpad != 0) {
@@ -212,10 +223,11 @@ __global__ __launch_bounds__(kNW * 64) void gemm_ring_kernel(const TIn* __restri
     for (int q = 0; q < 4; ++q) acc = mfma32<TIn>(b[q], a[q], acc);
   };
 
-  // Chunk c lives in slot c % P (the chunk count is a multiple of P,
-  // checked on the host): one code path into the loop, so that the compiler
-  // sees the same copies in flight on entry and around the back edge and can
-  // tell every slot's copies apart.  Chunks 0 .. P-2 first.
+  // Chunk c lives in slot c % P (the chunk count is a multiple of P, or any
+  // count for P = 2; checked on the host): one code path into the loop, so
+  // that the compiler sees the same copies in flight on entry and around
+  // the back edge and can tell every slot's copies apart.  Chunks 0 .. P-2
+  // first.
   static_for<P - 1>([&](auto jc) __attribute__((always_inline)) {
     constexpr int jj = decltype(jc)::value;
     issue(jj, jj);
@@ -231,18 +243,28 @@ __global__ __launch_bounds__(kNW * 64) void gemm_ring_kernel(const TIn* __restri
       __builtin_amdgcn_sched_barrier(0);
     });
   }
-  // last P chunks: only the first still has a chunk to issue
-  static_for<P>([&](auto jc) __attribute__((always_inline)) {
-    constexpr int jj = decltype(jc)::value;
-    if constexpr (jj == 0) {
-      arrive<OPS * (P - 2)>();
-      issue(P - 1, c0 + P - 1);
-    } else {
-      arrive<OPS * (P - 1 - jj)>();
-    }
-    compute(jj);
-    __builtin_amdgcn_sched_barrier(0);
-  });
+  // Two slots and an odd chunk count (K <= 64 among them): the loop has
+  // issued the last chunk, into slot 0, and nothing follows it.  Either
+  // way one chunk is in flight in slot 0 here.
+  bool odd = false;
+  if constexpr (P == 2) odd = (nchunks & 1) != 0;
+  if (odd) {
+    arrive<0>();
+    compute(0);
+  } else {
+    // last P chunks: only the first still has a chunk to issue
+    static_for<P>([&](auto jc) __attribute__((always_inline)) {
+      constexpr int jj = decltype(jc)::value;
+      if constexpr (jj == 0) {
+        arrive<OPS * (P - 2)>();
+        issue(P - 1, c0 + P - 1);
+      } else {
+        arrive<OPS * (P - 1 - jj)>();
+      }
+      compute(jj);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  }
 
   // Every wave is done with the ring: stage the epilogue in it (4 KiB per
   // wave at most: 32 rows x 32 fp32 outputs).
@@ -252,12 +274,15 @@ __global__ __launch_bounds__(kNW * 64) void gemm_ring_kernel(const TIn* __restri
   else stage_w = (wave & 1 ? sa[1] : sa[0]) + (wave >> 1) * (kOpBytes / 2);
   static_assert(32 * 32 * sizeof(TOut) <= (size_t)kOpBytes / 2, "staging area");
   const f32x16 accs[1][1] = {{acc}};
-  if (scale != nullptr || res != nullptr || out_scale != nullptr)
-    tile::write_tile<32, 32, TIn, TOut, EPI, true>(accs, bias, C, ldc, m0 + 32 * wm, n0 + 32 * wn, lane, stage_w, scale,
-                                                   res, out_scale);
+  const int mw = m0 + 32 * wm, nw = n0 + 32 * wn;
+  if (M < kTile || N < kTile)
+    tile::write_tile<32, 32, TIn, TOut, EPI, true, true>(accs, bias, C, ldc, mw, nw, lane, stage_w, scale, res,
+                                                         out_scale, M, N);
+  else if (scale != nullptr || res != nullptr || out_scale != nullptr)
+    tile::write_tile<32, 32, TIn, TOut, EPI, true>(accs, bias, C, ldc, mw, nw, lane, stage_w, scale, res, out_scale);
   else
-    tile::write_tile<32, 32, TIn, TOut, EPI, false>(accs, bias, C, ldc, m0 + 32 * wm, n0 + 32 * wn, lane, stage_w,
-                                                    nullptr, nullptr, nullptr);
+    tile::write_tile<32, 32, TIn, TOut, EPI, false>(accs, bias, C, ldc, mw, nw, lane, stage_w, nullptr, nullptr,
+                                                    nullptr);
 }
 
 template <typename TIn, typename TOut, int EPI, bool BROW, int P>

@@ -119,6 +119,9 @@ struct DirectLoader {
     for (int p = 0; p < NV; ++p) {
       const int row = (NW * p + wave) * 8 + rl;
       voff[p] = (uint32_t)(row * ld * 2 + ((pc ^ sw(row)) << 4));
+      // a tile taller than what is left of the operand (a 64-row tile of a
+      // problem with fewer rows): rows past the end load nothing
+      if (r0 + row >= rows_total) voff[p] = 0xFFFFFFF0u;
     }
     rows64 = (uint32_t)(64 * ld * 2);
   }
@@ -226,11 +229,17 @@ __device__ __forceinline__ void raster(int bid, int tiles_m, int tiles_n, int pa
 // spread the banks), then read back 16 bytes per lane along rows and stored:
 // one wave instruction covers whole row segments of the band.  Bands are
 // processed one after another so that few values are live at a time.
-template <int WM, int WN, typename TIn, typename TOut, int EPI, bool EXTRAS>
+//
+// MASK: the sub-tile may reach past row m_lim or column n_lim of C (a tile
+// larger than the problem); outputs there are neither computed from real
+// operands nor stored, and the bias, scale and residual past them are not
+// read.  (16-byte output chunks lie wholly on one side: n_lim is a multiple
+// of 8, of 16 for 1-byte outputs.)
+template <int WM, int WN, typename TIn, typename TOut, int EPI, bool EXTRAS, bool MASK = false>
 __device__ __forceinline__ void write_tile(const f32x16 (&acc)[WM / 32][WN / 32], const TIn* __restrict__ bias,
                                           TOut* __restrict__ C, int ldc, int m_w, int n_w, int lane, char* stage,
                                           const float* __restrict__ scale, const TOut* __restrict__ res,
-                                          const float* __restrict__ out_scale) {
+                                          const float* __restrict__ out_scale, int m_lim = 0, int n_lim = 0) {
   constexpr int TM = WM / 32, TN = WN / 32;
   constexpr int OSZ = (int)sizeof(TOut);
   constexpr int CPR = WN * OSZ / 16;           // 16-byte chunks per staged row
@@ -246,8 +255,12 @@ __device__ __forceinline__ void write_tile(const f32x16 (&acc)[WM / 32][WN / 32]
   for (int j = 0; j < TN; ++j)
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      if constexpr (epi_has_bias<EPI>()) bq[j][q] = *(const u32x2*)(bias + n_w + j * 32 + 8 * q + 4 * h);
-      else bq[j][q] = u32x2{0u, 0u};
+      if constexpr (epi_has_bias<EPI>()) {
+        if (!MASK || n_w + j * 32 + 8 * q + 4 * h < n_lim) bq[j][q] = *(const u32x2*)(bias + n_w + j * 32 + 8 * q + 4 * h);
+        else bq[j][q] = u32x2{0u, 0u};
+      } else {
+        bq[j][q] = u32x2{0u, 0u};
+      }
     }
 
 #pragma unroll
@@ -260,8 +273,9 @@ __device__ __forceinline__ void write_tile(const f32x16 (&acc)[WM / 32][WN / 32]
         const int col = n_w + j * 32 + 8 * q + 4 * h;
         f32x4 sc = f32x4{1.0f, 1.0f, 1.0f, 1.0f}, r = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
         if constexpr (EXTRAS) {
-          if (scale) sc = *(const f32x4*)(scale + col);
-          if (res) r = load4<TOut>(res + (int64_t)(m_w + i * 32 + m_l) * ldc + col);
+          const bool in = !MASK || (col < n_lim && m_w + i * 32 + m_l < m_lim);
+          if (scale && in) sc = *(const f32x4*)(scale + col);
+          if (res && in) r = load4<TOut>(res + (int64_t)(m_w + i * 32 + m_l) * ldc + col);
         }
         float v[4];
 #pragma unroll
@@ -296,7 +310,8 @@ __device__ __forceinline__ void write_tile(const f32x16 (&acc)[WM / 32][WN / 32]
     for (int t = 0; t < 32 / RPI; ++t) {
       const int r = t * RPI + lane / CPR, c = lane % CPR;
       const u32x4 d = *(const u32x4*)(stage + r * (WN * OSZ) + ((c ^ (r & SWM)) << 4));
-      *(u32x4*)((char*)(C + (int64_t)(m_w + i * 32 + r) * ldc + n_w) + c * 16) = d;
+      if (!MASK || (m_w + i * 32 + r < m_lim && n_w + c * (16 / OSZ) < n_lim))
+        *(u32x4*)((char*)(C + (int64_t)(m_w + i * 32 + r) * ldc + n_w) + c * 16) = d;
     }
     __builtin_amdgcn_sched_barrier(0);
   }

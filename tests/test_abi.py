@@ -141,13 +141,13 @@ def test_fp8_output_needs_16_columns_in_tile_kernels(lib):
     (8192, 8192, 8192, "row", "col", "tile", "tile_256x256x64_m16"),
     (4096, 4096, 4096, "row", "row", "tile", "tile_256x256x64"),
     (4096, 4096, 4096, "row", "col", "tile", "tile_256x256x64_m16"),
-    (1024, 1024, 1024, "row", "row", "tile", "tile_64x64_ring8"),  # 16 chunks of 64 through 8 slots
+    (1024, 1024, 1024, "row", "row", "tile", "tile_64x64_ring4"),  # 16 chunks of 64 through 4 slots
     (128, 64, 256, "row", "col", "tile", "tile_64x64_ring4"),  # 4 chunks of 64
     (32, 8192, 8192, "row", "col", "skinny", "skinny_32n_8w_5x256k"),
     (1, 4096, 4096, "row", "col", "skinny", "skinny_32n_8w_5x256k"),
     (32, 4096, 768, "row", "col", "skinny", "skinny_32n_4w_2x256k"),  # three chunks of 256
     (32, 4096, 192, "row", "col", "skinny", "skinny_32n_2w_2x128k"),  # two chunks of 128, the first padded
-    (32, 4096, 128, "row", "col", "generic", "generic"),  # K too short for a skinny ring, M for a tile
+    (32, 4096, 128, "row", "col", "tile", "tile_64x64_ring2"),  # K too short for a skinny ring: one masked tile row
     (32, 8192, 8200, "row", "col", "skinny", "skinny_32n_8w_5x256k"),  # 33 chunks of 256, the first padded
     (32, 8192, 8320, "row", "col", "skinny", "skinny_32n_4w_8x128k"),  # whole chunks of 128 come first
     (32, 8192, 8196, "row", "col", "generic", "generic"),  # K not a multiple of 8
@@ -157,19 +157,26 @@ def test_fp8_output_needs_16_columns_in_tile_kernels(lib):
     (32, 4096, 200, "row", "row", "skinny", "skinny_rowb_32n_2w_2x128k"),  # two chunks of 128, the first padded
     (32, 8192, 8192, "col", "row", "generic", "generic"),  # column-major A: no decode-shape kernel
     (2000, 8200, 4096, "row", "col", "tile", "tile_256x256x64_m16"),  # last tile row and column shifted back
-    (1000, 1000, 1024, "row", "col", "tile", "tile_64x64_ring8"),  # 16 x 16 edge-tiled 64 x 64 tiles
+    (1000, 1000, 1024, "row", "col", "tile", "tile_64x64_ring4"),  # 16 x 16 edge-tiled 64 x 64 tiles
     (3000, 2000, 4096, "row", "row", "tile", "tile_128x128x64"),  # 24 x 16 tiles of 128
     (1000, 1000, 1024, "col", "col", "tile", "tile_64x64x64"),
     (1001, 1000, 1024, "col", "col", "generic", "generic"),  # column-major A needs M % 8
     (1000, 1004, 1024, "row", "col", "generic", "generic"),  # N % 8
     (37, 53, 29, "row", "row", "generic", "generic"),
     (256, 256, 100, "col", "row", "generic", "generic"),  # K not a multiple of 8
-    (1024, 1024, 1000, "row", "col", "tile", "tile_64x64_ring8"),  # K % 64 = 40: a partial first chunk
-    (1024, 1024, 320, "row", "row", "tile", "tile_64x64x64"),  # 5 chunks: no ring size divides it
+    (1024, 1024, 1000, "row", "col", "tile", "tile_64x64_ring4"),  # K % 64 = 40: a partial first chunk
+    (1024, 1024, 1536, "row", "row", "tile", "tile_64x64_ring4"),  # 24 chunks: 4 divides (as does 8)
+    (1024, 1024, 1152, "row", "row", "tile", "tile_64x64_ring2"),  # 18 chunks
+    (1024, 1024, 320, "row", "row", "tile", "tile_64x64_ring2"),  # 5 chunks: two slots take an odd count
     (1024, 1024, 384, "row", "col", "tile", "tile_64x64_ring2"),  # 6 chunks
     (4096, 4096, 4040, "row", "col", "tile", "tile_256x256x64_m16"),
     (256, 256, 72, "col", "row", "tile", "tile_64x64x64"),
-    (256, 256, 64, "row", "row", "generic", "generic"),  # one k-step: the tile pipeline needs two
+    (256, 256, 64, "row", "row", "tile", "tile_64x64_ring2"),  # one chunk
+    (256, 256, 64, "col", "row", "generic", "generic"),  # one k-step: the two-stage pipeline needs two
+    (48, 40, 64, "row", "row", "tile", "tile_64x64_ring2"),  # M and N below the tile: masked
+    (63, 1000, 320, "row", "col", "tile", "tile_64x64_ring2"),
+    (1, 8, 8, "row", "row", "tile", "tile_64x64_ring2"),
+    (40, 4096, 4096, "row", "col", "tile", "tile_64x64_ring4"),  # M just past the skinny kernels
 ])
 def test_auto_selection(lib, M, N, K, la, lb, want_kernel, want_name):
     h = gb.gemm_epi_plan(M, N, K, "bf16", "bf16", la, lb, "none")
@@ -208,7 +215,9 @@ def test_select_forces_and_validates(lib):
         assert gb.gemm_epi_plan_describe(h)[:2] == ("skinny", 1)  # first config that fits
         assert gb.gemm_epi_plan_select(h, "skinny", 0) == 2  # four chunks of 256 do not fill five slots
         assert gb.gemm_epi_plan_select(h, "skinny", 3) == 0
-        assert gb.gemm_epi_plan_select(h, "tile", -1) == 2  # M = 32 holds no 64 x 64 tile
+        assert gb.gemm_epi_plan_select(h, "tile", -1) == 0  # one masked 64 x 64 tile row
+        assert gb.gemm_epi_plan_describe(h) == ("tile", 6, "tile_64x64_ring4")  # 16 chunks
+        assert gb.gemm_epi_plan_select(h, "tile", 0) == 2  # M = 32 holds no 256 x 256 tile
     finally:
         gb.gemm_epi_destroy(h)
     h = gb.gemm_epi_plan(512, 512, 320, "bf16", "bf16", "row", "row", "bias")
@@ -276,12 +285,12 @@ def _describe(*args):
 def test_tuning_table_drives_the_plan(lib, tmp_path):
     gb.gemm_epi_tuning_clear()
     args = (1024, 1024, 1024, "f16", "f16", "row", "row", "relu")
-    assert _describe(*args)[:2] == ("tile", 5)  # static rule: 64 x 64 fills the CUs, 16 chunks ring through 8 slots
+    assert _describe(*args)[:2] == ("tile", 6)  # static rule: 64 x 64 fills the CUs, 16 chunks ring through 4 slots
     f = tmp_path / "t.txt"
     f.write_text("# a comment\n\n1024 1024 1024 0 0 0 0 1 2 1 12.5  # tile config 1\n")
     assert gb.gemm_epi_tuning_load(f) == 0 and gb.gemm_epi_tuning_size() == 1
     assert _describe(*args)[:2] == ("tile", 1)
-    assert _describe(1024, 1024, 1024, "f16", "f16", "row", "row", "none")[:2] == ("tile", 5)  # other epilogue
+    assert _describe(1024, 1024, 1024, "f16", "f16", "row", "row", "none")[:2] == ("tile", 6)  # other epilogue
     # plan_select(AUTO) restores the tuned choice
     h = gb.gemm_epi_plan(*args)
     try:
@@ -294,7 +303,7 @@ def test_tuning_table_drives_the_plan(lib, tmp_path):
     g = tmp_path / "saved.txt"
     assert gb.gemm_epi_tuning_save(g) == 0
     gb.gemm_epi_tuning_clear()
-    assert gb.gemm_epi_tuning_size() == 0 and _describe(*args)[:2] == ("tile", 5)
+    assert gb.gemm_epi_tuning_size() == 0 and _describe(*args)[:2] == ("tile", 6)
     assert gb.gemm_epi_tuning_load(g) == 0 and _describe(*args)[:2] == ("tile", 1)
     lines = [l for l in g.read_text().splitlines() if l and not l.startswith("#")]
     assert lines == ["1024 1024 1024 0 0 0 0 1 2 1 12.500"]

@@ -3,8 +3,10 @@ A row-major, B row-major through transposing LDS reads or column-major) with
 the oracle: bit-exact on integer operands for every exact epilogue, every
 K padding (the first chunk partial), chunk counts of one to several ring
 turns, shifted edge tiles, leading dimensions, the optional scale, residual
-and FP8 output; within the tolerance on random operands and on the two
-workloads the ring serves (1024^3 row-major ReLU and 128 x 64 x 256)."""
+and FP8 output; problems smaller than the tile (M or N below 64, masked)
+and odd chunk counts through two slots; within the tolerance on random
+operands and on the two workloads the ring serves (1024^3 row-major ReLU
+and 128 x 64 x 256)."""
 import numpy as np
 import pytest
 import torch
@@ -88,3 +90,47 @@ def test_ring_extras_fp8_and_strides(config, lb):
     for in_dt, out_dt, epi, pads, extras in (("bf16", "bf16", "bias_relu", (8, 16, 24), False),
                                              ("f16", "f32", "relu", (64, 8, 8), True)):
         assert run_strided(M, N, K, in_dt, out_dt, "row", lb, epi, pads, "tile", config, extras) == name
+
+
+# Problems smaller than the tile: M or N below 64 take one tile row or
+# column, masked past the end (C carries a sentinel in 64 rows past row M
+# and in its row padding; no output there may change).  K of one chunk, of
+# an odd number of chunks (two slots only) and with a partial first chunk.
+SMALL = [(1, 8, 8), (33, 40, 64), (48, 56, 200), (63, 8, 320), (17, 136, 64), (200, 24, 136), (40, 264, 128),
+         (64, 48, 72), (7, 16, 1000)]
+
+
+@pytest.mark.parametrize("lb", LBS)
+@pytest.mark.parametrize("M,N,K", SMALL)
+def test_ring_small_problems_bitexact(lb, M, N, K):
+    for in_dt, out_dt, epi, pads, extras in (("bf16", "bf16", "bias_relu", (8, 16, 24), False),
+                                             ("f16", "f32", "relu", (64, 8, 8), True),
+                                             ("f16", "f16", "bias", (0, 0, 0), True)):
+        assert run_strided(M, N, K, in_dt, out_dt, "row", lb, epi, pads, "tile", 7, extras,
+                           extra_rows=64) == "tile_64x64_ring2"
+    if N % 16 == 0:
+        assert run_strided(M, N, K, "bf16", "fp8", "row", lb, "bias", (8, 8, 16), "tile", 7, False,
+                           extra_rows=64) == "tile_64x64_ring2"
+    # the automatic plan takes the same kernel where no other fits
+    bits = inputs.integer_inputs(M, N, K, "bf16", "row", lb, True, seed=M * N + K)
+    name = check_case(bits, M, N, K, "bf16", "bf16", "row", lb, "bias_gelu", "auto", -1, False)
+    assert name.startswith("tile_64x64_ring") or name.startswith("skinny_"), name
+
+
+@pytest.mark.parametrize("config", [5, 6])
+@pytest.mark.parametrize("lb", LBS)
+def test_ring_small_problems_deep_rings_bitexact(config, lb):
+    name, P = RINGS[config]
+    for M, N in ((33, 40), (63, 8), (5, 200)):
+        K = _k(P, 1, 24)
+        assert run_strided(M, N, K, "bf16", "bf16", "row", lb, "bias_relu", (8, 16, 24), "tile", config, True,
+                           extra_rows=64) == name
+
+
+@pytest.mark.parametrize("lb", LBS)
+def test_ring_small_problems_random_tolerance(lb):
+    for M, N, K in ((48, 56, 200), (33, 264, 1000)):
+        for in_dt in ("bf16", "f16"):
+            bits = inputs.make_inputs(M, N, K, in_dt, "row", lb, True, float(np.sqrt(K)), 0.1, seed=M + K)
+            assert check_case(bits, M, N, K, in_dt, in_dt, "row", lb, "bias_gelu", "tile", 7, False) == \
+                "tile_64x64_ring2"

@@ -32,7 +32,10 @@ def _pad(mat, ld, fill):
     return out
 
 
-def run_strided(M, N, K, in_dt, out_dt, la, lb, epi, pads, kernel="auto", config=-1, extras=False):
+def run_strided(M, N, K, in_dt, out_dt, la, lb, epi, pads, kernel="auto", config=-1, extras=False, extra_rows=0):
+    """Run with leading dimensions padded by pads = (A, B, C), NaN in A's and
+    B's padding, a sentinel in C's padding and in extra_rows rows of C past
+    row M; check C's M x N outputs bit for bit and that no padding changed."""
     bits = inputs.integer_inputs(M, N, K, in_dt, la, lb, epi.startswith("bias"), seed=M + N + K)
     a_shape = (M, K) if la == "row" else (K, M)
     b_shape = (K, N) if lb == "row" else (N, K)
@@ -42,7 +45,7 @@ def run_strided(M, N, K, in_dt, out_dt, la, lb, epi, pads, kernel="auto", config
     bias = parity.to_device(bits["bias"], in_dt) if bits["bias"] is not None else None
     sentinel = {"f16": 0x3C01, "bf16": 0x3F81, "f32": 0x3F800001, "fp8": 0x39}[out_dt]
     np_out = {"f32": np.uint32, "fp8": np.uint8}.get(out_dt, np.uint16)
-    C = parity.to_device_out(np.full(M * ldc, sentinel, np_out), out_dt)
+    C = parity.to_device_out(np.full((M + extra_rows) * ldc, sentinel, np_out), out_dt)
     plan = gb.Plan(M, N, K, in_dt, out_dt, la, lb, epi, kernel, config, lda=lda, ldb=ldb, ldc=ldc)
     ex = inputs.extras_inputs(M, N, out_dt, seed=3, integer=True) if extras else None
     res = None
@@ -51,7 +54,8 @@ def run_strided(M, N, K, in_dt, out_dt, la, lb, epi, pads, kernel="auto", config
     sc = torch.from_numpy(ex["scale"]).cuda() if extras else None
     plan.run(A, B, bias, C, scale=sc, residual=res)
     torch.cuda.synchronize()
-    got = parity.out_bits(C).reshape(M, ldc)
+    got_all = parity.out_bits(C).reshape(M + extra_rows, ldc)
+    got = got_all[:M]
     name = plan.name
     plan.close()
     y, c = oracle.gemm_epi(bits["A"], bits["B"], bits["bias"], M, N, K, in_dt, out_dt, la, lb, epi,
@@ -60,6 +64,7 @@ def run_strided(M, N, K, in_dt, out_dt, la, lb, epi, pads, kernel="auto", config
     mism = np.count_nonzero(got[:, :N] != c.reshape(M, N).astype(got.dtype))
     assert mism == 0, f"{name}: {mism} of {M * N} outputs differ"
     assert np.all(got[:, N:] == sentinel), f"{name}: padding of C was written"
+    assert np.all(got_all[M:] == sentinel), f"{name}: rows of C past M were written"
     return name
 
 
