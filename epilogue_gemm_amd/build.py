@@ -29,6 +29,17 @@ FLAGS = [
 ]
 
 
+# Per-unit flags.  The row-major-B 16x16x32 tile kernel uses the generic
+# machine scheduler: under the default AMDGPU scheduler its accumulators are
+# copied between AGPRs and VGPRs around every MFMA (about 400 extra moves
+# per two k-steps); the generic one keeps them in place.  Its other kernels
+# are built as usual.
+UNIT_FLAGS = {
+    "gemm_tile16_rowb_f16.hip": ["-mllvm", "-misched=ilpmin"],
+    "gemm_tile16_rowb_bf16.hip": ["-mllvm", "-misched=ilpmin"],
+}
+
+
 def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
 
@@ -55,7 +66,8 @@ def _up_to_date(src: str) -> bool:
 
 def _compile(src: str) -> str:
     obj = _obj(src)
-    cmd = [HIPCC, "-x", "hip", *FLAGS, "-MMD", "-MF", obj + ".d", "-c", src, "-o", obj]
+    extra = UNIT_FLAGS.get(os.path.basename(src), [])
+    cmd = [HIPCC, "-x", "hip", *FLAGS, *extra, "-MMD", "-MF", obj + ".d", "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")

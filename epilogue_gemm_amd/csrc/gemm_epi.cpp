@@ -28,6 +28,7 @@ static const TileConfig kTile[] = {
     {64, 64, 4, "tile_64x64_ring8", 32, 8},
     {64, 64, 4, "tile_64x64_ring4", 32, 4},
     {64, 64, 4, "tile_64x64_ring2", 32, 2},
+    {256, 256, 4, "tile_256x256x64_m16_rowb", 16, 0, true},
 };
 
 int tile_num_configs() { return (int)(sizeof(kTile) / sizeof(kTile[0])); }
@@ -41,14 +42,18 @@ bool tile_supports(int cfg, const Problem& p) {
   // E4M3 output; M % 8 when A is column-major; leading dimensions likewise),
   // and K a multiple of 8 (16-byte chunks) spanning at least two k-steps of
   // 64 (a partial one first, when K % 64 != 0).
-  // The 16x16x32 configuration takes k-contiguous operands only (A
-  // row-major, B column-major).
+  // The 16x16x32 configurations take A row-major and B column-major, or B
+  // row-major (its buffer range, K + 64 rows of ldb elements, must fit
+  // 32-bit byte offsets).
   // The ring configurations take A row-major (either B); a row-major B's
   // buffer range (K + 64 rows of ldb elements) must fit 32-bit byte
   // offsets.
   const TileConfig& c = kTile[cfg];
   const int n_align = p.out_dt == GEMM_EPI_FP8_E4M3 ? 16 : 8;
-  if (c.mfma == 16 && (p.la != GEMM_EPI_ROW_MAJOR || p.lb != GEMM_EPI_COL_MAJOR)) return false;
+  if (c.mfma == 16 &&
+      (p.la != GEMM_EPI_ROW_MAJOR || p.lb != (c.brow ? GEMM_EPI_ROW_MAJOR : GEMM_EPI_COL_MAJOR) ||
+       (c.brow && (p.K + 64) * p.ldb * 2 >= ((int64_t)1 << 32))))
+    return false;
   if (c.ring > 0 && (p.la != GEMM_EPI_ROW_MAJOR ||
                      (p.lb == GEMM_EPI_ROW_MAJOR && (p.K + 64) * p.ldb * 2 >= ((int64_t)1 << 32))))
     return false;
@@ -65,11 +70,11 @@ bool tile_supports(int cfg, const Problem& p) {
 
 int tile_choose(const Problem& p) {
   // Largest tile that still gives at least one workgroup per CU; else the
-  // smallest tile that fits (most parallelism).  With both operands
-  // k-contiguous the 256 x 256 tile runs on 16x16x32 MFMAs with 4 waves
-  // (8192^3 bf16: 759 us against 829 us for 8 waves on 32x32x16); a
-  // register-staged operand keeps the 4-wave 32x32x16 kernel (8 waves
-  // measured 12 % slower at 4096^3 with B row-major).
+  // smallest tile that fits (most parallelism).  With A row-major the 256 x
+  // 256 tile runs on 16x16x32 MFMAs with 4 waves (8192^3 bf16 with B
+  // column-major: 759 us against 829 us for 8 waves on 32x32x16); a
+  // register-staged A keeps the 4-wave 32x32x16 kernel (8 waves measured
+  // 12 % slower at 4096^3).
   const bool direct = p.la == GEMM_EPI_ROW_MAJOR && p.lb == GEMM_EPI_COL_MAJOR;
   int fallback = -1;
   for (int c = 0; c < 3; ++c) {
@@ -82,6 +87,9 @@ int tile_choose(const Problem& p) {
     fallback = c;
   }
   if (fallback == 0 && direct) return 4;
+  // both operands n- or k-contiguous along their rows (A row-major, B
+  // row-major): the 16x16x32 kernel with transposing reads of B
+  if (fallback == 0 && tile_supports(8, p)) return 8;
   // 64 x 64 tiles, or a problem no two-stage tile fits (M or N below 64,
   // K <= 64): a ring whose slot count divides the chunk count -- four slots
   // first (1024^3 fp16 ReLU: 5.0 us warm, 7.3 us on rotated operands,
@@ -94,6 +102,11 @@ int tile_choose(const Problem& p) {
 }
 
 LaunchFn tile_launcher(int cfg, const Problem& p) {
+  if (kTile[cfg].brow) {
+    if (p.in_dt == GEMM_EPI_F16) return tile16_rowb_launcher_f16(p.out_dt, p.la, p.lb, p.epi);
+    if (p.in_dt == GEMM_EPI_BF16) return tile16_rowb_launcher_bf16(p.out_dt, p.la, p.lb, p.epi);
+    return nullptr;
+  }
   const bool f32 = p.out_dt == GEMM_EPI_F32, fp8 = p.out_dt == GEMM_EPI_FP8_E4M3;
   if (p.in_dt == GEMM_EPI_F16)
     return (fp8 ? tile_launcher_f16_fp8 : f32 ? tile_launcher_f16_f32 : tile_launcher_f16_f16)(cfg, p.la, p.lb, p.epi);

@@ -1,6 +1,6 @@
 // gemm_tile16.hpp -- the 256x256 tile kernel of gemm_tile.hpp built on
-// v_mfma_f32_16x16x32_{f16,bf16} with four waves, for k-contiguous operands
-// (A row-major, B column-major).
+// v_mfma_f32_16x16x32_{f16,bf16} with four waves, for A row-major and B
+// either column-major (k contiguous) or row-major (n contiguous, BROW).
 //
 // Why 16x16x32.  A 32x32x16 MFMA reads and rewrites 16 fp32 accumulators per
 // lane for 32 768 FLOP; a 16x16x32 one reads and rewrites 4 for 16 384 FLOP,
@@ -26,7 +26,22 @@
 // (row & 7) (swz16 in gemm_tile.hpp: measured free of bank conflicts).  With B's fragment as the first
 // operand the 16x16 result arrives transposed: lane l holds
 // C[m = l % 16][n = 4 (l / 16) + e], e = 0..3 -- four consecutive columns of
-// one row.  (Tile-level fusion of load -> GEMM -> epilogue -> store:
+// one row.
+//
+// Row-major B (BROW).  A stage holds 64 k-rows of 256 n (512 bytes each);
+// 16-byte chunk c of k-row r sits at position c ^ 2 tau(r), tau(r) = (r & 3)
+// + 4 ((r >> 3) & 1), filled by direct copies of two k-rows per wave
+// instruction (RowB256 below).  B's fragment -- eight consecutive k of one
+// column per lane -- comes from two transposing reads ds_read_b64_tr_b16 of
+// four k-rows each: in each 16-lane group, lane 4 i + a gives the address
+// of columns nb + 4 a .. + 3 of k-row kb + i, and lane j receives column
+// nb + j at k-rows kb .. kb + 3.  With group g reading k-rows 8 g .. 8 g + 7
+// of the substep, the 32 lanes of a read's half see tau = i + 4 (g & 1),
+// eight distinct values, and fetch 32 distinct 8-byte words modulo 256
+// bytes: one pass, no bank conflict.  The position of fragment f is
+// 2 (f ^ tau) + (a >> 1): a per-lane base XOR 32 f bytes, eight offsets
+// kept in registers; the substep and the second read are immediates.
+// (Tile-level fusion of load -> GEMM -> epilogue -> store:
 // TileFusion "基础GEMM示例"; epilogue on the accumulator fragment: csdn
 // "从零开始学习 TileLang" ch.10 sec. 10.8; pipelining and rasterisation:
 // atlascloud.ai "Writing high-performance kernels in TileLang", section
@@ -41,6 +56,46 @@ namespace tile16 {
 using tile::DirectLoader;
 using tile::kBK;
 using tile::kRowBytes;
+using tile::lds_ptr;
+
+// Direct copies of a row-major B tile, 64 k-rows of 256 columns, into the
+// layout above: wave instruction i (0..7) of a k-step moves k-rows 2 t and
+// 2 t + 1, t = wave + 4 i, to bytes 1024 t .. + 1023 of the stage; lane l
+// takes k-row 2 t + l / 32, position l % 32, so it loads chunk
+// (l % 32) ^ 2 tau, and tau = 2 (wave & 1) + l / 32 + 4 (i & 1).  The
+// buffer starts at k = -kpad (the K-tail shift of DirectLoader) and ends
+// with the last k-row; its range must fit 32-bit offsets (host check).
+struct RowB256 {
+  __amdgpu_buffer_rsrc_t rsrc;
+  uint32_t voff[2];  // instructions with i even, odd
+  uint32_t row_bytes;
+  int wave;
+
+  __device__ __forceinline__ RowB256(const void* B, int n0, int K, int ldb, int kpad, int lane, int wave_) {
+    const char* base = (const char*)B + (int64_t)n0 * 2 - (int64_t)kpad * ldb * 2;
+    rsrc = tile::make_rsrc(base, (uint32_t)((int64_t)(K + kpad) * ldb * 2 - (int64_t)n0 * 2));
+    row_bytes = (uint32_t)ldb * 2u;
+    wave = wave_;
+    const int h = lane >> 5, pos = lane & 31;
+#pragma unroll
+    for (int v = 0; v < 2; ++v) {
+      const int tau = 2 * (wave & 1) + h + 4 * v;
+      voff[v] = (uint32_t)h * row_bytes + (uint32_t)((pos ^ (2 * tau)) << 4);
+    }
+  }
+  __device__ __forceinline__ void issue(char* dst, int kt, int i) const {
+    const int t = wave + 4 * i;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr)(dst + t * 1024), 16, voff[i & 1],
+                                             (uint32_t)(kt * kBK + 2 * t) * row_bytes, 0, 0);
+  }
+  // k-step 0 of a shifted k axis: k-rows below kpad load as zeros
+  __device__ __forceinline__ void issue_first(char* dst, int i, int lane, int kpad) const {
+    const int t = wave + 4 * i;
+    const uint32_t v = 2 * t + (lane >> 5) < kpad ? 0xFFFFFFF0u : voff[i & 1];
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr)(dst + t * 1024), 16, v, (uint32_t)(2 * t) * row_bytes,
+                                             0, 0);
+  }
+};
 
 template <typename TIn>
 __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
@@ -125,7 +180,7 @@ __device__ __forceinline__ void write_tile16(const f32x4 (&acc)[WM / 16][WN / 16
   });
 }
 
-template <typename TIn, typename TOut, int EPI>
+template <typename TIn, typename TOut, int EPI, bool BROW>
 __global__ __launch_bounds__(256) void gemm_tile16_kernel(const TIn* __restrict__ A, const TIn* __restrict__ B,
                                                           const TIn* __restrict__ bias, TOut* __restrict__ C, int M,
                                                           int N, int K, int tiles_m, int tiles_n, int panel, int lda,
@@ -159,7 +214,9 @@ __global__ __launch_bounds__(256) void gemm_tile16_kernel(const TIn* __restrict_
   const int kpad = (-K) & (kBK - 1);
 
   const DirectLoader<BM, NW, true> da(A, m0, M, lda, kpad, tid, wave);
+  // (only one of the two B movers is used)
   const DirectLoader<BN, NW, true> db(B, n0, N, ldb, kpad, tid, wave);
+  const RowB256 rb(B, n0, K, ldb, kpad, lane, wave);
 
   // Fragment rows w0 + 16 f + lane % 16 (w0 a multiple of 64) have the
   // swizzle swz16(lane % 16), so one per-lane offset per operand and substep
@@ -173,6 +230,15 @@ __global__ __launch_bounds__(256) void gemm_tile16_kernel(const TIn* __restrict_
     aoff[kk] = a_row + (((4 * kk + (lane >> 4)) ^ sl) << 4);
     boff[kk] = b_row + (((4 * kk + (lane >> 4)) ^ sl) << 4);
   }
+  // row-major B: fragment f at k-row 8 g + i (+ 32 kk, + 4 for the second
+  // read), bytes 256 wn + 32 (f ^ tau) + 8 a
+  int btr[TN];
+  if constexpr (BROW) {
+    const int g = lane >> 4, ti = (lane >> 2) & 3, ta = lane & 3;
+    const int tau = ti + 4 * (g & 1);
+#pragma unroll
+    for (int f = 0; f < TN; ++f) btr[f] = (8 * g + ti) * 512 + 256 * wn + 32 * (f ^ tau) + 8 * ta;
+  }
 
   f32x4 acc[TM][TN];
 #pragma unroll
@@ -185,8 +251,21 @@ __global__ __launch_bounds__(256) void gemm_tile16_kernel(const TIn* __restrict_
   // read f of a substep: B's fragments first (the first row of MFMAs needs
   // all of them), then A's in the order the rows use them
   auto read_frag = [&](const Stage& st, int kk, int f, u32x4 (&xa)[TM], u32x4 (&xb)[TN]) __attribute__((always_inline)) {
-    if (f < TN) xb[f] = *(const u32x4*)(st.b + boff[kk] + f * 16 * kRowBytes);
-    else xa[f - TN] = *(const u32x4*)(st.a + aoff[kk] + (f - TN) * 16 * kRowBytes);
+    if (f < TN) {
+      if constexpr (BROW) {
+        typedef short s4v __attribute__((vector_size(8)));
+        typedef __attribute__((address_space(3))) s4v lds_s4v;
+        char* p0 = st.b + btr[f] + kk * 32 * 512;
+        const s4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4v*)(lds_ptr)p0);
+        const s4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4v*)(lds_ptr)(p0 + 4 * 512));
+        const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+        xb[f] = u32x4{l2.x, l2.y, h2.x, h2.y};
+      } else {
+        xb[f] = *(const u32x4*)(st.b + boff[kk] + f * 16 * kRowBytes);
+      }
+    } else {
+      xa[f - TN] = *(const u32x4*)(st.a + aoff[kk] + (f - TN) * 16 * kRowBytes);
+    }
   };
 
   constexpr int NMF = TM * TN;  // 64 MFMAs per substep
@@ -215,6 +294,7 @@ __global__ __launch_bounds__(256) void gemm_tile16_kernel(const TIn* __restrict_
             constexpr int d = decltype(d_c)::value;
             if constexpr (d * NMF / NDL == slot) {
               if constexpr (d < NDA) da.issue(dl_dst.a, kt + 2, d);
+              else if constexpr (BROW) rb.issue(dl_dst.b, kt + 2, d - NDA);
               else db.issue(dl_dst.b, kt + 2, d - NDA);
             }
           });
@@ -242,18 +322,21 @@ __global__ __launch_bounds__(256) void gemm_tile16_kernel(const TIn* __restrict_
 #pragma unroll
       for (int d = 0; d < NDL; ++d) {
         if (d < NDA) da.issue(s_first.a, 0, d);
+        else if constexpr (BROW) rb.issue(s_first.b, 0, d - NDA);
         else db.issue(s_first.b, 0, d - NDA);
       }
     } else {
 #pragma unroll
       for (int d = 0; d < NDL; ++d) {
         if (d < NDA) da.issue_first(s_first.a, d, lane, kpad);
+        else if constexpr (BROW) rb.issue_first(s_first.b, d - NDA, lane, kpad);
         else db.issue_first(s_first.b, d - NDA, lane, kpad);
       }
     }
 #pragma unroll
     for (int d = 0; d < NDL; ++d) {
       if (d < NDA) da.issue(s_second.a, 1, d);
+      else if constexpr (BROW) rb.issue(s_second.b, 1, d - NDA);
       else db.issue(s_second.b, 1, d - NDA);
     }
     // tile 0 complete; tile 1's copies may stay in flight
@@ -290,30 +373,36 @@ __global__ __launch_bounds__(256) void gemm_tile16_kernel(const TIn* __restrict_
                                                 nullptr, nullptr, nullptr);
 }
 
-template <typename TIn, typename TOut, int EPI>
+template <typename TIn, typename TOut, int EPI, bool BROW>
 hipError_t launch(const LaunchArgs& a) {
   const int tiles_m = (a.M + 255) / 256, tiles_n = (a.N + 255) / 256;
   const int panel = tiles_m < 4 ? tiles_m : 4;
-  hipLaunchKernelGGL((gemm_tile16_kernel<TIn, TOut, EPI>), dim3(tiles_m * tiles_n), dim3(256), 0, a.stream,
+  hipLaunchKernelGGL((gemm_tile16_kernel<TIn, TOut, EPI, BROW>), dim3(tiles_m * tiles_n), dim3(256), 0, a.stream,
                      (const TIn*)a.A, (const TIn*)a.B, (const TIn*)a.bias, (TOut*)a.C, a.M, a.N, a.K, tiles_m,
                      tiles_n, panel, a.lda, a.ldb, a.ldc, a.scale, (const TOut*)a.residual, a.out_scale);
   return hipGetLastError();
 }
 
-// Only A row-major with B column-major (both k-contiguous) is served.
-template <typename TIn, typename TOut>
-LaunchFn pick(int la, int lb, int epi) {
-  if (la != GEMM_EPI_ROW_MAJOR || lb != GEMM_EPI_COL_MAJOR) return nullptr;
+template <typename TIn, typename TOut, bool BROW>
+LaunchFn pick_epi(int epi) {
   switch (epi) {
-    case GEMM_EPI_NONE: return &launch<TIn, TOut, GEMM_EPI_NONE>;
-    case GEMM_EPI_RELU: return &launch<TIn, TOut, GEMM_EPI_RELU>;
-    case GEMM_EPI_BIAS_RELU: return &launch<TIn, TOut, GEMM_EPI_BIAS_RELU>;
-    case GEMM_EPI_BIAS_GELU: return &launch<TIn, TOut, GEMM_EPI_BIAS_GELU>;
-    case GEMM_EPI_BIAS: return &launch<TIn, TOut, GEMM_EPI_BIAS>;
-    case GEMM_EPI_SILU: return &launch<TIn, TOut, GEMM_EPI_SILU>;
-    case GEMM_EPI_BIAS_SILU: return &launch<TIn, TOut, GEMM_EPI_BIAS_SILU>;
+    case GEMM_EPI_NONE: return &launch<TIn, TOut, GEMM_EPI_NONE, BROW>;
+    case GEMM_EPI_RELU: return &launch<TIn, TOut, GEMM_EPI_RELU, BROW>;
+    case GEMM_EPI_BIAS_RELU: return &launch<TIn, TOut, GEMM_EPI_BIAS_RELU, BROW>;
+    case GEMM_EPI_BIAS_GELU: return &launch<TIn, TOut, GEMM_EPI_BIAS_GELU, BROW>;
+    case GEMM_EPI_BIAS: return &launch<TIn, TOut, GEMM_EPI_BIAS, BROW>;
+    case GEMM_EPI_SILU: return &launch<TIn, TOut, GEMM_EPI_SILU, BROW>;
+    case GEMM_EPI_BIAS_SILU: return &launch<TIn, TOut, GEMM_EPI_BIAS_SILU, BROW>;
     default: return nullptr;
   }
+}
+
+// A row-major with B column-major (both k-contiguous), or with B
+// row-major when BROW.
+template <typename TIn, typename TOut, bool BROW>
+LaunchFn pick(int la, int lb, int epi) {
+  if (la != GEMM_EPI_ROW_MAJOR || lb != (BROW ? GEMM_EPI_ROW_MAJOR : GEMM_EPI_COL_MAJOR)) return nullptr;
+  return pick_epi<TIn, TOut, BROW>(epi);
 }
 
 }  // namespace tile16

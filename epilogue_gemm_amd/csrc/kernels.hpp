@@ -24,8 +24,9 @@ struct TileConfig {
   int bm, bn;  // workgroup tile
   int waves;   // waves per workgroup
   const char* name;
-  int mfma;    // MFMA block: 32 (32x32x16, any layout) or 16 (16x16x32, k-contiguous operands only)
+  int mfma;    // MFMA block: 32 (32x32x16, any layout) or 16 (16x16x32, A row-major)
   int ring;    // 0: two LDS stages; P > 0: the deep ring of P slots (gemm_ring.hpp, A row-major only)
+  bool brow;   // 16x16x32 only: B row-major (transposing LDS reads) instead of column-major
 };
 int tile_num_configs();
 const TileConfig& tile_config(int cfg);
@@ -39,6 +40,9 @@ LaunchFn tile_launcher_bf16_bf16(int cfg, int la, int lb, int epi);
 LaunchFn tile_launcher_bf16_f32(int cfg, int la, int lb, int epi);
 LaunchFn tile_launcher_f16_fp8(int cfg, int la, int lb, int epi);
 LaunchFn tile_launcher_bf16_fp8(int cfg, int la, int lb, int epi);
+// the row-major-B 16x16x32 configuration, one unit per input format
+LaunchFn tile16_rowb_launcher_f16(int out_dt, int la, int lb, int epi);
+LaunchFn tile16_rowb_launcher_bf16(int out_dt, int la, int lb, int epi);
 
 // ---- skinny: weight-streaming kernel for M <= 32 --------------------------
 struct SkinnyConfig {

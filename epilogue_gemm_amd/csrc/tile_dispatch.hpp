@@ -16,10 +16,11 @@ LaunchFn pick_config(int cfg, int la, int lb, int epi) {
     case 1: return pick_layout<128, 128, 4, TIn, TOut>(la, lb, epi);
     case 2: return pick_layout<64, 64, 4, TIn, TOut>(la, lb, epi);
     case 3: return pick_layout<256, 256, 8, TIn, TOut>(la, lb, epi);
-    case 4: return tile16::pick<TIn, TOut>(la, lb, epi);
+    case 4: return tile16::pick<TIn, TOut, false>(la, lb, epi);
     case 5: return ring::pick<TIn, TOut, 8>(la, lb, epi);
     case 6: return ring::pick<TIn, TOut, 4>(la, lb, epi);
     case 7: return ring::pick<TIn, TOut, 2>(la, lb, epi);
+    // 8, the row-major-B 16x16x32 kernel: gemm_tile16_rowb_*.hip
     default: return nullptr;
   }
 }

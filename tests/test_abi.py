@@ -139,7 +139,9 @@ def test_fp8_output_needs_16_columns_in_tile_kernels(lib):
 
 @pytest.mark.parametrize("M,N,K,la,lb,want_kernel,want_name", [
     (8192, 8192, 8192, "row", "col", "tile", "tile_256x256x64_m16"),
-    (4096, 4096, 4096, "row", "row", "tile", "tile_256x256x64"),
+    (4096, 4096, 4096, "row", "row", "tile", "tile_256x256x64_m16_rowb"),  # B through transposing LDS reads
+    (8192, 8192, 8192, "row", "row", "tile", "tile_256x256x64_m16_rowb"),
+    (4096, 4096, 4096, "col", "row", "tile", "tile_256x256x64"),  # column-major A: register-staged
     (4096, 4096, 4096, "row", "col", "tile", "tile_256x256x64_m16"),
     (1024, 1024, 1024, "row", "row", "tile", "tile_64x64_ring4"),  # 16 chunks of 64 through 4 slots
     (128, 64, 256, "row", "col", "tile", "tile_64x64_ring4"),  # 4 chunks of 64
@@ -190,7 +192,7 @@ def test_auto_selection(lib, M, N, K, la, lb, want_kernel, want_name):
 def test_select_forces_and_validates(lib):
     h = gb.gemm_epi_plan(512, 512, 256, "f16", "f32", "row", "col", "none")
     try:
-        assert gb.gemm_epi_num_configs("tile") == 8
+        assert gb.gemm_epi_num_configs("tile") == 9
         assert gb.gemm_epi_num_configs("skinny") == 10
         assert gb.gemm_epi_num_configs("generic") == 1
         assert gb.gemm_epi_num_configs("auto") == 0
@@ -202,7 +204,8 @@ def test_select_forces_and_validates(lib):
         assert gb.gemm_epi_plan_describe(h)[0] == "generic"
         assert gb.gemm_epi_plan_select(h, "skinny", -1) == 2  # M = 512 > 32: unsupported, plan unchanged
         assert gb.gemm_epi_plan_describe(h)[0] == "generic"
-        assert gb.gemm_epi_plan_select(h, "tile", 8) == 1  # no such config
+        assert gb.gemm_epi_plan_select(h, "tile", 9) == 1  # no such config
+        assert gb.gemm_epi_plan_select(h, "tile", 8) == 2  # 16x16x32 with row-major B only
         assert gb.gemm_epi_plan_select(h, "tile", 5) == 2  # ring of 8: 4 chunks are too few
         assert gb.gemm_epi_plan_select(h, "tile", 6) == 0  # ring of 4
         assert lib.gemm_epi_plan_select(ctypes.c_void_p(h), 9, 0) == 1  # bad enum

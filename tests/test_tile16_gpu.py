@@ -1,8 +1,9 @@
-"""Parity of the 16x16x32-MFMA tile configuration (four waves, 256 x 256
-tiles; A row-major and B column-major only) with the oracle: bit-exact on
-integer operands for every epilogue that is exact, K tails of every
-padding, shifted edge tiles, leading dimensions, the optional scale,
-residual and FP8 output; within the tolerance on random operands."""
+"""Parity of the 16x16x32-MFMA tile configurations (four waves, 256 x 256
+tiles; A row-major, B column-major or -- through transposing LDS reads --
+row-major) with the oracle: bit-exact on integer operands for every
+epilogue that is exact, K tails of every padding, shifted edge tiles,
+leading dimensions, the optional scale, residual and FP8 output; within the
+tolerance on random operands."""
 import numpy as np
 import pytest
 import torch
@@ -15,7 +16,8 @@ from tests.test_strides_gpu import run_strided
 
 pytestmark = pytest.mark.gpu
 
-NAMES = {4: "tile_256x256x64_m16"}
+NAMES = {4: "tile_256x256x64_m16", 8: "tile_256x256x64_m16_rowb"}
+LB = {4: "col", 8: "row"}
 CFGS = list(NAMES)
 
 
@@ -32,8 +34,8 @@ def _gpu():
 def test_tile16_integer_bitexact(config, in_dt, out_dt):
     M, N, K = 512, 768, 640
     for epi in EPIS:
-        bits = inputs.integer_inputs(M, N, K, in_dt, "row", "col", epi.startswith("bias"), seed=len(epi))
-        name = check_case(bits, M, N, K, in_dt, out_dt, "row", "col", epi, "tile", config, epi in BITWISE_EPIS)
+        bits = inputs.integer_inputs(M, N, K, in_dt, "row", LB[config], epi.startswith("bias"), seed=len(epi))
+        name = check_case(bits, M, N, K, in_dt, out_dt, "row", LB[config], epi, "tile", config, epi in BITWISE_EPIS)
         assert name == NAMES[config]
 
 
@@ -46,8 +48,8 @@ def test_tile16_integer_bitexact(config, in_dt, out_dt):
 def test_tile16_ktails_and_edges_bitexact(config, K):
     M, N = 264, 520
     for in_dt, out_dt, epi in (("bf16", "bf16", "bias_relu"), ("f16", "f32", "none")):
-        bits = inputs.integer_inputs(M, N, K, in_dt, "row", "col", epi.startswith("bias"), seed=K)
-        name = check_case(bits, M, N, K, in_dt, out_dt, "row", "col", epi, "tile", config, True)
+        bits = inputs.integer_inputs(M, N, K, in_dt, "row", LB[config], epi.startswith("bias"), seed=K)
+        name = check_case(bits, M, N, K, in_dt, out_dt, "row", LB[config], epi, "tile", config, True)
         assert name == NAMES[config]
 
 
@@ -55,8 +57,8 @@ def test_tile16_ktails_and_edges_bitexact(config, K):
 @pytest.mark.parametrize("M,N,K", [(1024, 1024, 1024), (768, 512, 2056)])
 def test_tile16_random_bias_gelu(config, M, N, K):
     for in_dt in ("bf16", "f16"):
-        bits = inputs.make_inputs(M, N, K, in_dt, "row", "col", True, float(np.sqrt(K)), 0.1, seed=M + K)
-        check_case(bits, M, N, K, in_dt, in_dt, "row", "col", "bias_gelu", "tile", config, False)
+        bits = inputs.make_inputs(M, N, K, in_dt, "row", LB[config], True, float(np.sqrt(K)), 0.1, seed=M + K)
+        check_case(bits, M, N, K, in_dt, in_dt, "row", LB[config], "bias_gelu", "tile", config, False)
 
 
 @pytest.mark.parametrize("config", CFGS)
@@ -65,7 +67,7 @@ def test_tile16_extras_integer_bitexact(config, edge):
     M, N, K = (264, 520, 328) if edge else (512, 512, 320)
     for in_dt, out_dt in (("bf16", "bf16"), ("f16", "f32")):
         for epi, use_s, use_r in EXTRA_CASES:
-            name = check_ex(M, N, K, in_dt, out_dt, "row", "col", epi, "tile", config, use_s, use_r, True,
+            name = check_ex(M, N, K, in_dt, out_dt, "row", LB[config], epi, "tile", config, use_s, use_r, True,
                             seed=13 + len(epi))
             assert name == NAMES[config]
 
@@ -74,11 +76,11 @@ def test_tile16_extras_integer_bitexact(config, edge):
 def test_tile16_silu_and_fp8_output(config):
     M, N, K = 512, 528, 352
     for integer in (True, False):
-        name = check_ex(M, N, K, "bf16", "fp8", "row", "col", "bias_gelu" if not integer else "bias", "tile",
+        name = check_ex(M, N, K, "bf16", "fp8", "row", LB[config], "bias_gelu" if not integer else "bias", "tile",
                         config, False, False, integer, seed=40 + integer, use_oscale=True)
         assert name == NAMES[config]
     for epi in ("silu", "bias_silu"):
-        check_ex(M, N, K, "bf16", "bf16", "row", "col", epi, "tile", config, True, True, False, seed=len(epi))
+        check_ex(M, N, K, "bf16", "bf16", "row", LB[config], epi, "tile", config, True, True, False, seed=len(epi))
 
 
 @pytest.mark.parametrize("config", CFGS)
@@ -87,5 +89,5 @@ def test_tile16_strided_integer_bitexact(config):
     for in_dt, out_dt, epi, pads, extras in (("bf16", "bf16", "bias_relu", (8, 16, 24), False),
                                              ("f16", "f32", "relu", (64, 8, 8), True),
                                              ("bf16", "fp8", "bias", (16, 8, 16), False)):
-        name = run_strided(M, N, K, in_dt, out_dt, "row", "col", epi, pads, "tile", config, extras)
+        name = run_strided(M, N, K, in_dt, out_dt, "row", LB[config], epi, pads, "tile", config, extras)
         assert name == NAMES[config]
