@@ -56,9 +56,10 @@ PEAK_HBM_GBS = 8000.0
 CSRC = os.path.join(ROOT, "epilogue_gemm_amd", "csrc")
 # sources that define each kernel family's device code and launch shape
 _FAMILY_SOURCES = {
-    "tile": ["common.hpp", "kernels.hpp", "gemm_tile.hpp", "gemm_tile16.hpp", "tile_dispatch.hpp",
+    "tile": ["common.hpp", "kernels.hpp", "gemm_tile.hpp", "gemm_tile16.hpp", "gemm_ring.hpp", "tile_dispatch.hpp",
              "gemm_tile_bf16_bf16.hip", "gemm_tile_bf16_f32.hip", "gemm_tile_bf16_fp8.hip", "gemm_tile_f16_f16.hip",
-             "gemm_tile_f16_f32.hip", "gemm_tile_f16_fp8.hip", "gemm_epi.cpp"],
+             "gemm_tile_f16_f32.hip", "gemm_tile_f16_fp8.hip", "gemm_tile16_rowb_f16.hip",
+             "gemm_tile16_rowb_bf16.hip", "gemm_epi.cpp"],
     "skinny": ["common.hpp", "kernels.hpp", "gemm_skinny.hip", "gemm_epi.cpp"],
 }
 
