@@ -24,22 +24,22 @@
 //     the lane's second operand of O^T = V^T P^T for 16 keys: P never leaves
 //     the registers (bf16 adds a second operand, the rounded remainder, so
 //     that the weights keep about 16 bits);
-//   * O^T accumulates with V^T (from LDS) as first operand, so lane (i, h)
-//     holds 32 of query i's 64 outputs: the rescale by exp(m_old - m_new) is
-//     per lane, and the two halves of a query exchange their partial sums l
-//     once at the end.
-// K goes to LDS by direct buffer loads (rows of 128 bytes, 16-byte chunks
-// XOR-swizzled by row); V is transposed on the way (each thread loads two
-// key rows of 8 values and writes 8 d-rows of two keys), so that both MFMA
-// operand reads are 16-byte LDS reads free of bank conflicts.  Two LDS
-// stages: block kb + 1 is loaded while block kb is multiplied.
+//   * O^T accumulates with V^T as first operand, so lane (i, h) holds 32 of
+//     query i's 64 outputs: the rescale by exp(m_old - m_new) is per lane,
+//     and the two halves of a query exchange their partial sums l once at
+//     the end.
+// K and V go to LDS as they are stored, by direct buffer loads (key rows of
+// 128 bytes, 16-byte chunks XOR-swizzled by row); V^T's fragments -- eight
+// consecutive keys of one d per lane -- come from gfx950's transposing LDS
+// read ds_read_b64_tr_b16, two per fragment.  A ring of three LDS slots:
+// the blocks of the next two iterations are in flight while one is
+// multiplied.
 #include "gemm_tile.hpp"
 
 namespace ge {
 namespace attn {
 
 using tile::lds_ptr;
-using tile::load16;
 using tile::make_rsrc;
 using tile::swz;
 
@@ -48,12 +48,6 @@ constexpr int kBM = 128;      // queries per workgroup (4 waves x 32)
 constexpr int kBN = 64;       // keys per block
 constexpr int kRow = kD * 2;  // bytes of one LDS row (64 16-bit values)
 constexpr int kStage = kBN * kRow;
-
-// 16-bit element j (0..7) of a 128-bit register
-__device__ __forceinline__ uint32_t half_of(const u32x4& v, int j) {
-  const uint32_t w = v[j >> 1];
-  return (j & 1) ? (w >> 16) : (w & 0xffffu);
-}
 
 // a, b rounded to nearest even in T and packed (one v_cvt_pk_{f16,bf16}_f32)
 // a.x + a.y + acc for two packed 16-bit values (v_dot2c_f32_{f16,bf16} with
@@ -91,15 +85,32 @@ __device__ __forceinline__ float partner32(float x, int upper) {
   return __builtin_bit_cast(float, upper ? r[0] : r[1]);
 }
 
+// V's LDS rows (one key, 64 d-values) keep 16-byte chunk c at position
+// c ^ 4 ((key >> 1) & 1): a transposing read's half-wave takes four
+// consecutive key rows at the same four chunks, which then fall on 16
+// distinct 16-byte bank groups.
+__device__ __forceinline__ int vswz(int key) { return 4 * ((key >> 1) & 1); }
+
+template <int J>
+__device__ __forceinline__ char* kslot() {
+  __shared__ __attribute__((aligned(1024))) char s[2 * kStage];
+  return s;
+}
+template <int J>
+__device__ __forceinline__ char* vslot() {
+  __shared__ __attribute__((aligned(1024))) char s[2 * kStage];
+  return s;
+}
+
 template <typename T, bool CAUSAL>
 __global__ __launch_bounds__(512) void attn_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                                                        const T* __restrict__ V, T* __restrict__ O, int S, int H,
                                                        float scale_log2) {
-  // Two buffers of K and of V^T, each holding one block per key parity.
-  __shared__ __attribute__((aligned(1024))) char sK0[2 * kStage];
-  __shared__ __attribute__((aligned(1024))) char sK1[2 * kStage];
-  __shared__ __attribute__((aligned(1024))) char sV0[2 * kStage];
-  __shared__ __attribute__((aligned(1024))) char sV1[2 * kStage];
+  // Three ring slots of K and of V, each holding one block per key parity
+  // (one __shared__ object per slot, so that the compiler can tell a read
+  // of one slot from a direct load in flight into another).
+  char* const sk[3] = {kslot<0>(), kslot<1>(), kslot<2>()};
+  char* const sv[3] = {vslot<0>(), vslot<1>(), vslot<2>()};
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -108,7 +119,6 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(const T* __restrict__ Q, 
   // can multiply while the other computes its softmax -- and merge their
   // partial results at the end.
   const int qg = wave & 3, kp = wave >> 2;
-  const int pt = tid & 255;  // thread index within the parity's four waves
   const int il = lane & 31, h = lane >> 5;
   const int q0 = blockIdx.x * kBM, hd = blockIdx.y, b = blockIdx.z;
   const int64_t rs = (int64_t)H * kD;  // elements between consecutive sequence positions
@@ -125,55 +135,53 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(const T* __restrict__ Q, 
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) asm volatile("" : "+v"(qf[kk]));
 
-  // K: direct loads, 8 wave instructions of 1 KiB per block, 2 per wave of
-  // the parity; instruction t fills rows 8 t .. 8 t + 7, lane L row
-  // 8 t + L / 8 at chunk position L % 8, which holds logical chunk
-  // (L % 8) ^ swz(row)
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + base, (uint32_t)(((int64_t)(S - 1) * rs + kD) * 2));
-  uint32_t kvoff[2];
+  // K and V: direct loads, 8 wave instructions of 1 KiB per block and
+  // operand, 2 per wave of the parity; instruction t fills rows 8 t ..
+  // 8 t + 7, lane L row 8 t + L / 8 at chunk position L % 8, which holds
+  // logical chunk (L % 8) ^ swz(row) for K and (L % 8) ^ vswz(row) for V.
+  const uint32_t range = (uint32_t)(((int64_t)(S - 1) * rs + kD) * 2);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + base, range);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + base, range);
+  uint32_t kvoff[2], vvoff[2];
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int row = 8 * (2 * qg + u) + (lane >> 3);
     kvoff[u] = (uint32_t)(row * rs * 2 + (((lane & 7) ^ swz(row)) << 4));
+    vvoff[u] = (uint32_t)(row * rs * 2 + (((lane & 7) ^ vswz(row)) << 4));
   }
-  auto load_k = [&](char* st, int kb) __attribute__((always_inline)) {
+  const int poff = kp * kStage;
+  auto load_kv = [&](auto jc, int kb) __attribute__((always_inline)) {
+    constexpr int j = decltype(jc)::value;
+    const uint32_t so = (uint32_t)((int64_t)kb * kBN * rs * 2);
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr)(st + (2 * qg + u) * 1024), 16, kvoff[u],
-                                               (uint32_t)((int64_t)kb * kBN * rs * 2), 0, 0);
-  };
-
-  // V: thread (ng, kg) of the parity loads keys 2 kg, 2 kg + 1, d = 8 ng .. + 7
-  // and writes V^T rows d at keys 2 kg, 2 kg + 1
-  const int ng = pt & 7, kg = pt >> 3;
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + base, (uint32_t)(((int64_t)(S - 1) * rs + kD) * 2));
-  const uint32_t vvoff = (uint32_t)((2 * kg) * rs * 2 + ng * 16);
-  u32x4 vr[2];
-  auto load_v = [&](int kb) __attribute__((always_inline)) {
-#pragma unroll
-    for (int u = 0; u < 2; ++u) vr[u] = load16(rv, vvoff, (uint32_t)(((int64_t)kb * kBN + u) * rs * 2));
-  };
-  auto store_v = [&](char* st) __attribute__((always_inline)) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int d = 8 * ng + j;
-      *(uint32_t*)(st + d * kRow + (((kg >> 2) ^ swz(d)) << 4) + 4 * (kg & 3)) =
-          half_of(vr[0], j) | (half_of(vr[1], j) << 16);
+    for (int u = 0; u < 2; ++u) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr)(kslot<j>() + poff + (2 * qg + u) * 1024), 16, kvoff[u],
+                                               so, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr)(vslot<j>() + poff + (2 * qg + u) * 1024), 16, vvoff[u],
+                                               so, 0, 0);
     }
   };
 
-  // MFMA operand read offsets.  S^T: lane (r, h) reads key row kappa(r) of
-  // group g, chunk 2 kk + h.  O^T: lane (r, h) reads V^T row 32 dt + r,
-  // chunk 4 g + 2 t + h.
+  // MFMA operand reads.  S^T: lane (r, h) reads key row kappa(r) of group
+  // g, chunk 2 kk + h.  O^T: V^T's fragment -- d-row 32 dt + r, keys
+  // 32 g + 16 t + 8 h .. + 7 -- from two transposing reads of V's key rows:
+  // in 16-lane group G = l / 16, lane 4 i + a addresses key row
+  // 32 g + 16 t + 8 (G >> 1) + i (+ 4), d-values 32 dt + 16 (G & 1) + 4 a .. + 3.
   const int kr = (il & 0x13) | ((il & 4) << 1) | ((il & 8) >> 1);  // kappa: swap bits 2 and 3
   auto k_off = [&](int g, int kk) __attribute__((always_inline)) {
     const int row = 32 * g + kr;
     return row * kRow + (((2 * kk + h) ^ swz(row)) << 4);
   };
-  auto v_off = [&](int dt, int g, int t) __attribute__((always_inline)) {
-    const int row = 32 * dt + il;
-    return row * kRow + (((4 * g + 2 * t + h) ^ swz(row)) << 4);
-  };
+  // Key rows 8 (G >> 1) + i and + 4 have the same vswz (bit 1 of i), so
+  // one byte offset per d-tile dt serves every (g, t) and both reads:
+  // + (32 g + 16 t) rows, + 4 rows for the second read.
+  const int tg = lane >> 4, ti = (lane >> 2) & 3, ta = lane & 3;
+  int vt_base[2];
+#pragma unroll
+  for (int dt = 0; dt < 2; ++dt) {
+    const int chunk = 4 * dt + 2 * (tg & 1) + (ta >> 1);
+    vt_base[dt] = (8 * (tg >> 1) + ti) * kRow + ((chunk ^ vswz(ti)) << 4) + 8 * (ta & 1);
+  }
 
   f32x16 acc_o[2] = {f32x16{}, f32x16{}};
   float m_run = -__builtin_inff();  // running maximum of the raw scores
@@ -181,14 +189,49 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(const T* __restrict__ Q, 
 
   const int nblk = CAUSAL ? (q0 + kBM) / kBN : S / kBN;  // >= 2: each parity has a block
 
-  auto block = [&](int kb, const char* sk, const char* sv) __attribute__((always_inline)) {
+  auto block = [&](int kb, const char* skp, const char* svp) __attribute__((always_inline)) {
     // S^T for the two 32-key groups
     f32x16 s[2];
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
       s[g] = f32x16{};
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) s[g] = mfma32<T>(*(const u32x4*)(sk + k_off(g, kk)), qf[kk], s[g]);
+      for (int kk = 0; kk < 4; ++kk) s[g] = mfma32<T>(*(const u32x4*)(skp + k_off(g, kk)), qf[kk], s[g]);
+    }
+    // V^T's eight fragments of the block, [dt][g][t], while the MFMAs run.
+    // The sixteen transposing reads are one asm statement that also waits
+    // for them: the compiler has no alias information for the builtin form
+    // of this read and would make it wait for every direct load in flight,
+    // the next blocks' included.  (The block's V is in LDS: the barrier
+    // before this iteration waited for it.)
+    u32x2 vh[2][2][2][2];  // [dt][g][t][read]
+    {
+      const uint32_t b0 = (uint32_t)(uintptr_t)(lds_ptr)(svp + vt_base[0]);
+      const uint32_t b1 = (uint32_t)(uintptr_t)(lds_ptr)(svp + vt_base[1]);
+      asm volatile(
+          "ds_read_b64_tr_b16 %0, %16 offset:0\n"
+          "ds_read_b64_tr_b16 %1, %16 offset:512\n"
+          "ds_read_b64_tr_b16 %2, %16 offset:2048\n"
+          "ds_read_b64_tr_b16 %3, %16 offset:2560\n"
+          "ds_read_b64_tr_b16 %4, %16 offset:4096\n"
+          "ds_read_b64_tr_b16 %5, %16 offset:4608\n"
+          "ds_read_b64_tr_b16 %6, %16 offset:6144\n"
+          "ds_read_b64_tr_b16 %7, %16 offset:6656\n"
+          "ds_read_b64_tr_b16 %8, %17 offset:0\n"
+          "ds_read_b64_tr_b16 %9, %17 offset:512\n"
+          "ds_read_b64_tr_b16 %10, %17 offset:2048\n"
+          "ds_read_b64_tr_b16 %11, %17 offset:2560\n"
+          "ds_read_b64_tr_b16 %12, %17 offset:4096\n"
+          "ds_read_b64_tr_b16 %13, %17 offset:4608\n"
+          "ds_read_b64_tr_b16 %14, %17 offset:6144\n"
+          "ds_read_b64_tr_b16 %15, %17 offset:6656\n"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(vh[0][0][0][0]), "=&v"(vh[0][0][0][1]), "=&v"(vh[0][0][1][0]), "=&v"(vh[0][0][1][1]),
+            "=&v"(vh[0][1][0][0]), "=&v"(vh[0][1][0][1]), "=&v"(vh[0][1][1][0]), "=&v"(vh[0][1][1][1]),
+            "=&v"(vh[1][0][0][0]), "=&v"(vh[1][0][0][1]), "=&v"(vh[1][0][1][0]), "=&v"(vh[1][0][1][1]),
+            "=&v"(vh[1][1][0][0]), "=&v"(vh[1][1][0][1]), "=&v"(vh[1][1][1][0]), "=&v"(vh[1][1][1][1])
+          : "v"(b0), "v"(b1)
+          : "memory");
     }
     // causal: keys after the query count as -inf
     if constexpr (CAUSAL) {
@@ -254,50 +297,61 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(const T* __restrict__ Q, 
         }
 #pragma unroll
         for (int dt = 0; dt < 2; ++dt) {
-          const u32x4 vf = *(const u32x4*)(sv + v_off(dt, g, t));
+          const u32x2 l2 = vh[dt][g][t][0], h2 = vh[dt][g][t][1];
+          const u32x4 vf = u32x4{l2.x, l2.y, h2.x, h2.y};
           acc_o[dt] = mfma32<T>(vf, p, acc_o[dt]);
           if constexpr (kSplitP<T>) acc_o[dt] = mfma32<T>(vf, plo, acc_o[dt]);
         }
       }
   };
 
-  auto barrier = [&]() __attribute__((always_inline)) {
+  // Ring of three slots: iteration it multiplies block 2 it + kp from slot
+  // it % 3 after issuing the loads of block 2 (it + 2) + kp into slot
+  // (it + 2) % 3, whose previous block (it - 1) every wave has finished (the
+  // barrier that ended iteration it - 1).  Each barrier first waits until
+  // at most that iteration's own loads (4 per wave) are outstanding: the
+  // block of iteration it + 1 is then in LDS.  The loads are issued on
+  // every iteration (past the last block, block kp again, never used): a
+  // load under a condition leaves the compiler unsure which slot is in
+  // flight, and it then waits for every load before each LDS read.
+  auto barrier_vm = [&](bool keep) __attribute__((always_inline)) {
     asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(0);  // vmcnt(0) expcnt(0) lgkmcnt(0)
+    if (keep) __builtin_amdgcn_s_waitcnt(waitcnt_vm(4) & ~(15 << 8));  // vmcnt(4) lgkmcnt(0)
+    else __builtin_amdgcn_s_waitcnt(0);
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   };
-
-  // Iteration it: parity kp multiplies block 2 it + kp from buffer it % 2
-  // while it loads block 2 it + 2 + kp into the other buffer.
-  const int poff = kp * kStage;
-  load_k(sK0 + poff, kp);
-  load_v(kp);
-  store_v(sV0 + poff);
-  barrier();
   const int niter = (nblk + 1) / 2;
-  auto step = [&](int it, const char* ck, const char* cv, char* nk, char* nv) __attribute__((always_inline)) {
-    const int kb = 2 * it + kp, nkb = kb + 2;
-    const bool more = nkb < nblk;
-    if (more) {
-      load_k(nk + poff, nkb);
-      load_v(nkb);
-    }
-    if (kb < nblk) block(kb, ck + poff, cv + poff);
-    if (more) store_v(nv + poff);
-    barrier();
+  load_kv(std::integral_constant<int, 0>{}, kp);
+  load_kv(std::integral_constant<int, 1>{}, 2 + kp < nblk ? 2 + kp : kp);
+  barrier_vm(true);
+  auto step = [&](auto jc, int it) __attribute__((always_inline)) {
+    constexpr int j = decltype(jc)::value;
+    const int kb = 2 * it + kp, nkb = kb + 4;
+    load_kv(std::integral_constant<int, (j + 2) % 3>{}, nkb < nblk ? nkb : kp);
+    if (kb < nblk) block(kb, kslot<j>() + poff, vslot<j>() + poff);
+    barrier_vm(true);
   };
-  for (int it = 0; it < niter; it += 2) {
-    step(it, sK0, sV0, sK1, sV1);
-    if (it + 1 < niter) step(it + 1, sK1, sV1, sK0, sV0);
+  // whole turns of the ring (one path around the back edge, so that the
+  // compiler sees the same loads in flight at the loop head on every
+  // entry), then the last one or two iterations
+  int it = 0;
+  for (; it + 3 <= niter; it += 3) {
+    step(std::integral_constant<int, 0>{}, it);
+    step(std::integral_constant<int, 1>{}, it + 1);
+    step(std::integral_constant<int, 2>{}, it + 2);
   }
+  if (it < niter) step(std::integral_constant<int, 0>{}, it);
+  if (it + 1 < niter) step(std::integral_constant<int, 1>{}, it + 1);
+  // the loads past the last block land before any wave reuses the slots
+  barrier_vm(false);
 
   // Merge the two parities of each query group: parity 1 leaves (m, l, o)
-  // in LDS (the stages are free after the last barrier), parity 0 combines
+  // in LDS (the slots are free after the last barrier), parity 0 combines
   // o = a0 o0 + a1 o1 and l = a0 l0 + a1 l1 with a = exp(m_p - max m).
-  float* xo0 = (float*)sV0 + qg * 16 * 64;  // o of d-tile 0: [qg][x][lane]
-  float* xo1 = (float*)sV1 + qg * 16 * 64;  // o of d-tile 1
-  float* xm = (float*)sK0 + qg * 2 * 64;    // m, l: [qg][2][lane]
+  float* xo0 = (float*)sv[0] + qg * 16 * 64;  // o of d-tile 0: [qg][x][lane]
+  float* xo1 = (float*)sv[1] + qg * 16 * 64;  // o of d-tile 1
+  float* xm = (float*)sk[0] + qg * 2 * 64;    // m, l: [qg][2][lane]
   if (kp == 1) {
 #pragma unroll
     for (int x = 0; x < 16; ++x) {
@@ -307,7 +361,7 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(const T* __restrict__ Q, 
     xm[lane] = m_run;
     xm[64 + lane] = l_run;
   }
-  barrier();
+  barrier_vm(false);
   if (kp == 1) return;
   const float m1 = xm[lane], l1 = xm[64 + lane];
   const float m = fmaxf(m_run, m1);
