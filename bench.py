@@ -371,7 +371,7 @@ def _run_variants(w, sets, args, binding, inputs, parity, torch):
     return variants
 
 
-def _bench_attention(steps, warmup, torch, binding, inputs, parity):
+def _bench_attention(steps, warmup, torch, binding, inputs, parity, graph=True):
     """The attention forward workloads (B, H, S, D = 4, 8, 1024, 64, fp16, full
     and causal): TFLOP/s of 4 B H S^2 D (half when causal) per launch."""
     recs = []
@@ -385,9 +385,18 @@ def _bench_attention(steps, warmup, torch, binding, inputs, parity):
 
         ms, per = _time(launch, 1, steps, warmup, torch)
         tf = w.flops / (ms * 1e-3) / 1e12
-        recs.append({"workload": w.name, "B": w.B, "S": w.S, "H": w.H, "D": w.D, "causal": w.causal,
-                     "ms_per_step": round(ms, 5), "per_launch": per, "TFLOP/s": round(tf, 1), "steps": steps,
-                     "roofline": _roofline("mfma", tf, PEAK_BF16_TFLOPS, "TFLOP/s", None)})
+        rec = {"workload": w.name, "B": w.B, "S": w.S, "H": w.H, "D": w.D, "causal": w.causal,
+               "ms_per_step": round(ms, 5), "per_launch": per, "TFLOP/s": round(tf, 1), "steps": steps,
+               "roofline": _roofline("mfma", tf, PEAK_BF16_TFLOPS, "TFLOP/s", None)}
+        if graph:
+            # about as long as the host needs to enqueue one launch from
+            # Python: replayed from a graph as well (same output as eager)
+            ref = o.clone()
+            gmean, gper = _time_graph(launch, 1, 100, 20, torch)
+            rec["graph"] = {"ms_per_launch": round(gmean, 6), "per_replay": gper,
+                            "TFLOP/s": round(w.flops / (gmean * 1e-3) / 1e12, 1), "launches_per_graph": 100,
+                            "replay_equals_eager": bool(torch.equal(o.view(torch.uint8), ref.view(torch.uint8)))}
+        recs.append(rec)
         del q, k, v, o
     return recs
 
@@ -471,7 +480,8 @@ def main(argv=None):
             workloads[w.name] = rec
     if sel in ("all", "attention") and not args.no_variants:
         say("attention")
-        attention = _bench_attention(max(args.steps, 50), max(args.warmup, 10), torch, binding, inputs, parity)
+        attention = _bench_attention(max(args.steps, 50), max(args.warmup, 10), torch, binding, inputs, parity,
+                                     not args.no_graph)
 
     if args.calib_copy:
         src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB

@@ -33,7 +33,11 @@
 // consecutive keys of one d per lane -- come from gfx950's transposing LDS
 // read ds_read_b64_tr_b16, two per fragment.  A ring of three LDS slots:
 // the blocks of the next two iterations are in flight while one is
-// multiplied.
+// multiplied.  Workgroups are renumbered so that each XCD takes a
+// contiguous range of (batch, head, query block), the query blocks of a
+// head together, and its L2 serves their common keys and values (B, S, H =
+// 4, 1024, 8, fp16: 14.5 against 16.5 us with the blocks of a head spread
+// over all eight XCDs).
 #include "gemm_tile.hpp"
 
 namespace ge {
@@ -120,7 +124,13 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(const T* __restrict__ Q, 
   // partial results at the end.
   const int qg = wave & 3, kp = wave >> 2;
   const int il = lane & 31, h = lane >> 5;
-  const int q0 = blockIdx.x * kBM, hd = blockIdx.y, b = blockIdx.z;
+  // Workgroup i runs on XCD i % 8 (round-robin dispatch): renumber so that
+  // the query blocks of one (batch, head) share an XCD and its L2 holds
+  // their keys and values once.
+  const int nqb = gridDim.x, ntot = nqb * gridDim.y * gridDim.z;
+  int lin = blockIdx.x + nqb * (blockIdx.y + gridDim.y * blockIdx.z);
+  if ((ntot & 7) == 0) lin = (lin & 7) * (ntot >> 3) + (lin >> 3);
+  const int q0 = (lin % nqb) * kBM, hd = (lin / nqb) % H, b = lin / nqb / H;
   const int64_t rs = (int64_t)H * kD;  // elements between consecutive sequence positions
   const int64_t base = ((int64_t)b * S * H + hd) * kD;
   const int qi = q0 + qg * 32 + il;  // this lane's query
@@ -190,48 +200,64 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(const T* __restrict__ Q, 
   const int nblk = CAUSAL ? (q0 + kBM) / kBN : S / kBN;  // >= 2: each parity has a block
 
   auto block = [&](int kb, const char* skp, const char* svp) __attribute__((always_inline)) {
+    // The block's operand fragments, all in one asm statement that waits
+    // for them (one LDS round trip per block): K's eight for S^T -- g = 1
+    // takes the g = 0 chunk of kk ^ 2, 32 rows down, since swz(32 + r) =
+    // swz(r) ^ 4 -- and V^T's eight, [dt][g][t], two transposing reads
+    // each.  The builtin form of the transposing read carries no alias
+    // information, so the compiler would make it wait for every direct load
+    // in flight, the next blocks' included.  (The block is in LDS: the
+    // barrier before this iteration waited for it.)
+    u32x2 vh[2][2][2][2];  // [dt][g][t][read]
+    u32x4 kf[2][4];
+    {
+      uint32_t ka[4];
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) ka[kk] = (uint32_t)(uintptr_t)(lds_ptr)(skp + k_off(0, kk));
+      const uint32_t b0 = (uint32_t)(uintptr_t)(lds_ptr)(svp + vt_base[0]);
+      const uint32_t b1 = (uint32_t)(uintptr_t)(lds_ptr)(svp + vt_base[1]);
+      asm volatile(
+          "ds_read_b128 %16, %24 offset:0\n"
+          "ds_read_b128 %17, %25 offset:0\n"
+          "ds_read_b128 %18, %26 offset:0\n"
+          "ds_read_b128 %19, %27 offset:0\n"
+          "ds_read_b128 %20, %26 offset:4096\n"
+          "ds_read_b128 %21, %27 offset:4096\n"
+          "ds_read_b128 %22, %24 offset:4096\n"
+          "ds_read_b128 %23, %25 offset:4096\n"
+          "ds_read_b64_tr_b16 %0, %28 offset:0\n"
+          "ds_read_b64_tr_b16 %1, %28 offset:512\n"
+          "ds_read_b64_tr_b16 %2, %28 offset:2048\n"
+          "ds_read_b64_tr_b16 %3, %28 offset:2560\n"
+          "ds_read_b64_tr_b16 %4, %28 offset:4096\n"
+          "ds_read_b64_tr_b16 %5, %28 offset:4608\n"
+          "ds_read_b64_tr_b16 %6, %28 offset:6144\n"
+          "ds_read_b64_tr_b16 %7, %28 offset:6656\n"
+          "ds_read_b64_tr_b16 %8, %29 offset:0\n"
+          "ds_read_b64_tr_b16 %9, %29 offset:512\n"
+          "ds_read_b64_tr_b16 %10, %29 offset:2048\n"
+          "ds_read_b64_tr_b16 %11, %29 offset:2560\n"
+          "ds_read_b64_tr_b16 %12, %29 offset:4096\n"
+          "ds_read_b64_tr_b16 %13, %29 offset:4608\n"
+          "ds_read_b64_tr_b16 %14, %29 offset:6144\n"
+          "ds_read_b64_tr_b16 %15, %29 offset:6656\n"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(vh[0][0][0][0]), "=&v"(vh[0][0][0][1]), "=&v"(vh[0][0][1][0]), "=&v"(vh[0][0][1][1]),
+            "=&v"(vh[0][1][0][0]), "=&v"(vh[0][1][0][1]), "=&v"(vh[0][1][1][0]), "=&v"(vh[0][1][1][1]),
+            "=&v"(vh[1][0][0][0]), "=&v"(vh[1][0][0][1]), "=&v"(vh[1][0][1][0]), "=&v"(vh[1][0][1][1]),
+            "=&v"(vh[1][1][0][0]), "=&v"(vh[1][1][0][1]), "=&v"(vh[1][1][1][0]), "=&v"(vh[1][1][1][1]),
+            "=&v"(kf[0][0]), "=&v"(kf[0][1]), "=&v"(kf[0][2]), "=&v"(kf[0][3]),
+            "=&v"(kf[1][0]), "=&v"(kf[1][1]), "=&v"(kf[1][2]), "=&v"(kf[1][3])
+          : "v"(ka[0]), "v"(ka[1]), "v"(ka[2]), "v"(ka[3]), "v"(b0), "v"(b1)
+          : "memory");
+    }
     // S^T for the two 32-key groups
     f32x16 s[2];
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
       s[g] = f32x16{};
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) s[g] = mfma32<T>(*(const u32x4*)(skp + k_off(g, kk)), qf[kk], s[g]);
-    }
-    // V^T's eight fragments of the block, [dt][g][t], while the MFMAs run.
-    // The sixteen transposing reads are one asm statement that also waits
-    // for them: the compiler has no alias information for the builtin form
-    // of this read and would make it wait for every direct load in flight,
-    // the next blocks' included.  (The block's V is in LDS: the barrier
-    // before this iteration waited for it.)
-    u32x2 vh[2][2][2][2];  // [dt][g][t][read]
-    {
-      const uint32_t b0 = (uint32_t)(uintptr_t)(lds_ptr)(svp + vt_base[0]);
-      const uint32_t b1 = (uint32_t)(uintptr_t)(lds_ptr)(svp + vt_base[1]);
-      asm volatile(
-          "ds_read_b64_tr_b16 %0, %16 offset:0\n"
-          "ds_read_b64_tr_b16 %1, %16 offset:512\n"
-          "ds_read_b64_tr_b16 %2, %16 offset:2048\n"
-          "ds_read_b64_tr_b16 %3, %16 offset:2560\n"
-          "ds_read_b64_tr_b16 %4, %16 offset:4096\n"
-          "ds_read_b64_tr_b16 %5, %16 offset:4608\n"
-          "ds_read_b64_tr_b16 %6, %16 offset:6144\n"
-          "ds_read_b64_tr_b16 %7, %16 offset:6656\n"
-          "ds_read_b64_tr_b16 %8, %17 offset:0\n"
-          "ds_read_b64_tr_b16 %9, %17 offset:512\n"
-          "ds_read_b64_tr_b16 %10, %17 offset:2048\n"
-          "ds_read_b64_tr_b16 %11, %17 offset:2560\n"
-          "ds_read_b64_tr_b16 %12, %17 offset:4096\n"
-          "ds_read_b64_tr_b16 %13, %17 offset:4608\n"
-          "ds_read_b64_tr_b16 %14, %17 offset:6144\n"
-          "ds_read_b64_tr_b16 %15, %17 offset:6656\n"
-          "s_waitcnt lgkmcnt(0)"
-          : "=&v"(vh[0][0][0][0]), "=&v"(vh[0][0][0][1]), "=&v"(vh[0][0][1][0]), "=&v"(vh[0][0][1][1]),
-            "=&v"(vh[0][1][0][0]), "=&v"(vh[0][1][0][1]), "=&v"(vh[0][1][1][0]), "=&v"(vh[0][1][1][1]),
-            "=&v"(vh[1][0][0][0]), "=&v"(vh[1][0][0][1]), "=&v"(vh[1][0][1][0]), "=&v"(vh[1][0][1][1]),
-            "=&v"(vh[1][1][0][0]), "=&v"(vh[1][1][0][1]), "=&v"(vh[1][1][1][0]), "=&v"(vh[1][1][1][1])
-          : "v"(b0), "v"(b1)
-          : "memory");
+      for (int kk = 0; kk < 4; ++kk) s[g] = mfma32<T>(kf[g][kk], qf[kk], s[g]);
     }
     // causal: keys after the query count as -inf
     if constexpr (CAUSAL) {
