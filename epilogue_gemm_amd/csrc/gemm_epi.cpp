@@ -45,21 +45,22 @@ bool tile_supports(int cfg, const Problem& p) {
   // The 16x16x32 configurations take A row-major and B column-major, or B
   // row-major (its buffer range, K + 64 rows of ldb elements, must fit
   // 32-bit byte offsets).
-  // The ring configurations take A row-major (either B); a row-major B's
-  // buffer range (K + 64 rows of ldb elements) must fit 32-bit byte
-  // offsets.
+  // The ring configurations take A and B in either layout; a row-major B's
+  // buffer range (K + 64 rows of ldb elements) and a column-major A's (K +
+  // 64 columns of lda elements) must fit 32-bit byte offsets.
   const TileConfig& c = kTile[cfg];
   const int n_align = p.out_dt == GEMM_EPI_FP8_E4M3 ? 16 : 8;
   if (c.mfma == 16 &&
       (p.la != GEMM_EPI_ROW_MAJOR || p.lb != (c.brow ? GEMM_EPI_ROW_MAJOR : GEMM_EPI_COL_MAJOR) ||
        (c.brow && (p.K + 64) * p.ldb * 2 >= ((int64_t)1 << 32))))
     return false;
-  if (c.ring > 0 && (p.la != GEMM_EPI_ROW_MAJOR ||
+  if (c.ring > 0 && ((p.la == GEMM_EPI_COL_MAJOR && (p.K + 64) * p.lda * 2 >= ((int64_t)1 << 32)) ||
                      (p.lb == GEMM_EPI_ROW_MAJOR && (p.K + 64) * p.ldb * 2 >= ((int64_t)1 << 32))))
     return false;
-  // The ring configurations also take M and N below the tile (masked) and
-  // K <= 64; the chunk count must be a multiple of the slot count, save
-  // for two slots, which take any.
+  // The ring configurations also take M and N below the tile (masked), K
+  // <= 64, and with A column-major any M (the last tile row masked); the
+  // chunk count must be a multiple of the slot count, save for two slots,
+  // which take any.
   const int64_t chunks = (p.K + 63) / 64;
   if (c.ring > 0)
     return p.M >= 1 && p.N >= n_align && p.N % n_align == 0 && p.K >= 8 && p.K % 8 == 0 &&

@@ -41,7 +41,9 @@
 // k < 0 load as zeros.  The last tile row and column
 // are shifted back to end at M and N (they recompute part of a neighbour
 // with the same k order, so with identical values); a problem with fewer
-// than 64 rows or columns takes one tile there, masked past the end.  (Pipelined tile copies and block rasterisation:
+// than 64 rows or columns takes one tile there, masked past the end.  With
+// A column-major the last tile row is not shifted (its first row would not
+// fall on a 16-byte chunk when M % 8 != 0) but masked past M.  (Pipelined tile copies and block rasterisation:
 // atlascloud.ai "Writing high-performance kernels in TileLang", section
 // "Écrivons un GEMM"; epilogue on the accumulator fragment: csdn
 // "从零开始学习 TileLang" ch.10 sec. 10.8; small problems that leave the
@@ -94,7 +96,8 @@ __device__ __forceinline__ void arrive() {
 }
 
 // Row-major B (K x N, n contiguous) into a slot: 64 k-rows of the tile's 64
-// columns, 128 bytes each.  Instruction t (of 8, wave w issues t = w and
+// columns, 128 bytes each.  (A column-major A, M x K with m contiguous, is
+// loaded the same way with m for n: 64 k-rows of the tile's 64 rows.)  Instruction t (of 8, wave w issues t = w and
 // w + 4) fills k-rows 8 t .. 8 t + 7: lane L takes k-row 8 t + L / 8 and
 // lands at chunk position L % 8, so it loads n-chunk (L % 8) ^ 2 ((L / 8) & 3)
 // of that k-row (8 t is a multiple of 4, so the swizzle depends on L only).
@@ -114,8 +117,10 @@ struct RowBLoader {
     wave = wave_;
     const int chunk = (lane & 7) ^ (2 * ((lane >> 3) & 3));
     voff = (uint32_t)(lane >> 3) * row_bytes + (uint32_t)(chunk << 4);
-    // fewer than 64 columns (N < 64): columns past N load nothing (N is a
-    // multiple of 8, so a 16-byte chunk lies wholly on one side)
+    // columns past N load nothing (N < 64, or the unshifted last tile row
+    // of a column-major A: a chunk that starts before N is loaded whole,
+    // its tail from the padding of a leading dimension that is a multiple
+    // of 8, and feeds only outputs that are not stored)
     if (n0 + 8 * chunk >= N) voff = 0xFFFFFFF0u;
   }
   // instruction i (0, 1) of chunk kt
@@ -134,7 +139,7 @@ struct RowBLoader {
   }
 };
 
-template <typename TIn, typename TOut, int EPI, bool BROW, int P>
+template <typename TIn, typename TOut, int EPI, bool BROW, int P, bool ACOL>
 __global__ __launch_bounds__(kNW * 64) void gemm_ring_kernel(const TIn* __restrict__ A, const TIn* __restrict__ B,
                                                              const TIn* __restrict__ bias, TOut* __restrict__ C,
                                                              int M, int N, int K, int tiles_m, int tiles_n, int panel,
@@ -152,8 +157,10 @@ __global__ __launch_bounds__(kNW * 64) void gemm_ring_kernel(const TIn* __restri
   tile::raster(blockIdx.x, tiles_m, tiles_n, panel, tm, tn);
   // A problem smaller than the tile (M or N below 64) is covered by one
   // tile row or column at 0, its rows or columns past the end loading
-  // nothing and storing nothing (MASK below).
-  const int m0 = max(0, min(tm * kTile, M - kTile)), n0 = max(0, min(tn * kTile, N - kTile));
+  // nothing and storing nothing (MASK below); a column-major A keeps its
+  // last tile row in place, masked past M.
+  const int m0 = ACOL ? tm * kTile : max(0, min(tm * kTile, M - kTile));
+  const int n0 = max(0, min(tn * kTile, N - kTile));
   const int kpad = (-K) & (kBK - 1);
   const int nchunks = (K + kpad) / kBK;
 
@@ -162,6 +169,7 @@ __global__ __launch_bounds__(kNW * 64) void gemm_ring_kernel(const TIn* __restri
   slots<P>(sa, sb, std::make_integer_sequence<int, P>{});
 
   const DirectLoader<kTile, kNW> da(A, m0, M, lda, kpad, tid, wave);
+  const RowBLoader ra(A, m0, M, K, lda, kpad, lane, wave);  // A column-major
   // (only one of the two B movers is used)
   const DirectLoader<kTile, kNW> db(B, n0, N, ldb, kpad, tid, wave);
   const RowBLoader rb(B, n0, N, K, ldb, kpad, lane, wave);
@@ -170,14 +178,16 @@ __global__ __launch_bounds__(kNW * 64) void gemm_ring_kernel(const TIn* __restri
     if (c == 0 && kpad != 0) {
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        da.issue_first(sa[j], i, lane, kpad);
+        if constexpr (ACOL) ra.issue_first(sa[j], i, kpad);
+        else da.issue_first(sa[j], i, lane, kpad);
         if constexpr (BROW) rb.issue_first(sb[j], i, kpad);
         else db.issue_first(sb[j], i, lane, kpad);
       }
     } else {
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        da.issue(sa[j], c, i);
+        if constexpr (ACOL) ra.issue(sa[j], c, i);
+        else da.issue(sa[j], c, i);
         if constexpr (BROW) rb.issue(sb[j], c, i);
         else db.issue(sb[j], c, i);
       }
@@ -200,21 +210,28 @@ __global__ __launch_bounds__(kNW * 64) void gemm_ring_kernel(const TIn* __restri
   // chunk ^ 2 i, bytes 8 (a % 2) within it.
   const int s16 = lane & 15, ti = s16 >> 2, ta = s16 & 3, tg = (lane >> 4) & 1;
   const int tr_off = (8 * h + ti) * kRowBytes + (((4 * wn + 2 * tg + (ta >> 1)) ^ (2 * ti)) << 4) + 8 * (ta & 1);
+  // column-major A: the same with the wave's rows 32 wm .. for its columns
+  const int tr_off_a = (8 * h + ti) * kRowBytes + (((4 * wm + 2 * tg + (ta >> 1)) ^ (2 * ti)) << 4) + 8 * (ta & 1);
 
   f32x16 acc = f32x16{};
+  // eight consecutive k of one row (column) per lane from a k-row layout:
+  // two transposing reads, k-rows 16 q + 8 h + i and + 4
+  auto read_tr = [&](const char* p0) __attribute__((always_inline)) {
+    typedef short s4v __attribute__((vector_size(8)));
+    typedef __attribute__((address_space(3))) s4v lds_s4v;
+    const s4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4v*)(lds_ptr)p0);
+    const s4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4v*)(lds_ptr)(p0 + 4 * kRowBytes));
+    const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+    return u32x4{l2.x, l2.y, h2.x, h2.y};
+  };
   auto compute = [&](int j) __attribute__((always_inline)) {
     u32x4 a[4], b[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      a[q] = *(const u32x4*)(sa[j] + a_off[q]);
+      if constexpr (ACOL) a[q] = read_tr(sa[j] + 16 * q * kRowBytes + tr_off_a);
+      else a[q] = *(const u32x4*)(sa[j] + a_off[q]);
       if constexpr (BROW) {
-        typedef short s4v __attribute__((vector_size(8)));
-        typedef __attribute__((address_space(3))) s4v lds_s4v;
-        char* p0 = sb[j] + 16 * q * kRowBytes + tr_off;
-        const s4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4v*)(lds_ptr)p0);
-        const s4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4v*)(lds_ptr)(p0 + 4 * kRowBytes));
-        const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-        b[q] = u32x4{l2.x, l2.y, h2.x, h2.y};
+        b[q] = read_tr(sb[j] + 16 * q * kRowBytes + tr_off);
       } else {
         b[q] = *(const u32x4*)(sb[j] + b_off[q]);
       }
@@ -275,7 +292,7 @@ __global__ __launch_bounds__(kNW * 64) void gemm_ring_kernel(const TIn* __restri
   static_assert(32 * 32 * sizeof(TOut) <= (size_t)kOpBytes / 2, "staging area");
   const f32x16 accs[1][1] = {{acc}};
   const int mw = m0 + 32 * wm, nw = n0 + 32 * wn;
-  if (M < kTile || N < kTile)
+  if (M < kTile || N < kTile || (ACOL && M % kTile != 0))
     tile::write_tile<32, 32, TIn, TOut, EPI, true, true>(accs, bias, C, ldc, mw, nw, lane, stage_w, scale, res,
                                                          out_scale, M, N);
   else if (scale != nullptr || res != nullptr || out_scale != nullptr)
@@ -285,35 +302,37 @@ __global__ __launch_bounds__(kNW * 64) void gemm_ring_kernel(const TIn* __restri
                                                     nullptr);
 }
 
-template <typename TIn, typename TOut, int EPI, bool BROW, int P>
+template <typename TIn, typename TOut, int EPI, bool BROW, int P, bool ACOL>
 hipError_t launch(const LaunchArgs& a) {
   const int tiles_m = (a.M + kTile - 1) / kTile, tiles_n = (a.N + kTile - 1) / kTile;
   const int panel = tiles_m < 4 ? tiles_m : 4;
-  hipLaunchKernelGGL((gemm_ring_kernel<TIn, TOut, EPI, BROW, P>), dim3(tiles_m * tiles_n), dim3(kNW * 64), 0,
+  hipLaunchKernelGGL((gemm_ring_kernel<TIn, TOut, EPI, BROW, P, ACOL>), dim3(tiles_m * tiles_n), dim3(kNW * 64), 0,
                      a.stream, (const TIn*)a.A, (const TIn*)a.B, (const TIn*)a.bias, (TOut*)a.C, a.M, a.N, a.K,
                      tiles_m, tiles_n, panel, a.lda, a.ldb, a.ldc, a.scale, (const TOut*)a.residual, a.out_scale);
   return hipGetLastError();
 }
 
-template <typename TIn, typename TOut, bool BROW, int P>
+template <typename TIn, typename TOut, bool BROW, int P, bool ACOL>
 LaunchFn pick_epi(int epi) {
   switch (epi) {
-    case GEMM_EPI_NONE: return &launch<TIn, TOut, GEMM_EPI_NONE, BROW, P>;
-    case GEMM_EPI_RELU: return &launch<TIn, TOut, GEMM_EPI_RELU, BROW, P>;
-    case GEMM_EPI_BIAS_RELU: return &launch<TIn, TOut, GEMM_EPI_BIAS_RELU, BROW, P>;
-    case GEMM_EPI_BIAS_GELU: return &launch<TIn, TOut, GEMM_EPI_BIAS_GELU, BROW, P>;
-    case GEMM_EPI_BIAS: return &launch<TIn, TOut, GEMM_EPI_BIAS, BROW, P>;
-    case GEMM_EPI_SILU: return &launch<TIn, TOut, GEMM_EPI_SILU, BROW, P>;
-    case GEMM_EPI_BIAS_SILU: return &launch<TIn, TOut, GEMM_EPI_BIAS_SILU, BROW, P>;
+    case GEMM_EPI_NONE: return &launch<TIn, TOut, GEMM_EPI_NONE, BROW, P, ACOL>;
+    case GEMM_EPI_RELU: return &launch<TIn, TOut, GEMM_EPI_RELU, BROW, P, ACOL>;
+    case GEMM_EPI_BIAS_RELU: return &launch<TIn, TOut, GEMM_EPI_BIAS_RELU, BROW, P, ACOL>;
+    case GEMM_EPI_BIAS_GELU: return &launch<TIn, TOut, GEMM_EPI_BIAS_GELU, BROW, P, ACOL>;
+    case GEMM_EPI_BIAS: return &launch<TIn, TOut, GEMM_EPI_BIAS, BROW, P, ACOL>;
+    case GEMM_EPI_SILU: return &launch<TIn, TOut, GEMM_EPI_SILU, BROW, P, ACOL>;
+    case GEMM_EPI_BIAS_SILU: return &launch<TIn, TOut, GEMM_EPI_BIAS_SILU, BROW, P, ACOL>;
     default: return nullptr;
   }
 }
 
-// A row-major only; B either layout.
+// A and B in either layout
 template <typename TIn, typename TOut, int P>
 LaunchFn pick(int la, int lb, int epi) {
-  if (la != GEMM_EPI_ROW_MAJOR) return nullptr;
-  return lb == GEMM_EPI_ROW_MAJOR ? pick_epi<TIn, TOut, true, P>(epi) : pick_epi<TIn, TOut, false, P>(epi);
+  const bool brow = lb == GEMM_EPI_ROW_MAJOR;
+  if (la == GEMM_EPI_ROW_MAJOR)
+    return brow ? pick_epi<TIn, TOut, true, P, false>(epi) : pick_epi<TIn, TOut, false, P, false>(epi);
+  return brow ? pick_epi<TIn, TOut, true, P, true>(epi) : pick_epi<TIn, TOut, false, P, true>(epi);
 }
 
 }  // namespace ring

@@ -157,12 +157,12 @@ def test_fp8_output_needs_16_columns_in_tile_kernels(lib):
     (32, 4096, 1152, "row", "row", "skinny", "skinny_rowb_64n_8w_6x128k"),  # nine chunks of 128
     (32, 40, 1152, "row", "row", "skinny", "skinny_rowb_32n_4w_8x128k"),  # N < 64: 32-column workgroups
     (32, 4096, 200, "row", "row", "skinny", "skinny_rowb_32n_2w_2x128k"),  # two chunks of 128, the first padded
-    (32, 8192, 8192, "col", "row", "generic", "generic"),  # column-major A: no decode-shape kernel
+    (32, 8192, 8192, "col", "row", "tile", "tile_64x64_ring4"),  # column-major A: no decode-shape kernel; ring
     (2000, 8200, 4096, "row", "col", "tile", "tile_256x256x64_m16"),  # last tile row and column shifted back
     (1000, 1000, 1024, "row", "col", "tile", "tile_64x64_ring4"),  # 16 x 16 edge-tiled 64 x 64 tiles
     (3000, 2000, 4096, "row", "row", "tile", "tile_128x128x64"),  # 24 x 16 tiles of 128
-    (1000, 1000, 1024, "col", "col", "tile", "tile_64x64x64"),
-    (1001, 1000, 1024, "col", "col", "generic", "generic"),  # column-major A needs M % 8
+    (1000, 1000, 1024, "col", "col", "tile", "tile_64x64_ring4"),  # column-major A through transposing reads
+    (1001, 1000, 1024, "col", "col", "generic", "generic"),  # packed column-major A: lda = 1001, unaligned
     (1000, 1004, 1024, "row", "col", "generic", "generic"),  # N % 8
     (37, 53, 29, "row", "row", "generic", "generic"),
     (256, 256, 100, "col", "row", "generic", "generic"),  # K not a multiple of 8
@@ -172,9 +172,11 @@ def test_fp8_output_needs_16_columns_in_tile_kernels(lib):
     (1024, 1024, 320, "row", "row", "tile", "tile_64x64_ring2"),  # 5 chunks: two slots take an odd count
     (1024, 1024, 384, "row", "col", "tile", "tile_64x64_ring2"),  # 6 chunks
     (4096, 4096, 4040, "row", "col", "tile", "tile_256x256x64_m16"),
-    (256, 256, 72, "col", "row", "tile", "tile_64x64x64"),
+    (256, 256, 72, "col", "row", "tile", "tile_64x64_ring2"),  # two chunks
     (256, 256, 64, "row", "row", "tile", "tile_64x64_ring2"),  # one chunk
-    (256, 256, 64, "col", "row", "generic", "generic"),  # one k-step: the two-stage pipeline needs two
+    (256, 256, 64, "col", "row", "tile", "tile_64x64_ring2"),  # one chunk
+    (8, 8, 8, "col", "col", "tile", "tile_64x64_ring2"),
+    (4096, 4096, 4096, "col", "col", "tile", "tile_256x256x64"),  # two-stage, register-staged A
     (48, 40, 64, "row", "row", "tile", "tile_64x64_ring2"),  # M and N below the tile: masked
     (63, 1000, 320, "row", "col", "tile", "tile_64x64_ring2"),
     (1, 8, 8, "row", "row", "tile", "tile_64x64_ring2"),

@@ -1,5 +1,7 @@
 """Parity of the deep-ring 64 x 64 tile configurations (8, 4 or 2 LDS slots;
-A row-major, B row-major through transposing LDS reads or column-major) with
+A row-major, or column-major through transposing LDS reads (the last tile
+row masked, M any with lda a multiple of 8); B row-major through
+transposing LDS reads or column-major) with
 the oracle: bit-exact on integer operands for every exact epilogue, every
 K padding (the first chunk partial), chunk counts of one to several ring
 turns, shifted edge tiles, leading dimensions, the optional scale, residual
@@ -134,3 +136,69 @@ def test_ring_small_problems_random_tolerance(lb):
             bits = inputs.make_inputs(M, N, K, in_dt, "row", lb, True, float(np.sqrt(K)), 0.1, seed=M + K)
             assert check_case(bits, M, N, K, in_dt, in_dt, "row", lb, "bias_gelu", "tile", 7, False) == \
                 "tile_64x64_ring2"
+
+
+# ---------------------------------------------------------------------------
+# A column-major: 64 k-rows of the tile's rows in LDS, read through
+# transposing reads like a row-major B; the last tile row is not shifted
+# back but masked past M, so M need not be a multiple of 8 (with lda one)
+# ---------------------------------------------------------------------------
+
+def _pads_cola(M, pb=16, pc=24):
+    """Padding of A, B and C: A's leading dimension (M + pad) a multiple of 8."""
+    return ((-M) % 8 + 8, pb, pc)
+
+
+@pytest.mark.parametrize("config", list(RINGS))
+@pytest.mark.parametrize("lb", LBS)
+@pytest.mark.parametrize("in_dt,out_dt", [("f16", "f16"), ("bf16", "bf16"), ("f16", "f32")])
+def test_ring_col_a_integer_bitexact(config, lb, in_dt, out_dt):
+    name, P = RINGS[config]
+    M, N, K = 192, 256, _k(P, 2)
+    for epi in EPIS:
+        bits = inputs.integer_inputs(M, N, K, in_dt, "col", lb, epi.startswith("bias"), seed=len(epi) + 3 * config)
+        assert check_case(bits, M, N, K, in_dt, out_dt, "col", lb, epi, "tile", config, epi in BITWISE_EPIS) == name
+
+
+# K paddings and ring turns; M past a multiple of 64 by a ragged amount (the
+# unshifted last tile row, masked), N shifted back as before
+@pytest.mark.parametrize("config", list(RINGS))
+@pytest.mark.parametrize("lb", LBS)
+@pytest.mark.parametrize("M,kpad,turns", [(200, 0, 1), (203, 8, 2), (129, 24, 1), (77, 40, 2), (250, 56, 1)])
+def test_ring_col_a_edges_bitexact(config, lb, M, kpad, turns):
+    name, P = RINGS[config]
+    N, K = 136, _k(P, turns, kpad)
+    for in_dt, out_dt, epi, extras in (("bf16", "bf16", "bias_relu", False), ("f16", "f32", "none", True)):
+        assert run_strided(M, N, K, in_dt, out_dt, "col", lb, epi, _pads_cola(M), "tile", config, extras,
+                           extra_rows=64) == name
+
+
+@pytest.mark.parametrize("lb", LBS)
+@pytest.mark.parametrize("M,N,K", [(1, 8, 8), (33, 40, 64), (63, 8, 320), (17, 136, 64), (200, 24, 136),
+                                   (61, 264, 128), (7, 16, 1000), (100, 72, 200)])
+def test_ring_col_a_small_problems_bitexact(lb, M, N, K):
+    for in_dt, out_dt, epi, extras in (("bf16", "bf16", "bias_relu", False), ("f16", "f32", "relu", True),
+                                       ("f16", "f16", "bias", True)):
+        assert run_strided(M, N, K, in_dt, out_dt, "col", lb, epi, _pads_cola(M), "tile", 7, extras,
+                           extra_rows=64) == "tile_64x64_ring2"
+    if N % 16 == 0:
+        assert run_strided(M, N, K, "bf16", "fp8", "col", lb, "bias", _pads_cola(M, 8, 16), "tile", 7, False,
+                           extra_rows=64) == "tile_64x64_ring2"
+    # the automatic plan takes a ring where no other kernel fits (packed
+    # operands: M a multiple of 8 keeps A's columns 16-byte aligned)
+    if M % 8 == 0:
+        bits = inputs.integer_inputs(M, N, K, "bf16", "col", lb, True, seed=M * N + K)
+        name = check_case(bits, M, N, K, "bf16", "bf16", "col", lb, "bias_gelu", "auto", -1, False)
+        assert name.startswith("tile_64x64_ring"), name
+
+
+@pytest.mark.parametrize("config", list(RINGS))
+@pytest.mark.parametrize("lb", LBS)
+def test_ring_col_a_random_tolerance(config, lb):
+    name, P = RINGS[config]
+    M, N, K = 320, 384, _k(P, 2, 16)
+    for in_dt in ("bf16", "f16"):
+        for epi in ("bias_gelu", "relu"):
+            bits = inputs.make_inputs(M, N, K, in_dt, "col", lb, epi.startswith("bias"), float(np.sqrt(K)), 0.1,
+                                      seed=M + K + 1)
+            assert check_case(bits, M, N, K, in_dt, in_dt, "col", lb, epi, "tile", config, False) == name
