@@ -4,9 +4,9 @@
 //
 // The blocked form with an online softmax: each workgroup owns 128 queries
 // of one (batch, head) and streams the keys and values in blocks of 64
-// through LDS, keeping per query the running maximum m, the running sum l
+// through LDS, keeping per query a running maximum m, the running sum l
 // and the unnormalised output o, rescaled by exp(m_old - m_new) whenever
-// the maximum grows, and divides by l at the end (csdn "从零开始学习
+// m moves, and divides by l at the end (csdn "从零开始学习
 // TileLang", ch.13 "FlashAttention", sec. 13.6-13.8; ainew.jp "TileLang で
 // GPU カーネル設計を解説", section 6).  Scores are scaled by log2(e) / sqrt(D)
 // so that exp is the hardware exp2 (sec. 9.6 of the same tutorial).
@@ -272,63 +272,85 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(const T* __restrict__ Q, 
           }
       }
     }
-    // block maximum over the query's 64 scores (32 here, 32 in lane ^ 32)
-    float mx = s[0][0];
+    // The block's probabilities p = 2^(s log2(e)/sqrt(D) - moff), rounded to
+    // the input format as the MFMA multiplies them, and the lane's sum of
+    // them.  bf16 keeps 8 significant bits, so its P is carried as two bf16
+    // parts: p_hi = bf16(p) and p_lo = bf16(p - p_hi) (the difference is
+    // exact in fp32), multiplied by two MFMAs into the same accumulator;
+    // the weights then hold about 16 bits, like fp16's single part holds 11.
+    u32x4 pp[2][2], pl[2][2];
+    auto probs = [&](float moff) __attribute__((always_inline)) {
+      float lb = 0.0f;
 #pragma unroll
-    for (int x = 1; x < 16; ++x) mx = fmaxf(mx, s[0][x]);
+      for (int g = 0; g < 2; ++g)
 #pragma unroll
-    for (int x = 0; x < 16; ++x) mx = fmaxf(mx, s[1][x]);
-    mx = fmaxf(mx, partner32(mx, h));
-    // The reference point m_run moves only when a score exceeds it by more
-    // than 2^8 in probability (any lane of the wave): the probabilities
-    // then stay below 256, well inside the 16-bit formats, and the rescale
-    // of o and l (and its vector work) is skipped for most blocks.
-    if (__builtin_amdgcn_ballot_w64((mx - m_run) * scale_log2 > 8.0f)) {
-      const float m_new = fmaxf(m_run, mx);
-      // (a causal query group can meet only masked keys in its parity's
-      // first blocks: a lane whose m is still -inf keeps it, with alpha 1
-      // and o = l = 0, when another lane moves)
-      const float alpha = m_new == -__builtin_inff() ? 1.0f : __builtin_amdgcn_exp2f((m_run - m_new) * scale_log2);
-      m_run = m_new;
-      l_run *= alpha;
+        for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int dt = 0; dt < 2; ++dt) acc_o[dt] *= alpha;
-    }
-    const float moff = m_run == -__builtin_inff() ? 0.0f : m_run * scale_log2;
-#pragma unroll
-    for (int g = 0; g < 2; ++g)
-#pragma unroll
-      for (int x = 0; x < 16; ++x) s[g][x] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[g][x], scale_log2, -moff));
-    // O^T += V^T P^T, 16 keys at a time; l += the rounded P's row sums.
-    // bf16 keeps 8 significant bits, so its P is carried as two bf16 parts:
-    // p_hi = bf16(p) and p_lo = bf16(p - p_hi) (the difference is exact in
-    // fp32), multiplied by two MFMAs into the same accumulator.  The
-    // weights then hold about 16 bits, like fp16's single part holds 11.
-#pragma unroll
-    for (int g = 0; g < 2; ++g)
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        u32x4 p, plo;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const float a = s[g][8 * t + 2 * w], b = s[g][8 * t + 2 * w + 1];
-          p[w] = pack2<T>(a, b);
-          l_run = add_pair<T>(p[w], l_run);
-          if constexpr (kSplitP<T>) {
-            const float ah = __builtin_bit_cast(float, p[w] << 16);
-            const float bh = __builtin_bit_cast(float, p[w] & 0xffff0000u);
-            plo[w] = pack2<T>(a - ah, b - bh);
-            l_run = add_pair<T>(plo[w], l_run);
+          for (int w = 0; w < 4; ++w) {
+            const float a = __builtin_amdgcn_exp2f(__builtin_fmaf(s[g][8 * t + 2 * w], scale_log2, -moff));
+            const float b = __builtin_amdgcn_exp2f(__builtin_fmaf(s[g][8 * t + 2 * w + 1], scale_log2, -moff));
+            pp[g][t][w] = pack2<T>(a, b);
+            lb = add_pair<T>(pp[g][t][w], lb);
+            if constexpr (kSplitP<T>) {
+              const float ah = __builtin_bit_cast(float, pp[g][t][w] << 16);
+              const float bh = __builtin_bit_cast(float, pp[g][t][w] & 0xffff0000u);
+              pl[g][t][w] = pack2<T>(a - ah, b - bh);
+              lb = add_pair<T>(pl[g][t][w], lb);
+            }
           }
-        }
+      return lb;
+    };
+    // The reference point m_run (a running maximum of the raw scores) moves
+    // only when the probabilities at the current one would leave the range
+    // kept for them.  First, with every lane's m_run set, the probabilities
+    // at m_run: if each lane's sum of its 32 stays below 2^15, so does
+    // every one of them (they are not negative), well inside the 16-bit
+    // formats, and they are used as they are -- most blocks, with no block
+    // maximum computed.
+    float lb = 0.0f;
+    bool done = false;
+    if (!__builtin_amdgcn_ballot_w64(m_run == -__builtin_inff())) {
+      lb = probs(m_run * scale_log2);
+      done = !__builtin_amdgcn_ballot_w64(!(lb < 32768.0f));
+    }
+    if (!done) {
+      // block maximum over the query's 64 scores (32 here, 32 in lane ^ 32)
+      float mx = s[0][0];
+#pragma unroll
+      for (int x = 1; x < 16; ++x) mx = fmaxf(mx, s[0][x]);
+#pragma unroll
+      for (int x = 0; x < 16; ++x) mx = fmaxf(mx, s[1][x]);
+      mx = fmaxf(mx, partner32(mx, h));
+      // m_run moves where a score exceeds it by more than 2^8 in
+      // probability (any lane of the wave): the probabilities then stay
+      // below 256
+      if (__builtin_amdgcn_ballot_w64((mx - m_run) * scale_log2 > 8.0f)) {
+        const float m_new = fmaxf(m_run, mx);
+        // (a causal query group can meet only masked keys in its parity's
+        // first blocks: a lane whose m is still -inf keeps it, with alpha 1
+        // and o = l = 0, when another lane moves)
+        const float alpha =
+            m_new == -__builtin_inff() ? 1.0f : __builtin_amdgcn_exp2f((m_run - m_new) * scale_log2);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt) acc_o[dt] *= alpha;
+      }
+      lb = probs(m_run == -__builtin_inff() ? 0.0f : m_run * scale_log2);
+    }
+    l_run += lb;
+    // O^T += V^T P^T, 16 keys at a time
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int dt = 0; dt < 2; ++dt) {
           const u32x2 l2 = vh[dt][g][t][0], h2 = vh[dt][g][t][1];
           const u32x4 vf = u32x4{l2.x, l2.y, h2.x, h2.y};
-          acc_o[dt] = mfma32<T>(vf, p, acc_o[dt]);
-          if constexpr (kSplitP<T>) acc_o[dt] = mfma32<T>(vf, plo, acc_o[dt]);
+          acc_o[dt] = mfma32<T>(vf, pp[g][t], acc_o[dt]);
+          if constexpr (kSplitP<T>) acc_o[dt] = mfma32<T>(vf, pl[g][t], acc_o[dt]);
         }
-      }
   };
 
   // Ring of three slots: iteration it multiplies block 2 it + kp from slot
