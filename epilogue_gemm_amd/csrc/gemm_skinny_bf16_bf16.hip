@@ -1,0 +1,9 @@
+// gemm_skinny_bf16_bf16.hip -- decode-shape kernel instantiations for bf16 inputs and
+// bf16 output (one translation unit per format pair, so they compile in parallel).
+#include "gemm_skinny.hpp"
+
+namespace ge {
+
+LaunchFn skinny_launcher_bf16_bf16(int cfg, int epi) { return skinny_pick<bf16, bf16>(cfg, epi); }
+
+}  // namespace ge

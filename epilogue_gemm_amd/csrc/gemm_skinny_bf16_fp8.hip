@@ -1,0 +1,9 @@
+// gemm_skinny_bf16_fp8.hip -- decode-shape kernel instantiations for bf16 inputs and
+// FP8 E4M3 output (one translation unit per format pair, so they compile in parallel).
+#include "gemm_skinny.hpp"
+
+namespace ge {
+
+LaunchFn skinny_launcher_bf16_fp8(int cfg, int epi) { return skinny_pick<bf16, fp8e4m3>(cfg, epi); }
+
+}  // namespace ge

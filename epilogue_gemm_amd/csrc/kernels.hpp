@@ -62,6 +62,13 @@ int skinny_choose(const Problem& p);
 // one chunk per ring slot (1: no split)
 int skinny_split(int cfg, const Problem& p);
 LaunchFn skinny_launcher(int cfg, const Problem& p);
+// one unit per (input, output) format pair (gemm_skinny_<in>_<out>.hip)
+LaunchFn skinny_launcher_f16_f16(int cfg, int epi);
+LaunchFn skinny_launcher_f16_f32(int cfg, int epi);
+LaunchFn skinny_launcher_f16_fp8(int cfg, int epi);
+LaunchFn skinny_launcher_bf16_bf16(int cfg, int epi);
+LaunchFn skinny_launcher_bf16_f32(int cfg, int epi);
+LaunchFn skinny_launcher_bf16_fp8(int cfg, int epi);
 
 // ---- cache eviction for cold-cache timing (flush.hip) ------------------------
 // Bytes of the scratch buffer flush_caches reads: twice the 256 MB
