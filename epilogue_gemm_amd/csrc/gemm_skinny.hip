@@ -36,12 +36,17 @@ bool skinny_supports(int cfg, const Problem& p) {
   // multiples of 8); 32 rows of B and all of A must be addressable by one
   // buffer resource
   // (row-major B: the workgroup's buffer spans all K rows, K ldb 2 < 2^32)
+  // A column-major B takes any N and any ldc: with N % 8 != 0 or N < 32
+  // the last workgroup is not shifted back but masked past N, and a quad of
+  // outputs that reaches past N, or rows of C not 4-element aligned, are
+  // stored element by element.  A row-major B keeps N % 8 = 0, N >= the
+  // workgroup's columns and 16-byte rows of C.
   const SkinnyConfig& c = kSkinny[cfg];
-  const bool b_ok = c.brow ? p.lb == GEMM_EPI_ROW_MAJOR && p.K * p.ldb * 2 < ((int64_t)1 << 32)
-                           : p.lb == GEMM_EPI_COL_MAJOR && 32 * p.ldb * 2 < ((int64_t)1 << 32);
-  return p.M >= 1 && p.M <= 32 && p.la == GEMM_EPI_ROW_MAJOR && b_ok && p.N >= c.cols && p.N % 8 == 0 && p.K % 8 == 0 &&
-         (p.K + c.kc - 1) / c.kc >= c.stages && p.lda % 8 == 0 && p.ldb % 8 == 0 && p.ldc % 8 == 0 &&
-         p.M * p.lda * 2 < ((int64_t)1 << 32);
+  const bool b_ok = c.brow ? p.lb == GEMM_EPI_ROW_MAJOR && p.K * p.ldb * 2 < ((int64_t)1 << 32) && p.N >= c.cols &&
+                                 p.N % 8 == 0 && p.ldc % 8 == 0
+                           : p.lb == GEMM_EPI_COL_MAJOR && 32 * p.ldb * 2 < ((int64_t)1 << 31);
+  return p.M >= 1 && p.M <= 32 && p.la == GEMM_EPI_ROW_MAJOR && b_ok && p.N >= 1 && p.K % 8 == 0 &&
+         (p.K + c.kc - 1) / c.kc >= c.stages && p.lda % 8 == 0 && p.ldb % 8 == 0 && p.M * p.lda * 2 < ((int64_t)1 << 32);
 }
 
 int skinny_split(int cfg, const Problem& p) {

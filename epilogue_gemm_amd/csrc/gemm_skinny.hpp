@@ -116,7 +116,12 @@ __device__ __forceinline__ void arrive() {
   asm volatile("" ::: "memory");
 }
 
-template <typename TIn, typename TOut, int NW, int P, int KC, int EPI, bool BROW, int CW, int BPOL>
+// RAG (column-major B only): N % 8 != 0, N < 32 or rows of C not 4-element
+// aligned -- the last workgroup masked past N instead of shifted back, and
+// outputs past N or on unaligned rows handled element by element.  A launch
+// takes the plain form whenever it can, so that its code is as without
+// these cases.
+template <typename TIn, typename TOut, int NW, int P, int KC, int EPI, bool BROW, int CW, int BPOL, bool RAG>
 __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const TIn* __restrict__ A, const TIn* __restrict__ B,
                                                               const TIn* __restrict__ bias, TOut* __restrict__ C,
                                                               int M, int N, int K, int lda, int ldb, int ldc,
@@ -150,8 +155,12 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const TIn* __restr
   // another chunk), so its fp32 sums of them may differ in the last bit:
   // it stores only the columns from n_own on, which no other workgroup
   // writes.  (n0 is a multiple of 8, n_own of 32, so an output quad lies
-  // wholly on one side.)
-  const int n0 = min((int)blockIdx.x * CW, N - CW);
+  // wholly on one side.)  With N % 8 != 0 or N < 32 (column-major B) the
+  // last workgroup is not shifted: B's rows past N load as zeros, and
+  // outputs, bias, scale and residual past N are neither read nor stored.
+  static_assert(!(RAG && BROW), "row-major B: N % 8 = 0 and N >= CW");
+  constexpr bool shift = !RAG;
+  const int n0 = shift ? min((int)blockIdx.x * CW, N - CW) : (int)blockIdx.x * CW;
   const int n_own = (int)blockIdx.x * CW;
   const int hc = wave / NWH, wi = wave % NWH;  // column half, wave within it
   // Split K (part != NULL): workgroup (b, s) of the gridDim.y splits takes
@@ -197,6 +206,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const TIn* __restr
   // is what turns rows past M into zeros.
   // kz: byte offset of the lane's 16-byte chunk within its row segment.
   uint32_t vb[ND], sb[ND], vas[ND], kz[ND];  // (ND = NDA)
+  bool bmask[ND];
 #pragma unroll
   for (int d = 0; d < ND; ++d) {
     const int t = wave * ND + d;
@@ -205,6 +215,10 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const TIn* __restr
     const int r0 = (1024 * t) / RB;  // first row of the instruction (wave-uniform)
     kz[d] = (uint32_t)((p ^ (r & 15)) << 4);
     vb[d] = (uint32_t)(r - r0) * row_bytes + kz[d];
+    // rows past N (unshifted last workgroup): past the buffer's range, in
+    // every chunk
+    bmask[d] = RAG && n0 + r >= N;
+    if (bmask[d]) vb[d] = 0xFFFFFFF0u;
     sb[d] = (uint32_t)r0 * row_bytes;
     vas[d] = (uint32_t)r * a_row_bytes + kz[d];
   }
@@ -255,7 +269,8 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const TIn* __restr
       if constexpr (!BROW) {
 #pragma unroll
         for (int d = 0; d < ND; ++d)
-          load_lds16<BPOL>(rb, slot[j] + (wave * ND + d) * 1024, kz[d] < pad2 ? 0xFFFFFFF0u : vb[d] - pad2, sb[d]);
+          load_lds16<BPOL>(rb, slot[j] + (wave * ND + d) * 1024,
+                           kz[d] < pad2 || bmask[d] ? 0xFFFFFFF0u : vb[d] - pad2, sb[d]);
       }
 #pragma unroll
       for (int d = 0; d < ND; ++d)
@@ -308,7 +323,20 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const TIn* __restr
   const int oq = tid & (CW / 4 - 1);  // this thread's column quad
   u32x2 bias_q = u32x2{0u, 0u};
   if constexpr (epi_has_bias<EPI>())
-    if (tid < NG) bias_q = *(const u32x2*)(bias + n0 + 4 * oq);
+    if (tid < NG) {
+      const int nb = n0 + 4 * oq;
+      if (!RAG || nb + 4 <= N) {
+        bias_q = *(const u32x2*)(bias + nb);
+      } else {
+        // a quad reaching past N (unshifted last workgroup): element by element
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (nb + e < N) {
+            const uint32_t v = bits16(bias[nb + e]);
+            bias_q[e >> 1] |= (e & 1) ? (v << 16) : v;
+          }
+      }
+    }
   __builtin_amdgcn_sched_barrier(0);
 
   // Chunk c lives in slot (c + off) % P, so that the last P chunks sit in
@@ -407,6 +435,26 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const TIn* __restr
   auto finish = [&](int om, f32x4 z) __attribute__((always_inline)) {
     const int n = n0 + 4 * oq;
     if (n < n_own) return;
+    if constexpr (RAG) {
+      if (n >= N) return;
+    }
+    if (RAG && (n + 4 > N || (ldc & 3) != 0)) {
+      // a quad reaching past N, or rows of C not 4-element aligned:
+      // element by element
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (n + e >= N) break;
+        float b = 0.0f;
+        if constexpr (epi_has_bias<EPI>())
+          b = to_f32(__builtin_bit_cast(TIn, (uint16_t)((e & 1) ? (bias_q[e >> 1] >> 16) : (bias_q[e >> 1] & 0xffffu))));
+        const float s = scale ? scale[n + e] : 1.0f;
+        const float rv = res ? out_to_f32(res[(int64_t)om * ldc + n + e]) : 0.0f;
+        const float v = epilogue_ex<EPI>(z[e], b, scale != nullptr, s, res != nullptr, rv, out_scale != nullptr,
+                                         out_scale ? *out_scale : 1.0f);
+        C[(int64_t)om * ldc + n + e] = from_f32<TOut>(v);
+      }
+      return;
+    }
     f32x4 sc = f32x4{1.0f, 1.0f, 1.0f, 1.0f}, r = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     if (scale) sc = *(const f32x4*)(scale + n);
     if (res) r = load4<TOut>(res + (int64_t)om * ldc + n);
@@ -495,15 +543,24 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const TIn* __restr
 
 template <typename TIn, typename TOut, int NW, int P, int KC, int EPI, bool BROW, int CW, int BPOL>
 hipError_t launch_skinny(const LaunchArgs& a) {
+  const bool rag = !BROW && (a.N % 8 != 0 || a.N < CW || a.ldc % 4 != 0);
   // split K when the caller gave a workspace: partial blocks, then one
   // arrival counter per column block
   const int nblocks = (a.N + CW - 1) / CW;
   float* part = a.split > 1 ? (float*)a.workspace : nullptr;
   unsigned* arrivals = a.split > 1 ? (unsigned*)((char*)a.workspace + (size_t)nblocks * a.split * (128 * CW)) : nullptr;
-  hipLaunchKernelGGL((gemm_skinny_kernel<TIn, TOut, NW, P, KC, EPI, BROW, CW, BPOL>), dim3(nblocks, a.split > 1 ? a.split : 1),
-                     dim3(NW * 64), 0, a.stream, (const TIn*)a.A, (const TIn*)a.B, (const TIn*)a.bias, (TOut*)a.C,
-                     a.M, a.N, a.K, a.lda, a.ldb, a.ldc, part, arrivals, a.scale, (const TOut*)a.residual,
-                     a.out_scale);
+  const dim3 grid(nblocks, a.split > 1 ? a.split : 1), block(NW * 64);
+  if constexpr (!BROW) {
+    if (rag) {
+      hipLaunchKernelGGL((gemm_skinny_kernel<TIn, TOut, NW, P, KC, EPI, BROW, CW, BPOL, true>), grid, block, 0,
+                         a.stream, (const TIn*)a.A, (const TIn*)a.B, (const TIn*)a.bias, (TOut*)a.C, a.M, a.N, a.K,
+                         a.lda, a.ldb, a.ldc, part, arrivals, a.scale, (const TOut*)a.residual, a.out_scale);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((gemm_skinny_kernel<TIn, TOut, NW, P, KC, EPI, BROW, CW, BPOL, false>), grid, block, 0, a.stream,
+                     (const TIn*)a.A, (const TIn*)a.B, (const TIn*)a.bias, (TOut*)a.C, a.M, a.N, a.K, a.lda, a.ldb,
+                     a.ldc, part, arrivals, a.scale, (const TOut*)a.residual, a.out_scale);
   return hipGetLastError();
 }
 

@@ -127,10 +127,12 @@ gemm_epi_status gemm_epi_plan(gemm_epi_plan_t* out, int64_t M, int64_t N, int64_
  * of M x K, so >= K; column-major: columns, >= M); ldb likewise for B
  * (row-major >= N, column-major >= K); ldc between rows of C (>= N), which
  * a residual (gemm_epi_run_ex) shares.  0 keeps the packed value.  The
- * kernel is chosen again: the fast kernels need every leading dimension a
- * multiple of 8 elements (ldc of 16 for FP8_E4M3 output in the tile
- * kernels), else the generic kernel runs.  Padding between rows is never
- * read or written.  Host only.
+ * kernel is chosen again: the fast kernels need lda and ldb multiples of 8
+ * elements and, save the decode-shape kernel with a column-major B (M <=
+ * 32, any ldc), ldc too (16 for FP8_E4M3 output in the tile kernels), else
+ * the generic kernel runs.  Padding between rows is never written; a fast
+ * kernel may read A's or B's padding up to the next multiple of 8
+ * elements of a row, which enters no stored output.  Host only.
  * Errors: INVALID_ARG (NULL plan, a leading dimension below its minimum),
  * UNSUPPORTED (an operand then spans 2^31 elements or more); the plan is
  * unchanged on error. */

@@ -153,6 +153,9 @@ def test_fp8_output_needs_16_columns_in_tile_kernels(lib):
     (32, 8192, 8200, "row", "col", "skinny", "skinny_32n_8w_5x256k"),  # 33 chunks of 256, the first padded
     (32, 8192, 8320, "row", "col", "skinny", "skinny_32n_4w_8x128k"),  # whole chunks of 128 come first
     (32, 8192, 8196, "row", "col", "generic", "generic"),  # K not a multiple of 8
+    (32, 50257, 4096, "row", "col", "skinny", "skinny_32n_8w_5x256k"),  # N % 8 != 0: last workgroup masked
+    (8, 13, 256, "row", "col", "skinny", "skinny_32n_2w_2x128k"),  # N below the workgroup's 32 columns
+    (32, 50257, 4096, "row", "row", "generic", "generic"),  # packed row-major B: ldb = 50257, unaligned rows
     (32, 8192, 8192, "row", "row", "skinny", "skinny_rowb_64n_8w_6x128k"),  # N-contiguous B: transposing LDS reads
     (32, 4096, 1152, "row", "row", "skinny", "skinny_rowb_64n_8w_6x128k"),  # nine chunks of 128
     (32, 40, 1152, "row", "row", "skinny", "skinny_rowb_32n_4w_8x128k"),  # N < 64: 32-column workgroups
