@@ -58,13 +58,17 @@ bool tile_supports(int cfg, const Problem& p) {
                      (p.lb == GEMM_EPI_ROW_MAJOR && (p.K + 64) * p.ldb * 2 >= ((int64_t)1 << 32))))
     return false;
   // The ring configurations also take M and N below the tile (masked), K
-  // <= 64, and with A column-major any M (the last tile row masked); the
-  // chunk count must be a multiple of the slot count, save for two slots,
-  // which take any.
+  // <= 64, with A column-major any M (the last tile row masked), and any N
+  // and ldc (the last tile column masked, edge outputs element by element);
+  // the chunk count must be a multiple of the slot count, save for two
+  // slots, which take any.
   const int64_t chunks = (p.K + 63) / 64;
-  if (c.ring > 0)
-    return p.M >= 1 && p.N >= n_align && p.N % n_align == 0 && p.K >= 8 && p.K % 8 == 0 &&
-           (chunks % c.ring == 0 || c.ring == 2) && p.lda % 8 == 0 && p.ldb % 8 == 0 && p.ldc % n_align == 0;
+  if (c.ring > 0) {
+    const int out_bytes = p.out_dt == GEMM_EPI_F32 ? 4 : p.out_dt == GEMM_EPI_FP8_E4M3 ? 1 : 2;
+    if (c.ring == 8 && ring_ragged(p.N, p.ldc, out_bytes, p.lb == GEMM_EPI_ROW_MAJOR)) return false;
+    return p.M >= 1 && p.N >= 1 && p.K >= 8 && p.K % 8 == 0 && (chunks % c.ring == 0 || c.ring == 2) &&
+           p.lda % 8 == 0 && p.ldb % 8 == 0;
+  }
   return p.M >= c.bm && p.N >= c.bn && p.N % n_align == 0 && (p.la == GEMM_EPI_ROW_MAJOR || p.M % 8 == 0) &&
          p.K % 8 == 0 && p.K > 64 && p.lda % 8 == 0 && p.ldb % 8 == 0 && p.ldc % n_align == 0;
 }

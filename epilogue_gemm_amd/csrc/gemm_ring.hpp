@@ -43,7 +43,9 @@
 // with the same k order, so with identical values); a problem with fewer
 // than 64 rows or columns takes one tile there, masked past the end.  With
 // A column-major the last tile row is not shifted (its first row would not
-// fall on a 16-byte chunk when M % 8 != 0) but masked past M.  (Pipelined tile copies and block rasterisation:
+// fall on a 16-byte chunk when M % 8 != 0) but masked past M; likewise the
+// last tile column when N % 8 != 0 or C's rows are not 16-byte aligned
+// (RAG), whose edge outputs the epilogue then handles element by element.  (Pipelined tile copies and block rasterisation:
 // atlascloud.ai "Writing high-performance kernels in TileLang", section
 // "Écrivons un GEMM"; epilogue on the accumulator fragment: csdn
 // "从零开始学习 TileLang" ch.10 sec. 10.8; small problems that leave the
@@ -139,7 +141,7 @@ struct RowBLoader {
   }
 };
 
-template <typename TIn, typename TOut, int EPI, bool BROW, int P, bool ACOL>
+template <typename TIn, typename TOut, int EPI, bool BROW, int P, bool ACOL, bool RAG>
 __global__ __launch_bounds__(kNW * 64) void gemm_ring_kernel(const TIn* __restrict__ A, const TIn* __restrict__ B,
                                                              const TIn* __restrict__ bias, TOut* __restrict__ C,
                                                              int M, int N, int K, int tiles_m, int tiles_n, int panel,
@@ -160,7 +162,7 @@ __global__ __launch_bounds__(kNW * 64) void gemm_ring_kernel(const TIn* __restri
   // nothing and storing nothing (MASK below); a column-major A keeps its
   // last tile row in place, masked past M.
   const int m0 = ACOL ? tm * kTile : max(0, min(tm * kTile, M - kTile));
-  const int n0 = max(0, min(tn * kTile, N - kTile));
+  const int n0 = RAG ? tn * kTile : max(0, min(tn * kTile, N - kTile));
   const int kpad = (-K) & (kBK - 1);
   const int nchunks = (K + kpad) / kBK;
 
@@ -292,7 +294,10 @@ __global__ __launch_bounds__(kNW * 64) void gemm_ring_kernel(const TIn* __restri
   static_assert(32 * 32 * sizeof(TOut) <= (size_t)kOpBytes / 2, "staging area");
   const f32x16 accs[1][1] = {{acc}};
   const int mw = m0 + 32 * wm, nw = n0 + 32 * wn;
-  if (M < kTile || N < kTile || (ACOL && M % kTile != 0))
+  if constexpr (RAG)
+    tile::write_tile<32, 32, TIn, TOut, EPI, true, true, true>(accs, bias, C, ldc, mw, nw, lane, stage_w, scale, res,
+                                                               out_scale, M, N);
+  else if (M < kTile || N < kTile || (ACOL && M % kTile != 0))
     tile::write_tile<32, 32, TIn, TOut, EPI, true, true>(accs, bias, C, ldc, mw, nw, lane, stage_w, scale, res,
                                                          out_scale, M, N);
   else if (scale != nullptr || res != nullptr || out_scale != nullptr)
@@ -306,8 +311,20 @@ template <typename TIn, typename TOut, int EPI, bool BROW, int P, bool ACOL>
 hipError_t launch(const LaunchArgs& a) {
   const int tiles_m = (a.M + kTile - 1) / kTile, tiles_n = (a.N + kTile - 1) / kTile;
   const int panel = tiles_m < 4 ? tiles_m : 4;
-  hipLaunchKernelGGL((gemm_ring_kernel<TIn, TOut, EPI, BROW, P, ACOL>), dim3(tiles_m * tiles_n), dim3(kNW * 64), 0,
-                     a.stream, (const TIn*)a.A, (const TIn*)a.B, (const TIn*)a.bias, (TOut*)a.C, a.M, a.N, a.K,
+  // N or ldc off the 16-byte output chunks (or, row-major B, N off its
+  // 8-column chunks): the masked instance (not built for eight slots, which
+  // the plan does not offer for these problems: see ring_ragged)
+  if constexpr (P != 8) {
+    if (ring_ragged(a.N, a.ldc, (int)sizeof(TOut), BROW)) {
+      hipLaunchKernelGGL((gemm_ring_kernel<TIn, TOut, EPI, BROW, P, ACOL, true>), dim3(tiles_m * tiles_n),
+                         dim3(kNW * 64), 0, a.stream, (const TIn*)a.A, (const TIn*)a.B, (const TIn*)a.bias,
+                         (TOut*)a.C, a.M, a.N, a.K, tiles_m, tiles_n, panel, a.lda, a.ldb, a.ldc, a.scale,
+                         (const TOut*)a.residual, a.out_scale);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((gemm_ring_kernel<TIn, TOut, EPI, BROW, P, ACOL, false>), dim3(tiles_m * tiles_n), dim3(kNW * 64),
+                     0, a.stream, (const TIn*)a.A, (const TIn*)a.B, (const TIn*)a.bias, (TOut*)a.C, a.M, a.N, a.K,
                      tiles_m, tiles_n, panel, a.lda, a.ldb, a.ldc, a.scale, (const TOut*)a.residual, a.out_scale);
   return hipGetLastError();
 }

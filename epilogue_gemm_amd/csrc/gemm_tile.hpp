@@ -235,7 +235,10 @@ __device__ __forceinline__ void raster(int bid, int tiles_m, int tiles_n, int pa
 // operands nor stored, and the bias, scale and residual past them are not
 // read.  (16-byte output chunks lie wholly on one side: n_lim is a multiple
 // of 8, of 16 for 1-byte outputs.)
-template <int WM, int WN, typename TIn, typename TOut, int EPI, bool EXTRAS, bool MASK = false>
+// RAGC (with MASK): n_lim any, and ldc any: groups of four columns and
+// 16-byte output chunks that reach past n_lim, or rows of C whose chunks
+// are not 16-byte aligned, are read and stored element by element.
+template <int WM, int WN, typename TIn, typename TOut, int EPI, bool EXTRAS, bool MASK = false, bool RAGC = false>
 __device__ __forceinline__ void write_tile(const f32x16 (&acc)[WM / 32][WN / 32], const TIn* __restrict__ bias,
                                           TOut* __restrict__ C, int ldc, int m_w, int n_w, int lane, char* stage,
                                           const float* __restrict__ scale, const TOut* __restrict__ res,
@@ -256,8 +259,17 @@ __device__ __forceinline__ void write_tile(const f32x16 (&acc)[WM / 32][WN / 32]
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       if constexpr (epi_has_bias<EPI>()) {
-        if (!MASK || n_w + j * 32 + 8 * q + 4 * h < n_lim) bq[j][q] = *(const u32x2*)(bias + n_w + j * 32 + 8 * q + 4 * h);
-        else bq[j][q] = u32x2{0u, 0u};
+        const int col = n_w + j * 32 + 8 * q + 4 * h;
+        if (!MASK || (RAGC ? col + 4 <= n_lim : col < n_lim)) {
+          bq[j][q] = *(const u32x2*)(bias + col);
+        } else {
+          bq[j][q] = u32x2{0u, 0u};
+          if constexpr (RAGC) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (col + e < n_lim) bq[j][q][e >> 1] |= (uint32_t)bits16(bias[col + e]) << (16 * (e & 1));
+          }
+        }
       } else {
         bq[j][q] = u32x2{0u, 0u};
       }
@@ -273,9 +285,28 @@ __device__ __forceinline__ void write_tile(const f32x16 (&acc)[WM / 32][WN / 32]
         const int col = n_w + j * 32 + 8 * q + 4 * h;
         f32x4 sc = f32x4{1.0f, 1.0f, 1.0f, 1.0f}, r = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
         if constexpr (EXTRAS) {
-          const bool in = !MASK || (col < n_lim && m_w + i * 32 + m_l < m_lim);
-          if (scale && in) sc = *(const f32x4*)(scale + col);
-          if (res && in) r = load4<TOut>(res + (int64_t)(m_w + i * 32 + m_l) * ldc + col);
+          const int row = m_w + i * 32 + m_l;
+          if constexpr (RAGC) {
+            // whole groups of four on 4-element aligned rows as vectors,
+            // the others element by element
+            if (row < m_lim && col < n_lim) {
+              const bool whole = col + 4 <= n_lim;
+              const int64_t at = (int64_t)row * ldc + col;
+              const bool rvec = whole && (at & 3) == 0;  // the residual's four on one aligned vector
+              if (scale && whole) sc = *(const f32x4*)(scale + col);
+              if (res && rvec) r = load4<TOut>(res + at);
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                if (col + e < n_lim) {
+                  if (scale && !whole) sc[e] = scale[col + e];
+                  if (res && !rvec) r[e] = out_to_f32(res[at + e]);
+                }
+            }
+          } else {
+            const bool in = !MASK || (col < n_lim && row < m_lim);
+            if (scale && in) sc = *(const f32x4*)(scale + col);
+            if (res && in) r = load4<TOut>(res + (int64_t)row * ldc + col);
+          }
         }
         float v[4];
 #pragma unroll
@@ -310,8 +341,27 @@ __device__ __forceinline__ void write_tile(const f32x16 (&acc)[WM / 32][WN / 32]
     for (int t = 0; t < 32 / RPI; ++t) {
       const int r = t * RPI + lane / CPR, c = lane % CPR;
       const u32x4 d = *(const u32x4*)(stage + r * (WN * OSZ) + ((c ^ (r & SWM)) << 4));
-      if (!MASK || (m_w + i * 32 + r < m_lim && n_w + c * (16 / OSZ) < n_lim))
+      if constexpr (RAGC) {
+        constexpr int EPC = 16 / OSZ;  // outputs per chunk
+        const int row = m_w + i * 32 + r, col0 = n_w + c * EPC;
+        if (row < m_lim && col0 < n_lim) {
+          const int64_t at = (int64_t)row * ldc + col0;
+          TOut* dst = C + at;
+          if (col0 + EPC <= n_lim && at % EPC == 0) {
+            *(u32x4*)dst = d;
+          } else {
+#pragma unroll
+            for (int e = 0; e < EPC; ++e)
+              if (col0 + e < n_lim) {
+                if constexpr (OSZ == 2) ((uint16_t*)dst)[e] = (uint16_t)(d[e >> 1] >> (16 * (e & 1)));
+                else if constexpr (OSZ == 4) ((uint32_t*)dst)[e] = d[e];
+                else ((uint8_t*)dst)[e] = (uint8_t)(d[e >> 2] >> (8 * (e & 3)));
+              }
+          }
+        }
+      } else if (!MASK || (m_w + i * 32 + r < m_lim && n_w + c * (16 / OSZ) < n_lim)) {
         *(u32x4*)((char*)(C + (int64_t)(m_w + i * 32 + r) * ldc + n_w) + c * 16) = d;
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
   }

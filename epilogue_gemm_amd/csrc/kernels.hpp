@@ -29,6 +29,13 @@ struct TileConfig {
   bool brow;   // 16x16x32 only: B row-major (transposing LDS reads) instead of column-major
 };
 int tile_num_configs();
+// A ring problem whose N or ldc is off the 16-byte output chunks (or, with
+// a row-major B, N off its 8-column chunks): the ring kernels then mask
+// their last tile column (two and four slots only).
+inline bool ring_ragged(int64_t N, int64_t ldc, int out_bytes, bool brow) {
+  const int epc = 16 / out_bytes;
+  return N % epc != 0 || ldc % epc != 0 || (brow && N % 8 != 0);
+}
 const TileConfig& tile_config(int cfg);
 bool tile_supports(int cfg, const Problem& p);
 int tile_choose(const Problem& p);  // -1 when no config fits

@@ -128,11 +128,14 @@ def test_run_ex_rejects_invalid_arguments_without_touching_the_device(lib):
         gb.gemm_epi_destroy(h)
 
 
-def test_fp8_output_needs_16_columns_in_tile_kernels(lib):
-    for N, want in ((528, "tile"), (520, "generic")):
+def test_fp8_output_off_16_columns_takes_the_masked_ring(lib):
+    # FP8 rows of C in 16-byte chunks: with N % 16 != 0 the ring kernel
+    # masks its last tile column (both take the ring here: 16 x 9 tiles
+    # of 64)
+    for N, want in ((528, "tile_64x64_ring4"), (520, "tile_64x64_ring4")):
         h = gb.gemm_epi_plan(1024, N, 256, "bf16", "fp8", "row", "col", "none")
         try:
-            assert gb.gemm_epi_plan_describe(h)[0] == want, N
+            assert gb.gemm_epi_plan_describe(h)[2] == want, N
         finally:
             gb.gemm_epi_destroy(h)
 
@@ -166,7 +169,7 @@ def test_fp8_output_needs_16_columns_in_tile_kernels(lib):
     (3000, 2000, 4096, "row", "row", "tile", "tile_128x128x64"),  # 24 x 16 tiles of 128
     (1000, 1000, 1024, "col", "col", "tile", "tile_64x64_ring4"),  # column-major A through transposing reads
     (1001, 1000, 1024, "col", "col", "generic", "generic"),  # packed column-major A: lda = 1001, unaligned
-    (1000, 1004, 1024, "row", "col", "generic", "generic"),  # N % 8
+    (1000, 1004, 1024, "row", "col", "tile", "tile_64x64_ring4"),  # N % 8 != 0: last tile column masked
     (37, 53, 29, "row", "row", "generic", "generic"),
     (256, 256, 100, "col", "row", "generic", "generic"),  # K not a multiple of 8
     (1024, 1024, 1000, "row", "col", "tile", "tile_64x64_ring4"),  # K % 64 = 40: a partial first chunk
@@ -190,6 +193,25 @@ def test_auto_selection(lib, M, N, K, la, lb, want_kernel, want_name):
     try:
         kern, cfg, name = gb.gemm_epi_plan_describe(h)
         assert (kern, name) == (want_kernel, want_name)
+    finally:
+        gb.gemm_epi_destroy(h)
+
+
+def test_eight_slot_ring_refuses_ragged_columns(lib):
+    # the masked ring instance exists for two and four slots only
+    for N, ldc in ((77, 0), (256, 260)):
+        h = gb.gemm_epi_plan(256, N, 512, "bf16", "bf16", "row", "col", "none")
+        try:
+            if ldc:
+                assert gb.gemm_epi_plan_set_ld(h, 0, 0, ldc) == 0
+            assert gb.gemm_epi_plan_select(h, "tile", 5) == 2
+            assert gb.gemm_epi_plan_select(h, "tile", 6) == 0
+            assert gb.gemm_epi_plan_select(h, "tile", 7) == 0
+        finally:
+            gb.gemm_epi_destroy(h)
+    h = gb.gemm_epi_plan(256, 256, 512, "bf16", "bf16", "row", "col", "none")
+    try:
+        assert gb.gemm_epi_plan_select(h, "tile", 5) == 0
     finally:
         gb.gemm_epi_destroy(h)
 

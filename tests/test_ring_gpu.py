@@ -202,3 +202,46 @@ def test_ring_col_a_random_tolerance(config, lb):
             bits = inputs.make_inputs(M, N, K, in_dt, "col", lb, epi.startswith("bias"), float(np.sqrt(K)), 0.1,
                                       seed=M + K + 1)
             assert check_case(bits, M, N, K, in_dt, in_dt, "col", lb, epi, "tile", config, False) == name
+
+
+# ---------------------------------------------------------------------------
+# N off the 16-byte output chunks (or a row-major B's 8-column chunks), or
+# rows of C not 16-byte aligned: the ring kernels (two and four slots) mask
+# their last tile column instead of shifting it back, and the epilogue
+# reads bias, scale and residual and stores C element by element where a
+# group reaches past N or a row is unaligned
+# ---------------------------------------------------------------------------
+
+def _pads_ragged(M, N, K, la, lb, pc):
+    """Paddings that keep A's and B's leading dimensions multiples of 8."""
+    pa = ((-M) % 8 + 8) if la == "col" else 8
+    pb = ((-N) % 8 + 8) if lb == "row" else 16
+    return (pa, pb, pc)
+
+
+@pytest.mark.parametrize("config", [6, 7])
+@pytest.mark.parametrize("la", ["row", "col"])
+@pytest.mark.parametrize("lb", LBS)
+@pytest.mark.parametrize("M,N,ldc_pad", [(100, 77, 3), (130, 1004, 0), (33, 13, 0), (70, 200, 4), (64, 129, 15)])
+def test_ring_ragged_n_bitexact(config, la, lb, M, N, ldc_pad):
+    name, P = RINGS[config]
+    K = _k(P, 1, 24)
+    for in_dt, out_dt, epi, extras in (("bf16", "bf16", "bias_relu", False), ("f16", "f32", "relu", True),
+                                       ("f16", "f16", "bias", True)):
+        assert run_strided(M, N, K, in_dt, out_dt, la, lb, epi, _pads_ragged(M, N, K, la, lb, ldc_pad), "tile",
+                           config, extras, extra_rows=64) == name
+    # FP8 output: rows of C in 16-byte chunks of 16 outputs
+    assert run_strided(M, N, K, "bf16", "fp8", la, lb, "bias_relu", _pads_ragged(M, N, K, la, lb, ldc_pad), "tile",
+                       config, True, extra_rows=64) == name
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 1001, 512), (512, 5003, 256), (48, 77, 1000)])
+def test_ring_ragged_n_packed_auto(M, N, K):
+    # packed C of odd width: the automatic plan takes a masked ring
+    for in_dt, out_dt, epi in (("bf16", "bf16", "bias_gelu"), ("f16", "f32", "bias")):
+        bits = inputs.integer_inputs(M, N, K, in_dt, "row", "col", True, seed=N + M)
+        name = check_case(bits, M, N, K, in_dt, out_dt, "row", "col", epi, "auto", -1, epi != "bias_gelu")
+        assert name.startswith("tile_64x64_ring"), name
+    # a row-major B of odd width needs a padded ldb: through the strided path
+    assert run_strided(M, N, K, "bf16", "bf16", "row", "row", "bias_relu", (8, (-N) % 8 + 8, 0), "auto", -1,
+                       False).startswith("tile_64x64_ring")
