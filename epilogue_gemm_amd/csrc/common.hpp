@@ -165,6 +165,16 @@ __device__ __forceinline__ uint16_t bits16(T x) {
   return __builtin_bit_cast(uint16_t, x);
 }
 
+// Two outputs in a 16-bit format, rounded to nearest even and packed (a
+// in the low half): one v_cvt_pk_{f16,bf16}_f32 for the pair, the same
+// rounding as two single conversions.
+template <typename TOut>
+__device__ __forceinline__ uint32_t pack2_out(float a, float b) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  typedef TOut t2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2){a, b}, t2));
+}
+
 // Four consecutive outputs of one row -> one vector store.
 template <typename TOut>
 __device__ __forceinline__ void store4(TOut* p, float v0, float v1, float v2, float v3) {
@@ -173,10 +183,7 @@ __device__ __forceinline__ void store4(TOut* p, float v0, float v1, float v2, fl
   } else if constexpr (sizeof(TOut) == 4) {
     *reinterpret_cast<f32x4*>(p) = f32x4{v0, v1, v2, v3};
   } else {
-    u32x2 w;
-    w.x = (uint32_t)bits16(from_f32<TOut>(v0)) | ((uint32_t)bits16(from_f32<TOut>(v1)) << 16);
-    w.y = (uint32_t)bits16(from_f32<TOut>(v2)) | ((uint32_t)bits16(from_f32<TOut>(v3)) << 16);
-    *reinterpret_cast<u32x2*>(p) = w;
+    *reinterpret_cast<u32x2*>(p) = u32x2{pack2_out<TOut>(v0, v1), pack2_out<TOut>(v2, v3)};
   }
 }
 

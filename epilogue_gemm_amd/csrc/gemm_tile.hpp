@@ -329,9 +329,7 @@ __device__ __forceinline__ void write_tile(const f32x16 (&acc)[WM / 32][WN / 32]
           *(f32x4*)(stage + m_l * (WN * 4) + ((c ^ (m_l & SWM)) << 4)) = f32x4{v[0], v[1], v[2], v[3]};
         } else {
           const int c = 4 * j + q;
-          u32x2 w;
-          w.x = (uint32_t)bits16(from_f32<TOut>(v[0])) | ((uint32_t)bits16(from_f32<TOut>(v[1])) << 16);
-          w.y = (uint32_t)bits16(from_f32<TOut>(v[2])) | ((uint32_t)bits16(from_f32<TOut>(v[3])) << 16);
+          const u32x2 w = u32x2{pack2_out<TOut>(v[0], v[1]), pack2_out<TOut>(v[2], v[3])};
           *(u32x2*)(stage + m_l * (WN * 2) + ((c ^ (m_l & SWM)) << 4) + 8 * h) = w;
         }
       }

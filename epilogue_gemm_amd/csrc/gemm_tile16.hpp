@@ -126,12 +126,19 @@ __device__ __forceinline__ void write_tile16(const f32x4 (&acc)[WM / 16][WN / 16
   const bool has_os = EXTRAS && out_scale != nullptr;
   const float os = has_os ? *out_scale : 1.0f;
 
-  // bias of this lane's four columns in each 16-column block
-  u32x2 bq[TN];
+  // bias of this lane's four columns in each 16-column block, in fp32
+  // once (every row block reuses them)
+  f32x4 bq[TN];
 #pragma unroll
   for (int j = 0; j < TN; ++j) {
-    if constexpr (epi_has_bias<EPI>()) bq[j] = *(const u32x2*)(bias + n_w + j * 16 + 4 * g);
-    else bq[j] = u32x2{0u, 0u};
+    if constexpr (epi_has_bias<EPI>()) {
+      const u32x2 w = *(const u32x2*)(bias + n_w + j * 16 + 4 * g);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        bq[j][e] = to_f32(__builtin_bit_cast(TIn, (uint16_t)((e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xffffu))));
+    } else {
+      bq[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
   }
 
   static_for<TM>([&](auto i_c) __attribute__((always_inline)) {
@@ -146,15 +153,9 @@ __device__ __forceinline__ void write_tile16(const f32x4 (&acc)[WM / 16][WN / 16
       }
       float v[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float b = 0.0f;
-        if constexpr (epi_has_bias<EPI>()) {
-          const uint32_t w = bq[j][e >> 1];
-          b = to_f32(__builtin_bit_cast(TIn, (uint16_t)((e & 1) ? (w >> 16) : (w & 0xffffu))));
-        }
-        v[e] = epilogue_ex<EPI>(acc[i][j][e], b, EXTRAS && scale != nullptr, sc[e], EXTRAS && res != nullptr, r[e],
-                                has_os, os);
-      }
+      for (int e = 0; e < 4; ++e)
+        v[e] = epilogue_ex<EPI>(acc[i][j][e], bq[j][e], EXTRAS && scale != nullptr, sc[e], EXTRAS && res != nullptr,
+                                r[e], has_os, os);
       // columns j*16 + 4g .. +3 of row m_l
       if constexpr (OSZ == 1) {
         *(uint32_t*)(stage + m_l * WN + ((j ^ (m_l & SWM)) << 4) + 4 * g) = pack4_e4m3(v[0], v[1], v[2], v[3]);
@@ -163,9 +164,7 @@ __device__ __forceinline__ void write_tile16(const f32x4 (&acc)[WM / 16][WN / 16
         *(f32x4*)(stage + m_l * (WN * 4) + ((c ^ (m_l & SWM)) << 4)) = f32x4{v[0], v[1], v[2], v[3]};
       } else {
         const int c = 2 * j + (g >> 1);
-        u32x2 w;
-        w.x = (uint32_t)bits16(from_f32<TOut>(v[0])) | ((uint32_t)bits16(from_f32<TOut>(v[1])) << 16);
-        w.y = (uint32_t)bits16(from_f32<TOut>(v[2])) | ((uint32_t)bits16(from_f32<TOut>(v[3])) << 16);
+        const u32x2 w = u32x2{pack2_out<TOut>(v[0], v[1]), pack2_out<TOut>(v[2], v[3])};
         *(u32x2*)(stage + m_l * (WN * 2) + ((c ^ (m_l & SWM)) << 4) + 8 * (g & 1)) = w;
       }
     }
