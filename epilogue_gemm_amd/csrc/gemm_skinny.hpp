@@ -14,7 +14,9 @@
 //     there is no reduction across workgroups and bias and activation are
 //     applied exactly once (when N % 32 != 0 the last workgroup is shifted
 //     back to end at N: it also computes some of its neighbour's columns,
-//     in another k order, and stores only the columns it owns);
+//     in another k order, and stores only the columns it owns; with N % 8
+//     != 0, N < 32 or unaligned rows of C a second instance masks it past
+//     N instead, see RAG);
 //   - K is walked in chunks of KC values.  A chunk of B is 32 rows x KC
 //     k-values, and every row segment of it (2 KC bytes) is contiguous in
 //     memory: the NW waves copy it into one LDS ring slot with 128-bit
