@@ -69,8 +69,12 @@ bool tile_supports(int cfg, const Problem& p) {
     return p.M >= 1 && p.N >= 1 && p.K >= 8 && p.K % 8 == 0 && (chunks % c.ring == 0 || c.ring == 2) &&
            p.lda % 8 == 0 && p.ldb % 8 == 0;
   }
-  return p.M >= c.bm && p.N >= c.bn && p.N % n_align == 0 && (p.la == GEMM_EPI_ROW_MAJOR || p.M % 8 == 0) &&
-         p.K % 8 == 0 && p.K > 64 && p.lda % 8 == 0 && p.ldb % 8 == 0 && p.ldc % n_align == 0;
+  // The 16x16x32 configuration with a column-major B also takes any N
+  // and ldc: its last tile column is then masked, not shifted.
+  const bool any_n = c.mfma == 16 && !c.brow;
+  return p.M >= c.bm && p.N >= c.bn && (any_n || p.N % n_align == 0) &&
+         (p.la == GEMM_EPI_ROW_MAJOR || p.M % 8 == 0) && p.K % 8 == 0 && p.K > 64 && p.lda % 8 == 0 &&
+         p.ldb % 8 == 0 && (any_n || p.ldc % n_align == 0);
 }
 
 int tile_choose(const Problem& p) {
@@ -92,6 +96,10 @@ int tile_choose(const Problem& p) {
     fallback = c;
   }
   if (fallback == 0 && direct) return 4;
+  // N or ldc off the 16-byte output chunks leaves configurations 0-2; a
+  // problem of at least 256 tiles of 256 x 256 still takes the 16x16x32
+  // kernel, its last tile column masked
+  if (fallback < 0 && direct && ((p.M + 255) / 256) * ((p.N + 255) / 256) >= 256 && tile_supports(4, p)) return 4;
   // both operands n- or k-contiguous along their rows (A row-major, B
   // row-major): the 16x16x32 kernel with transposing reads of B
   if (fallback == 0 && tile_supports(8, p)) return 8;

@@ -112,11 +112,16 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
 // residual and output scale on the accumulators, conversion, then each
 // 16-row band through a private LDS staging area (16-byte chunks swizzled by
 // row) and out with 16-byte stores along rows.
-template <int WM, int WN, typename TIn, typename TOut, int EPI, bool EXTRAS>
+// RAGC: columns from n_lim on are not stored (the unshifted last tile
+// column of a problem whose N or ldc is off the 16-byte output chunks);
+// groups of four columns and 16-byte chunks that reach past n_lim, or lie
+// on a row that is not 16-byte aligned, are read and stored element by
+// element.
+template <int WM, int WN, typename TIn, typename TOut, int EPI, bool EXTRAS, bool RAGC = false>
 __device__ __forceinline__ void write_tile16(const f32x4 (&acc)[WM / 16][WN / 16], const TIn* __restrict__ bias,
                                             TOut* __restrict__ C, int ldc, int m_w, int n_w, int lane, char* stage,
                                             const float* __restrict__ scale, const TOut* __restrict__ res,
-                                            const float* __restrict__ out_scale) {
+                                            const float* __restrict__ out_scale, int n_lim = 0) {
   constexpr int TM = WM / 16, TN = WN / 16;
   constexpr int OSZ = (int)sizeof(TOut);
   constexpr int CPR = WN * OSZ / 16;              // 16-byte chunks per staged row
@@ -132,10 +137,16 @@ __device__ __forceinline__ void write_tile16(const f32x4 (&acc)[WM / 16][WN / 16
 #pragma unroll
   for (int j = 0; j < TN; ++j) {
     if constexpr (epi_has_bias<EPI>()) {
-      const u32x2 w = *(const u32x2*)(bias + n_w + j * 16 + 4 * g);
+      const int col = n_w + j * 16 + 4 * g;
+      if (!RAGC || col + 4 <= n_lim) {
+        const u32x2 w = *(const u32x2*)(bias + col);
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        bq[j][e] = to_f32(__builtin_bit_cast(TIn, (uint16_t)((e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xffffu))));
+        for (int e = 0; e < 4; ++e)
+          bq[j][e] = to_f32(__builtin_bit_cast(TIn, (uint16_t)((e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xffffu))));
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bq[j][e] = col + e < n_lim ? to_f32(bias[col + e]) : 0.0f;
+      }
     } else {
       bq[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     }
@@ -148,8 +159,24 @@ __device__ __forceinline__ void write_tile16(const f32x4 (&acc)[WM / 16][WN / 16
       const int col = n_w + j * 16 + 4 * g;
       f32x4 sc = f32x4{1.0f, 1.0f, 1.0f, 1.0f}, r = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
       if constexpr (EXTRAS) {
-        if (scale) sc = *(const f32x4*)(scale + col);
-        if (res) r = load4<TOut>(res + (int64_t)(m_w + i * 16 + m_l) * ldc + col);
+        if constexpr (RAGC) {
+          // whole groups of four on 4-element aligned rows as vectors, the
+          // others element by element
+          const bool whole = col + 4 <= n_lim;
+          const int64_t at = (int64_t)(m_w + i * 16 + m_l) * ldc + col;
+          const bool rvec = whole && (at & 3) == 0;
+          if (scale && whole) sc = *(const f32x4*)(scale + col);
+          if (res && rvec) r = load4<TOut>(res + at);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (col + e < n_lim) {
+              if (scale && !whole) sc[e] = scale[col + e];
+              if (res && !rvec) r[e] = out_to_f32(res[at + e]);
+            }
+        } else {
+          if (scale) sc = *(const f32x4*)(scale + col);
+          if (res) r = load4<TOut>(res + (int64_t)(m_w + i * 16 + m_l) * ldc + col);
+        }
       }
       float v[4];
 #pragma unroll
@@ -173,13 +200,36 @@ __device__ __forceinline__ void write_tile16(const f32x4 (&acc)[WM / 16][WN / 16
     for (int t = 0; t < 16 / RPI; ++t) {
       const int r = t * RPI + lane / CPR, c = lane % CPR;
       const u32x4 d = *(const u32x4*)(stage + r * (WN * OSZ) + ((c ^ (r & SWM)) << 4));
-      *(u32x4*)((char*)(C + (int64_t)(m_w + i * 16 + r) * ldc + n_w) + c * 16) = d;
+      if constexpr (RAGC) {
+        constexpr int EPC = 16 / OSZ;  // outputs per chunk
+        const int col0 = n_w + c * EPC;
+        if (col0 < n_lim) {
+          const int64_t at = (int64_t)(m_w + i * 16 + r) * ldc + col0;
+          TOut* dst = C + at;
+          if (col0 + EPC <= n_lim && at % EPC == 0) {
+            *(u32x4*)dst = d;
+          } else {
+#pragma unroll
+            for (int e = 0; e < EPC; ++e)
+              if (col0 + e < n_lim) {
+                if constexpr (OSZ == 2) ((uint16_t*)dst)[e] = (uint16_t)(d[e >> 1] >> (16 * (e & 1)));
+                else if constexpr (OSZ == 4) ((uint32_t*)dst)[e] = d[e];
+                else ((uint8_t*)dst)[e] = (uint8_t)(d[e >> 2] >> (8 * (e & 3)));
+              }
+          }
+        }
+      } else {
+        *(u32x4*)((char*)(C + (int64_t)(m_w + i * 16 + r) * ldc + n_w) + c * 16) = d;
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
   });
 }
 
-template <typename TIn, typename TOut, int EPI, bool BROW>
+// RAG (B column-major only): N or ldc off the 16-byte output chunks -- the
+// last tile column is not shifted back but masked past N (B's rows past N
+// load as zeros) and the epilogue handles its edge element by element.
+template <typename TIn, typename TOut, int EPI, bool BROW, bool RAG>
 __global__ __launch_bounds__(256) void gemm_tile16_kernel(const TIn* __restrict__ A, const TIn* __restrict__ B,
                                                           const TIn* __restrict__ bias, TOut* __restrict__ C, int M,
                                                           int N, int K, int tiles_m, int tiles_n, int panel, int lda,
@@ -208,8 +258,10 @@ __global__ __launch_bounds__(256) void gemm_tile16_kernel(const TIn* __restrict_
   int tm, tn;
   tile::raster(blockIdx.x, tiles_m, tiles_n, panel, tm, tn);
   // the last tile row or column is shifted back to end at M or N (it
-  // rewrites part of its neighbour with identical values)
-  const int m0 = min(tm * BM, M - BM), n0 = min(tn * BN, N - BN);
+  // rewrites part of its neighbour with identical values); RAG keeps the
+  // last tile column in place
+  static_assert(!(RAG && BROW), "row-major B: N % 8 = 0");
+  const int m0 = min(tm * BM, M - BM), n0 = RAG ? tn * BN : min(tn * BN, N - BN);
   const int kpad = (-K) & (kBK - 1);
 
   const DirectLoader<BM, NW, true> da(A, m0, M, lda, kpad, tid, wave);
@@ -365,20 +417,30 @@ __global__ __launch_bounds__(256) void gemm_tile16_kernel(const TIn* __restrict_
   static_assert(16 * WN * sizeof(TOut) <= (size_t)A_BYTES, "staging area");
   char* const stage_w = wave == 0 ? sA0 : wave == 1 ? sA1 : wave == 2 ? sB0 : sB1;
   if (scale != nullptr || res != nullptr || out_scale != nullptr)
-    write_tile16<WM, WN, TIn, TOut, EPI, true>(acc, bias, C, ldc, m0 + wm * WM, n0 + wn * WN, lane, stage_w, scale,
-                                               res, out_scale);
+    write_tile16<WM, WN, TIn, TOut, EPI, true, RAG>(acc, bias, C, ldc, m0 + wm * WM, n0 + wn * WN, lane, stage_w,
+                                                    scale, res, out_scale, N);
   else
-    write_tile16<WM, WN, TIn, TOut, EPI, false>(acc, bias, C, ldc, m0 + wm * WM, n0 + wn * WN, lane, stage_w,
-                                                nullptr, nullptr, nullptr);
+    write_tile16<WM, WN, TIn, TOut, EPI, false, RAG>(acc, bias, C, ldc, m0 + wm * WM, n0 + wn * WN, lane, stage_w,
+                                                     nullptr, nullptr, nullptr, N);
 }
 
 template <typename TIn, typename TOut, int EPI, bool BROW>
 hipError_t launch(const LaunchArgs& a) {
   const int tiles_m = (a.M + 255) / 256, tiles_n = (a.N + 255) / 256;
   const int panel = tiles_m < 4 ? tiles_m : 4;
-  hipLaunchKernelGGL((gemm_tile16_kernel<TIn, TOut, EPI, BROW>), dim3(tiles_m * tiles_n), dim3(256), 0, a.stream,
-                     (const TIn*)a.A, (const TIn*)a.B, (const TIn*)a.bias, (TOut*)a.C, a.M, a.N, a.K, tiles_m,
-                     tiles_n, panel, a.lda, a.ldb, a.ldc, a.scale, (const TOut*)a.residual, a.out_scale);
+  if constexpr (!BROW) {
+    constexpr int EPC = 16 / (int)sizeof(TOut);
+    if (a.N % EPC != 0 || a.ldc % EPC != 0) {
+      hipLaunchKernelGGL((gemm_tile16_kernel<TIn, TOut, EPI, BROW, true>), dim3(tiles_m * tiles_n), dim3(256), 0,
+                         a.stream, (const TIn*)a.A, (const TIn*)a.B, (const TIn*)a.bias, (TOut*)a.C, a.M, a.N, a.K,
+                         tiles_m, tiles_n, panel, a.lda, a.ldb, a.ldc, a.scale, (const TOut*)a.residual,
+                         a.out_scale);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((gemm_tile16_kernel<TIn, TOut, EPI, BROW, false>), dim3(tiles_m * tiles_n), dim3(256), 0,
+                     a.stream, (const TIn*)a.A, (const TIn*)a.B, (const TIn*)a.bias, (TOut*)a.C, a.M, a.N, a.K,
+                     tiles_m, tiles_n, panel, a.lda, a.ldb, a.ldc, a.scale, (const TOut*)a.residual, a.out_scale);
   return hipGetLastError();
 }
 

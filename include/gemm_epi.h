@@ -128,9 +128,10 @@ gemm_epi_status gemm_epi_plan(gemm_epi_plan_t* out, int64_t M, int64_t N, int64_
  * (row-major >= N, column-major >= K); ldc between rows of C (>= N), which
  * a residual (gemm_epi_run_ex) shares.  0 keeps the packed value.  The
  * kernel is chosen again: the fast kernels need lda and ldb multiples of 8
- * elements; the decode-shape kernel with a column-major B and the 64 x 64
- * ring tiles take any N and ldc, the other tile kernels need them
- * multiples of 8 (16 for FP8_E4M3 output), else the generic kernel runs.
+ * elements; the decode-shape kernel and the 256 x 256 16x16x32 tiles with
+ * a column-major B, and the 64 x 64 ring tiles, take any N and ldc, the
+ * other tile kernels need them multiples of 8 (16 for FP8_E4M3 output),
+ * else the generic kernel runs.
  * Padding between rows is never written; a fast kernel may read A's or B's
  * padding up to the next multiple of 8 elements of a row, which enters no
  * stored output.  Host only.

@@ -170,6 +170,8 @@ def test_fp8_output_off_16_columns_takes_the_masked_ring(lib):
     (1000, 1000, 1024, "col", "col", "tile", "tile_64x64_ring4"),  # column-major A through transposing reads
     (1001, 1000, 1024, "col", "col", "generic", "generic"),  # packed column-major A: lda = 1001, unaligned
     (1000, 1004, 1024, "row", "col", "tile", "tile_64x64_ring4"),  # N % 8 != 0: last tile column masked
+    (4096, 50257, 4096, "row", "col", "tile", "tile_256x256x64_m16"),  # odd N, packed C: masked 256-wide tiles
+    (4096, 50257, 4096, "row", "row", "generic", "generic"),  # packed row-major B of odd width: unaligned
     (37, 53, 29, "row", "row", "generic", "generic"),
     (256, 256, 100, "col", "row", "generic", "generic"),  # K not a multiple of 8
     (1024, 1024, 1000, "row", "col", "tile", "tile_64x64_ring4"),  # K % 64 = 40: a partial first chunk

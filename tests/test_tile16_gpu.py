@@ -91,3 +91,23 @@ def test_tile16_strided_integer_bitexact(config):
                                              ("bf16", "fp8", "bias", (16, 8, 16), False)):
         name = run_strided(M, N, K, in_dt, out_dt, "row", LB[config], epi, pads, "tile", config, extras)
         assert name == NAMES[config]
+
+
+# N or ldc off the 16-byte output chunks (B column-major): the last tile
+# column stays in place, masked past N, and its edge is read and stored
+# element by element; C carries a sentinel in its padding and in 64 rows
+# past M, and packed rows of odd width are all unaligned
+@pytest.mark.parametrize("M,N,K,ldc_pad", [(512, 300, 256, 0), (300, 777, 200, 0), (256, 1003, 136, 5),
+                                           (264, 520, 264, 4), (256, 264, 192, 3)])
+def test_tile16_ragged_n_bitexact(M, N, K, ldc_pad):
+    for in_dt, out_dt, epi, extras in (("bf16", "bf16", "bias_relu", False), ("f16", "f32", "relu", True),
+                                       ("f16", "f16", "bias", True), ("bf16", "fp8", "bias", True)):
+        assert run_strided(M, N, K, in_dt, out_dt, "row", "col", epi, (8, 16, ldc_pad), "tile", 4, extras,
+                           extra_rows=64) == NAMES[4]
+
+
+def test_tile16_ragged_n_random_tolerance():
+    M, N, K = 512, 777, 1000
+    for in_dt in ("bf16", "f16"):
+        bits = inputs.make_inputs(M, N, K, in_dt, "row", "col", True, float(np.sqrt(K)), 0.1, seed=777)
+        assert check_case(bits, M, N, K, in_dt, in_dt, "row", "col", "bias_gelu", "tile", 4, False) == NAMES[4]
