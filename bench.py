@@ -59,7 +59,9 @@ _FAMILY_SOURCES = {
     "tile": ["common.hpp", "kernels.hpp", "gemm_tile.hpp", "gemm_tile16.hpp", "gemm_ring.hpp", "tile_dispatch.hpp",
              "gemm_tile_bf16_bf16.hip", "gemm_tile_bf16_f32.hip", "gemm_tile_bf16_fp8.hip", "gemm_tile_f16_f16.hip",
              "gemm_tile_f16_f32.hip", "gemm_tile_f16_fp8.hip", "gemm_tile16_rowb_f16.hip",
-             "gemm_tile16_rowb_bf16.hip", "gemm_epi.cpp"],
+             "gemm_tile16_rowb_bf16.hip", "gemm_ring_bf16_bf16.hip", "gemm_ring_bf16_f32.hip",
+             "gemm_ring_bf16_fp8.hip", "gemm_ring_f16_f16.hip", "gemm_ring_f16_f32.hip", "gemm_ring_f16_fp8.hip",
+             "gemm_epi.cpp"],
     "skinny": ["common.hpp", "kernels.hpp", "gemm_skinny.hpp", "gemm_skinny.hip", "gemm_skinny_f16_f16.hip",
                "gemm_skinny_f16_f32.hip", "gemm_skinny_f16_fp8.hip", "gemm_skinny_bf16_bf16.hip",
                "gemm_skinny_bf16_f32.hip", "gemm_skinny_bf16_fp8.hip", "gemm_epi.cpp"],

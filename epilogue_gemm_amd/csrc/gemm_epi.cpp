@@ -121,6 +121,15 @@ LaunchFn tile_launcher(int cfg, const Problem& p) {
     return nullptr;
   }
   const bool f32 = p.out_dt == GEMM_EPI_F32, fp8 = p.out_dt == GEMM_EPI_FP8_E4M3;
+  if (kTile[cfg].ring > 0) {
+    if (p.in_dt == GEMM_EPI_F16)
+      return (fp8 ? ring_launcher_f16_fp8 : f32 ? ring_launcher_f16_f32 : ring_launcher_f16_f16)(cfg, p.la, p.lb,
+                                                                                              p.epi);
+    if (p.in_dt == GEMM_EPI_BF16)
+      return (fp8 ? ring_launcher_bf16_fp8 : f32 ? ring_launcher_bf16_f32 : ring_launcher_bf16_bf16)(cfg, p.la, p.lb,
+                                                                                                  p.epi);
+    return nullptr;
+  }
   if (p.in_dt == GEMM_EPI_F16)
     return (fp8 ? tile_launcher_f16_fp8 : f32 ? tile_launcher_f16_f32 : tile_launcher_f16_f16)(cfg, p.la, p.lb, p.epi);
   if (p.in_dt == GEMM_EPI_BF16)

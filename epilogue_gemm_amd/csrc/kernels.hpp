@@ -47,6 +47,13 @@ LaunchFn tile_launcher_bf16_bf16(int cfg, int la, int lb, int epi);
 LaunchFn tile_launcher_bf16_f32(int cfg, int la, int lb, int epi);
 LaunchFn tile_launcher_f16_fp8(int cfg, int la, int lb, int epi);
 LaunchFn tile_launcher_bf16_fp8(int cfg, int la, int lb, int epi);
+// the ring configurations (5-7), one unit per (input, output) format pair
+LaunchFn ring_launcher_f16_f16(int cfg, int la, int lb, int epi);
+LaunchFn ring_launcher_f16_f32(int cfg, int la, int lb, int epi);
+LaunchFn ring_launcher_f16_fp8(int cfg, int la, int lb, int epi);
+LaunchFn ring_launcher_bf16_bf16(int cfg, int la, int lb, int epi);
+LaunchFn ring_launcher_bf16_f32(int cfg, int la, int lb, int epi);
+LaunchFn ring_launcher_bf16_fp8(int cfg, int la, int lb, int epi);
 // the row-major-B 16x16x32 configuration, one unit per input format
 LaunchFn tile16_rowb_launcher_f16(int out_dt, int la, int lb, int epi);
 LaunchFn tile16_rowb_launcher_bf16(int out_dt, int la, int lb, int epi);
