@@ -222,7 +222,9 @@ def attention_fwd(q, k, v, o, causal=False, stream=None):
         if t.shape != q.shape or t.dtype != q.dtype:
             raise ValueError(f"{name}: shape/dtype differ from q")
     B, S, H, D = q.shape
-    s = (stream or torch.cuda.current_stream()).cuda_stream
+    if _dtype_name(q) not in ("f16", "bf16"):
+        raise ValueError(f"q: dtype {q.dtype}; expected float16 or bfloat16")
+    s = stream.cuda_stream if stream is not None else _current_stream_handle(torch)
     st = gemm_epi_attention_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), B, S, H, D,
                                 _dtype_name(q), causal, s)
     if st != OK:
@@ -275,10 +277,25 @@ def gemm_epi_plan_describe(plan):
 # ---- convenience over torch tensors (device memory + stream only) ----------
 
 _TORCH_DTYPE_NAMES = {"float16": "f16", "bfloat16": "bf16", "float32": "f32", "float8_e4m3fn": "fp8"}
+_NAME_OF_DTYPE = {}  # torch.dtype -> format name (None: not a format of the library), filled on use
 
 
-def _dtype_name(t) -> str:
-    return _TORCH_DTYPE_NAMES[str(t.dtype).replace("torch.", "")]
+def _dtype_name(t):
+    d = t.dtype
+    try:
+        return _NAME_OF_DTYPE[d]
+    except KeyError:
+        n = _NAME_OF_DTYPE[d] = _TORCH_DTYPE_NAMES.get(str(d).replace("torch.", ""))
+        return n
+
+
+def _current_stream_handle(torch) -> int:
+    """hipStream_t of torch's current stream on the current device (the raw
+    handle without building a Stream object, where torch offers it)."""
+    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    if raw is not None:
+        return raw(torch.cuda.current_device())
+    return torch.cuda.current_stream().cuda_stream
 
 
 class Plan:
@@ -310,6 +327,7 @@ class Plan:
                 self.handle = None
                 raise GemmEpiError("gemm_epi_plan_select", st)
         self.kernel, self.config, self.name = gemm_epi_plan_describe(self.handle)
+        self._run = load_library().gemm_epi_run
 
     def _check(self, t, name, dtype, numel):
         if t is None:
@@ -318,8 +336,9 @@ class Plan:
             raise ValueError(f"{name}: expected a contiguous CUDA tensor")
         if _dtype_name(t) != dtype:
             raise ValueError(f"{name}: dtype {t.dtype} does not match {dtype}")
-        if t.numel() < numel or (name not in ("A", "B", "C", "residual") and t.numel() != numel):
-            raise ValueError(f"{name}: {t.numel()} elements, expected {numel}")
+        n = t.numel()
+        if n < numel or (n != numel and name not in ("A", "B", "C", "residual")):
+            raise ValueError(f"{name}: {n} elements, expected {numel}")
         return t.data_ptr()
 
     @property
@@ -341,7 +360,7 @@ class Plan:
         b = self._check(B, "B", self.in_dtype, self._extent["B"])
         bi = self._check(bias, "bias", self.in_dtype, self.N)
         c = self._check(C, "C", self.out_dtype, self._extent["C"])
-        s = (stream or torch.cuda.current_stream()).cuda_stream
+        s = stream.cuda_stream if stream is not None else _current_stream_handle(torch)
         if scale is not None or residual is not None or out_scale is not None:
             sc = self._check(scale, "scale", "f32", self.N)
             r = self._check(residual, "residual", self.out_dtype, self._extent["C"])
@@ -356,7 +375,7 @@ class Plan:
                 raise GemmEpiError("gemm_epi_run_ex", st)
             return
         if workspace is None:
-            st = gemm_epi_run(self.handle, a, b, bi, c, s)
+            st = self._run(self.handle, a, b, bi, c, s)
             fn = "gemm_epi_run"
         else:
             if not workspace.is_cuda or not workspace.is_contiguous():
@@ -378,7 +397,7 @@ class Plan:
         b = self._check(B, "B", self.in_dtype, self._extent["B"])
         bi = self._check(bias, "bias", self.in_dtype, self.N)
         c = self._check(C, "C", self.out_dtype, self._extent["C"])
-        s = (stream or torch.cuda.current_stream()).cuda_stream
+        s = stream.cuda_stream if stream is not None else _current_stream_handle(torch)
         st, us = gemm_epi_tune(self.handle, a, b, bi, c, iters, s, TUNE_COLD if cold else 0)
         if st != OK:
             raise GemmEpiError("gemm_epi_tune", st)
