@@ -106,7 +106,10 @@ __device__ __forceinline__ char* vslot() {
   return s;
 }
 
-template <typename T, bool CAUSAL>
+// RAGS: S not a multiple of 128 -- the last query block reaches past S
+// (its query rows read row S - 1 and are not stored) and the last key block
+// may too (rows past S load as zeros, their scores count as -inf).
+template <typename T, bool CAUSAL, bool RAGS = false>
 __global__ __launch_bounds__(512) void attn_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                                                        const T* __restrict__ V, T* __restrict__ O, int S, int H,
                                                        float scale_log2) {
@@ -136,9 +139,10 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(const T* __restrict__ Q, 
   const int qi = q0 + qg * 32 + il;  // this lane's query
 
   // Q fragments of this lane's query: d = 16 kk + 8 h .. + 7
+  const int qrow = RAGS ? min(qi, S - 1) : qi;
   u32x4 qf[4];
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) qf[kk] = *(const u32x4*)(Q + base + qi * rs + 16 * kk + 8 * h);
+  for (int kk = 0; kk < 4; ++kk) qf[kk] = *(const u32x4*)(Q + base + qrow * rs + 16 * kk + 8 * h);
   // pass them through an empty asm here, so that the wait for these loads
   // is placed before the key loop and not, conservatively, inside it (where
   // it would also wait for the next block's loads)
@@ -165,10 +169,16 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(const T* __restrict__ Q, 
     const uint32_t so = (uint32_t)((int64_t)kb * kBN * rs * 2);
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr)(kslot<j>() + poff + (2 * qg + u) * 1024), 16, kvoff[u],
-                                               so, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr)(vslot<j>() + poff + (2 * qg + u) * 1024), 16, vvoff[u],
-                                               so, 0, 0);
+      uint32_t ko = kvoff[u], vo = vvoff[u];
+      // a key row at or past S: an offset past the buffer's range, which
+      // loads zeros without a memory access (the check covers the
+      // per-lane offset, not the block offset `so`)
+      if constexpr (RAGS)
+        if (kb * kBN + 8 * (2 * qg + u) + (lane >> 3) >= S) ko = vo = 0xFFFFFFF0u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr)(kslot<j>() + poff + (2 * qg + u) * 1024), 16, ko, so, 0,
+                                               0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr)(vslot<j>() + poff + (2 * qg + u) * 1024), 16, vo, so, 0,
+                                               0);
     }
   };
 
@@ -197,7 +207,10 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(const T* __restrict__ Q, 
   float m_run = -__builtin_inff();  // running maximum of the raw scores
   float l_run = 0.0f;               // this half's running sum of exp
 
-  const int nblk = CAUSAL ? (q0 + kBM) / kBN : S / kBN;  // >= 2: each parity has a block
+  // key blocks (>= 2 unless RAGS with S <= 64: parity 1 then has none and
+  // merges m = -inf, l = 0, o = 0)
+  const int nkb = RAGS ? (S + kBN - 1) / kBN : S / kBN;
+  const int nblk = CAUSAL ? (RAGS ? min((q0 + kBM) / kBN, nkb) : (q0 + kBM) / kBN) : nkb;
 
   auto block = [&](int kb, const char* skp, const char* svp) __attribute__((always_inline)) {
     // The block's operand fragments, all in one asm statement that waits
@@ -269,6 +282,19 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(const T* __restrict__ Q, 
             const int q = x >> 2, e = x & 3;
             const int key = kb * kBN + 32 * g + 16 * (q >> 1) + 8 * h + 4 * (q & 1) + e;
             if (key > qi) s[g][x] = -__builtin_inff();
+          }
+      }
+    }
+    // keys at or past S count as -inf
+    if constexpr (RAGS) {
+      if (kb * kBN + kBN > S) {
+#pragma unroll
+        for (int g = 0; g < 2; ++g)
+#pragma unroll
+          for (int x = 0; x < 16; ++x) {
+            const int q = x >> 2, e = x & 3;
+            const int key = kb * kBN + 32 * g + 16 * (q >> 1) + 8 * h + 4 * (q & 1) + e;
+            if (key >= S) s[g][x] = -__builtin_inff();
           }
       }
     }
@@ -420,6 +446,7 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(const T* __restrict__ Q, 
   // 8 q + 4 h .. + 3 of its query
   const float inv = 1.0f / (lh + partner32(lh, h));
   const float c0 = a0 * inv, c1 = a1 * inv;
+  if (RAGS && qi >= S) return;
   T* orow = O + base + qi * rs;
 #pragma unroll
   for (int dt = 0; dt < 2; ++dt) {
@@ -440,8 +467,12 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(const T* __restrict__ Q, 
 template <typename T, bool CAUSAL>
 hipError_t launch(const void* Q, const void* K, const void* V, void* O, int B, int S, int H, hipStream_t stream) {
   const float scale_log2 = (float)(1.4426950408889634 / 8.0);  // log2(e) / sqrt(64)
-  hipLaunchKernelGGL((attn_fwd_kernel<T, CAUSAL>), dim3(S / kBM, H, B), dim3(512), 0, stream, (const T*)Q,
-                     (const T*)K, (const T*)V, (T*)O, S, H, scale_log2);
+  if (S % kBM != 0)
+    hipLaunchKernelGGL((attn_fwd_kernel<T, CAUSAL, true>), dim3((S + kBM - 1) / kBM, H, B), dim3(512), 0, stream,
+                       (const T*)Q, (const T*)K, (const T*)V, (T*)O, S, H, scale_log2);
+  else
+    hipLaunchKernelGGL((attn_fwd_kernel<T, CAUSAL>), dim3(S / kBM, H, B), dim3(512), 0, stream, (const T*)Q,
+                       (const T*)K, (const T*)V, (T*)O, S, H, scale_log2);
   return hipGetLastError();
 }
 
@@ -454,7 +485,7 @@ extern "C" gemm_epi_status gemm_epi_attention_fwd(const void* Q, const void* K, 
   if (!Q || !K || !V || !O || B <= 0 || S <= 0 || H <= 0 || D <= 0) return GEMM_EPI_ERR_INVALID_ARG;
   if (dtype != GEMM_EPI_F16 && dtype != GEMM_EPI_BF16) return GEMM_EPI_ERR_INVALID_ARG;
   const int64_t n = B * S * H * D;
-  if (D != ge::attn::kD || S % ge::attn::kBM != 0 || n >= ((int64_t)1 << 31) || S / ge::attn::kBM > 65535 ||
+  if (D != ge::attn::kD || n >= ((int64_t)1 << 31) || (S + ge::attn::kBM - 1) / ge::attn::kBM > 65535 ||
       H > 65535 || B > 65535)
     return GEMM_EPI_ERR_UNSUPPORTED;
   for (const void* p : {Q, K, V, (const void*)O})

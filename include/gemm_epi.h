@@ -305,14 +305,17 @@ int gemm_epi_tuning_size(void);
  * lets query i see keys j <= i only.  fp32 scores and accumulation, an
  * online softmax over blocks of 64 keys, probabilities carried into the
  * second product as one fp16 value (F16) or as a bf16 value plus its bf16
- * remainder (BF16), O rounded once.  (Scaled dot-product attention
+ * remainder (BF16), O rounded once.  Any S >= 1: with S not a multiple of
+ * 128 the last query block and key block are masked past S (nothing past
+ * row S - 1 of a (b, h) slice is read into a result or written).  (Scaled
+ * dot-product attention
  * and its blocked form with an online softmax: csdn "从零开始学习 TileLang",
  * ch.13 "FlashAttention", sec. 13.1, 13.6-13.8; layout, causal rule and the
  * B, H, S, D = 4, 8, 1024, 64 example: ainew.jp "TileLang で GPU カーネル設計を
  * 解説", section 6.)
  * Errors: INVALID_ARG (a NULL pointer, B/S/H/D <= 0, dtype not F16/BF16),
- * UNSUPPORTED (D != 64, S not a multiple of 128, B*S*H*D >= 2^31, a pointer
- * not 16-byte aligned), HIP (the launch failed). */
+ * UNSUPPORTED (D != 64, more than 65535 blocks of 128 queries, B*S*H*D >=
+ * 2^31, a pointer not 16-byte aligned), HIP (the launch failed). */
 gemm_epi_status gemm_epi_attention_fwd(const void* Q, const void* K, const void* V, void* O, int64_t B, int64_t S,
                                        int64_t H, int64_t D, gemm_epi_dtype dtype, int causal, void* stream);
 

@@ -435,7 +435,8 @@ def test_attention_validates_without_touching_the_device(lib):
     assert gb.gemm_epi_attention_fwd(p, p, p, p, 0, 128, 1, 64, "f16", 0, None) == 1
     assert gb.gemm_epi_attention_fwd(p, p, p, p, 1, 128, 1, 64, "fp8", 0, None) == 1
     assert gb.gemm_epi_attention_fwd(p, p, p, p, 1, 128, 1, 128, "bf16", 1, None) == 2  # D = 128
-    assert gb.gemm_epi_attention_fwd(p, p, p, p, 1, 192, 1, 64, "bf16", 1, None) == 2  # S % 128
+    # more than 65535 query blocks of 128 (any S is taken: the last block masked)
+    assert gb.gemm_epi_attention_fwd(p, p, p, p, 1, 128 * 65535 + 1, 1, 64, "bf16", 1, None) == 2
     assert gb.gemm_epi_attention_fwd(p + 8, p, p, p, 1, 128, 1, 64, "bf16", 1, None) == 2  # alignment
     assert gb.gemm_epi_attention_fwd(p, p, p, p, 1 << 12, 1 << 12, 1 << 4, 64, "bf16", 0, None) == 2  # 2^34 elements
 

@@ -60,6 +60,29 @@ def test_attention_small_full_parity(dtype, causal, B, S, H):
     print(f"attention {dtype} causal={causal} B{B} S{S} H{H}: rel_fro={r['rel_fro']:.2e} max_abs={r['max_abs']:.2e}")
 
 
+# S not a multiple of 128: the last query block reaches past S (those rows
+# are not stored), the last key block is masked past S (its rows there load
+# as zeros); S <= 64 leaves the second key parity without a block.  A guard
+# of NaN past the output tensor must stay untouched.
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("B,S,H", [(1, 1, 1), (2, 50, 3), (1, 64, 1), (1, 77, 2), (2, 130, 1), (3, 200, 2),
+                                   (1, 1000, 2)])
+def test_attention_ragged_s_parity(dtype, causal, B, S, H):
+    D = 64
+    d = inputs.attention_inputs(B, S, H, D, dtype, seed=S + 7 * H)
+    q, k, v = (parity.to_device(d[n], dtype).view(B, S, H, D) for n in ("Q", "K", "V"))
+    n, guard = B * S * H * D, 4096
+    o_all = torch.full((n + guard,), float("nan"), dtype=q.dtype, device="cuda")
+    gb.attention_fwd(q, k, v, o_all[:n].view(B, S, H, D), causal=causal)
+    torch.cuda.synchronize()
+    bits = parity.out_bits(o_all)
+    assert np.all(bits[n:] == bits[n + guard - 1]), "output written past the tensor"
+    y, o = oracle.attention(d["Q"], d["K"], d["V"], B, S, H, D, dtype, causal)
+    r = check(bits[:n].reshape(B, S, H, D), y, o, dtype, f"B{B} S{S} H{H} {dtype} causal={causal}")
+    print(f"attention ragged {dtype} causal={causal} B{B} S{S} H{H}: rel_fro={r['rel_fro']:.2e}")
+
+
 @pytest.mark.parametrize("name", list(inputs.ATTENTION_WORKLOADS))
 def test_attention_workload_sampled_rows(name):
     w = inputs.ATTENTION_WORKLOADS[name]
@@ -105,7 +128,7 @@ def test_attention_rejects_unsupported():
     p = t.data_ptr()
     st = torch.cuda.current_stream().cuda_stream
     assert gb.gemm_epi_attention_fwd(p, p, p, p, B, S, H, 32, "f16", 0, st) == 2  # D != 64
-    assert gb.gemm_epi_attention_fwd(p, p, p, p, B, 100, H, 64, "f16", 0, st) == 2  # S % 128
+    assert gb.gemm_epi_attention_fwd(p, p, p, p, B, 128 * 65535 + 1, H, 64, "f16", 0, st) == 2  # query blocks
     assert gb.gemm_epi_attention_fwd(p + 2, p, p, p, B, S, H, 64, "f16", 0, st) == 2  # unaligned
     assert gb.gemm_epi_attention_fwd(None, p, p, p, B, S, H, 64, "f16", 0, st) == 1
     assert gb.gemm_epi_attention_fwd(p, p, p, p, B, S, H, 64, "f32", 0, st) == 1
