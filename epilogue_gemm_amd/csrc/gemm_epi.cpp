@@ -160,7 +160,8 @@ void ge::set_last_hip_error(int code) { g_last_hip_error = code; }
 
 gemm_epi_status ge::check_run_args(gemm_epi_plan_t plan, const void* A, const void* B, const void* bias,
                                    const void* C) {
-  if (!plan || !A || !B || !C) return GEMM_EPI_ERR_INVALID_ARG;
+  // with K = 0 A and B are never read (and may be NULL)
+  if (!plan || !C || (plan->p.K > 0 && (!A || !B))) return GEMM_EPI_ERR_INVALID_ARG;
   const bool need_bias = plan->p.epi == GEMM_EPI_BIAS_RELU || plan->p.epi == GEMM_EPI_BIAS_GELU ||
                          plan->p.epi == GEMM_EPI_BIAS || plan->p.epi == GEMM_EPI_BIAS_SILU;
   if (need_bias != (bias != nullptr)) return GEMM_EPI_ERR_INVALID_ARG;
@@ -186,6 +187,13 @@ bool uses_bias(int epi) {
 // family cannot run it.
 bool resolve(gemm_epi_plan_s* pl, int kernel, int config) {
   const ge::Problem& p = pl->p;
+  // K = 0 (C = act(bias) with the extras): the generic kernel only -- the
+  // fast families stream K in 16-byte chunks
+  if (p.K == 0 && kernel != GEMM_EPI_KERNEL_GENERIC) {
+    if (kernel != GEMM_EPI_KERNEL_AUTO) return false;
+    kernel = GEMM_EPI_KERNEL_GENERIC;
+    config = 0;
+  }
   if (kernel == GEMM_EPI_KERNEL_AUTO) {
     // a measured choice for this exact problem comes first
     int tk, tc;
@@ -308,7 +316,7 @@ extern "C" {
 gemm_epi_status gemm_epi_plan(gemm_epi_plan_t* out, int64_t M, int64_t N, int64_t K, gemm_epi_dtype in_dtype,
                               gemm_epi_dtype out_dtype, gemm_epi_layout layout_a, gemm_epi_layout layout_b,
                               gemm_epi_epilogue epilogue) {
-  if (!out || M <= 0 || N <= 0 || K <= 0) return GEMM_EPI_ERR_INVALID_ARG;
+  if (!out || M <= 0 || N <= 0 || K < 0) return GEMM_EPI_ERR_INVALID_ARG;
   if (!valid_enum_args(in_dtype, out_dtype, layout_a, layout_b, epilogue)) return GEMM_EPI_ERR_INVALID_ARG;
   const int64_t lim = (int64_t)1 << 31;
   if (M >= lim || N >= lim || K >= lim || M * K >= lim || K * N >= lim || M * N >= lim)
@@ -355,7 +363,8 @@ gemm_epi_status gemm_epi_run_ex(gemm_epi_plan_t plan, const void* A, const void*
 
 gemm_epi_status gemm_epi_tune(gemm_epi_plan_t plan, const void* A, const void* B, const void* bias, void* C,
                               int iters, int flags, void* stream, float* best_us) {
-  if (!plan || !A || !B || !C || iters <= 0 || (flags & ~GEMM_EPI_TUNE_COLD)) return GEMM_EPI_ERR_INVALID_ARG;
+  if (!plan || !C || (plan->p.K > 0 && (!A || !B)) || iters <= 0 || (flags & ~GEMM_EPI_TUNE_COLD))
+    return GEMM_EPI_ERR_INVALID_ARG;
   if (uses_bias(plan->p.epi) != (bias != nullptr)) return GEMM_EPI_ERR_INVALID_ARG;
   if (!aligned16(A) || !aligned16(B) || !aligned16(C) || (bias && !aligned16(bias))) return GEMM_EPI_ERR_INVALID_ARG;
   // candidates: every configuration of the fast families that can run the

@@ -113,7 +113,10 @@ typedef struct gemm_epi_plan_s* gemm_epi_plan_t;
  * small host plan object only.  *out is written only on GEMM_EPI_OK.
  * The kernel is the tuning table's entry for this problem when there is one
  * that can run it (gemm_epi_tune), else the static rule.
- * Errors: INVALID_ARG (out == NULL, M/N/K <= 0, unknown enum, out_dtype
+ * K = 0 is the degenerate product: the sum over k is empty, so C =
+ * act(bias) with the optional scale, residual and output scale applied to
+ * zero products; it runs on the generic kernel, and A and B may be NULL.
+ * Errors: INVALID_ARG (out == NULL, M or N <= 0, K < 0, unknown enum, out_dtype
  * not allowed), UNSUPPORTED (any of M*K, K*N, M*N >= 2^31 elements),
  * NO_MEMORY. */
 gemm_epi_status gemm_epi_plan(gemm_epi_plan_t* out, int64_t M, int64_t N, int64_t K, gemm_epi_dtype in_dtype,
@@ -149,7 +152,8 @@ gemm_epi_status gemm_epi_plan_set_ld(gemm_epi_plan_t plan, int64_t lda, int64_t 
  *
  * A, B, bias, C are device pointers owned by the caller, who keeps them
  * alive until the stream has passed the kernel.  bias must be non-NULL
- * exactly when the epilogue uses it.  C must not overlap A, B or bias.
+ * exactly when the epilogue uses it (A and B may be NULL when K = 0).
+ * C must not overlap A, B or bias.
  * A plan is immutable during run, so concurrent runs of one plan on
  * different streams are safe.  Pointers that are not 16-byte aligned send
  * the call to the generic kernel.

@@ -238,8 +238,9 @@ static double* make_table(int fmt) {
   return t;
 }
 
+/* K = 0 is allowed: the sum over k is empty (0) and A and B may be NULL. */
 static int check_args(int64_t M, int64_t N, int64_t K, int in_fmt, int out_fmt, int la, int lb, int epi) {
-  if (M <= 0 || N <= 0 || K <= 0) return -1;
+  if (M <= 0 || N <= 0 || K < 0) return -1;
   if (in_fmt != ORC_F16 && in_fmt != ORC_BF16) return -1;
   if (out_fmt != in_fmt && out_fmt != ORC_F32 && out_fmt != ORC_FP8) return -1;
   if ((la != ORC_ROW && la != ORC_COL) || (lb != ORC_ROW && lb != ORC_COL)) return -1;
@@ -283,7 +284,7 @@ int oracle_gemm_epi_ex(int64_t M, int64_t N, int64_t K, int in_fmt, int out_fmt,
                        const void* A, const void* B, const void* bias, const uint32_t* scale, const void* residual,
                        const uint32_t* out_scale, double* y_out, void* c_out, int nthreads) {
   if (check_args(M, N, K, in_fmt, out_fmt, la, lb, epi)) return -1;
-  if (!A || !B || (epi_has_bias(epi) && !bias)) return -1;
+  if ((K > 0 && (!A || !B)) || (epi_has_bias(epi) && !bias)) return -1;
   if (residual && out_fmt == ORC_FP8) return -1;
   const extras_t ex = {scale, residual, out_scale, out_fmt};
   double* tab = make_table(in_fmt);
@@ -317,7 +318,7 @@ int oracle_gemm_epi_points_ex(int64_t M, int64_t N, int64_t K, int in_fmt, int o
                               const void* residual, const uint32_t* out_scale, int64_t count, const int64_t* rows,
                               const int64_t* cols, double* y_out, uint32_t* bits_out, int nthreads) {
   if (check_args(M, N, K, in_fmt, out_fmt, la, lb, epi)) return -1;
-  if (!A || !B || (epi_has_bias(epi) && !bias) || count < 0 || (count && (!rows || !cols))) return -1;
+  if ((K > 0 && (!A || !B)) || (epi_has_bias(epi) && !bias) || count < 0 || (count && (!rows || !cols))) return -1;
   if (residual && out_fmt == ORC_FP8) return -1;
   for (int64_t p = 0; p < count; ++p)
     if (rows[p] < 0 || rows[p] >= M || cols[p] < 0 || cols[p] >= N) return -1;

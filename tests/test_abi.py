@@ -58,7 +58,7 @@ def test_status_strings(lib):
 def test_plan_rejects_invalid_arguments(lib):
     ok = dict(M=64, N=64, K=64, in_dtype="f16", out_dtype="f16", layout_a="row", layout_b="row", epilogue="none")
     assert gb.gemm_epi_plan_status(**ok) == 0
-    for k, v in [("M", 0), ("N", -1), ("K", 0)]:
+    for k, v in [("M", 0), ("N", -1), ("K", -1)]:
         assert gb.gemm_epi_plan_status(**{**ok, k: v}) == 1
     assert gb.gemm_epi_plan_status(**{**ok, "in_dtype": "f32", "out_dtype": "f32"}) == 1  # f32 input
     assert gb.gemm_epi_plan_status(**{**ok, "out_dtype": "bf16"}) == 1  # mixed 16-bit formats
@@ -71,6 +71,26 @@ def test_plan_rejects_invalid_arguments(lib):
         assert gb.gemm_epi_plan_status(64, 64, 64, *args, raw=True) == 1
     # null out pointer
     assert lib.gemm_epi_plan(None, 64, 64, 64, 0, 0, 0, 0, 0) == 1
+
+
+def test_k_zero_is_the_degenerate_product_on_the_generic_kernel(lib):
+    # K = 0: C = act(bias) (+ extras) from an empty sum; only the generic
+    # kernel takes it, and A and B may be NULL
+    for la, lb, epi in (("row", "col", "bias_gelu"), ("col", "row", "none"), ("row", "row", "bias")):
+        h = gb.gemm_epi_plan(32, 8192, 0, "bf16", "bf16", la, lb, epi)
+        try:
+            assert gb.gemm_epi_plan_describe(h)[0] == "generic"
+            assert gb.gemm_epi_workspace_size(h) == 0
+            for fam in ("tile", "skinny"):
+                assert gb.gemm_epi_plan_select(h, fam, 0) == 2
+                assert gb.gemm_epi_plan_select(h, fam, -1) == 2
+            assert gb.gemm_epi_plan_select(h, "auto", -1) == 0
+            assert gb.gemm_epi_plan_describe(h)[0] == "generic"
+            bias = 0x1000 if epi.startswith("bias") else None
+            assert gb.gemm_epi_run(h, None, None, bias, None, None) == 1  # C is still required
+            assert gb.gemm_epi_run(h, None, None, None if bias else 0x1000, 0x1000, None) == 1  # bias rule
+        finally:
+            gb.gemm_epi_destroy(h)
 
 
 def test_plan_rejects_oversized(lib):

@@ -193,3 +193,47 @@ def test_generic_launch_beyond_2_30_columns():
     _, want = oracle.gemm_epi(parity.out_bits(A), bsel, None, 1, cols.size, 1, "bf16", "bf16", "row", "row", "none")
     assert np.array_equal(got, want.reshape(-1).astype(np.uint16))
     del B, C
+
+
+# K = 0, the degenerate product: the sum over k is empty, so C is the
+# epilogue of zero -- act(bias), with the optional scale, residual and output
+# scale -- on the generic kernel, with A and B passed as NULL.  Integer bias
+# values keep the exact epilogues bit for bit; GELU and SiLU within the
+# tolerance.
+@pytest.mark.parametrize("in_dt,out_dt", [("bf16", "bf16"), ("f16", "f32"), ("f16", "f16"), ("bf16", "fp8")])
+@pytest.mark.parametrize("la,lb", [("row", "col"), ("col", "row")])
+def test_k_zero_is_the_epilogue_of_an_empty_sum(in_dt, out_dt, la, lb):
+    M, N = 37, 200
+    empty = np.zeros(0, np.uint16)
+    for epi in ("none", "relu", "silu", "bias", "bias_relu", "bias_gelu", "bias_silu"):
+        bits = inputs.integer_inputs(M, N, 8, in_dt, la, lb, epi.startswith("bias"), seed=len(epi))
+        bias = bits["bias"]
+        plan = gb.Plan(M, N, 0, in_dt, out_dt, la, lb, epi)
+        assert plan.name == "generic"
+        C = parity.empty_out(M * N, out_dt)
+        C.fill_(float("nan"))
+        plan.run(None, None, parity.to_device(bias, in_dt) if bias is not None else None, C)
+        torch.cuda.synchronize()
+        plan.close()
+        got = parity.out_bits(C)
+        y, c = oracle.gemm_epi(empty, empty, bias, M, N, 0, in_dt, out_dt, la, lb, epi)
+        if epi in ("none", "relu", "bias", "bias_relu"):
+            assert np.array_equal(got.reshape(-1), c.reshape(-1).astype(got.dtype)), epi
+        else:
+            r = parity.compare(got.reshape(-1), c.reshape(-1), y.reshape(-1), out_dt)
+            assert r["ok"], f"{epi}: {r}"
+    if out_dt in ("bf16", "f32"):
+        # with the extras: act(s * 0 + bias) + r, times q
+        bits = inputs.integer_inputs(M, N, 8, in_dt, la, lb, True, seed=11)
+        ex = inputs.extras_inputs(M, N, out_dt, seed=11, integer=True)
+        plan = gb.Plan(M, N, 0, in_dt, out_dt, la, lb, "bias_relu")
+        C = parity.empty_out(M * N, out_dt)
+        q = torch.tensor([0.5], dtype=torch.float32, device="cuda")
+        plan.run(None, None, parity.to_device(bits["bias"], in_dt), C, scale=torch.from_numpy(ex["scale"]).cuda(),
+                 residual=parity.to_device_out(ex["residual"], out_dt), out_scale=q)
+        torch.cuda.synchronize()
+        plan.close()
+        got = parity.out_bits(C)
+        y, c = oracle.gemm_epi(empty, empty, bits["bias"], M, N, 0, in_dt, out_dt, la, lb, "bias_relu",
+                               scale=ex["scale"], residual=ex["residual"], out_scale=0.5)
+        assert np.array_equal(got.reshape(-1), c.reshape(-1).astype(got.dtype))

@@ -375,6 +375,36 @@ def test_rejects_bad_arguments():
         oracle.gemm_epi(A, A, None, 2, 3, 2, "f16", "f16", "row", "row", "none")  # size mismatch
 
 
+# K = 0: the sum over k is empty, so the product is zero and the output is the
+# epilogue of zero -- act(bias), scaled zero, the residual added, the output
+# scale applied -- for every layout (A and B are empty arrays).
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+def test_k_zero_is_the_epilogue_of_an_empty_sum(fmt):
+    M, N = 3, 11
+    e = np.zeros(0, np.uint16)
+    vals = np.array([-3.0, -1.0, -0.5, 0.0, 0.25, 0.5, 1.0, 2.0, 3.0, 6.0, -6.0])
+    bias = oracle.encode_array(fmt, vals).astype(np.uint16)
+    bd = np.array([oracle.decode(fmt, int(b)) for b in bias])
+    t = torch.from_numpy(bd)
+    want = {"none": np.zeros(N), "relu": np.zeros(N), "silu": np.zeros(N), "bias": bd,
+            "bias_relu": np.maximum(bd, 0.0),
+            "bias_gelu": torch.nn.functional.gelu(t, approximate="tanh").numpy(),
+            "bias_silu": torch.nn.functional.silu(t).numpy()}
+    for la, lb in (("row", "col"), ("col", "row")):
+        for epi, w in want.items():
+            y, c = oracle.gemm_epi(e, e, bias if epi.startswith("bias") else None, M, N, 0, fmt, "f32", la, lb, epi)
+            # (the page constants of GELU agree with the tanh form to ~4e-12)
+            assert np.allclose(y, np.broadcast_to(w, (M, N)), rtol=1e-9, atol=1e-12), (la, lb, epi)
+            if epi in ("none", "relu", "bias", "bias_relu"):
+                assert np.array_equal(y, np.broadcast_to(w, (M, N)))
+    # with the extras: act(s * 0 + bias) + r, times q
+    scale = np.full(N, 7.0, np.float32)
+    res = np.arange(M * N, dtype=np.float32)
+    y, _ = oracle.gemm_epi(e, e, bias, M, N, 0, fmt, "f32", "row", "col", "bias_relu", scale=scale, residual=res,
+                           out_scale=0.5)
+    assert np.array_equal(y, 0.5 * (np.maximum(bd, 0.0)[None, :] + np.arange(M * N).reshape(M, N)))
+
+
 # --------------------------------------------------------------------------
 # further epilogues: SiLU, per-column scale, residual
 # --------------------------------------------------------------------------
