@@ -345,6 +345,36 @@ def test_generic_integer_bitexact(M, N, K, la, lb):
             check_case(bits, M, N, K, in_dt, out_dt, la, lb, epi, "generic", 0, epi in BITWISE_EPIS)
 
 
+# The generic kernel's tiling: 64 x 64 outputs per workgroup, K through LDS
+# 16 at a time (the last step stopping at K), so shapes straddling those
+# steps and tiles, and every layout, keep the bits of a per-output loop.
+@pytest.mark.parametrize("M,N,K", [(64, 64, 16), (129, 63, 17), (130, 200, 15), (200, 130, 33), (70, 300, 1001)])
+@pytest.mark.parametrize("la,lb", [("row", "col"), ("col", "row")])
+def test_generic_tiles_and_k_steps_bitexact(M, N, K, la, lb):
+    for in_dt, out_dt, epi in (("bf16", "bf16", "bias_relu"), ("f16", "f32", "none"), ("f16", "fp8", "bias")):
+        bits = inputs.integer_inputs(M, N, K, in_dt, la, lb, epi.startswith("bias"), seed=M + N + K)
+        assert check_case(bits, M, N, K, in_dt, out_dt, la, lb, epi, "generic", 0, True) == "generic"
+
+
+def test_generic_random_tolerance_large_odd_k():
+    M, N, K = 300, 520, 1001
+    for la, lb in (("row", "col"), ("col", "col")):
+        bits = inputs.make_inputs(M, N, K, "bf16", la, lb, True, float(np.sqrt(K)), 0.1, seed=K)
+        got, name = run_gpu(bits, M, N, K, "bf16", "bf16", la, lb, "bias_gelu")
+        assert name == "generic"  # K % 8 != 0: the fast kernels do not apply
+        y, c = oracle_full(bits, M, N, K, "bf16", "bf16", la, lb, "bias_gelu")
+        r = parity.compare(got, c, y, "bf16")
+        assert r["ok"], r
+
+
+# More than 65535 row tiles of 64: the grid's y extent stops at 65535 and
+# each workgroup loops over the row tiles past it.
+def test_generic_rows_past_the_grid_y_extent():
+    M, N, K = 64 * 65535 + 100, 3, 8
+    bits = inputs.integer_inputs(M, N, K, "bf16", "row", "col", True, seed=5)
+    assert check_case(bits, M, N, K, "bf16", "bf16", "row", "col", "bias_relu", "generic", 0, True) == "generic"
+
+
 # ---------------------------------------------------------------------------
 # random operands: tolerance
 # ---------------------------------------------------------------------------
