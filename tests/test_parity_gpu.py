@@ -490,3 +490,38 @@ def test_workload_full_size(name):
         r = parity.compare(got[rows, cols], c, y, w.out_dtype)
     print(f"[workload] {w.name} kernel={kname} {r}", flush=True)
     assert r["ok"], r
+
+
+# The same workloads, shapes and automatic plans on integer operands, where
+# every fp32 sum is exact: the whole output against the oracle, bit for bit
+# for the exact epilogues; for 8192^3 the first and the last band of 256
+# rows (a tile row each, both edges of the raster) in full, and bias+GELU
+# under the tolerance rule.
+@pytest.mark.parametrize("name", list(inputs.WORKLOADS))
+def test_workload_integer_outputs(name):
+    w = inputs.WORKLOADS[name]
+    bits = inputs.integer_inputs(w.M, w.N, w.K, w.in_dtype, w.layout_a, w.layout_b, w.epilogue.startswith("bias"),
+                                 seed=w.seed + 1)
+    print(f"[workload-int] {w.name}", flush=True)
+    got, kname = run_gpu(bits, w.M, w.N, w.K, w.in_dtype, w.out_dtype, w.layout_a, w.layout_b, w.epilogue)
+    got = got.reshape(w.M, w.N)
+    assert kname != "generic"
+    exact = w.epilogue in BITWISE_EPIS
+    if w.M * w.N * w.K <= 2**37:
+        y, c = oracle_full(bits, w.M, w.N, w.K, w.in_dtype, w.out_dtype, w.layout_a, w.layout_b, w.epilogue)
+        got_s, c, y = got.reshape(-1), c.reshape(-1), y.reshape(-1)
+    else:
+        band = np.concatenate([np.arange(256), np.arange(w.M - 256, w.M)])
+        rows = np.repeat(band, w.N)
+        cols = np.tile(np.arange(w.N), band.size)
+        y, c = oracle.gemm_epi_points(bits["A"], bits["B"], bits["bias"], w.M, w.N, w.K, w.in_dtype, w.out_dtype,
+                                      w.layout_a, w.layout_b, w.epilogue, rows, cols)
+        got_s = got[rows, cols]
+    c = c.astype(got_s.dtype)
+    if exact:
+        mism = np.count_nonzero(got_s != c)
+        assert mism == 0, f"{w.name} {kname}: {mism} of {got_s.size} outputs differ"
+    else:
+        r = parity.compare(got_s, c, y, w.out_dtype)
+        assert r["ok"], r
+    print(f"[workload-int] {w.name} kernel={kname} {got_s.size} outputs", flush=True)
