@@ -117,6 +117,35 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
 // groups of four columns and 16-byte chunks that reach past n_lim, or lie
 // on a row that is not 16-byte aligned, are read and stored element by
 // element.
+// Four consecutive outputs of the output format as stored (raw bits), and
+// their fp32 values.
+template <typename T>
+struct Raw4 {
+  using type = u32x2;  // 16-bit formats
+};
+template <>
+struct Raw4<float> {
+  using type = f32x4;
+};
+template <>
+struct Raw4<fp8e4m3> {
+  using type = uint32_t;
+};
+template <typename T>
+__device__ __forceinline__ f32x4 raw4_to_f32(typename Raw4<T>::type w) {
+  if constexpr (sizeof(T) == 1) {
+    return f32x4{__builtin_amdgcn_cvt_f32_fp8((int)w, 0), __builtin_amdgcn_cvt_f32_fp8((int)w, 1),
+                 __builtin_amdgcn_cvt_f32_fp8((int)w, 2), __builtin_amdgcn_cvt_f32_fp8((int)w, 3)};
+  } else if constexpr (sizeof(T) == 4) {
+    return w;
+  } else {
+    return f32x4{to_f32(__builtin_bit_cast(T, (uint16_t)(w.x & 0xffffu))),
+                 to_f32(__builtin_bit_cast(T, (uint16_t)(w.x >> 16))),
+                 to_f32(__builtin_bit_cast(T, (uint16_t)(w.y & 0xffffu))),
+                 to_f32(__builtin_bit_cast(T, (uint16_t)(w.y >> 16)))};
+  }
+}
+
 template <int WM, int WN, typename TIn, typename TOut, int EPI, bool EXTRAS, bool RAGC = false>
 __device__ __forceinline__ void write_tile16(const f32x4 (&acc)[WM / 16][WN / 16], const TIn* __restrict__ bias,
                                             TOut* __restrict__ C, int ldc, int m_w, int n_w, int lane, char* stage,
@@ -152,8 +181,31 @@ __device__ __forceinline__ void write_tile16(const f32x4 (&acc)[WM / 16][WN / 16
     }
   }
 
+  // The extras on aligned columns: the column scale once, and each band's
+  // residual (raw bits) loaded while the band before it is worked on, so
+  // that no band waits on its own loads.
+  constexpr bool PIPE = EXTRAS && !RAGC;
+  using RawT = typename Raw4<TOut>::type;
+  f32x4 scq[PIPE ? TN : 1];
+  RawT rq[2][PIPE ? TN : 1];
+  if constexpr (PIPE) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int col = n_w + j * 16 + 4 * g;
+      scq[j] = scale ? *(const f32x4*)(scale + col) : f32x4{1.0f, 1.0f, 1.0f, 1.0f};
+      if (res) rq[0][j] = *(const RawT*)(res + (int64_t)(m_w + m_l) * ldc + col);
+    }
+  }
+
   static_for<TM>([&](auto i_c) __attribute__((always_inline)) {
     constexpr int i = decltype(i_c)::value;
+    if constexpr (PIPE && i + 1 < TM) {
+      if (res) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          rq[(i + 1) & 1][j] = *(const RawT*)(res + (int64_t)(m_w + (i + 1) * 16 + m_l) * ldc + n_w + j * 16 + 4 * g);
+      }
+    }
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       const int col = n_w + j * 16 + 4 * g;
@@ -174,8 +226,8 @@ __device__ __forceinline__ void write_tile16(const f32x4 (&acc)[WM / 16][WN / 16
               if (res && !rvec) r[e] = out_to_f32(res[at + e]);
             }
         } else {
-          if (scale) sc = *(const f32x4*)(scale + col);
-          if (res) r = load4<TOut>(res + (int64_t)(m_w + i * 16 + m_l) * ldc + col);
+          sc = scq[j];
+          if (res) r = raw4_to_f32<TOut>(rq[i & 1][j]);
         }
       }
       float v[4];
